@@ -1,0 +1,170 @@
+/*
+ * msda.h — C ABI of the multi-scale deformable attention (MSDeformAttn) core
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operation ("Deformable DETR: Deformable Transformers for End-to-End
+ * Object Detection" paper notes, phdsky.com, "Core insights / Insight 2",
+ * the MSDeformAttn equation; tensor semantics from the xdnf.cn "Deformable DETR
+ * model walkthrough", "encoder" section):
+ *
+ *   out[b,q,m*D+d] = sum_{l<L} sum_{k<K} A[b,q,m,l,k] *
+ *                    bilinear(value[b, level l, :, :, m, d], loc[b,q,m,l,k,:])
+ *
+ * with bilinear sampling in the align_corners=False pixel convention (a
+ * normalised coordinate u maps to the pixel coordinate u*W_l - 0.5), zero
+ * padding outside the map, and A normalised over the L*K samples of one query
+ * and head.
+ *
+ * Conventions shared by every entry point:
+ *  - Tensors are dense, row-major, batch-first, and live in DEVICE memory,
+ *    except spatial_shapes and level_start_index, which are HOST arrays
+ *    (the launch configuration needs them; reading device copies would force a
+ *    device-to-host sync).
+ *  - value is [B, S, M, D] with S = sum_l H_l*W_l; level l occupies rows
+ *    level_start_index[l] .. +H_l*W_l, row-major (y, x) inside a level.
+ *  - Locations are (x, y): x along the width. spatial_shapes is (H, W).
+ *  - The caller (PyTorch) allocates and owns all memory; the library allocates
+ *    nothing and keeps no state between calls. All entry points are reentrant.
+ *  - Every call validates its arguments on the host BEFORE any device work, so
+ *    an error never leaves partial output. On success the work is enqueued on
+ *    `stream` (a hipStream_t; NULL = the default stream) and the call returns
+ *    without synchronising; faults surface at the caller's next sync.
+ *  - Non-finite or far-outside sampling locations contribute zero and receive
+ *    zero gradients.
+ *  - batch == 0 or num_query == 0 is an empty call: it succeeds and touches
+ *    no tensor (NULL is accepted for the empty ones), except that
+ *    msda_backward with num_query == 0 and batch > 0 still zero-fills
+ *    grad_value (no contributions).
+ *  - Return value: MSDA_OK (0) or a negative msda_status; msda_last_error()
+ *    gives a human-readable detail for the calling thread's last failure.
+ */
+#ifndef MSDA_H
+#define MSDA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__) || defined(__clang__)
+#define MSDA_API __attribute__((visibility("default")))
+#else
+#define MSDA_API
+#endif
+
+#define MSDA_ABI_VERSION 1
+#define MSDA_MAX_LEVELS 16
+
+typedef enum {
+    MSDA_OK = 0,
+    MSDA_E_NULL = -1,        /* a required pointer is NULL                                */
+    MSDA_E_DIM = -2,         /* a size is negative, zero where it must not be, or too
+                                large for 32-bit indexing                                 */
+    MSDA_E_SHAPE = -3,       /* sum_l H_l*W_l != num_value, or encoder refs with Nq != S  */
+    MSDA_E_LEVEL_INDEX = -4, /* level_start_index is not the exclusive prefix sum         */
+    MSDA_E_UNSUPPORTED = -5, /* dtype, level count or flags outside what is compiled      */
+    MSDA_E_ALIGN = -6,       /* a device pointer is not aligned to its element size       */
+    MSDA_E_HIP = -7          /* the HIP runtime reported an error at launch               */
+} msda_status;
+
+typedef enum {
+    MSDA_F32 = 0,  /* IEEE binary32                                       */
+    MSDA_BF16 = 1  /* bfloat16 (value only; arithmetic is still fp32)     */
+} msda_dtype;
+
+/* Sizes of one call. */
+typedef struct {
+    int32_t batch;                      /* B                                           */
+    int32_t heads;                      /* M                                           */
+    int32_t channels;                   /* D, channels per head                        */
+    int32_t levels;                     /* L, 1..MSDA_MAX_LEVELS                       */
+    int32_t points;                     /* K, sampling points per head and level       */
+    int64_t num_value;                  /* S = sum_l H_l*W_l                           */
+    int64_t num_query;                  /* Nq                                          */
+    const int64_t *spatial_shapes;      /* HOST [L][2] = (H_l, W_l)                    */
+    const int64_t *level_start_index;   /* HOST [L], exclusive prefix sum of H_l*W_l   */
+} msda_shape;
+
+/* Flag for msda_backward: add into grad_value instead of overwriting it. */
+#define MSDA_BWD_ACCUMULATE 1u
+
+/* Host helper: level_start_index as the exclusive prefix sum of H_l*W_l
+ * (walkthrough page, "transformer" section: the start of each level in the
+ * flattened sequence). Writes lsi_out[L] and *num_value_out = S. No device
+ * work. */
+MSDA_API int msda_level_start_index(int32_t levels, const int64_t *spatial_shapes,
+                           int64_t *lsi_out, int64_t *num_value_out);
+
+/* Reference points, [B, Nq, L, 2] fp32 (x, y).
+ *  Encoder mode (query_ref == NULL; requires num_query == num_value): query q
+ *  is pixel (i, j) of level lq, q = level_start_index[lq] + i*W_lq + j, and
+ *    ref[b,q,l] = ((j+0.5)/(vr[b,lq,x]*W_lq) * vr[b,l,x],
+ *                  (i+0.5)/(vr[b,lq,y]*H_lq) * vr[b,l,y])
+ *  (juhe.plus debug-build notes, "Key point 1: get_reference_points"; the
+ *  walkthrough page's "encoder" section).
+ *  Decoder mode (query_ref = u [B, Nq, 2]): ref[b,q,l] = u[b,q] * vr[b,l]
+ *  (the notes' "decoder data flow"; the walkthrough page's "Decoder").
+ *  valid_ratios: [B, L, 2] fp32, (x = width ratio, y = height ratio), or NULL
+ *  for all ones (no padding masks). ref_out is fully overwritten. */
+MSDA_API int msda_reference_points(const msda_shape *shape, const float *valid_ratios,
+                          const float *query_ref, float *ref_out, void *stream);
+
+/* Sampling locations from 2-d reference points (walkthrough page, "encoder";
+ * paper notes, "Key code"): offsets are in pixels of level l and are
+ * normalised by (W_l, H_l):
+ *   loc[b,q,m,l,k,:] = ref[b,q,l,:] + offset_px[b,q,m,l,k,:] / (W_l, H_l)
+ * ref [B,Nq,L,2], offset_px and loc_out [B,Nq,M,L,K,2], all fp32. */
+MSDA_API int msda_sampling_locations(const msda_shape *shape, const float *ref,
+                            const float *offset_px, float *loc_out, void *stream);
+
+/* Attention weights: softmax of logits [B,Nq,M,L*K] over the L*K samples of
+ * each (b, q, m), so that they sum to 1 over all levels and points (paper
+ * notes, "Insight 2"). weights_out [B,Nq,M,L,K] fp32; may alias logits. */
+MSDA_API int msda_attention_softmax(const msda_shape *shape, const float *logits,
+                           float *weights_out, void *stream);
+
+/* Forward of the core (the bracketed sum of the MSDeformAttn equation).
+ *  value              [B,S,M,D]        fp32 or bf16 (value_dtype), 4-byte
+ *                                      (fp32) / 2-byte (bf16) aligned
+ *  sampling_locations [B,Nq,M,L,K,2]   fp32, normalised (x, y)
+ *  attention_weights  [B,Nq,M,L,K]     fp32
+ *  output             [B,Nq,M*D]       fp32, fully overwritten (m-major)
+ * Accumulation is fp32 for both value dtypes. */
+MSDA_API int msda_forward(const msda_shape *shape, const void *value, msda_dtype value_dtype,
+                 const float *sampling_locations, const float *attention_weights,
+                 float *output, void *stream);
+
+/* Backward of the core: the exact derivative of msda_forward given
+ * grad_output [B,Nq,M*D] fp32 (the op is trained end to end through autograd:
+ * walkthrough page, "encoder"; paper notes, "Key code").
+ *  grad_value              [B,S,M,D]      fp32 (also for bf16 value); zeroed on
+ *                                         the stream first unless flags has
+ *                                         MSDA_BWD_ACCUMULATE. Accumulated with
+ *                                         device atomics, so the summation
+ *                                         order (and the last bits) may differ
+ *                                         between runs.
+ *  grad_sampling_locations [B,Nq,M,L,K,2] fp32, fully overwritten
+ *  grad_attention_weights  [B,Nq,M,L,K]   fp32, fully overwritten
+ * At an integer pixel coordinate the location gradient is the right
+ * derivative (the cell [floor(x), floor(x)+1] is used). */
+MSDA_API int msda_backward(const msda_shape *shape, const void *value, msda_dtype value_dtype,
+                  const float *sampling_locations, const float *attention_weights,
+                  const float *grad_output, float *grad_value,
+                  float *grad_sampling_locations, float *grad_attention_weights,
+                  unsigned flags, void *stream);
+
+/* Static English name of a status code. */
+MSDA_API const char *msda_status_string(int status);
+
+/* Detail text for the calling thread's most recent failed call ("" if none). */
+MSDA_API const char *msda_last_error(void);
+
+/* MSDA_ABI_VERSION of the built library. */
+MSDA_API int msda_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSDA_H */

@@ -1,0 +1,21 @@
+"""Multi-scale deformable attention (MSDeformAttn) core for AMD MI355X (gfx950).
+
+The computation runs in the hand-written HIP kernels of ``libmsda.so`` behind
+the C ABI in ``include/msda.h``; this package only marshals torch tensors into
+that ABI. Entry points (same names as the C ABI):
+
+    msda_reference_points, msda_sampling_locations, msda_attention_softmax,
+    msda_forward, msda_backward
+
+plus ``MSDeformAttnFunction`` (autograd over forward/backward) and
+``ms_deform_attn`` (location formation + softmax + core in one call).
+"""
+from ._binding import (MSDAError, declared_symbols, level_start_index_host, load, msda_attention_softmax,
+                       msda_backward, msda_forward, msda_reference_points, msda_sampling_locations)
+from .autograd import MSDeformAttnFunction, ms_deform_attn
+
+__all__ = [
+    "MSDAError", "MSDeformAttnFunction", "declared_symbols", "level_start_index_host", "load",
+    "ms_deform_attn", "msda_attention_softmax", "msda_backward", "msda_forward", "msda_reference_points",
+    "msda_sampling_locations",
+]

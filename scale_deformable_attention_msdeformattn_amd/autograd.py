@@ -1,0 +1,37 @@
+"""torch.autograd wrapper over the HIP core (allocation and calls only).
+
+``MSDeformAttnFunction.apply(value, spatial_shapes, level_start_index,
+sampling_locations, attention_weights)`` keeps the argument order of the core
+op on the walkthrough page ("encoder" section), minus its batch-chunk knob,
+which these kernels do not need.
+"""
+import torch
+
+from . import _binding as B
+
+
+class MSDeformAttnFunction(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, value, spatial_shapes, level_start_index, sampling_locations, attention_weights):
+        out = B.msda_forward(value, spatial_shapes, level_start_index, sampling_locations, attention_weights)
+        ctx.save_for_backward(value, sampling_locations, attention_weights)
+        ctx.shapes = spatial_shapes
+        ctx.lsi = level_start_index
+        return out
+
+    @staticmethod
+    def backward(ctx, grad_output):
+        value, loc, attn = ctx.saved_tensors
+        gv, gl, ga = B.msda_backward(value, ctx.shapes, ctx.lsi, loc, attn, grad_output.contiguous())
+        if value.dtype != torch.float32:
+            gv = gv.to(value.dtype)
+        return gv, None, None, gl, ga
+
+
+def ms_deform_attn(value, spatial_shapes, reference_points, offsets_px, logits, points):
+    """Location formation + L*K softmax + core forward, all in the HIP library
+    (no autograd through the first two steps)."""
+    loc = B.msda_sampling_locations(spatial_shapes, reference_points, offsets_px)
+    attn = B.msda_attention_softmax(spatial_shapes, logits, points)
+    lsi, _ = B.level_start_index_host(spatial_shapes)
+    return B.msda_forward(value, spatial_shapes, lsi, loc, attn)

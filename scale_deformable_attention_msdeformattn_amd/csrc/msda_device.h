@@ -1,0 +1,103 @@
+// Device-side helpers for the gfx950 kernels of libmsda.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msda {
+
+constexpr int kWave = 64;
+
+// Buffer resource over [base, base + bytes). Buffer loads whose byte offset is
+// at or beyond `bytes` return 0 and buffer atomics there are dropped; the
+// kernels use that hardware range check to implement zero padding.
+// Word 3 selects 32-bit raw data, as for every CDNA raw buffer access.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// An offset that is out of range for every resource the kernels build
+// (each covers fewer than 2^31 bytes).
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+__device__ __forceinline__ float4 load_f32x4(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// Four bf16 values (8 bytes) widened exactly to fp32.
+__device__ __forceinline__ float4 load_bf16x4(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    const auto u = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    const uint32_t lo = u[0], hi = u[1];
+    float4 f;
+    f.x = __uint_as_float(lo << 16);
+    f.y = __uint_as_float(lo & 0xffff0000u);
+    f.z = __uint_as_float(hi << 16);
+    f.w = __uint_as_float(hi & 0xffff0000u);
+    return f;
+}
+
+template <typename VT> struct ValueTraits;
+template <> struct ValueTraits<float> {
+    static constexpr int kBytes = 4;
+    __device__ static float4 load4(__amdgpu_buffer_rsrc_t r, uint32_t off) { return load_f32x4(r, off); }
+};
+template <> struct ValueTraits<uint16_t> {  // bf16 bit patterns
+    static constexpr int kBytes = 2;
+    __device__ static float4 load4(__amdgpu_buffer_rsrc_t r, uint32_t off) { return load_bf16x4(r, off); }
+};
+
+// One axis of a bilinear sample in the align_corners=False convention:
+// the continuous pixel coordinate is x = u*n - 0.5; returns the cell start
+// c = floor(x) (as float) and the fraction f = x - c in [0, 1].
+//
+// x is formed with one fma, and then the fraction is re-formed exactly with a
+// second fma around the candidate cell (u*n is exact in the fma, and so is
+// c + 0.5), so floor(x) is decided on the exact value of u*n - 0.5 — the same
+// decision an exact (fp64) evaluation makes — and f carries an absolute error
+// below 2^-24 instead of one ulp of x.
+__device__ __forceinline__ void cell_1d(float u, float n, float &c, float &f)
+{
+    const float x = __builtin_fmaf(u, n, -0.5f);
+    c = __builtin_floorf(x);
+    f = __builtin_fmaf(u, n, -(c + 0.5f));
+    const bool below = f < 0.0f;  // x rounded up onto the next integer
+    c = below ? c - 1.0f : c;
+    f = below ? f + 1.0f : f;
+}
+
+// Whether a sample can touch the map at all. Non-finite and far-outside
+// locations are rejected here, before any conversion to integer.
+__device__ __forceinline__ bool sample_in_range(float u, float v, float Wf, float Hf)
+{
+    const float x = __builtin_fmaf(u, Wf, -0.5f);
+    const float y = __builtin_fmaf(v, Hf, -0.5f);
+    return (x > -2.0f) & (x < Wf + 1.0f) & (y > -2.0f) & (y < Hf + 1.0f);
+}
+
+// Sum over the lanes of aligned groups of N lanes (N a power of two <= 64);
+// every lane of a group ends with the group's sum.
+template <int N> __device__ __forceinline__ float group_sum(float v)
+{
+#pragma unroll
+    for (int o = 1; o < N; o <<= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+// Map a workgroup id to a logical tile so that each of the 8 XCDs (which
+// receive workgroups round-robin and have private L2 caches) processes one
+// contiguous range of tiles. `n` is the grid size and must be a multiple of 8
+// (the map is then a permutation of [0, n)); tiles at or beyond the real tile
+// count are skipped by the caller.
+__device__ __forceinline__ uint32_t xcd_tile(uint32_t bid, uint32_t n)
+{
+    const uint32_t per = n / 8u;
+    return (bid % 8u) * per + bid / 8u;
+}
+
+__host__ __device__ constexpr uint32_t round_up8(uint32_t n) { return (n + 7u) & ~7u; }
+
+}  // namespace msda

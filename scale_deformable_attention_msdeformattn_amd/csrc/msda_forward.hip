@@ -1,0 +1,240 @@
+// Forward of the MSDeformAttn core on gfx950.
+//
+//   out[b,q,m*D+d] = sum_{l,k} A[b,q,m,l,k] * bilinear(value_l[b,:,:,m,d], loc[b,q,m,l,k])
+//
+// (paper notes, phdsky.com, "Insight 2", the bracketed sum of the MSDeformAttn
+// equation; bilinear sampling with zero padding and align_corners=False from
+// the xdnf.cn walkthrough's "encoder" section.)
+//
+// Fast path, C = M*D = 256 channels (the pages' d_model): one wavefront per
+// query (b, q), all heads at once; lane t owns channels 4t..4t+3, so the 64
+// lanes cover one 1 KB (fp32) / 512 B (bf16) value row and every gather is a
+// 16 B (8 B) vector load per lane.
+//  phase 1: the M*L*K samples of the query are spread over the lanes (one
+//           sample per lane per pass); each lane forms the cell, the four
+//           corner byte offsets (out-of-range offset for corners off the map)
+//           and the four weights A*w_c, and parks them in LDS. This math runs
+//           once per sample, not once per channel lane.
+//  phase 2: a wave-uniform loop over (l, k); lanes read their head's record
+//           from LDS (a broadcast to the lanes of one head), gather the four
+//           corners with bounds-checked buffer loads (off-map corners read 0)
+//           and accumulate in fp32.
+// Generic path (any M, D): one thread per output element.
+#include "msda_device.h"
+#include "msda_internal.h"
+
+namespace msda {
+namespace {
+
+constexpr int kWaves = 4;               // waves per workgroup (queries per workgroup)
+constexpr int kBlock = kWaves * kWave;  // 256 threads
+
+struct LevelRec {  // one level, as read by lane-varying level index from LDS
+    float Wf, Hf;
+    int32_t W, start;
+};
+
+template <typename VT, int M, int L, int K>
+__global__ void __launch_bounds__(kBlock)
+forward_c256_kernel(Geometry g, const VT *__restrict__ value, const float2 *__restrict__ loc,
+                    const float *__restrict__ attn, float4 *__restrict__ out, uint32_t grid)
+{
+    constexpr int C = 256;
+    constexpr int D = C / M;
+    constexpr int LPH = D / 4;               // lanes per head
+    constexpr int LK = L * K;
+    constexpr int NS = M * LK;               // samples per query
+    constexpr uint32_t RB = C * sizeof(VT);  // bytes per value row (one pixel, all heads)
+    static_assert(D % 4 == 0 && LPH >= 1 && LPH <= kWave, "C=256 path needs 4 | D");
+
+    __shared__ LevelRec s_lv[L];
+    __shared__ int4 s_off[kWaves][NS];
+    __shared__ float4 s_w[kWaves][NS];
+
+    const int lane = threadIdx.x % kWave;
+    // wave-uniform by construction; readfirstlane lets the compiler keep the
+    // per-wave query, batch and buffer descriptor in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    if (threadIdx.x < L) {
+        const int l = threadIdx.x;
+        s_lv[l] = LevelRec{(float)g.lv.W[l], (float)g.lv.H[l], g.lv.W[l], g.lv.start[l]};
+    }
+    __syncthreads();
+
+    const int64_t nq_total = (int64_t)g.B * g.Nq;
+    const int64_t gq = (int64_t)xcd_tile(blockIdx.x, grid) * kWaves + wave;
+    const bool active = gq < nq_total;
+
+    // ---- phase 1: per-sample geometry, one sample per lane per pass ----
+    if (active) {
+#pragma unroll
+        for (int s0 = 0; s0 < NS; s0 += kWave) {
+            const int s = s0 + lane;
+            if (NS % kWave == 0 || s < NS) {
+                const int l = (s / K) % L;
+                const LevelRec lv = s_lv[l];
+                float2 u = loc[gq * NS + s];
+                const float a = attn[gq * NS + s];
+                const bool in = sample_in_range(u.x, u.y, lv.Wf, lv.Hf);
+                u.x = in ? u.x : 0.0f;
+                u.y = in ? u.y : 0.0f;
+                float cx, fx, cy, fy;
+                cell_1d(u.x, lv.Wf, cx, fx);
+                cell_1d(u.y, lv.Hf, cy, fy);
+                const bool x0ok = (cx >= 0.0f) & (cx < lv.Wf);
+                const bool x1ok = (cx >= -1.0f) & (cx + 1.0f < lv.Wf);
+                const bool y0ok = in & (cy >= 0.0f) & (cy < lv.Hf);
+                const bool y1ok = in & (cy >= -1.0f) & (cy + 1.0f < lv.Hf);
+                const int row = lv.start + (int)cy * lv.W + (int)cx;
+                const uint32_t o00 = (uint32_t)row * RB;
+                const uint32_t o10 = o00 + (uint32_t)lv.W * RB;
+                int4 o;
+                o.x = (int)((y0ok & x0ok) ? o00 : kOutOfRange);
+                o.y = (int)((y0ok & x1ok) ? o00 + RB : kOutOfRange);
+                o.z = (int)((y1ok & x0ok) ? o10 : kOutOfRange);
+                o.w = (int)((y1ok & x1ok) ? o10 + RB : kOutOfRange);
+                const float wy0 = a * (1.0f - fy), wy1 = a * fy;
+                s_off[wave][s] = o;
+                s_w[wave][s] = make_float4(wy0 * (1.0f - fx), wy0 * fx, wy1 * (1.0f - fx), wy1 * fx);
+            }
+        }
+    }
+    __syncthreads();
+    if (!active) return;
+
+    // ---- phase 2: gather + blend + reduce, wave-uniform (l, k) loop ----
+    const int b = (int)(gq / g.Nq);
+    const __amdgpu_buffer_rsrc_t rsrc =
+        make_rsrc(value + (int64_t)b * g.S * C, (uint32_t)g.S * RB);
+    const uint32_t lane_off = (uint32_t)lane * 4u * sizeof(VT);
+    const int m = lane / LPH;
+    const int4 *offs = &s_off[wave][m * LK];
+    const float4 *ws = &s_w[wave][m * LK];
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int i = 0; i < LK; ++i) {
+        const int4 o = offs[i];
+        const float4 w = ws[i];
+        const float4 v00 = ValueTraits<VT>::load4(rsrc, (uint32_t)o.x + lane_off);
+        const float4 v01 = ValueTraits<VT>::load4(rsrc, (uint32_t)o.y + lane_off);
+        const float4 v10 = ValueTraits<VT>::load4(rsrc, (uint32_t)o.z + lane_off);
+        const float4 v11 = ValueTraits<VT>::load4(rsrc, (uint32_t)o.w + lane_off);
+        acc.x = __builtin_fmaf(w.x, v00.x, acc.x);
+        acc.y = __builtin_fmaf(w.x, v00.y, acc.y);
+        acc.z = __builtin_fmaf(w.x, v00.z, acc.z);
+        acc.w = __builtin_fmaf(w.x, v00.w, acc.w);
+        acc.x = __builtin_fmaf(w.y, v01.x, acc.x);
+        acc.y = __builtin_fmaf(w.y, v01.y, acc.y);
+        acc.z = __builtin_fmaf(w.y, v01.z, acc.z);
+        acc.w = __builtin_fmaf(w.y, v01.w, acc.w);
+        acc.x = __builtin_fmaf(w.z, v10.x, acc.x);
+        acc.y = __builtin_fmaf(w.z, v10.y, acc.y);
+        acc.z = __builtin_fmaf(w.z, v10.z, acc.z);
+        acc.w = __builtin_fmaf(w.z, v10.w, acc.w);
+        acc.x = __builtin_fmaf(w.w, v11.x, acc.x);
+        acc.y = __builtin_fmaf(w.w, v11.y, acc.y);
+        acc.z = __builtin_fmaf(w.w, v11.z, acc.z);
+        acc.w = __builtin_fmaf(w.w, v11.w, acc.w);
+    }
+    out[gq * (C / 4) + lane] = acc;
+}
+
+// Generic path: one thread per output element (b, q, m, d).
+template <typename VT>
+__device__ __forceinline__ float load_scalar(const VT *p);
+template <> __device__ __forceinline__ float load_scalar<float>(const float *p) { return *p; }
+template <> __device__ __forceinline__ float load_scalar<uint16_t>(const uint16_t *p)
+{
+    return __uint_as_float((uint32_t)*p << 16);
+}
+
+template <typename VT>
+__global__ void __launch_bounds__(256)
+forward_generic_kernel(Geometry g, const VT *__restrict__ value, const float2 *__restrict__ loc,
+                       const float *__restrict__ attn, float *__restrict__ out)
+{
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int C = g.M * g.D;
+    if (t >= (int64_t)g.B * g.Nq * C) return;
+    const int64_t bq = t / C;
+    const int c = (int)(t - bq * C);
+    const int m = c / g.D;
+    const int b = (int)(bq / g.Nq);
+    const VT *vb = value + (int64_t)b * g.S * C + c;
+    float acc = 0.0f;
+    for (int l = 0; l < g.L; ++l) {
+        const int W = g.lv.W[l], H = g.lv.H[l];
+        const float Wf = (float)W, Hf = (float)H;
+        for (int k = 0; k < g.K; ++k) {
+            const int64_t s = ((bq * g.M + m) * g.L + l) * g.K + k;
+            const float2 u = loc[s];
+            const float a = attn[s];
+            if (!sample_in_range(u.x, u.y, Wf, Hf)) continue;
+            float cx, fx, cy, fy;
+            cell_1d(u.x, Wf, cx, fx);
+            cell_1d(u.y, Hf, cy, fy);
+            const int x0 = (int)cx, y0 = (int)cy;
+#pragma unroll
+            for (int dy = 0; dy < 2; ++dy)
+#pragma unroll
+                for (int dx = 0; dx < 2; ++dx) {
+                    const int xi = x0 + dx, yi = y0 + dy;
+                    if (xi < 0 || xi >= W || yi < 0 || yi >= H) continue;
+                    const float w = (dx ? fx : 1.0f - fx) * (dy ? fy : 1.0f - fy);
+                    const int64_t row = g.lv.start[l] + (int64_t)yi * W + xi;
+                    acc = __builtin_fmaf(a * w, load_scalar<VT>(vb + row * C), acc);
+                }
+        }
+    }
+    out[t] = acc;
+}
+
+template <typename VT, int M, int L, int K>
+hipError_t launch_c256(const Geometry &g, const void *value, const float *loc, const float *attn,
+                       float *out, hipStream_t st)
+{
+    const uint32_t tiles = (uint32_t)((g.queries() + kWaves - 1) / kWaves);
+    const uint32_t grid = round_up8(tiles);
+    hipLaunchKernelGGL((forward_c256_kernel<VT, M, L, K>), dim3(grid), dim3(kBlock), 0, st, g,
+                       static_cast<const VT *>(value), reinterpret_cast<const float2 *>(loc), attn,
+                       reinterpret_cast<float4 *>(out), grid);
+    return hipGetLastError();
+}
+
+template <typename VT>
+hipError_t launch_typed(const Geometry &g, const void *value, const float *loc, const float *attn,
+                        float *out, hipStream_t st)
+{
+    const bool c256 = g.M * g.D == 256 && (reinterpret_cast<uintptr_t>(value) % (4 * sizeof(VT))) == 0 &&
+                      (reinterpret_cast<uintptr_t>(out) % 16) == 0;
+    if (c256 && g.L == 4 && g.K == 4) {
+        switch (g.M) {
+        case 8: return launch_c256<VT, 8, 4, 4>(g, value, loc, attn, out, st);
+        case 4: return launch_c256<VT, 4, 4, 4>(g, value, loc, attn, out, st);
+        case 16: return launch_c256<VT, 16, 4, 4>(g, value, loc, attn, out, st);
+        default: break;
+        }
+    }
+    if (c256 && g.M == 8) {
+        if (g.L == 1 && g.K == 4) return launch_c256<VT, 8, 1, 4>(g, value, loc, attn, out, st);
+        if (g.L == 4 && g.K == 8) return launch_c256<VT, 8, 4, 8>(g, value, loc, attn, out, st);
+        if (g.L == 3 && g.K == 4) return launch_c256<VT, 8, 3, 4>(g, value, loc, attn, out, st);
+        if (g.L == 4 && g.K == 1) return launch_c256<VT, 8, 4, 1>(g, value, loc, attn, out, st);
+    }
+    const int64_t n = g.queries() * g.M * g.D;
+    hipLaunchKernelGGL((forward_generic_kernel<VT>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                       g, static_cast<const VT *>(value), reinterpret_cast<const float2 *>(loc), attn,
+                       out);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_forward(const Geometry &g, const void *value, msda_dtype vt, const float *loc,
+                          const float *attn, float *out, hipStream_t st)
+{
+    if (vt == MSDA_BF16) return launch_typed<uint16_t>(g, value, loc, attn, out, st);
+    return launch_typed<float>(g, value, loc, attn, out, st);
+}
+
+}  // namespace msda

@@ -1,0 +1,175 @@
+"""The C-ABI boundary on the CPU: the library loads, exports every entry point
+include/msda.h declares, and rejects bad arguments on the host with the
+documented status code before any device work. No compute call is made (no
+GPU here); every call below fails validation."""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+from scale_deformable_attention_msdeformattn_amd import _binding as B
+from tests.conftest import golden
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from scale_deformable_attention_msdeformattn_amd import build
+        build.build()
+    return B.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = B.declared_symbols()
+    assert set(declared) >= {"msda_reference_points", "msda_forward", "msda_backward",
+                             "msda_sampling_locations", "msda_attention_softmax", "msda_status_string"}
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    for name in declared:
+        assert name in exported, name
+        assert hasattr(lib, name)
+    # nothing else leaks out under the msda_ prefix
+    assert {n for n in exported if n.startswith("msda_")} == set(declared)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.msda_abi_version() == 1
+    assert lib.msda_status_string(0) == b"ok"
+    for code in range(-7, 0):
+        assert lib.msda_status_string(code) not in (b"", b"unknown status")
+    assert lib.msda_status_string(-99) == b"unknown status"
+
+
+def test_level_start_index_helper_on_page1_pyramid(lib):
+    g = golden("pyramid_76x106.json")
+    lsi, S = B.level_start_index_host(g["spatial_shapes"])
+    assert lsi == g["level_start_index"] and S == g["S"]
+
+
+def _shape(B_=2, M=8, D=32, K=4, shapes=((76, 106), (38, 53), (19, 27), (8, 13)), S=None, Nq=None, lsi=None):
+    S_true = sum(h * w for h, w in shapes)
+    if lsi is None:  # exclusive prefix sum, written out so that invalid shapes reach the library
+        lsi = [sum(h * w for h, w in shapes[:i]) for i in range(len(shapes))]
+    sh = B.Shape(shapes, B_, M, D, K, Nq if Nq is not None else S_true, lsi)
+    sh.c.num_value = S_true if S is None else S
+    return sh
+
+
+FAKE = ctypes.c_void_p(0x10000)        # never dereferenced: every call below fails validation first
+MISALIGNED = ctypes.c_void_p(0x10002)
+
+# The fake device pointers above must never reach a kernel; these tests are for
+# a host without a GPU, where even a validation slip could not launch anything.
+cpu_only = pytest.mark.skipif(__import__("torch").cuda.is_available(),
+                              reason="fake-pointer validation tests run on a host without a GPU")
+
+
+def _fwd(lib, sh, value=FAKE, dtype=B.MSDA_F32, loc=FAKE, attn=FAKE, out=FAKE):
+    return lib.msda_forward(sh.ptr if sh is not None else None, value, dtype, loc, attn, out, None)
+
+
+def _bwd(lib, sh, flags=0, value=FAKE, grads=(FAKE, FAKE, FAKE, FAKE)):
+    return lib.msda_backward(sh.ptr, value, B.MSDA_F32, FAKE, FAKE, grads[0], grads[1], grads[2], grads[3],
+                             flags, None)
+
+
+@cpu_only
+def test_null_arguments(lib):
+    assert _fwd(lib, None) == B.MSDA_E_NULL
+    for kw in ("value", "loc", "attn", "out"):
+        assert _fwd(lib, _shape(), **{kw: None}) == B.MSDA_E_NULL, kw
+    sh = _shape()
+    sh.c.spatial_shapes = None
+    assert _fwd(lib, sh) == B.MSDA_E_NULL
+    for i in range(4):
+        grads = [FAKE] * 4
+        grads[i] = None
+        assert _bwd(lib, _shape(), grads=tuple(grads)) == B.MSDA_E_NULL
+    assert lib.msda_reference_points(_shape().ptr, None, None, None, None) == B.MSDA_E_NULL
+    assert lib.msda_sampling_locations(_shape().ptr, FAKE, None, FAKE, None) == B.MSDA_E_NULL
+    assert lib.msda_attention_softmax(_shape().ptr, None, FAKE, None) == B.MSDA_E_NULL
+    assert b"NULL" in lib.msda_last_error()
+
+
+@cpu_only
+def test_bad_dimensions(lib):
+    for field in ("heads", "channels", "points"):
+        sh = _shape()
+        setattr(sh.c, field, 0)
+        assert _fwd(lib, sh) == B.MSDA_E_DIM, field
+    sh = _shape()
+    sh.c.num_query = -1
+    assert _fwd(lib, sh) == B.MSDA_E_DIM
+    sh = _shape()
+    sh.c.batch = -2
+    assert _fwd(lib, sh) == B.MSDA_E_DIM
+    assert _fwd(lib, _shape(shapes=((0, 5), (2, 2)))) == B.MSDA_E_DIM
+    # index width: one batch of value at 2^29 elements or more is refused
+    big = _shape(B_=1, M=8, D=32, shapes=((2048, 1024),))
+    assert _fwd(lib, big) == B.MSDA_E_DIM
+    many = _shape(B_=1 << 12, M=8, D=32, shapes=((256, 256),))
+    assert _fwd(lib, many) == B.MSDA_E_DIM
+
+
+@cpu_only
+def test_shape_and_level_index_mismatch(lib):
+    assert _fwd(lib, _shape(S=10686)) == B.MSDA_E_SHAPE
+    assert _fwd(lib, _shape(lsi=[0, 8056, 10070, 10584])) == B.MSDA_E_LEVEL_INDEX
+    assert _fwd(lib, _shape(lsi=[0, 2014, 2527, 2631])) == B.MSDA_E_LEVEL_INDEX
+    # encoder reference points need Nq == S
+    sh = _shape(Nq=300)
+    assert lib.msda_reference_points(sh.ptr, None, None, FAKE, None) == B.MSDA_E_SHAPE
+
+
+@cpu_only
+def test_unsupported(lib):
+    assert _fwd(lib, _shape(), dtype=7) == B.MSDA_E_UNSUPPORTED
+    many_levels = tuple((2, 2) for _ in range(17))
+    assert _fwd(lib, _shape(shapes=many_levels)) == B.MSDA_E_UNSUPPORTED
+    assert _bwd(lib, _shape(), flags=2) == B.MSDA_E_UNSUPPORTED
+
+
+@cpu_only
+def test_misaligned(lib):
+    assert _fwd(lib, _shape(), value=MISALIGNED) == B.MSDA_E_ALIGN
+    assert _fwd(lib, _shape(), loc=ctypes.c_void_p(0x10004)) == B.MSDA_E_ALIGN
+    assert _fwd(lib, _shape(), out=ctypes.c_void_p(0x10001)) == B.MSDA_E_ALIGN
+    assert _bwd(lib, _shape(), grads=(FAKE, MISALIGNED, FAKE, FAKE)) == B.MSDA_E_ALIGN
+    assert lib.msda_sampling_locations(_shape().ptr, ctypes.c_void_p(0x10004), FAKE, FAKE, None) == B.MSDA_E_ALIGN
+    # bf16 value only needs 2-byte alignment, but an odd address is refused
+    assert _fwd(lib, _shape(), value=ctypes.c_void_p(0x10001), dtype=B.MSDA_BF16) == B.MSDA_E_ALIGN
+
+
+def test_python_binding_refuses_cpu_tensors_and_wrong_dtypes():
+    import torch
+    v = torch.zeros(1, 80, 2, 4)
+    loc = torch.zeros(1, 80, 2, 2, 2, 2)
+    a = torch.zeros(1, 80, 2, 2, 2)
+    with pytest.raises(ValueError, match="GPU"):
+        B.msda_forward(v, [[8, 8], [4, 4]], [0, 64], loc, a)
+    with pytest.raises(ValueError, match="float32 or bfloat16"):
+        B.msda_forward(v.double(), [[8, 8], [4, 4]], [0, 64], loc, a)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(RuntimeError, match="libmsda.so not found"):
+        B.load()
+
+
+@cpu_only
+def test_empty_batch_or_queries_is_a_no_op(lib):
+    """B = 0 or Nq = 0: nothing to compute; the call succeeds without touching
+    any pointer (NULL tensors are accepted for empty extents)."""
+    for field in ("batch", "num_query"):
+        sh = _shape()
+        setattr(sh.c, field, 0)
+        assert _fwd(lib, sh, value=None, loc=None, attn=None, out=None) == B.MSDA_OK, field
+        assert lib.msda_sampling_locations(sh.ptr, None, None, None, None) == B.MSDA_OK
+        assert lib.msda_attention_softmax(sh.ptr, None, None, None) == B.MSDA_OK
+    sh = _shape()
+    sh.c.batch = 0
+    assert _bwd(lib, sh, grads=(None, None, None, None)) == B.MSDA_OK
