@@ -41,6 +41,7 @@
 #ifndef MSDA_H
 #define MSDA_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -53,7 +54,7 @@ extern "C" {
 #define MSDA_API
 #endif
 
-#define MSDA_ABI_VERSION 1
+#define MSDA_ABI_VERSION 2
 #define MSDA_MAX_LEVELS 16
 
 typedef enum {
@@ -65,7 +66,8 @@ typedef enum {
     MSDA_E_LEVEL_INDEX = -4, /* level_start_index is not the exclusive prefix sum         */
     MSDA_E_UNSUPPORTED = -5, /* dtype, level count or flags outside what is compiled      */
     MSDA_E_ALIGN = -6,       /* a device pointer is not aligned to its element size       */
-    MSDA_E_HIP = -7          /* the HIP runtime reported an error at launch               */
+    MSDA_E_HIP = -7,         /* the HIP runtime reported an error at launch               */
+    MSDA_E_WORKSPACE = -8    /* msda_backward's workspace is NULL or smaller than needed  */
 } msda_status;
 
 typedef enum {
@@ -135,24 +137,33 @@ MSDA_API int msda_forward(const msda_shape *shape, const void *value, msda_dtype
                  const float *sampling_locations, const float *attention_weights,
                  float *output, void *stream);
 
+/* Bytes of device workspace msda_backward needs for these sizes (0 when the
+ * sizes have no tiled fast path; the call then needs none). Host only. */
+MSDA_API int msda_backward_workspace_size(const msda_shape *shape, size_t *bytes);
+
 /* Backward of the core: the exact derivative of msda_forward given
  * grad_output [B,Nq,M*D] fp32 (the op is trained end to end through autograd:
  * walkthrough page, "encoder"; paper notes, "Key code").
- *  grad_value              [B,S,M,D]      fp32 (also for bf16 value); zeroed on
- *                                         the stream first unless flags has
- *                                         MSDA_BWD_ACCUMULATE. Accumulated with
- *                                         device atomics, so the summation
- *                                         order (and the last bits) may differ
- *                                         between runs.
+ *  grad_value              [B,S,M,D]      fp32 (also for bf16 value); fully
+ *                                         overwritten, or added into when flags
+ *                                         has MSDA_BWD_ACCUMULATE
  *  grad_sampling_locations [B,Nq,M,L,K,2] fp32, fully overwritten
  *  grad_attention_weights  [B,Nq,M,L,K]   fp32, fully overwritten
+ *  workspace               device scratch of at least
+ *                          msda_backward_workspace_size() bytes, 256-byte
+ *                          aligned, owned by the caller; its contents on entry
+ *                          do not matter and are clobbered. Calls that overlap
+ *                          in time must use different workspaces.
  * At an integer pixel coordinate the location gradient is the right
- * derivative (the cell [floor(x), floor(x)+1] is used). */
+ * derivative (the cell [floor(x), floor(x)+1] is used).
+ * grad_value is accumulated without float atomics on the tiled fast path
+ * (value and gradient rows 16-byte aligned, M*D == 256 and compiled (L, K));
+ * other sizes use float atomics, whose summation order varies run to run. */
 MSDA_API int msda_backward(const msda_shape *shape, const void *value, msda_dtype value_dtype,
                   const float *sampling_locations, const float *attention_weights,
                   const float *grad_output, float *grad_value,
                   float *grad_sampling_locations, float *grad_attention_weights,
-                  unsigned flags, void *stream);
+                  void *workspace, size_t workspace_bytes, unsigned flags, void *stream);
 
 /* Static English name of a status code. */
 MSDA_API const char *msda_status_string(int status);

@@ -25,6 +25,7 @@ MSDA_E_LEVEL_INDEX = -4
 MSDA_E_UNSUPPORTED = -5
 MSDA_E_ALIGN = -6
 MSDA_E_HIP = -7
+MSDA_E_WORKSPACE = -8
 MSDA_F32 = 0
 MSDA_BF16 = 1
 MSDA_BWD_ACCUMULATE = 1
@@ -90,8 +91,11 @@ def load():
     lib.msda_attention_softmax.argtypes = [_shp, _vp, _vp, _vp]
     lib.msda_forward.restype = ctypes.c_int
     lib.msda_forward.argtypes = [_shp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp]
+    lib.msda_backward_workspace_size.restype = ctypes.c_int
+    lib.msda_backward_workspace_size.argtypes = [_shp, ctypes.POINTER(ctypes.c_size_t)]
     lib.msda_backward.restype = ctypes.c_int
-    lib.msda_backward.argtypes = [_shp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_uint, _vp]
+    lib.msda_backward.argtypes = [_shp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+                                  ctypes.c_uint, _vp]
     _lib = lib
     return lib
 
@@ -284,9 +288,18 @@ def msda_backward(value: torch.Tensor, spatial_shapes, level_start_index, sampli
         flags = MSDA_BWD_ACCUMULATE
     gl = torch.empty_like(loc)
     ga = torch.empty_like(attn)
+    nbytes = msda_backward_workspace_size(sh)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=value.device)
     _check(load().msda_backward(sh.ptr, _p(value), vt, _p(loc), _p(attn), _p(go), _p(grad_value), _p(gl),
-                                _p(ga), flags, _stream(go)), "msda_backward")
+                                _p(ga), _p(ws), nbytes, flags, _stream(go)), "msda_backward")
     return grad_value, gl, ga
+
+
+def msda_backward_workspace_size(shape: "Shape") -> int:
+    """Bytes of device workspace msda_backward needs for these sizes."""
+    n = ctypes.c_size_t()
+    _check(load().msda_backward_workspace_size(shape.ptr, ctypes.byref(n)), "msda_backward_workspace_size")
+    return int(n.value)
 
 
 def raw_call(name: str, *args):

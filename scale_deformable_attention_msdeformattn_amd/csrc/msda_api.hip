@@ -115,6 +115,7 @@ const char *msda_status_string(int status)
     case MSDA_E_UNSUPPORTED: return "unsupported";
     case MSDA_E_ALIGN: return "misaligned pointer";
     case MSDA_E_HIP: return "HIP runtime error";
+    case MSDA_E_WORKSPACE: return "workspace missing or too small";
     default: return "unknown status";
     }
 }
@@ -198,17 +199,27 @@ int msda_forward(const msda_shape *shape, const void *value, msda_dtype value_dt
                     "forward");
 }
 
+int msda_backward_workspace_size(const msda_shape *shape, size_t *bytes)
+{
+    msda::Geometry g;
+    if (!bytes) return fail(MSDA_E_NULL, "bytes is NULL");
+    if (int st = make_geometry(shape, g)) return st;
+    *bytes = (g.B == 0 || g.Nq == 0) ? 0 : msda::backward_workspace_bytes(g);
+    return ok();
+}
+
 int msda_backward(const msda_shape *shape, const void *value, msda_dtype value_dtype,
                   const float *sampling_locations, const float *attention_weights, const float *grad_output,
                   float *grad_value, float *grad_sampling_locations, float *grad_attention_weights,
-                  unsigned flags, void *stream)
+                  void *workspace, size_t workspace_bytes, unsigned flags, void *stream)
 {
     msda::Geometry g;
     if (int st = make_geometry(shape, g)) return st;
     if (flags & ~MSDA_BWD_ACCUMULATE) return fail(MSDA_E_UNSUPPORTED, "unknown flags 0x%x", flags);
+    const bool accumulate = (flags & MSDA_BWD_ACCUMULATE) != 0;
     if (g.B == 0) return ok();
     if (g.Nq == 0) {  // no queries: grad_value is all zeros (or left as is when accumulating)
-        if (flags & MSDA_BWD_ACCUMULATE) return ok();
+        if (accumulate) return ok();
         if (!grad_value) return fail(MSDA_E_NULL, "grad_value is NULL");
         if (!aligned(grad_value, 4)) return fail(MSDA_E_ALIGN, "grad_value needs 4-byte alignment");
         return launched(msda::launch_zero_fill(grad_value, (int64_t)g.B * g.S * g.M * g.D, (hipStream_t)stream),
@@ -220,14 +231,16 @@ int msda_backward(const msda_shape *shape, const void *value, msda_dtype value_d
     if (!aligned(grad_output, 4) || !aligned(grad_value, 4) || !aligned(grad_sampling_locations, 8) ||
         !aligned(grad_attention_weights, 4))
         return fail(MSDA_E_ALIGN, "gradient tensors need 4-byte (locations 8-byte) alignment");
-    hipStream_t st = (hipStream_t)stream;
-    if (!(flags & MSDA_BWD_ACCUMULATE)) {
-        if (int s = launched(msda::launch_zero_fill(grad_value, (int64_t)g.B * g.S * g.M * g.D, st), "zero_fill"))
-            return s;
+    if (msda::backward_uses_workspace(g, value, value_dtype, grad_output, grad_value)) {
+        const size_t need = msda::backward_workspace_bytes(g);
+        if (!workspace || workspace_bytes < need)
+            return fail(MSDA_E_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
+                        need);
+        if (!aligned(workspace, 256)) return fail(MSDA_E_ALIGN, "workspace needs 256-byte alignment");
     }
-    return launched(msda::launch_backward(g, value, value_dtype, sampling_locations, attention_weights,
-                                          grad_output, grad_value, grad_sampling_locations,
-                                          grad_attention_weights, st),
+    return launched(msda::launch_backward(g, value, value_dtype, sampling_locations, attention_weights, grad_output,
+                                          grad_value, grad_sampling_locations, grad_attention_weights, workspace,
+                                          accumulate, (hipStream_t)stream),
                     "backward");
 }
 

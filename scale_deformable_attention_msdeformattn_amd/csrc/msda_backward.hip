@@ -5,14 +5,34 @@
 //   grad_attn        = sum_d G_d * sum_c w_c v_c[d]
 //   grad_loc.x       = A * W_l * sum_d G_d * sum_c (d wx_c/d fx) wy_c v_c[d]
 //   grad_loc.y       = A * H_l * sum_d G_d * sum_c wx_c (d wy_c/d fy) v_c[d]
-//   grad_value[row_c] += A * w_c * G        (scattered, device atomics)
+//   grad_value[pix]  = sum over the samples with a corner c at pix of A * w_c * G
 //
-// Fast path (C = M*D = 256): the forward's wave-per-query layout. Phase 1
-// parks each sample's corner offsets and (fx, fy, A) in LDS; phase 2 gathers
-// the four corners, forms the per-lane partial dot products with the lane's
-// four channels of G, reduces them over the lanes of the head (DPP/permute),
-// and scatters A*w_c*G with buffer atomics whose out-of-range offsets (corners
-// off the map) are dropped by the hardware range check.
+// grad_value is a scatter: every sample adds to four pixels. On gfx950 float
+// atomics (global and LDS alike) sustain only a small fraction of the
+// required rate, so the fast path has no atomics on floats at all. It turns
+// the scatter into a gather owned by pixel tiles:
+//
+//  1. bin_count   : each workgroup takes a fixed range of queries and counts,
+//                   in an LDS histogram (integer LDS atomics), how many of its
+//                   samples touch each pixel tile of each (head, level).
+//  2. scan_columns: per tile, exclusive prefix of those counts over the
+//                   workgroups of the batch (in place) and the tile total.
+//  3. scan_bases  : exclusive prefix of the tile totals (record base offsets).
+//  4. main        : one wavefront per query (as the forward) computes
+//                   grad_attn and grad_loc, and writes each sample's index into
+//                   the record list of every tile it touches (positions from
+//                   an LDS cursor per tile: no global atomics).
+//  5. tile_accum  : one workgroup per tile sorts its records by cell in LDS,
+//                   then every pixel of the tile gathers A*w*G over the samples
+//                   of its four neighbouring cells in registers and is written
+//                   once with a plain store. Every pixel of grad_value belongs
+//                   to exactly one tile, so no zero fill is needed.
+//
+// Tiles are sized on the host from the expected sample density so that one
+// tile's records fit one LDS chunk; denser tiles take several chunks in turn.
+// Shapes outside the fast path use one thread per (b, q, m) with float atomics.
+#include <algorithm>
+
 #include "msda_device.h"
 #include "msda_internal.h"
 
@@ -21,6 +41,12 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kBlock = kWaves * kWave;
+constexpr int kQueriesPerGroup = 64;     // queries per workgroup of bin_count and main
+constexpr int kChunk = 1024;             // records per LDS chunk in tile_accum
+constexpr int kTilePix = 32;             // pixels per tile
+constexpr int kTileCells = 2 * kWave;    // cells per tile (the tile plus one row and column of halo)
+constexpr int kTaskSlots = 4;            // (cell, split) tasks per lane group in tile_accum
+constexpr int kBatch = 8;                // records in flight per task
 
 struct LevelRec {
     float Wf, Hf;
@@ -32,21 +58,166 @@ __device__ __forceinline__ float dot4(const float4 &a, const float4 &b)
     return __builtin_fmaf(a.w, b.w, __builtin_fmaf(a.z, b.z, __builtin_fmaf(a.y, b.y, a.x * b.x)));
 }
 
-__device__ __forceinline__ void atomic_add4(__amdgpu_buffer_rsrc_t r, uint32_t off, float s,
-                                            const float4 &g)
+// Orders this wave's LDS writes before its later LDS reads of other lanes'
+// data (one wavefront's LDS instructions execute in order).
+__device__ __forceinline__ void wave_lds_sync()
 {
-    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(s * g.x, r, off + 0u, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(s * g.y, r, off + 4u, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(s * g.z, r, off + 8u, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(s * g.w, r, off + 12u, 0, 0);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <typename VT, int M, int L, int K>
+// The pixel tiles (of one head and level) that a sample's in-map corners fall
+// in: up to four distinct ids, -1 for none. (cx, cy) is the sample's cell.
+struct SampleTiles {
+    int t[4];
+};
+
+__device__ __forceinline__ SampleTiles sample_tiles(const TilePlan &tp, int l, int W, int H, int cx, int cy)
+{
+    const int th = tp.th[l], tw = tp.tw[l], ntw = tp.ntw[l], base = tp.tbase[l];
+    const bool x0 = cx >= 0 && cx < W, x1 = cx + 1 >= 0 && cx + 1 < W;
+    const bool y0 = cy >= 0 && cy < H, y1 = cy + 1 >= 0 && cy + 1 < H;
+    const int tx0 = x0 ? cx / tw : -1, tx1 = x1 ? (cx + 1) / tw : -1;
+    const int ty0 = y0 ? cy / th : -1, ty1 = y1 ? (cy + 1) / th : -1;
+    // tile rows: ty0, and ty1 when it differs; tile columns likewise. The four
+    // combinations are distinct; slot (i, j) is fixed so nothing is indexed
+    // dynamically.
+    const int r0 = ty0, r1 = ty1 != ty0 ? ty1 : -1;
+    const int c0 = tx0, c1 = tx1 != tx0 ? tx1 : -1;
+    SampleTiles r;
+    r.t[0] = (r0 >= 0 && c0 >= 0) ? base + r0 * ntw + c0 : -1;
+    r.t[1] = (r0 >= 0 && c1 >= 0) ? base + r0 * ntw + c1 : -1;
+    r.t[2] = (r1 >= 0 && c0 >= 0) ? base + r1 * ntw + c0 : -1;
+    r.t[3] = (r1 >= 0 && c1 >= 0) ? base + r1 * ntw + c1 : -1;
+    return r;
+}
+
+// Cell (cx, cy) of a sample, or false if no corner can be on the map.
+__device__ __forceinline__ bool sample_cell(float2 u, float Wf, float Hf, int &cx, int &cy, float &fx, float &fy)
+{
+    const bool in = sample_in_range(u.x, u.y, Wf, Hf);
+    float cxf, cyf;
+    cell_1d(in ? u.x : 0.0f, Wf, cxf, fx);
+    cell_1d(in ? u.y : 0.0f, Hf, cyf, fy);
+    cx = (int)cxf;
+    cy = (int)cyf;
+    return in;
+}
+
+// ---------------------------------------------------------------- 1. bin_count
+
+constexpr int kBinThreads = 1024;
+
+template <int M, int L, int K>
+__global__ void __launch_bounds__(kBinThreads)
+bin_count_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, uint32_t *__restrict__ counts)
+{
+    constexpr int LK = L * K;
+    constexpr int NS = M * LK;
+    extern __shared__ uint32_t s_hist[];  // [M * tpb]
+    __shared__ LevelRec s_lv[L];
+    const int nkeys = M * tp.tpb;
+    for (int i = threadIdx.x; i < nkeys; i += kBinThreads) s_hist[i] = 0;
+    if (threadIdx.x < L) {
+        const int l = threadIdx.x;
+        s_lv[l] = LevelRec{(float)g.lv.W[l], (float)g.lv.H[l], g.lv.W[l], g.lv.start[l]};
+    }
+    __syncthreads();
+    const int w = blockIdx.x;
+    const int b = w / tp.wpb;
+    const int q0 = (w - b * tp.wpb) * tp.qpw;
+    const int q1 = min(q0 + tp.qpw, g.Nq);
+    const int64_t s_begin = ((int64_t)b * g.Nq + q0) * NS;
+    const int n = (q1 - q0) * NS;
+    for (int i = threadIdx.x; i < n; i += kBinThreads) {
+        const int m = (i / LK) % M;
+        const int l = (i / K) % L;
+        const LevelRec lv = s_lv[l];
+        int cx, cy;
+        float fx, fy;
+        if (!sample_cell(loc[s_begin + i], lv.Wf, lv.Hf, cx, cy, fx, fy)) continue;
+        const SampleTiles st = sample_tiles(tp, l, lv.W, (int)lv.Hf, cx, cy);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (st.t[j] >= 0) atomicAdd(&s_hist[m * tp.tpb + st.t[j]], 1u);
+    }
+    __syncthreads();
+    uint32_t *row = counts + (int64_t)w * nkeys;
+    for (int i = threadIdx.x; i < nkeys; i += kBinThreads) row[i] = s_hist[i];
+}
+
+// ------------------------------------------------------------- 2. scan_columns
+
+// One wavefront per key (b, m, tile): exclusive prefix over the workgroups of
+// batch b, in place, and the key's total.
 __global__ void __launch_bounds__(kBlock)
-backward_c256_kernel(Geometry g, const VT *__restrict__ value, const float2 *__restrict__ loc,
+scan_columns_kernel(int nkeys_per_batch, int wpb, int nkeys, uint32_t *__restrict__ counts,
+                    uint32_t *__restrict__ totals)
+{
+    const int key = blockIdx.x * kWaves + (int)(threadIdx.x / kWave);
+    const int lane = threadIdx.x % kWave;
+    if (key >= nkeys) return;
+    const int b = key / nkeys_per_batch;
+    const int local = key - b * nkeys_per_batch;
+    uint32_t carry = 0;
+    for (int w0 = 0; w0 < wpb; w0 += kWave) {
+        const int w = w0 + lane;
+        uint32_t *p = counts + ((int64_t)(b * wpb + w)) * nkeys_per_batch + local;
+        const uint32_t v = w < wpb ? *p : 0u;
+        uint32_t incl = v;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const uint32_t t = __shfl_up(incl, o, kWave);
+            if (lane >= o) incl += t;
+        }
+        if (w < wpb) *p = carry + incl - v;
+        carry += __shfl(incl, kWave - 1, kWave);
+    }
+    if (lane == 0) totals[key] = carry;
+}
+
+// --------------------------------------------------------------- 3. scan_bases
+
+// One workgroup: exclusive prefix of the key totals.
+__global__ void __launch_bounds__(1024)
+scan_bases_kernel(int nkeys, const uint32_t *__restrict__ totals, uint32_t *__restrict__ bases)
+{
+    __shared__ uint32_t s_part[1024];
+    const int per = (nkeys + 1023) / 1024;
+    const int i0 = threadIdx.x * per;
+    uint32_t sum = 0;
+    for (int i = i0; i < min(i0 + per, nkeys); ++i) sum += totals[i];
+    s_part[threadIdx.x] = sum;
+    __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {
+        const uint32_t t = threadIdx.x >= (unsigned)o ? s_part[threadIdx.x - o] : 0u;
+        __syncthreads();
+        s_part[threadIdx.x] += t;
+        __syncthreads();
+    }
+    uint32_t run = s_part[threadIdx.x] - sum;  // exclusive
+    for (int i = i0; i < min(i0 + per, nkeys); ++i) {
+        bases[i] = run;
+        run += totals[i];
+    }
+}
+
+// --------------------------------------------------------------------- 4. main
+
+// Waves per workgroup of the main kernel: as many as fit about 104 KB of LDS.
+template <int M, int L, int K> struct MainWaves {
+    static constexpr int kPerWave = 3 * M * (L * K + 1) * 16;
+    static constexpr int kValue = 104 * 1024 / kPerWave >= 16 ? 16 : 104 * 1024 / kPerWave >= 8 ? 8 : 4;
+};
+
+template <typename VT, int M, int L, int K>
+__global__ void __launch_bounds__((MainWaves<M, L, K>::kValue * kWave))
+backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, const float2 *__restrict__ loc,
                      const float *__restrict__ attn, const float4 *__restrict__ grad_out,
-                     float *__restrict__ grad_value, float2 *__restrict__ grad_loc,
-                     float *__restrict__ grad_attn, uint32_t grid)
+                     float2 *__restrict__ grad_loc, float *__restrict__ grad_attn,
+                     const uint32_t *__restrict__ offsets, const uint32_t *__restrict__ bases,
+                     uint32_t *__restrict__ records, uint32_t grid)
 {
     constexpr int C = 256;
     constexpr int D = C / M;
@@ -55,79 +226,84 @@ backward_c256_kernel(Geometry g, const VT *__restrict__ value, const float2 *__r
     constexpr int NS = M * LK;
     constexpr int PAD = LK + 1;  // per-head LDS stride in records (breaks bank aliasing)
     constexpr uint32_t RB = C * sizeof(VT);
-    constexpr uint32_t GRB = C * sizeof(float);  // grad_value row bytes
-    static_assert(GRB % RB == 0, "value rows are no wider than grad_value rows");
-    // value byte offset from a grad_value byte offset (a shift for bf16; the
-    // out-of-range marker 2^31 becomes 2^30, still beyond S*RB < 2^30)
-    auto vbytes = [](uint32_t o) { return o / (GRB / RB); };
+    constexpr int MW = MainWaves<M, L, K>::kValue;
+    constexpr int NT = MW * kWave;
 
+    extern __shared__ uint32_t s_cursor[];  // [M * tpb]
     __shared__ LevelRec s_lv[L];
-    __shared__ int4 s_off[kWaves][M * PAD];
-    __shared__ float4 s_geo[kWaves][M * PAD];   // (fx, fy, A, -)
-    __shared__ float4 s_res[kWaves][M * PAD];   // (grad_attn, grad_x, grad_y, -)
+    __shared__ int4 s_off[MW][M * PAD];
+    __shared__ float4 s_geo[MW][M * PAD];   // (fx, fy, A, -)
+    __shared__ float4 s_res[MW][M * PAD];   // (grad_attn, grad_x, grad_y, -)
 
     const int lane = threadIdx.x % kWave;
-    // wave-uniform by construction; readfirstlane lets the compiler keep the
-    // per-wave query, batch and buffer descriptor in scalar registers
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint32_t w = xcd_tile(blockIdx.x, grid);
+    const bool wg_active = w < (uint32_t)(g.B * tp.wpb);
+    const int b = wg_active ? (int)(w / tp.wpb) : 0;
+    const int q0 = wg_active ? (int)(w - b * tp.wpb) * tp.qpw : 0;
+    const int q1 = wg_active ? min(q0 + tp.qpw, g.Nq) : 0;
+    const int nkeys = M * tp.tpb;
     if (threadIdx.x < L) {
         const int l = threadIdx.x;
         s_lv[l] = LevelRec{(float)g.lv.W[l], (float)g.lv.H[l], g.lv.W[l], g.lv.start[l]};
     }
+    if (wg_active) {
+        const uint32_t *off = offsets + (int64_t)w * nkeys;
+        const uint32_t *bs = bases + (int64_t)b * nkeys;
+        for (int i = threadIdx.x; i < nkeys; i += NT) s_cursor[i] = bs[i] + off[i];
+    }
     __syncthreads();
+    if (!wg_active) return;
 
-    const int64_t gq = (int64_t)xcd_tile(blockIdx.x, grid) * kWaves + wave;
-    const bool active = gq < (int64_t)g.B * g.Nq;
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(value + (int64_t)b * g.S * C, (uint32_t)g.S * RB);
+    const uint32_t vlane = (uint32_t)lane * 4u * sizeof(VT);
+    const int m = lane / LPH;
 
-    if (active) {
+    for (int q = q0 + wave; q < q1; q += MW) {
+        const int64_t gq = (int64_t)b * g.Nq + q;
+        // ---- phase 1: per-sample geometry, one sample per lane per pass ----
 #pragma unroll
         for (int s0 = 0; s0 < NS; s0 += kWave) {
             const int s = s0 + lane;
             if (NS % kWave == 0 || s < NS) {
+                const int sm = s / LK;
                 const int l = (s / K) % L;
-                const int p = s + s / LK;  // padded slot
+                const int p = s + s / LK;
                 const LevelRec lv = s_lv[l];
-                float2 u = loc[gq * NS + s];
+                int cx, cy;
+                float fx, fy;
+                const bool in = sample_cell(loc[gq * NS + s], lv.Wf, lv.Hf, cx, cy, fx, fy);
                 const float a = attn[gq * NS + s];
-                const bool in = sample_in_range(u.x, u.y, lv.Wf, lv.Hf);
-                u.x = in ? u.x : 0.0f;
-                u.y = in ? u.y : 0.0f;
-                float cx, fx, cy, fy;
-                cell_1d(u.x, lv.Wf, cx, fx);
-                cell_1d(u.y, lv.Hf, cy, fy);
-                const bool x0ok = (cx >= 0.0f) & (cx < lv.Wf);
-                const bool x1ok = (cx >= -1.0f) & (cx + 1.0f < lv.Wf);
-                const bool y0ok = in & (cy >= 0.0f) & (cy < lv.Hf);
-                const bool y1ok = in & (cy >= -1.0f) & (cy + 1.0f < lv.Hf);
-                // byte offsets into grad_value rows (fp32, GRB bytes per row);
-                // value rows are addressed with the same offsets scaled by
-                // RB/GRB. Off-map corners get an offset that stays out of
-                // range of both resources after that scaling.
-                const uint32_t o00 = (uint32_t)(lv.start + (int)cy * lv.W + (int)cx) * GRB;
-                const uint32_t o10 = o00 + (uint32_t)lv.W * GRB;
+                const int H = (int)lv.Hf;
+                const bool x0ok = in & (cx >= 0) & (cx < lv.W);
+                const bool x1ok = in & (cx + 1 >= 0) & (cx + 1 < lv.W);
+                const bool y0ok = (cy >= 0) & (cy < H);
+                const bool y1ok = (cy + 1 >= 0) & (cy + 1 < H);
+                const uint32_t o00 = (uint32_t)(lv.start + cy * lv.W + cx) * RB;
+                const uint32_t o10 = o00 + (uint32_t)lv.W * RB;
                 int4 o;
                 o.x = (int)((y0ok & x0ok) ? o00 : kOutOfRange);
-                o.y = (int)((y0ok & x1ok) ? o00 + GRB : kOutOfRange);
+                o.y = (int)((y0ok & x1ok) ? o00 + RB : kOutOfRange);
                 o.z = (int)((y1ok & x0ok) ? o10 : kOutOfRange);
-                o.w = (int)((y1ok & x1ok) ? o10 + GRB : kOutOfRange);
+                o.w = (int)((y1ok & x1ok) ? o10 + RB : kOutOfRange);
                 s_off[wave][p] = o;
                 s_geo[wave][p] = make_float4(fx, fy, a, 0.0f);
+                if (in) {
+                    const SampleTiles st = sample_tiles(tp, l, lv.W, H, cx, cy);
+                    const uint32_t sidx = (uint32_t)(gq * NS + s);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (st.t[j] >= 0) records[atomicAdd(&s_cursor[sm * tp.tpb + st.t[j]], 1u)] = sidx;
+                }
             }
         }
-    }
-    __syncthreads();
-    if (active) {
-        const int b = (int)(gq / g.Nq);
-        const __amdgpu_buffer_rsrc_t vr = make_rsrc(value + (int64_t)b * g.S * C, (uint32_t)g.S * RB);
-        const __amdgpu_buffer_rsrc_t gr =
-            make_rsrc(grad_value + (int64_t)b * g.S * C, (uint32_t)g.S * GRB);
-        const uint32_t vlane = (uint32_t)lane * 4u * sizeof(VT);
-        const uint32_t glane = (uint32_t)lane * 16u;
-        const int m = lane / LPH;
+        wave_lds_sync();
+        // ---- phase 2: gathers, dot products with G, reductions over a head ----
         const float4 G = grad_out[gq * (C / 4) + lane];
         const int4 *offs = &s_off[wave][m * PAD];
         const float4 *geo = &s_geo[wave][m * PAD];
         float4 *res = &s_res[wave][m * PAD];
+#pragma unroll
         for (int l = 0; l < L; ++l) {
             const float Wf = (float)g.lv.W[l], Hf = (float)g.lv.H[l];
 #pragma unroll
@@ -135,12 +311,10 @@ backward_c256_kernel(Geometry g, const VT *__restrict__ value, const float2 *__r
                 const int i = l * K + k;
                 const int4 o = offs[i];
                 const float4 f = geo[i];
-                const uint32_t o00 = (uint32_t)o.x, o01 = (uint32_t)o.y;
-                const uint32_t o10 = (uint32_t)o.z, o11 = (uint32_t)o.w;
-                const float4 v00 = ValueTraits<VT>::load4(vr, vbytes(o00) + vlane);
-                const float4 v01 = ValueTraits<VT>::load4(vr, vbytes(o01) + vlane);
-                const float4 v10 = ValueTraits<VT>::load4(vr, vbytes(o10) + vlane);
-                const float4 v11 = ValueTraits<VT>::load4(vr, vbytes(o11) + vlane);
+                const float4 v00 = ValueTraits<VT>::load4(vr, (uint32_t)o.x + vlane);
+                const float4 v01 = ValueTraits<VT>::load4(vr, (uint32_t)o.y + vlane);
+                const float4 v10 = ValueTraits<VT>::load4(vr, (uint32_t)o.z + vlane);
+                const float4 v11 = ValueTraits<VT>::load4(vr, (uint32_t)o.w + vlane);
                 const float d00 = dot4(G, v00), d01 = dot4(G, v01);
                 const float d10 = dot4(G, v10), d11 = dot4(G, v11);
                 const float fx = f.x, fy = f.y, a = f.z;
@@ -152,28 +326,213 @@ backward_c256_kernel(Geometry g, const VT *__restrict__ value, const float2 *__r
                 gx = group_sum<LPH>(gx);
                 gy = group_sum<LPH>(gy);
                 if (lane % LPH == 0) res[i] = make_float4(ga, a * Wf * gx, a * Hf * gy, 0.0f);
-                const float ay0 = a * hy, ay1 = a * fy;
-                atomic_add4(gr, o00 + glane, ay0 * hx, G);
-                atomic_add4(gr, o01 + glane, ay0 * fx, G);
-                atomic_add4(gr, o10 + glane, ay1 * hx, G);
-                atomic_add4(gr, o11 + glane, ay1 * fx, G);
             }
         }
-    }
-    __syncthreads();
-    if (!active) return;
+        wave_lds_sync();
 #pragma unroll
-    for (int s0 = 0; s0 < NS; s0 += kWave) {
-        const int s = s0 + lane;
-        if (NS % kWave == 0 || s < NS) {
-            const float4 r = s_res[wave][s + s / LK];
-            grad_attn[gq * NS + s] = r.x;
-            grad_loc[gq * NS + s] = make_float2(r.y, r.z);
+        for (int s0 = 0; s0 < NS; s0 += kWave) {
+            const int s = s0 + lane;
+            if (NS % kWave == 0 || s < NS) {
+                const float4 r = s_res[wave][s + s / LK];
+                grad_attn[gq * NS + s] = r.x;
+                grad_loc[gq * NS + s] = make_float2(r.y, r.z);
+            }
         }
+        wave_lds_sync();
     }
 }
 
-// Generic path: one thread per (b, q, m), looping over the D channels.
+// --------------------------------------------------------------- 5. tile_accum
+
+// One workgroup per tile (b, m, level, tile). Its records are counting-sorted
+// by cell in LDS; then each lane group (LG lanes, 4 channels each, D = 4*LG)
+// takes (cell, split) tasks: it walks the cell's records (every S-th one for
+// split s), loads each record's G row once and accumulates A*w_c*G into four
+// corner accumulators, kBatch records at a time so that many loads are in
+// flight. The corner sums go to single-writer LDS slots (pixel, corner role,
+// split); finally every pixel adds its slots and is written once.
+template <int LG>
+__global__ void __launch_bounds__(kBlock)
+tile_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, const float *__restrict__ attn,
+                  const float4 *__restrict__ grad_out, float4 *__restrict__ grad_value,
+                  const uint32_t *__restrict__ records, const uint32_t *__restrict__ bases,
+                  const uint32_t *__restrict__ totals, int accumulate)
+{
+    constexpr int NG = kBlock / LG;
+    // (pixel, role, split) slots in use: npix*4 when cells >= NG, else at most 4*NG
+    constexpr int kPartSlots = 4 * (kTilePix > NG ? kTilePix : NG);
+    __shared__ uint32_t s_start[kTileCells + 1];
+    __shared__ uint32_t s_cur[kTileCells];
+    __shared__ float4 s_pay[kChunk];       // (fx, fy, A, bits(b*Nq+q))
+    __shared__ uint8_t s_cell[kChunk];
+    __shared__ uint16_t s_entry[kChunk];
+    __shared__ float4 s_part[kPartSlots][LG];
+
+    // consecutive keys (same batch and head, neighbouring tiles) read G rows of
+    // neighbouring queries: give each XCD (private L2) a contiguous key range
+    const int key = (int)xcd_tile(blockIdx.x, gridDim.x);
+    const int nkb = g.M * tp.tpb;
+    if (key >= g.B * nkb) return;
+    const int b = key / nkb;
+    const int m = (key - b * nkb) / tp.tpb;
+    const int tile = key - b * nkb - m * tp.tpb;
+    int l = 0;
+#pragma unroll
+    for (int i = 1; i < MSDA_MAX_LEVELS; ++i)
+        if (i < g.L && tile >= tp.tbase[i]) l = i;
+    int th = 1, tw = 1, ntw = 1, tb = 0, W = 1, H = 1, lstart = 0;
+#pragma unroll
+    for (int i = 0; i < MSDA_MAX_LEVELS; ++i)
+        if (i == l) {
+            th = tp.th[i];
+            tw = tp.tw[i];
+            ntw = tp.ntw[i];
+            tb = tp.tbase[i];
+            W = g.lv.W[i];
+            H = g.lv.H[i];
+            lstart = g.lv.start[i];
+        }
+    const int t_in = tile - tb;
+    const int ty = t_in / ntw, tx = t_in - ty * ntw;
+    const float Wf = (float)W, Hf = (float)H;
+    const int r0 = ty * th, r1 = min(r0 + th, H);
+    const int c0 = tx * tw, c1 = min(c0 + tw, W);
+    const int pw = c1 - c0, ph = r1 - r0;   // pixels of this tile
+    const int cw = pw + 1;                  // cell columns c0-1 .. c1-1
+    const int ncells = (ph + 1) * cw;       // cell rows r0-1 .. r1-1
+    const int npix = ph * pw;
+    const int S = ncells >= NG ? 1 : NG / ncells;   // lane groups per cell
+    const int ntask = ncells * S;
+    const int NS = g.M * g.L * g.K;
+    const uint32_t nsamples = (uint32_t)g.samples();
+    const int grp = threadIdx.x / LG;
+    const int lig = threadIdx.x % LG;
+
+    for (int i = threadIdx.x; i < npix * 4 * S * LG; i += kBlock)
+        s_part[i / LG][i % LG] = make_float4(0.f, 0.f, 0.f, 0.f);
+
+    const uint32_t rbeg = bases[key];
+    const uint32_t rtot = totals[key];
+    for (uint32_t c0r = 0; c0r < rtot; c0r += kChunk) {
+        const int n = (int)min((uint32_t)kChunk, rtot - c0r);
+        for (int i = threadIdx.x; i < ncells; i += kBlock) s_cur[i] = 0;
+        __syncthreads();
+        // this chunk's records: geometry and cell; count per cell
+        for (int i = threadIdx.x; i < n; i += kBlock) {
+            const uint32_t sidx = records[rbeg + c0r + i];
+            // the main kernel wrote each record for this tile with the same
+            // cell computation; the checks only keep a corrupt record from
+            // addressing outside loc/attn or the cell table
+            int cell = -1;
+            if (sidx < nsamples) {
+                int cx, cy;
+                float fx, fy;
+                sample_cell(loc[sidx], Wf, Hf, cx, cy, fx, fy);
+                s_pay[i] = make_float4(fx, fy, attn[sidx], __uint_as_float(sidx / (uint32_t)NS));
+                const int ry = cy - r0 + 1, rx = cx - c0 + 1;
+                if (ry >= 0 && ry <= ph && rx >= 0 && rx < cw) cell = ry * cw + rx;
+            }
+            s_cell[i] = cell < 0 ? (uint8_t)0xff : (uint8_t)cell;
+            if (cell >= 0) atomicAdd(&s_cur[cell], 1u);
+        }
+        __syncthreads();
+        // exclusive scan of the (at most kTileCells = 2 * kWave) cell counts, one wave
+        if (threadIdx.x < kWave) {
+            const int i0 = 2 * threadIdx.x;
+            const uint32_t a = i0 < ncells ? s_cur[i0] : 0u;
+            const uint32_t c = i0 + 1 < ncells ? s_cur[i0 + 1] : 0u;
+            uint32_t incl = a + c;
+#pragma unroll
+            for (int o = 1; o < kWave; o <<= 1) {
+                const uint32_t t = __shfl_up(incl, o, kWave);
+                if ((int)threadIdx.x >= o) incl += t;
+            }
+            const uint32_t ex = incl - a - c;
+            if (i0 < ncells) s_start[i0] = s_cur[i0] = ex;
+            if (i0 + 1 < ncells) s_start[i0 + 1] = s_cur[i0 + 1] = ex + a;
+            if (threadIdx.x == kWave - 1) s_start[ncells] = incl;
+        }
+        __syncthreads();
+        for (int i = threadIdx.x; i < n; i += kBlock)
+            if (s_cell[i] != 0xff) s_entry[atomicAdd(&s_cur[s_cell[i]], 1u)] = (uint16_t)i;
+        __syncthreads();
+        // (cell, split) tasks; each adds its four corner sums into its own
+        // (pixel, role, split) slots, which no other task touches
+        for (int t = 0; t < kTaskSlots; ++t) {
+            const int task = grp + t * NG;
+            if (task >= ntask) break;
+            const int cell = task / S, split = task - (task / S) * S;
+            float4 acc[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+            const uint32_t e_end = s_start[cell + 1];
+            for (uint32_t e0 = s_start[cell] + split; e0 < e_end; e0 += S * kBatch) {
+                float4 pay[kBatch], gv[kBatch];
+#pragma unroll
+                for (int j = 0; j < kBatch; ++j) {
+                    const uint32_t e = e0 + j * S;
+                    pay[j] = e < e_end ? s_pay[s_entry[e]] : make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+#pragma unroll
+                for (int j = 0; j < kBatch; ++j) {
+                    const uint32_t e = e0 + j * S;
+                    const uint32_t bq = __float_as_uint(pay[j].w);
+                    gv[j] = e < e_end ? grad_out[((int64_t)bq * g.M + m) * LG + lig] : make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+#pragma unroll
+                for (int j = 0; j < kBatch; ++j) {
+                    const float fx = pay[j].x, fy = pay[j].y, a = pay[j].z;
+                    const float ay0 = a * (1.0f - fy), ay1 = a * fy;
+                    const float w[4] = {ay0 * (1.0f - fx), ay0 * fx, ay1 * (1.0f - fx), ay1 * fx};
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        acc[r].x = __builtin_fmaf(w[r], gv[j].x, acc[r].x);
+                        acc[r].y = __builtin_fmaf(w[r], gv[j].y, acc[r].y);
+                        acc[r].z = __builtin_fmaf(w[r], gv[j].z, acc[r].z);
+                        acc[r].w = __builtin_fmaf(w[r], gv[j].w, acc[r].w);
+                    }
+                }
+            }
+            // role r: 0 top-left, 1 top-right, 2 bottom-left, 3 bottom-right
+            // corner of the cell; cell (ry, rx) (relative, halo row/column at
+            // 0) has its top-left corner at tile pixel (ry-1, rx-1)
+            const int ry = cell / cw, rx = cell - (cell / cw) * cw;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int py = ry - 1 + (r >> 1), px = rx - 1 + (r & 1);
+                if (py >= 0 && py < ph && px >= 0 && px < pw) {
+                    float4 &slot = s_part[((py * pw + px) * 4 + r) * S + split][lig];
+                    const float4 o = slot;
+                    slot = make_float4(o.x + acc[r].x, o.y + acc[r].y, o.z + acc[r].z, o.w + acc[r].w);
+                }
+            }
+        }
+        __syncthreads();  // LDS is reused by the next chunk
+    }
+    for (int pix = grp; pix < npix; pix += NG) {
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int i = 0; i < 4 * S; ++i) {
+            const float4 t = s_part[pix * 4 * S + i][lig];
+            v.x += t.x;
+            v.y += t.y;
+            v.z += t.z;
+            v.w += t.w;
+        }
+        const int py = r0 + pix / pw, px = c0 + pix % pw;
+        float4 *dst = grad_value + (((int64_t)b * g.S + lstart + (int64_t)py * W + px) * g.M + m) * LG + lig;
+        if (accumulate) {
+            const float4 o = *dst;
+            v.x += o.x;
+            v.y += o.y;
+            v.z += o.z;
+            v.w += o.w;
+        }
+        *dst = v;
+    }
+}
+
+// ------------------------------------------------------------ generic fallback
+
 template <typename VT>
 __device__ __forceinline__ float vload(const VT *p);
 template <> __device__ __forceinline__ float vload<float>(const float *p) { return *p; }
@@ -182,6 +541,8 @@ template <> __device__ __forceinline__ float vload<uint16_t>(const uint16_t *p)
     return __uint_as_float((uint32_t)*p << 16);
 }
 
+// One thread per (b, q, m), looping over the D channels; grad_value by float
+// atomics (must be zeroed first unless accumulating).
 template <typename VT>
 __global__ void __launch_bounds__(256)
 backward_generic_kernel(Geometry g, const VT *__restrict__ value, const float2 *__restrict__ loc,
@@ -233,56 +594,181 @@ backward_generic_kernel(Geometry g, const VT *__restrict__ value, const float2 *
     }
 }
 
-template <typename VT, int M, int L, int K>
-hipError_t launch_c256(const Geometry &g, const void *value, const float *loc, const float *attn,
-                       const float *go, float *gv, float *gl, float *ga, hipStream_t st)
+// ------------------------------------------------------------------- host side
+
+struct Workspace {
+    uint32_t *counts, *totals, *bases, *records;
+};
+
+inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+size_t layout(const Geometry &g, const TilePlan &tp, char *base, Workspace *ws)
 {
-    const uint32_t tiles = (uint32_t)((g.queries() + kWaves - 1) / kWaves);
-    const uint32_t grid = round_up8(tiles);
-    hipLaunchKernelGGL((backward_c256_kernel<VT, M, L, K>), dim3(grid), dim3(kBlock), 0, st, g,
+    const size_t nkeys = (size_t)g.B * g.M * tp.tpb;
+    const size_t ncount = (size_t)g.B * tp.wpb * g.M * tp.tpb;
+    const size_t nrec = 4 * (size_t)g.samples();
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        char *p = base ? base + off : nullptr;
+        off += align256(bytes);
+        return reinterpret_cast<uint32_t *>(p);
+    };
+    Workspace w;
+    w.counts = take(ncount * 4);
+    w.totals = take(nkeys * 4);
+    w.bases = take(nkeys * 4);
+    w.records = take(nrec * 4);
+    if (ws) *ws = w;
+    return off;
+}
+
+template <typename VT, int M, int L, int K>
+hipError_t launch_fast(const Geometry &g, const TilePlan &tp, const void *value, const float *loc,
+                       const float *attn, const float *go, float *gv, float *gl, float *ga, void *wsp,
+                       bool accumulate, hipStream_t st)
+{
+    Workspace ws;
+    layout(g, tp, static_cast<char *>(wsp), &ws);
+    const int nkb = M * tp.tpb;
+    const int nwg = g.B * tp.wpb;
+    const int nkeys = g.B * nkb;
+    const size_t hist_bytes = (size_t)nkb * 4;
+    hipLaunchKernelGGL((bin_count_kernel<M, L, K>), dim3(nwg), dim3(kBinThreads), hist_bytes, st, g, tp,
+                       reinterpret_cast<const float2 *>(loc), ws.counts);
+    hipLaunchKernelGGL(scan_columns_kernel, dim3((nkeys + kWaves - 1) / kWaves), dim3(kBlock), 0, st, nkb,
+                       tp.wpb, nkeys, ws.counts, ws.totals);
+    hipLaunchKernelGGL(scan_bases_kernel, dim3(1), dim3(1024), 0, st, nkeys, ws.totals, ws.bases);
+    const uint32_t grid = round_up8((uint32_t)nwg);
+    hipLaunchKernelGGL((backward_c256_kernel<VT, M, L, K>), dim3(grid), dim3(MainWaves<M, L, K>::kValue * kWave),
+                       hist_bytes, st, g, tp,
                        static_cast<const VT *>(value), reinterpret_cast<const float2 *>(loc), attn,
-                       reinterpret_cast<const float4 *>(go), gv, reinterpret_cast<float2 *>(gl), ga,
-                       grid);
+                       reinterpret_cast<const float4 *>(go), reinterpret_cast<float2 *>(gl), ga, ws.counts,
+                       ws.bases, ws.records, grid);
+    constexpr int LG = 256 / M / 4;
+    hipLaunchKernelGGL((tile_accum_kernel<LG>), dim3(round_up8((uint32_t)nkeys)), dim3(kBlock), 0, st, g, tp,
+                       reinterpret_cast<const float2 *>(loc), attn, reinterpret_cast<const float4 *>(go),
+                       reinterpret_cast<float4 *>(gv), ws.records, ws.bases, ws.totals, accumulate ? 1 : 0);
     return hipGetLastError();
 }
 
-template <typename VT>
-hipError_t launch_typed(const Geometry &g, const void *value, const float *loc, const float *attn,
-                        const float *go, float *gv, float *gl, float *ga, hipStream_t st)
+// Which (VT-independent) fast-path instantiation serves g, if any.
+enum class Fast { None, M8L4K4, M4L4K4, M16L4K4, M8L1K4, M8L4K8, M8L3K4, M8L4K1 };
+
+Fast fast_kind(const Geometry &g)
 {
-    const bool c256 = g.M * g.D == 256 &&
-                      (reinterpret_cast<uintptr_t>(value) % (4 * sizeof(VT))) == 0 &&
-                      (reinterpret_cast<uintptr_t>(go) % 16) == 0 &&
-                      (reinterpret_cast<uintptr_t>(gv) % 16) == 0;
-    if (c256 && g.L == 4 && g.K == 4) {
-        switch (g.M) {
-        case 8: return launch_c256<VT, 8, 4, 4>(g, value, loc, attn, go, gv, gl, ga, st);
-        case 4: return launch_c256<VT, 4, 4, 4>(g, value, loc, attn, go, gv, gl, ga, st);
-        case 16: return launch_c256<VT, 16, 4, 4>(g, value, loc, attn, go, gv, gl, ga, st);
-        default: break;
-        }
+    if (g.M * g.D != 256) return Fast::None;
+    if (g.L == 4 && g.K == 4) {
+        if (g.M == 8) return Fast::M8L4K4;
+        if (g.M == 4) return Fast::M4L4K4;
+        if (g.M == 16) return Fast::M16L4K4;
     }
-    if (c256 && g.M == 8) {
-        if (g.L == 1 && g.K == 4) return launch_c256<VT, 8, 1, 4>(g, value, loc, attn, go, gv, gl, ga, st);
-        if (g.L == 4 && g.K == 8) return launch_c256<VT, 8, 4, 8>(g, value, loc, attn, go, gv, gl, ga, st);
-        if (g.L == 3 && g.K == 4) return launch_c256<VT, 8, 3, 4>(g, value, loc, attn, go, gv, gl, ga, st);
-        if (g.L == 4 && g.K == 1) return launch_c256<VT, 8, 4, 1>(g, value, loc, attn, go, gv, gl, ga, st);
+    if (g.M == 8) {
+        if (g.L == 1 && g.K == 4) return Fast::M8L1K4;
+        if (g.L == 4 && g.K == 8) return Fast::M8L4K8;
+        if (g.L == 3 && g.K == 4) return Fast::M8L3K4;
+        if (g.L == 4 && g.K == 1) return Fast::M8L4K1;
+    }
+    return Fast::None;
+}
+
+template <typename VT>
+hipError_t launch_typed(const Geometry &g, const TilePlan *tpp, const void *value, const float *loc,
+                        const float *attn, const float *go, float *gv, float *gl, float *ga, void *ws,
+                        bool accumulate, hipStream_t st)
+{
+#define MSDA_FAST(M_, L_, K_) \
+    launch_fast<VT, M_, L_, K_>(g, *tpp, value, loc, attn, go, gv, gl, ga, ws, accumulate, st)
+    switch (tpp ? fast_kind(g) : Fast::None) {
+    case Fast::M8L4K4: return MSDA_FAST(8, 4, 4);
+    case Fast::M4L4K4: return MSDA_FAST(4, 4, 4);
+    case Fast::M16L4K4: return MSDA_FAST(16, 4, 4);
+    case Fast::M8L1K4: return MSDA_FAST(8, 1, 4);
+    case Fast::M8L4K8: return MSDA_FAST(8, 4, 8);
+    case Fast::M8L3K4: return MSDA_FAST(8, 3, 4);
+    case Fast::M8L4K1: return MSDA_FAST(8, 4, 1);
+    case Fast::None: break;
+    }
+#undef MSDA_FAST
+    if (!accumulate) {
+        hipError_t e = launch_zero_fill(gv, (int64_t)g.B * g.S * g.M * g.D, st);
+        if (e != hipSuccess) return e;
     }
     const int64_t n = g.queries() * g.M;
-    hipLaunchKernelGGL((backward_generic_kernel<VT>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
-                       st, g, static_cast<const VT *>(value), reinterpret_cast<const float2 *>(loc),
-                       attn, go, gv, reinterpret_cast<float2 *>(gl), ga);
+    hipLaunchKernelGGL((backward_generic_kernel<VT>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, g,
+                       static_cast<const VT *>(value), reinterpret_cast<const float2 *>(loc), attn, go, gv,
+                       reinterpret_cast<float2 *>(gl), ga);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_backward(const Geometry &g, const void *value, msda_dtype vt, const float *loc,
-                           const float *attn, const float *go, float *gv, float *gl, float *ga,
-                           hipStream_t st)
+// Tile sizes per level: the largest tile (at most kTilePix pixels and
+// kTileCells cells with its halo; squarer wins a tie, since it duplicates
+// fewer records) whose expected record count, with samples spread evenly over
+// the level, stays within 3/4 of one chunk (a 1x1 tile if none does).
+bool make_tile_plan(const Geometry &g, TilePlan &tp)
 {
-    if (vt == MSDA_BF16) return launch_typed<uint16_t>(g, value, loc, attn, go, gv, gl, ga, st);
-    return launch_typed<float>(g, value, loc, attn, go, gv, gl, ga, st);
+    if (fast_kind(g) == Fast::None) return false;
+    const double target = 0.75 * kChunk;
+    // every (cell, split) task needs a slot: cells <= kTaskSlots * lane groups
+    const int max_cells = std::min(kTileCells, kTaskSlots * (kBlock / (g.D / 4)));
+    int base = 0;
+    for (int l = 0; l < g.L; ++l) {
+        const int H = g.lv.H[l], W = g.lv.W[l];
+        const double per_cell = (double)g.Nq * g.K / ((double)H * W);
+        int bt = 1, bw = 1, barea = 0, bcells = 1 << 30;
+        for (int th = 1; th <= std::min(H, kTilePix); ++th)
+            for (int tw = 1; tw <= std::min(W, kTilePix / th); ++tw) {
+                const int cells = (th + 1) * (tw + 1);
+                if (cells > max_cells || cells * per_cell > target) continue;
+                const int area = th * tw;
+                if (area > barea || (area == barea && cells < bcells)) {
+                    barea = area;
+                    bcells = cells;
+                    bt = th;
+                    bw = tw;
+                }
+            }
+        tp.th[l] = bt;
+        tp.tw[l] = bw;
+        tp.ntw[l] = (W + bw - 1) / bw;
+        tp.tbase[l] = base;
+        base += ((H + bt - 1) / bt) * tp.ntw[l];
+    }
+    for (int l = g.L; l < MSDA_MAX_LEVELS; ++l) tp.th[l] = tp.tw[l] = tp.ntw[l] = 1, tp.tbase[l] = base;
+    tp.tpb = base;
+    tp.qpw = kQueriesPerGroup;
+    tp.wpb = (g.Nq + tp.qpw - 1) / tp.qpw;
+    // the per-workgroup histogram / cursors live in LDS; record indices are 32-bit
+    if ((size_t)g.M * tp.tpb * 4 > 64 * 1024) return false;
+    if ((uint64_t)g.samples() * 4 >= (1ull << 32)) return false;
+    return true;
+}
+
+size_t backward_workspace_bytes(const Geometry &g)
+{
+    TilePlan tp;
+    if (!make_tile_plan(g, tp)) return 0;
+    return layout(g, tp, nullptr, nullptr);
+}
+
+bool backward_uses_workspace(const Geometry &g, const void *value, msda_dtype vt, const float *go,
+                             const float *gv)
+{
+    TilePlan tp;
+    const size_t vb = vt == MSDA_BF16 ? 2 : 4;
+    return make_tile_plan(g, tp) && (reinterpret_cast<uintptr_t>(value) % (4 * vb)) == 0 &&
+           (reinterpret_cast<uintptr_t>(go) % 16) == 0 && (reinterpret_cast<uintptr_t>(gv) % 16) == 0;
+}
+
+hipError_t launch_backward(const Geometry &g, const void *value, msda_dtype vt, const float *loc,
+                           const float *attn, const float *go, float *gv, float *gl, float *ga, void *ws,
+                           bool accumulate, hipStream_t st)
+{
+    TilePlan tp;
+    const TilePlan *tpp = backward_uses_workspace(g, value, vt, go, gv) && make_tile_plan(g, tp) ? &tp : nullptr;
+    if (vt == MSDA_BF16) return launch_typed<uint16_t>(g, tpp, value, loc, attn, go, gv, gl, ga, ws, accumulate, st);
+    return launch_typed<float>(g, tpp, value, loc, attn, go, gv, gl, ga, ws, accumulate, st);
 }
 
 }  // namespace msda

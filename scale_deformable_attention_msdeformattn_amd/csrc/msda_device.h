@@ -78,12 +78,30 @@ __device__ __forceinline__ bool sample_in_range(float u, float v, float Wf, floa
     return (x > -2.0f) & (x < Wf + 1.0f) & (y > -2.0f) & (y < Hf + 1.0f);
 }
 
+// DPP lane moves (VALU, no LDS traffic): within quads, lanes swapped by
+// xor 1 and xor 2; within half-rows of 8, lane i <-> 7-i; within rows of 16,
+// lane i <-> 15-i.
+template <int CTRL> __device__ __forceinline__ float dpp_move(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
+}
+constexpr int kDppQuadXor1 = 0xb1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4e;      // quad_perm [2,3,0,1]
+constexpr int kDppHalfRowMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
 // Sum over the lanes of aligned groups of N lanes (N a power of two <= 64);
-// every lane of a group ends with the group's sum.
+// every lane of a group ends with the group's sum. Groups of up to 16 lanes
+// use DPP only (after the quad steps every lane of a quad holds the quad sum,
+// so a mirror adds the partner quad's sum, and likewise for half-rows).
 template <int N> __device__ __forceinline__ float group_sum(float v)
 {
+    if constexpr (N >= 2) v += dpp_move<kDppQuadXor1>(v);
+    if constexpr (N >= 4) v += dpp_move<kDppQuadXor2>(v);
+    if constexpr (N >= 8) v += dpp_move<kDppHalfRowMirror>(v);
+    if constexpr (N >= 16) v += dpp_move<kDppRowMirror>(v);
 #pragma unroll
-    for (int o = 1; o < N; o <<= 1) v += __shfl_xor(v, o, kWave);
+    for (int o = 16; o < N; o <<= 1) v += __shfl_xor(v, o, kWave);
     return v;
 }
 

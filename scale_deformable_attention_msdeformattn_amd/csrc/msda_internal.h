@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include "msda.h"
@@ -24,10 +25,31 @@ struct Geometry {
     int32_t B, M, D, L, K;
     int32_t S, Nq;
     Levels lv;
-    int64_t samples() const { return (int64_t)B * Nq * M * L * K; }
-    int64_t queries() const { return (int64_t)B * Nq; }
-    int32_t channels() const { return M * D; }
+    __host__ __device__ int64_t samples() const { return (int64_t)B * Nq * M * L * K; }
+    __host__ __device__ int64_t queries() const { return (int64_t)B * Nq; }
+    __host__ __device__ int32_t channels() const { return M * D; }
 };
+
+// Pixel tiling of grad_value for the scatter-free backward (per level: tile
+// height/width, tiles per row of tiles, first tile index), tiles per
+// (batch, head), and the query ranges of the binning workgroups.
+struct TilePlan {
+    int32_t th[MSDA_MAX_LEVELS];
+    int32_t tw[MSDA_MAX_LEVELS];
+    int32_t ntw[MSDA_MAX_LEVELS];
+    int32_t tbase[MSDA_MAX_LEVELS];
+    int32_t tpb;  // tiles per (batch, head)
+    int32_t qpw;  // queries per workgroup
+    int32_t wpb;  // workgroups per batch
+};
+
+// Whether the backward takes the tiled fast path for this call (it then needs
+// backward_workspace_bytes(g) bytes of workspace), and that size (0 when the
+// shape has no fast path).
+bool make_tile_plan(const Geometry &g, TilePlan &tp);
+bool backward_uses_workspace(const Geometry &g, const void *value, msda_dtype vt, const float *go,
+                             const float *gv);
+size_t backward_workspace_bytes(const Geometry &g);
 
 // Launchers (each returns a hipError_t from the launch).
 hipError_t launch_reference_points(const Geometry &g, const float *valid_ratios,
@@ -38,8 +60,11 @@ hipError_t launch_softmax(const Geometry &g, const float *logits, float *w, hipS
 hipError_t launch_forward(const Geometry &g, const void *value, msda_dtype vt, const float *loc,
                           const float *attn, float *out, hipStream_t st);
 hipError_t launch_zero_fill(float *p, int64_t n, hipStream_t st);
+// grad_value is fully overwritten unless `accumulate`. `workspace` must hold
+// backward_workspace_bytes(g) bytes when backward_uses_workspace(...) holds.
 hipError_t launch_backward(const Geometry &g, const void *value, msda_dtype vt, const float *loc,
                            const float *attn, const float *grad_out, float *grad_value,
-                           float *grad_loc, float *grad_attn, hipStream_t st);
+                           float *grad_loc, float *grad_attn, void *workspace, bool accumulate,
+                           hipStream_t st);
 
 }  // namespace msda

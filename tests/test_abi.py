@@ -35,9 +35,9 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.msda_abi_version() == 1
+    assert lib.msda_abi_version() == 2
     assert lib.msda_status_string(0) == b"ok"
-    for code in range(-7, 0):
+    for code in range(-8, 0):
         assert lib.msda_status_string(code) not in (b"", b"unknown status")
     assert lib.msda_status_string(-99) == b"unknown status"
 
@@ -70,9 +70,9 @@ def _fwd(lib, sh, value=FAKE, dtype=B.MSDA_F32, loc=FAKE, attn=FAKE, out=FAKE):
     return lib.msda_forward(sh.ptr if sh is not None else None, value, dtype, loc, attn, out, None)
 
 
-def _bwd(lib, sh, flags=0, value=FAKE, grads=(FAKE, FAKE, FAKE, FAKE)):
+def _bwd(lib, sh, flags=0, value=FAKE, grads=(FAKE, FAKE, FAKE, FAKE), ws=None, ws_bytes=0):
     return lib.msda_backward(sh.ptr, value, B.MSDA_F32, FAKE, FAKE, grads[0], grads[1], grads[2], grads[3],
-                             flags, None)
+                             ws, ws_bytes, flags, None)
 
 
 @cpu_only
@@ -173,3 +173,19 @@ def test_empty_batch_or_queries_is_a_no_op(lib):
     sh = _shape()
     sh.c.batch = 0
     assert _bwd(lib, sh, grads=(None, None, None, None)) == B.MSDA_OK
+
+
+@cpu_only
+def test_backward_workspace_size_and_check(lib):
+    """The encoder sizes take the tiled backward: it needs a workspace, and a
+    missing or short one is refused before any device work."""
+    sh = _shape()
+    n = B.msda_backward_workspace_size(sh)
+    # records (4 per sample) dominate: 4 * 4 B * B*Nq*M*L*K
+    assert n >= 16 * 2 * 10687 * 8 * 16
+    assert _bwd(lib, sh) == B.MSDA_E_WORKSPACE
+    assert _bwd(lib, sh, ws=FAKE, ws_bytes=n - 1) == B.MSDA_E_WORKSPACE
+    assert _bwd(lib, sh, ws=ctypes.c_void_p(0x10010), ws_bytes=n) == B.MSDA_E_ALIGN
+    # sizes without a fast path need none
+    assert B.msda_backward_workspace_size(_shape(M=3, D=5)) == 0
+    assert lib.msda_backward_workspace_size(sh.ptr, None) == B.MSDA_E_NULL
