@@ -43,9 +43,10 @@ def parse():
     return p.parse_args()
 
 
-def unique_value_bytes(loc, shapes, B, M, elem):
-    """Bytes of the distinct value rows (b, s, m) that at least one in-map
-    corner touches: what an ideal kernel must read of value."""
+def unique_value_bytes(loc, shapes, B, M, row_bytes):
+    """Bytes of the distinct value rows (b, s, m) -- D channels each -- that
+    at least one in-map corner touches: what an ideal kernel must read of
+    value."""
     import torch
     touched = torch.zeros(B, int((shapes[:, 0] * shapes[:, 1]).sum()), M, dtype=torch.bool, device=loc.device)
     _, Nq, _, L, K, _ = loc.shape
@@ -66,7 +67,7 @@ def unique_value_bytes(loc, shapes, B, M, elem):
                 midx = torch.arange(M, device=loc.device).view(1, 1, M, 1).expand_as(row)
                 touched[bidx[ok], row[ok], midx[ok]] = True
         start += H * W
-    return int(touched.sum().item()) * elem
+    return int(touched.sum().item()) * row_bytes
 
 
 def kernel_source_hash():
@@ -192,7 +193,7 @@ def main():
 
     # algorithmic bytes per launch
     loc = state["loc"]
-    vbytes = unique_value_bytes(loc, shapes.to(dev), B, M, elem)
+    vbytes = unique_value_bytes(loc, shapes.to(dev), B, M, D * elem)
     f32 = 4
     alg = {
         "reference_points": B * L * 2 * f32 + B * Nq * L * 2 * f32,

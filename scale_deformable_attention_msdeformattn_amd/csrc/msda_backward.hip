@@ -14,22 +14,24 @@
 //
 //  1. bin_count   : each workgroup takes a fixed range of queries and counts,
 //                   in an LDS histogram (integer LDS atomics), how many of its
-//                   samples touch each pixel tile of each (head, level).
-//  2. scan_columns: per tile, exclusive prefix of those counts over the
-//                   workgroups of the batch (in place) and the tile total.
-//  3. scan_bases  : exclusive prefix of the tile totals (record base offsets).
-//  4. main        : one wavefront per query (as the forward) computes
+//                   samples touch each pixel tile of each (head, level); each
+//                   non-zero count reserves the workgroup's range inside the
+//                   tile's record list with one global atomic add.
+//  2. scan_bases  : exclusive prefix of the tile totals (record base offsets).
+//  3. main        : one wavefront per query (as the forward) computes
 //                   grad_attn and grad_loc, and writes each sample's index into
 //                   the record list of every tile it touches (positions from
 //                   an LDS cursor per tile: no global atomics).
-//  5. tile_accum  : one workgroup per tile sorts its records by cell in LDS,
+//  4. tile_accum  : one workgroup per tile sorts its records by cell in LDS,
 //                   then every pixel of the tile gathers A*w*G over the samples
 //                   of its four neighbouring cells in registers and is written
 //                   once with a plain store. Every pixel of grad_value belongs
 //                   to exactly one tile, so no zero fill is needed.
 //
 // Tiles are sized on the host from the expected sample density so that one
-// tile's records fit one LDS chunk; denser tiles take several chunks in turn.
+// tile's records fit one LDS chunk; denser tiles take several chunks in turn,
+// and the densest (a few pixels with many records) skip the sort and split
+// their records over several workgroups whose partials meet in atomics.
 // Shapes outside the fast path use one thread per (b, q, m) with float atomics.
 #include <algorithm>
 
@@ -47,6 +49,9 @@ constexpr int kTilePix = 32;             // pixels per tile
 constexpr int kTileCells = 2 * kWave;    // cells per tile (the tile plus one row and column of halo)
 constexpr int kTaskSlots = 4;            // (cell, split) tasks per lane group in tile_accum
 constexpr int kBatch = 8;                // records in flight per task
+constexpr int kDirectPix = 4;            // tiles this small skip the per-cell sort
+constexpr int kDirectRecords = 768;      // records per workgroup in direct mode
+constexpr int kMaxSplit = 64;            // workgroups sharing one direct-mode tile
 
 struct LevelRec {
     float Wf, Hf;
@@ -109,12 +114,27 @@ __device__ __forceinline__ bool sample_cell(float2 u, float Wf, float Hf, int &c
 
 constexpr int kBinThreads = 1024;
 
+// Clear the per-tile record totals before bin_count adds into them.
+__global__ void __launch_bounds__(kBlock) clear_totals_kernel(int nkeys, uint32_t *__restrict__ totals)
+{
+    const int i = blockIdx.x * kBlock + threadIdx.x;
+    if (i < nkeys) totals[i] = 0;
+}
+
+// Workgroup w takes queries [q0, q1) of batch b. One thread per (query, head,
+// level) block of K samples: it counts, per distinct tile, how many of the
+// block's samples touch the tile, and adds that into an LDS histogram (one
+// add per distinct tile, so the K samples of a block do not contend). Then
+// every non-zero (w, tile) count reserves its range of the tile's record list
+// with one global atomic add; the returned offset is stored at
+// offsets[w][tile] (entries with a zero count are never read).
 template <int M, int L, int K>
 __global__ void __launch_bounds__(kBinThreads)
-bin_count_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, uint32_t *__restrict__ counts)
+bin_count_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, uint32_t *__restrict__ offsets,
+                 uint32_t *__restrict__ totals)
 {
     constexpr int LK = L * K;
-    constexpr int NS = M * LK;
+    constexpr int NB = M * L;  // blocks per query
     extern __shared__ uint32_t s_hist[];  // [M * tpb]
     __shared__ LevelRec s_lv[L];
     const int nkeys = M * tp.tpb;
@@ -128,82 +148,103 @@ bin_count_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, uint32
     const int b = w / tp.wpb;
     const int q0 = (w - b * tp.wpb) * tp.qpw;
     const int q1 = min(q0 + tp.qpw, g.Nq);
-    const int64_t s_begin = ((int64_t)b * g.Nq + q0) * NS;
-    const int n = (q1 - q0) * NS;
-    for (int i = threadIdx.x; i < n; i += kBinThreads) {
-        const int m = (i / LK) % M;
-        const int l = (i / K) % L;
+    const int64_t blk0 = ((int64_t)b * g.Nq + q0) * NB;  // first (query, head, level) block
+    const int nblk = (q1 - q0) * NB;
+    for (int i = threadIdx.x; i < nblk; i += kBinThreads) {
+        const int m = (i / L) % M;
+        const int l = i % L;
         const LevelRec lv = s_lv[l];
-        int cx, cy;
-        float fx, fy;
-        if (!sample_cell(loc[s_begin + i], lv.Wf, lv.Hf, cx, cy, fx, fy)) continue;
-        const SampleTiles st = sample_tiles(tp, l, lv.W, (int)lv.Hf, cx, cy);
+        const int H = (int)lv.Hf;
+        const float2 *u = loc + (blk0 + i) * K;
+        int tiles[K][4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (st.t[j] >= 0) atomicAdd(&s_hist[m * tp.tpb + st.t[j]], 1u);
+        for (int k = 0; k < K; ++k) {
+            int cx, cy;
+            float fx, fy;
+            const bool in = sample_cell(u[k], lv.Wf, lv.Hf, cx, cy, fx, fy);
+            const SampleTiles st = sample_tiles(tp, l, lv.W, H, cx, cy);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) tiles[k][j] = in ? st.t[j] : -1;
+        }
+        // one add per distinct tile: a (k, j) entry adds only if no earlier
+        // entry of the block holds the same tile; it adds the number of
+        // samples of the block holding that tile
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int t = tiles[k][j];
+                if (t < 0) continue;
+                bool first = true;
+#pragma unroll
+                for (int k2 = 0; k2 < K; ++k2)
+#pragma unroll
+                    for (int j2 = 0; j2 < 4; ++j2)
+                        if ((k2 < k || (k2 == k && j2 < j)) && tiles[k2][j2] == t) first = false;
+                if (!first) continue;
+                uint32_t cnt = 0;
+#pragma unroll
+                for (int k2 = 0; k2 < K; ++k2) {
+                    bool has = false;
+#pragma unroll
+                    for (int j2 = 0; j2 < 4; ++j2) has |= tiles[k2][j2] == t;
+                    cnt += has ? 1u : 0u;
+                }
+                atomicAdd(&s_hist[m * tp.tpb + t], cnt);
+            }
     }
     __syncthreads();
-    uint32_t *row = counts + (int64_t)w * nkeys;
-    for (int i = threadIdx.x; i < nkeys; i += kBinThreads) row[i] = s_hist[i];
-}
-
-// ------------------------------------------------------------- 2. scan_columns
-
-// One wavefront per key (b, m, tile): exclusive prefix over the workgroups of
-// batch b, in place, and the key's total.
-__global__ void __launch_bounds__(kBlock)
-scan_columns_kernel(int nkeys_per_batch, int wpb, int nkeys, uint32_t *__restrict__ counts,
-                    uint32_t *__restrict__ totals)
-{
-    const int key = blockIdx.x * kWaves + (int)(threadIdx.x / kWave);
-    const int lane = threadIdx.x % kWave;
-    if (key >= nkeys) return;
-    const int b = key / nkeys_per_batch;
-    const int local = key - b * nkeys_per_batch;
-    uint32_t carry = 0;
-    for (int w0 = 0; w0 < wpb; w0 += kWave) {
-        const int w = w0 + lane;
-        uint32_t *p = counts + ((int64_t)(b * wpb + w)) * nkeys_per_batch + local;
-        const uint32_t v = w < wpb ? *p : 0u;
-        uint32_t incl = v;
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-            const uint32_t t = __shfl_up(incl, o, kWave);
-            if (lane >= o) incl += t;
-        }
-        if (w < wpb) *p = carry + incl - v;
-        carry += __shfl(incl, kWave - 1, kWave);
+    uint32_t *row = offsets + (int64_t)w * nkeys;
+    uint32_t *tot = totals + (int64_t)b * nkeys;
+    for (int i = threadIdx.x; i < nkeys; i += kBinThreads) {
+        const uint32_t c = s_hist[i];
+        if (c) row[i] = atomicAdd(&tot[i], c);
     }
-    if (lane == 0) totals[key] = carry;
 }
 
-// --------------------------------------------------------------- 3. scan_bases
+// --------------------------------------------------------------- 2. scan_bases
 
-// One workgroup: exclusive prefix of the key totals.
+// One workgroup: exclusive prefix of the key totals (staged through LDS in
+// slices of kScanSlice keys).
+constexpr int kScanSlice = 8192;
 __global__ void __launch_bounds__(1024)
 scan_bases_kernel(int nkeys, const uint32_t *__restrict__ totals, uint32_t *__restrict__ bases)
 {
+    __shared__ uint32_t s_v[kScanSlice];
     __shared__ uint32_t s_part[1024];
-    const int per = (nkeys + 1023) / 1024;
-    const int i0 = threadIdx.x * per;
-    uint32_t sum = 0;
-    for (int i = i0; i < min(i0 + per, nkeys); ++i) sum += totals[i];
-    s_part[threadIdx.x] = sum;
-    __syncthreads();
-    for (int o = 1; o < 1024; o <<= 1) {
-        const uint32_t t = threadIdx.x >= (unsigned)o ? s_part[threadIdx.x - o] : 0u;
+    constexpr int per = kScanSlice / 1024;
+    uint32_t carry = 0;
+    for (int k0 = 0; k0 < nkeys; k0 += kScanSlice) {
+        for (int i = threadIdx.x; i < kScanSlice; i += 1024) s_v[i] = k0 + i < nkeys ? totals[k0 + i] : 0u;
         __syncthreads();
-        s_part[threadIdx.x] += t;
+        uint32_t sum = 0;
+#pragma unroll
+        for (int j = 0; j < per; ++j) sum += s_v[threadIdx.x * per + j];
+        s_part[threadIdx.x] = sum;
         __syncthreads();
-    }
-    uint32_t run = s_part[threadIdx.x] - sum;  // exclusive
-    for (int i = i0; i < min(i0 + per, nkeys); ++i) {
-        bases[i] = run;
-        run += totals[i];
+        for (int o = 1; o < 1024; o <<= 1) {
+            const uint32_t t = threadIdx.x >= (unsigned)o ? s_part[threadIdx.x - o] : 0u;
+            __syncthreads();
+            s_part[threadIdx.x] += t;
+            __syncthreads();
+        }
+        uint32_t run = carry + s_part[threadIdx.x] - sum;
+#pragma unroll
+        for (int j = 0; j < per; ++j) {
+            const int i = threadIdx.x * per + j;
+            const uint32_t v = s_v[i];
+            s_v[i] = run;
+            run += v;
+        }
+        carry += s_part[1023];
+        __syncthreads();
+        for (int i = threadIdx.x; i < kScanSlice; i += 1024)
+            if (k0 + i < nkeys) bases[k0 + i] = s_v[i];
+        __syncthreads();
     }
 }
 
-// --------------------------------------------------------------------- 4. main
+// --------------------------------------------------------------------- 3. main
 
 // Waves per workgroup of the main kernel: as many as fit about 104 KB of LDS.
 template <int M, int L, int K> struct MainWaves {
@@ -342,7 +383,7 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
     }
 }
 
-// --------------------------------------------------------------- 5. tile_accum
+// --------------------------------------------------------------- 4. tile_accum
 
 // One workgroup per tile (b, m, level, tile). Its records are counting-sorted
 // by cell in LDS; then each lane group (LG lanes, 4 channels each, D = 4*LG)
@@ -360,7 +401,8 @@ tile_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, const
 {
     constexpr int NG = kBlock / LG;
     // (pixel, role, split) slots in use: npix*4 when cells >= NG, else at most 4*NG
-    constexpr int kPartSlots = 4 * (kTilePix > NG ? kTilePix : NG);
+    constexpr int kPartSlots0 = 4 * (kTilePix > NG ? kTilePix : NG);
+    constexpr int kPartSlots = kPartSlots0 > kDirectPix * NG ? kPartSlots0 : kDirectPix * NG;
     __shared__ uint32_t s_start[kTileCells + 1];
     __shared__ uint32_t s_cur[kTileCells];
     __shared__ float4 s_pay[kChunk];       // (fx, fy, A, bits(b*Nq+q))
@@ -370,17 +412,19 @@ tile_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, const
 
     // consecutive keys (same batch and head, neighbouring tiles) read G rows of
     // neighbouring queries: give each XCD (private L2) a contiguous key range
-    const int key = (int)xcd_tile(blockIdx.x, gridDim.x);
-    const int nkb = g.M * tp.tpb;
-    if (key >= g.B * nkb) return;
-    const int b = key / nkb;
-    const int m = (key - b * nkb) / tp.tpb;
-    const int tile = key - b * nkb - m * tp.tpb;
+    // work item (b, m, level, tile, chunk); consecutive items (same batch and
+    // head, neighbouring tiles) read G rows of neighbouring queries, so each
+    // XCD (private L2) gets a contiguous item range
+    const int item = (int)xcd_tile(blockIdx.x, gridDim.x);
+    if (item >= g.B * g.M * tp.ipb) return;
+    const int bm = item / tp.ipb;
+    const int b = bm / g.M, m = bm - (bm / g.M) * g.M;
+    const int r_in = item - bm * tp.ipb;
     int l = 0;
 #pragma unroll
     for (int i = 1; i < MSDA_MAX_LEVELS; ++i)
-        if (i < g.L && tile >= tp.tbase[i]) l = i;
-    int th = 1, tw = 1, ntw = 1, tb = 0, W = 1, H = 1, lstart = 0;
+        if (i < g.L && r_in >= tp.ibase[i]) l = i;
+    int th = 1, tw = 1, ntw = 1, tb = 0, nch = 1, ib = 0, W = 1, H = 1, lstart = 0;
 #pragma unroll
     for (int i = 0; i < MSDA_MAX_LEVELS; ++i)
         if (i == l) {
@@ -388,11 +432,15 @@ tile_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, const
             tw = tp.tw[i];
             ntw = tp.ntw[i];
             tb = tp.tbase[i];
+            nch = tp.nchunk[i];
+            ib = tp.ibase[i];
             W = g.lv.W[i];
             H = g.lv.H[i];
             lstart = g.lv.start[i];
         }
-    const int t_in = tile - tb;
+    const int t_in = (r_in - ib) / nch;
+    const int chunk = r_in - ib - t_in * nch;
+    const int key = bm * tp.tpb + tb + t_in;
     const int ty = t_in / ntw, tx = t_in - ty * ntw;
     const float Wf = (float)W, Hf = (float)H;
     const int r0 = ty * th, r1 = min(r0 + th, H);
@@ -407,12 +455,99 @@ tile_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, const
     const uint32_t nsamples = (uint32_t)g.samples();
     const int grp = threadIdx.x / LG;
     const int lig = threadIdx.x % LG;
+    uint32_t rbeg = bases[key];
+    uint32_t rtot = totals[key];
+
+    if (npix <= kDirectPix) {
+        if (nch > 1) {  // this workgroup's share of the tile's records
+            const uint32_t per = (rtot + nch - 1) / nch;
+            const uint32_t lo = min(rtot, per * chunk);
+            rbeg += lo;
+            rtot = min(rtot - lo, per);
+        }
+        // Direct mode for small (dense) tiles: no sort. Lane groups stride over
+        // the records, kBatch at a time, and keep one accumulator per pixel of
+        // the tile; a record adds A*w to each pixel it is a corner of.
+        float4 acc[kDirectPix];
+#pragma unroll
+        for (int p = 0; p < kDirectPix; ++p) acc[p] = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (uint32_t i0 = grp; i0 < rtot; i0 += NG * kBatch) {
+            uint32_t sidx[kBatch];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                const uint32_t i = i0 + j * NG;
+                sidx[j] = i < rtot ? records[rbeg + i] : nsamples;
+            }
+            float2 u[kBatch];
+            float a[kBatch];
+            float4 gv[kBatch];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                const bool ok = sidx[j] < nsamples;  // see the chunked path below
+                u[j] = ok ? loc[sidx[j]] : make_float2(-1e30f, -1e30f);
+                a[j] = ok ? attn[sidx[j]] : 0.0f;
+                const uint32_t bq = ok ? sidx[j] / (uint32_t)NS : 0u;
+                gv[j] = ok ? grad_out[((int64_t)bq * g.M + m) * LG + lig] : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                int cx, cy;
+                float fx, fy;
+                const bool in = sample_cell(u[j], Wf, Hf, cx, cy, fx, fy);
+#pragma unroll
+                for (int p = 0; p < kDirectPix; ++p) {
+                    // pixel (py, px) of the tile is corner (px - (cx - c0), py - (cy - r0)) of the cell
+                    const int py = r0 + p / pw, px = c0 + p % pw;
+                    const int dx = px - cx, dy = py - cy;
+                    const bool hit = in && p < npix && (dx == 0 || dx == 1) && (dy == 0 || dy == 1);
+                    const float w = hit ? a[j] * (dx ? fx : 1.0f - fx) * (dy ? fy : 1.0f - fy) : 0.0f;
+                    acc[p].x = __builtin_fmaf(w, gv[j].x, acc[p].x);
+                    acc[p].y = __builtin_fmaf(w, gv[j].y, acc[p].y);
+                    acc[p].z = __builtin_fmaf(w, gv[j].z, acc[p].z);
+                    acc[p].w = __builtin_fmaf(w, gv[j].w, acc[p].w);
+                }
+            }
+        }
+        // reduce over the lane groups: slots [group * kDirectPix + p]
+#pragma unroll
+        for (int p = 0; p < kDirectPix; ++p) s_part[grp * kDirectPix + p][lig] = acc[p];
+        __syncthreads();
+        if (grp < npix) {
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int q = 0; q < NG; ++q) {
+                const float4 t = s_part[q * kDirectPix + grp][lig];
+                v.x += t.x;
+                v.y += t.y;
+                v.z += t.z;
+                v.w += t.w;
+            }
+            const int py = r0 + grp / pw, px = c0 + grp % pw;
+            float4 *dst = grad_value + (((int64_t)b * g.S + lstart + (int64_t)py * W + px) * g.M + m) * LG + lig;
+            if (nch > 1) {
+                // several workgroups share this tile: add the partial into the
+                // row (zeroed beforehand unless accumulating)
+                float *d = reinterpret_cast<float *>(dst);
+                atomicAdd(d + 0, v.x);
+                atomicAdd(d + 1, v.y);
+                atomicAdd(d + 2, v.z);
+                atomicAdd(d + 3, v.w);
+            } else {
+                if (accumulate) {
+                    const float4 o = *dst;
+                    v.x += o.x;
+                    v.y += o.y;
+                    v.z += o.z;
+                    v.w += o.w;
+                }
+                *dst = v;
+            }
+        }
+        return;
+    }
 
     for (int i = threadIdx.x; i < npix * 4 * S * LG; i += kBlock)
         s_part[i / LG][i % LG] = make_float4(0.f, 0.f, 0.f, 0.f);
 
-    const uint32_t rbeg = bases[key];
-    const uint32_t rtot = totals[key];
     for (uint32_t c0r = 0; c0r < rtot; c0r += kChunk) {
         const int n = (int)min((uint32_t)kChunk, rtot - c0r);
         for (int i = threadIdx.x; i < ncells; i += kBlock) s_cur[i] = 0;
@@ -531,6 +666,25 @@ tile_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, const
     }
 }
 
+// Zero the grad_value rows of the levels whose tiles are shared by several
+// workgroups (their partials are added with atomics). One thread per float4.
+__global__ void __launch_bounds__(kBlock)
+zero_split_levels_kernel(Geometry g, TilePlan tp, float4 *__restrict__ grad_value)
+{
+    const int64_t row4 = (int64_t)g.M * g.D / 4;  // float4s per value row
+    int64_t t = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    for (int l = 0; l < g.L; ++l) {
+        if (tp.nchunk[l] <= 1) continue;
+        const int64_t n = (int64_t)g.lv.H[l] * g.lv.W[l] * row4;
+        if (t < (int64_t)g.B * n) {
+            const int64_t b = t / n, r = t - b * n;
+            grad_value[((int64_t)b * g.S + g.lv.start[l]) * row4 + r] = make_float4(0.f, 0.f, 0.f, 0.f);
+            return;
+        }
+        t -= (int64_t)g.B * n;
+    }
+}
+
 // ------------------------------------------------------------ generic fallback
 
 template <typename VT>
@@ -633,10 +787,10 @@ hipError_t launch_fast(const Geometry &g, const TilePlan &tp, const void *value,
     const int nwg = g.B * tp.wpb;
     const int nkeys = g.B * nkb;
     const size_t hist_bytes = (size_t)nkb * 4;
+    hipLaunchKernelGGL(clear_totals_kernel, dim3((nkeys + kBlock - 1) / kBlock), dim3(kBlock), 0, st, nkeys,
+                       ws.totals);
     hipLaunchKernelGGL((bin_count_kernel<M, L, K>), dim3(nwg), dim3(kBinThreads), hist_bytes, st, g, tp,
-                       reinterpret_cast<const float2 *>(loc), ws.counts);
-    hipLaunchKernelGGL(scan_columns_kernel, dim3((nkeys + kWaves - 1) / kWaves), dim3(kBlock), 0, st, nkb,
-                       tp.wpb, nkeys, ws.counts, ws.totals);
+                       reinterpret_cast<const float2 *>(loc), ws.counts, ws.totals);
     hipLaunchKernelGGL(scan_bases_kernel, dim3(1), dim3(1024), 0, st, nkeys, ws.totals, ws.bases);
     const uint32_t grid = round_up8((uint32_t)nwg);
     hipLaunchKernelGGL((backward_c256_kernel<VT, M, L, K>), dim3(grid), dim3(MainWaves<M, L, K>::kValue * kWave),
@@ -645,7 +799,16 @@ hipError_t launch_fast(const Geometry &g, const TilePlan &tp, const void *value,
                        reinterpret_cast<const float4 *>(go), reinterpret_cast<float2 *>(gl), ga, ws.counts,
                        ws.bases, ws.records, grid);
     constexpr int LG = 256 / M / 4;
-    hipLaunchKernelGGL((tile_accum_kernel<LG>), dim3(round_up8((uint32_t)nkeys)), dim3(kBlock), 0, st, g, tp,
+    if (!accumulate) {
+        int64_t n = 0;
+        for (int l = 0; l < g.L; ++l)
+            if (tp.nchunk[l] > 1) n += (int64_t)g.B * g.lv.H[l] * g.lv.W[l] * g.M * g.D / 4;
+        if (n > 0)
+            hipLaunchKernelGGL(zero_split_levels_kernel, dim3((unsigned)((n + kBlock - 1) / kBlock)), dim3(kBlock), 0,
+                               st, g, tp, reinterpret_cast<float4 *>(gv));
+    }
+    const uint32_t items = (uint32_t)(g.B * g.M * tp.ipb);
+    hipLaunchKernelGGL((tile_accum_kernel<LG>), dim3(round_up8(items)), dim3(kBlock), 0, st, g, tp,
                        reinterpret_cast<const float2 *>(loc), attn, reinterpret_cast<const float4 *>(go),
                        reinterpret_cast<float4 *>(gv), ws.records, ws.bases, ws.totals, accumulate ? 1 : 0);
     return hipGetLastError();
@@ -712,7 +875,7 @@ bool make_tile_plan(const Geometry &g, TilePlan &tp)
     const double target = 0.75 * kChunk;
     // every (cell, split) task needs a slot: cells <= kTaskSlots * lane groups
     const int max_cells = std::min(kTileCells, kTaskSlots * (kBlock / (g.D / 4)));
-    int base = 0;
+    int base = 0, ibase = 0;
     for (int l = 0; l < g.L; ++l) {
         const int H = g.lv.H[l], W = g.lv.W[l];
         const double per_cell = (double)g.Nq * g.K / ((double)H * W);
@@ -729,14 +892,33 @@ bool make_tile_plan(const Geometry &g, TilePlan &tp)
                     bw = tw;
                 }
             }
+        if (barea <= kDirectPix) {
+            // too dense for the sorted path to pay off: a 2x2 tile in direct
+            // mode (no record limit) duplicates fewer records than 1x1
+            bt = std::min(H, 2);
+            bw = std::min(W, 2);
+        }
         tp.th[l] = bt;
         tp.tw[l] = bw;
         tp.ntw[l] = (W + bw - 1) / bw;
         tp.tbase[l] = base;
-        base += ((H + bt - 1) / bt) * tp.ntw[l];
+        const int ntiles = ((H + bt - 1) / bt) * tp.ntw[l];
+        base += ntiles;
+        // direct-mode tiles share their records among enough workgroups to
+        // give each about kDirectRecords of them
+        int nch = 1;
+        if (bt * bw <= kDirectPix) {
+            const double recs = per_cell * (bt + 1) * (bw + 1);
+            nch = (int)std::min<double>(kMaxSplit, std::max(1.0, std::ceil(recs / kDirectRecords)));
+        }
+        tp.nchunk[l] = nch;
+        tp.ibase[l] = ibase;
+        ibase += ntiles * nch;
     }
-    for (int l = g.L; l < MSDA_MAX_LEVELS; ++l) tp.th[l] = tp.tw[l] = tp.ntw[l] = 1, tp.tbase[l] = base;
+    for (int l = g.L; l < MSDA_MAX_LEVELS; ++l)
+        tp.th[l] = tp.tw[l] = tp.ntw[l] = tp.nchunk[l] = 1, tp.tbase[l] = base, tp.ibase[l] = ibase;
     tp.tpb = base;
+    tp.ipb = ibase;
     tp.qpw = kQueriesPerGroup;
     tp.wpb = (g.Nq + tp.qpw - 1) / tp.qpw;
     // the per-workgroup histogram / cursors live in LDS; record indices are 32-bit

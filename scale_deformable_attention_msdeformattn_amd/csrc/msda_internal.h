@@ -38,6 +38,9 @@ struct TilePlan {
     int32_t tw[MSDA_MAX_LEVELS];
     int32_t ntw[MSDA_MAX_LEVELS];
     int32_t tbase[MSDA_MAX_LEVELS];
+    int32_t nchunk[MSDA_MAX_LEVELS];  // workgroups sharing one tile's records
+    int32_t ibase[MSDA_MAX_LEVELS];   // first work item of the level within (batch, head)
+    int32_t ipb;  // work items (tile, chunk) per (batch, head)
     int32_t tpb;  // tiles per (batch, head)
     int32_t qpw;  // queries per workgroup
     int32_t wpb;  // workgroups per batch

@@ -51,27 +51,99 @@ reference_points_kernel(Geometry g, const float *__restrict__ vr, const float *_
 }
 
 // loc = ref + offset_px / (W_l, H_l) (walkthrough page, "encoder"; paper
-// notes, "Key code"). One thread per (b, q, m).
+// notes, "Key code"). One thread per (b, q, m, l): its K (x, y) pairs are
+// contiguous, so consecutive threads read and write consecutive 8K-byte runs.
+template <int K>
 __global__ void __launch_bounds__(kBlock)
-sampling_locations_kernel(Geometry g, const float2 *__restrict__ ref,
-                          const float2 *__restrict__ off, float2 *__restrict__ loc)
+sampling_locations_kernel(Geometry g, const float2 *__restrict__ ref, const float2 *__restrict__ off,
+                          float2 *__restrict__ loc)
 {
-    const int64_t row = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    if (row >= (int64_t)g.B * g.Nq * g.M) return;
-    const int64_t bq = row / g.M;
-    for (int l = 0; l < g.L; ++l) {
-        const float2 r = ref[bq * g.L + l];
-        const float Wf = (float)g.lv.W[l], Hf = (float)g.lv.H[l];
-        const int64_t base = (row * g.L + l) * g.K;
-        for (int k = 0; k < g.K; ++k) {
-            const float2 o = off[base + k];
-            loc[base + k] = make_float2(r.x + o.x / Wf, r.y + o.y / Hf);
+    const int64_t t = (int64_t)blockIdx.x * kBlock + threadIdx.x;  // (b, q, m, l)
+    if (t >= (int64_t)g.B * g.Nq * g.M * g.L) return;
+    const int l = (int)(t % g.L);
+    const int64_t bq = t / ((int64_t)g.L * g.M);
+    int W = 1, H = 1;
+#pragma unroll
+    for (int i = 0; i < MSDA_MAX_LEVELS; ++i)
+        if (i == l) {
+            W = g.lv.W[i];
+            H = g.lv.H[i];
+        }
+    const float Wf = (float)W, Hf = (float)H;
+    const float2 r = ref[bq * g.L + l];
+    const float2 *o = off + t * K;
+    float2 *out = loc + t * K;
+    if constexpr (K % 2 == 0) {
+        const float4 *o4 = reinterpret_cast<const float4 *>(o);
+        float4 *out4 = reinterpret_cast<float4 *>(out);
+#pragma unroll
+        for (int k = 0; k < K / 2; ++k) {
+            const float4 v = o4[k];
+            out4[k] = make_float4(r.x + v.x / Wf, r.y + v.y / Hf, r.x + v.z / Wf, r.y + v.w / Hf);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const float2 v = o[k];
+            out[k] = make_float2(r.x + v.x / Wf, r.y + v.y / Hf);
         }
     }
 }
 
+// Any K: one thread per sample.
+__global__ void __launch_bounds__(kBlock)
+sampling_locations_any_kernel(Geometry g, const float2 *__restrict__ ref, const float2 *__restrict__ off,
+                              float2 *__restrict__ loc)
+{
+    const int64_t s = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (s >= g.samples()) return;
+    const int64_t row = s / g.K;  // (b, q, m, l)
+    const int l = (int)(row % g.L);
+    const int64_t bq = row / ((int64_t)g.L * g.M);
+    int W = 1, H = 1;
+#pragma unroll
+    for (int i = 0; i < MSDA_MAX_LEVELS; ++i)
+        if (i == l) {
+            W = g.lv.W[i];
+            H = g.lv.H[i];
+        }
+    const float2 r = ref[bq * g.L + l];
+    const float2 v = off[s];
+    loc[s] = make_float2(r.x + v.x / (float)W, r.y + v.y / (float)H);
+}
+
 // Softmax over the L*K logits of one (b, q, m) (paper notes, "Insight 2": the
-// weights of a query and head sum to 1 over all levels and points).
+// weights of a query and head sum to 1 over all levels and points). One
+// thread per row; rows of N (a multiple of 4) use 16-byte loads and stores.
+template <int N>
+__global__ void __launch_bounds__(kBlock)
+softmax_vec_kernel(int64_t rows, const float4 *x, float4 *y)  // y may alias x
+{
+    const int64_t row = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (row >= rows) return;
+    float v[N];
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {
+        const float4 t = x[row * (N / 4) + i];
+        v[4 * i + 0] = t.x;
+        v[4 * i + 1] = t.y;
+        v[4 * i + 2] = t.z;
+        v[4 * i + 3] = t.w;
+    }
+    float mx = v[0];
+#pragma unroll
+    for (int i = 1; i < N; ++i) mx = fmaxf(mx, v[i]);
+    float sum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        v[i] = expf(v[i] - mx);
+        sum += v[i];
+    }
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i)
+        y[row * (N / 4) + i] = make_float4(v[4 * i] / sum, v[4 * i + 1] / sum, v[4 * i + 2] / sum, v[4 * i + 3] / sum);
+}
+
 __global__ void __launch_bounds__(kBlock)
 softmax_kernel(int64_t rows, int n, const float *x, float *y)  // y may alias x
 {
@@ -117,17 +189,40 @@ hipError_t launch_reference_points(const Geometry &g, const float *vr, const flo
 hipError_t launch_sampling_locations(const Geometry &g, const float *ref, const float *off,
                                      float *loc, hipStream_t st)
 {
-    hipLaunchKernelGGL(sampling_locations_kernel, dim3(blocks_for(g.queries() * g.M)), dim3(kBlock),
-                       0, st, g, reinterpret_cast<const float2 *>(ref),
-                       reinterpret_cast<const float2 *>(off), reinterpret_cast<float2 *>(loc));
+    const auto r = reinterpret_cast<const float2 *>(ref);
+    const auto o = reinterpret_cast<const float2 *>(off);
+    const auto d = reinterpret_cast<float2 *>(loc);
+    const bool a16 = (reinterpret_cast<uintptr_t>(off) % 16) == 0 && (reinterpret_cast<uintptr_t>(loc) % 16) == 0;
+    const unsigned rows = blocks_for(g.queries() * g.M * g.L);
+    if (g.K == 4 && a16)
+        hipLaunchKernelGGL(sampling_locations_kernel<4>, dim3(rows), dim3(kBlock), 0, st, g, r, o, d);
+    else if (g.K == 2 && a16)
+        hipLaunchKernelGGL(sampling_locations_kernel<2>, dim3(rows), dim3(kBlock), 0, st, g, r, o, d);
+    else if (g.K == 8 && a16)
+        hipLaunchKernelGGL(sampling_locations_kernel<8>, dim3(rows), dim3(kBlock), 0, st, g, r, o, d);
+    else
+        hipLaunchKernelGGL(sampling_locations_any_kernel, dim3(blocks_for(g.samples())), dim3(kBlock), 0, st, g, r,
+                           o, d);
     return hipGetLastError();
 }
 
 hipError_t launch_softmax(const Geometry &g, const float *logits, float *w, hipStream_t st)
 {
     const int64_t rows = g.queries() * g.M;
-    hipLaunchKernelGGL(softmax_kernel, dim3(blocks_for(rows)), dim3(kBlock), 0, st, rows, g.L * g.K,
-                       logits, w);
+    const int n = g.L * g.K;
+    const bool a16 = (reinterpret_cast<uintptr_t>(logits) % 16) == 0 && (reinterpret_cast<uintptr_t>(w) % 16) == 0;
+    const auto x4 = reinterpret_cast<const float4 *>(logits);
+    const auto y4 = reinterpret_cast<float4 *>(w);
+    if (a16 && n == 16)
+        hipLaunchKernelGGL(softmax_vec_kernel<16>, dim3(blocks_for(rows)), dim3(kBlock), 0, st, rows, x4, y4);
+    else if (a16 && n == 32)
+        hipLaunchKernelGGL(softmax_vec_kernel<32>, dim3(blocks_for(rows)), dim3(kBlock), 0, st, rows, x4, y4);
+    else if (a16 && n == 8)
+        hipLaunchKernelGGL(softmax_vec_kernel<8>, dim3(blocks_for(rows)), dim3(kBlock), 0, st, rows, x4, y4);
+    else if (a16 && n == 4)
+        hipLaunchKernelGGL(softmax_vec_kernel<4>, dim3(blocks_for(rows)), dim3(kBlock), 0, st, rows, x4, y4);
+    else
+        hipLaunchKernelGGL(softmax_kernel, dim3(blocks_for(rows)), dim3(kBlock), 0, st, rows, n, logits, w);
     return hipGetLastError();
 }
 
