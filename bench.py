@@ -4,21 +4,32 @@
 One step = one pass of the whole hot path over one batch of the encoder
 workload (B=2, M=8, D=32, L=4 levels 76x106/38x53/19x27/8x13, S=Nq=10687, K=4,
 fp32): reference points -> sampling locations -> L*K softmax -> core forward ->
-grad_value zero fill -> core backward, every kernel from libmsda.so, inputs
+core backward (grad_value, grad_sampling_locations, grad_attention_weights),
+every kernel from libmsda.so, inputs
 (seeded synthetic draws) resident in HBM before the timed region.
 
-Prints ONE JSON line. ``value`` is queries/s of that fwd+bwd step; the
-``roofline`` object is for the kernel with the largest share of the step, with
-its algorithmic bytes divided by its average duration measured here with HIP
-events on the stream it runs on; ``cpu_baseline`` is the fp64 oracle on the
-host. Per-kernel and forward-only figures are included as extra keys.
+Prints ONE JSON line. ``value`` is queries/s of that fwd+bwd step (a HIP graph
+of the step replayed K times). ``kernels`` gives every GPU kernel's average
+duration, timed live with HIP event pairs that the library records around each
+launch on the launch's own stream (msda_timing_*), and its algorithmic bytes
+per launch; ``roofline`` is for the kernel with the largest share of the step.
+``cpu_baseline`` is the fp64 oracle on the host.
 
-    python bench.py [--steps K] [--warmup W] [--workload encoder]
+    python bench.py [--steps K] [--warmup W] [--workload encoder_backward]
+
+Counter runs for the HBM traffic of the kernels (rocprofv3 --pmc, one counter
+per run) use ``--eager``; ``--copy-mib N`` runs only a plain elementwise copy
+of N MiB (the calibration kernel for FETCH_SIZE / WRITE_SIZE), and
+``--ingest-counters DIR [--copy-mib N]`` turns the four counter runs under DIR
+(fetch/, write/, copy_fetch/, copy_write/) into profiles/traffic.json.
 """
 import argparse
+import csv
+import glob
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -28,6 +39,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD's published peak
 METRIC = "MSDeformAttn fwd/bwd queries/s and effective HBM GB/s (% of peak), encoder shape"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+COPY_MIB_DEFAULT = 256
 
 
 def parse():
@@ -39,7 +51,10 @@ def parse():
                    help="workload name (the step always runs fwd+bwd)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP graph replay")
-    p.add_argument("--only", default=None, help="time only this kernel in a loop (for profiling runs)")
+    p.add_argument("--copy-mib", type=int, default=0,
+                   help="only run a plain copy of this many MiB, 5 times (counter calibration)")
+    p.add_argument("--ingest-counters", default=None, metavar="DIR",
+                   help="write profiles/traffic.json from rocprofv3 --pmc runs under DIR and exit")
     return p.parse_args()
 
 
@@ -70,12 +85,42 @@ def unique_value_bytes(loc, shapes, B, M, row_bytes):
     return int(touched.sum().item()) * row_bytes
 
 
+def algorithmic_bytes(B, M, D, Nq, S, L, K, vbytes):
+    """Bytes each kernel must move at the least (read + write, fp32 unless
+    noted), per launch. `vbytes` = the distinct value rows the samples touch.
+    Scratch-only kernels of the backward (binning, scans, clears) count the
+    op's own arrays they read, not their workspace traffic."""
+    f32 = 4
+    samples = B * Nq * M * L * K
+    rows = B * Nq * M * D * f32          # output / grad_output
+    grad_value = B * S * M * D * f32
+    return {
+        "reference_points_kernel": B * L * 2 * f32 + B * Nq * L * 2 * f32,
+        "sampling_locations_kernel": B * Nq * L * 2 * f32 + 2 * samples * 2 * f32,
+        "softmax_vec_kernel": 2 * samples * f32,
+        "forward_c256_kernel": vbytes + samples * 3 * f32 + rows,
+        "zero_fill_kernel": grad_value,
+        "clear_totals_kernel": 0,
+        "bin_count_kernel": samples * 2 * f32,
+        "scan_bases_kernel": 0,
+        # value rows, loc, A, grad_output in; grad_loc, grad_A out
+        "backward_c256_kernel": vbytes + samples * 3 * f32 + rows + samples * 3 * f32,
+        # grad_output, loc, A in; grad_value out
+        "tile_accum_kernel": rows + samples * 3 * f32 + grad_value,
+    }
+
+
 def kernel_source_hash():
+    """Hash of the kernel sources with comments and whitespace removed, so
+    that counter figures stay attached to the code they were measured on."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "scale_deformable_attention_msdeformattn_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(csrc, f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(f.encode() + " ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
@@ -87,17 +132,87 @@ def measured_traffic(kernel):
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    e = t.get(kernel)
-    if not e or e.get("source_hash") != kernel_source_hash():
+    if t.get("source_hash") != kernel_source_hash():
         return None
-    return e.get("bytes_per_launch")
+    e = t.get("kernels", {}).get(kernel)
+    return None if e is None else e.get("hbm_bytes_per_launch")
+
+
+def _counter_rows(d, counter):
+    """(kernel name, value in KiB) per dispatch from a rocprofv3 csv run."""
+    out = []
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") == counter:
+                    out.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    if not out:
+        raise SystemExit(f"no {counter} rows under {d}")
+    return out
+
+
+def _short_kernel_name(full):
+    """'void ns::(anonymous namespace)::name<T, 8>(args)' -> 'name'."""
+    head = full.replace("(anonymous namespace)", "")
+    head = head.split("<")[0].split("(")[0]
+    return head.split("::")[-1].split()[-1] if head.strip() else head
+
+
+def ingest_counters(d, copy_mib, workload):
+    """profiles/traffic.json from four rocprofv3 --pmc runs (csv output):
+    d/fetch and d/write of `bench.py --eager`, d/copy_fetch and d/copy_write
+    of `bench.py --copy-mib N`. Each kernel's per-dispatch KiB is averaged and
+    scaled by the copy kernel's known bytes over its counter reading."""
+    copy_kib = copy_mib * 1024.0
+
+    def copy_avg(sub, counter):
+        vals = [v for n, v in _counter_rows(os.path.join(d, sub), counter) if "vectorized_elementwise_kernel" in n]
+        return sum(vals) / len(vals)
+
+    fetch_scale = copy_kib / copy_avg("copy_fetch", "FETCH_SIZE")
+    write_scale = copy_kib / copy_avg("copy_write", "WRITE_SIZE")
+    names = list(algorithmic_bytes(1, 1, 1, 1, 1, 1, 1, 0))
+    kernels = {}
+    for counter, sub in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+        for full, v in _counter_rows(os.path.join(d, sub), counter):
+            short = _short_kernel_name(full)
+            if short not in names:
+                continue
+            e = kernels.setdefault(short, {"FETCH_SIZE": [], "WRITE_SIZE": []})
+            e[counter].append(v)
+    table = {}
+    for k, e in kernels.items():
+        if not e["FETCH_SIZE"] or not e["WRITE_SIZE"]:
+            continue
+        fk = sum(e["FETCH_SIZE"]) / len(e["FETCH_SIZE"])
+        wk = sum(e["WRITE_SIZE"]) / len(e["WRITE_SIZE"])
+        table[k] = {"fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
+                    "hbm_bytes_per_launch": int(round((fk * fetch_scale + wk * write_scale) * 1024)),
+                    "dispatches": len(e["FETCH_SIZE"])}
+    out = {"source_hash": kernel_source_hash(), "workload": workload,
+           "calibration": {"kernel": "torch elementwise copy (mul by 1) fp32", "copy_mib": copy_mib,
+                           "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4)},
+           "kernels": table}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
+def copy_calibration(mib):
+    import torch
+    n = mib * 1024 * 1024 // 4
+    src = torch.randn(n, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_mib": mib, "dispatches": 5}))
 
 
 def cpu_baseline(wl_name, min_seconds=10.0):
     """The fp64 oracle, as it stands (single-threaded C), on the same step:
     reference points, locations, softmax, forward and backward of the whole
     workload once."""
-    import numpy as np
     import oracle
     from scale_deformable_attention_msdeformattn_amd import workloads
     d = workloads.draw(wl_name, 0)
@@ -128,9 +243,15 @@ def cpu_baseline(wl_name, min_seconds=10.0):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards by batch or head without any exchange; see DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: this build runs on a "
+              "single GPU (the op shards by batch or by head with no exchange between GPUs)", file=sys.stderr)
         sys.exit(2)
+    if args.ingest_counters:
+        ingest_counters(args.ingest_counters, args.copy_mib or COPY_MIB_DEFAULT, args.workload)
+        return
+    if args.copy_mib:
+        copy_calibration(args.copy_mib)
+        return
 
     import numpy as np
     import torch
@@ -169,41 +290,22 @@ def main():
     def k_fwd():
         state["out"] = msda.msda_forward(value, shapes, lsi, state["loc"], state["A"])
 
-    def k_bwd():  # grad_value zero fill (a small kernel of its own) + backward
+    def k_bwd():
         state["grads"] = msda.msda_backward(value, shapes, lsi, state["loc"], state["A"], G)
 
-    kernels = [("reference_points", k_ref), ("sampling_locations", k_loc), ("attention_softmax", k_softmax),
-               ("forward", k_fwd), ("backward", k_bwd)]
+    calls = [("msda_reference_points", k_ref), ("msda_sampling_locations", k_loc),
+             ("msda_attention_softmax", k_softmax), ("msda_forward", k_fwd), ("msda_backward", k_bwd)]
 
     def step():
-        for _, f in kernels:
+        for _, f in calls:
             f()
 
     for _ in range(max(1, args.warmup)):
         step()
     torch.cuda.synchronize()
 
-    if args.only:
-        f = dict(kernels)[args.only]
-        for _ in range(args.steps):
-            f()
-        torch.cuda.synchronize()
-        print(json.dumps({"only": args.only, "steps": args.steps}))
-        return
-
-    # algorithmic bytes per launch
-    loc = state["loc"]
-    vbytes = unique_value_bytes(loc, shapes.to(dev), B, M, D * elem)
-    f32 = 4
-    alg = {
-        "reference_points": B * L * 2 * f32 + B * Nq * L * 2 * f32,
-        "sampling_locations": B * Nq * L * 2 * f32 + 2 * B * Nq * M * L * K * 2 * f32,
-        "attention_softmax": 2 * B * Nq * M * L * K * f32,
-        "forward": vbytes + B * Nq * M * L * K * 3 * f32 + B * Nq * M * D * f32,
-        # reads value, loc, A, G; writes grad_value (fp32), grad_loc, grad_A
-        "backward": vbytes + B * Nq * M * L * K * 3 * f32 + B * Nq * M * D * f32
-                    + B * S * M * D * f32 + B * Nq * M * L * K * 3 * f32,
-    }
+    vbytes = unique_value_bytes(state["loc"], shapes.to(dev), B, M, D * elem)
+    alg = algorithmic_bytes(B, M, D, Nq, S, L, K, vbytes)
 
     # ---- timed region 1: whole steps (graph replay unless --eager) ----
     graph = None
@@ -242,44 +344,46 @@ def main():
     torch.cuda.synchronize()
     step_ms = t0.elapsed_time(t1) / args.steps
 
-    # ---- timed region 2: per-kernel durations, events between the kernels of
-    # eager steps on the same stream ----
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)] for _ in range(args.steps)]
+    # ---- timed region 2: per entry point, events between the calls of eager
+    # steps on the same stream ----
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
         ev[i][0].record(stream)
-        for j, (_, f) in enumerate(kernels):
+        for j, (_, f) in enumerate(calls):
             f()
             ev[i][j + 1].record(stream)
     torch.cuda.synchronize()
-    per = {name: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)])) * 1e3
-           for j, (name, _) in enumerate(kernels)}  # microseconds
+    per_call = {name: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)])) * 1e3
+                for j, (name, _) in enumerate(calls)}  # microseconds
     eager_step_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][-1]) for i in range(args.steps)]))
 
-    # ---- timed region 3: the backward kernel alone (accumulate mode, so the
-    # zero fill that msda_backward otherwise enqueues first is left out) ----
-    acc = torch.zeros(B, S, M, D, dtype=torch.float32, device=dev)
-    b0 = torch.cuda.Event(enable_timing=True)
-    b1 = torch.cuda.Event(enable_timing=True)
-    b0.record(stream)
-    for _ in range(args.steps):
-        msda.msda_backward(value, shapes, lsi, state["loc"], state["A"], G, grad_value=acc)
-    b1.record(stream)
+    # ---- timed region 3: every GPU kernel, event pairs recorded by the
+    # library around each launch on its stream ----
     torch.cuda.synchronize()
-    bwd_kernel_us = b0.elapsed_time(b1) / args.steps * 1e3
-    per["grad_value_zero_fill"] = max(per["backward"] - bwd_kernel_us, 0.0)
-    per["backward"] = bwd_kernel_us
-    alg["grad_value_zero_fill"] = B * S * M * D * f32
+    msda.msda_timing_reset()
+    msda.msda_timing_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    msda.msda_timing_enable(False)
+    timing = msda.msda_timing_read()
+    msda.msda_timing_reset()
 
     kstats = {}
-    for name, us in per.items():
-        gbps = alg[name] / (us * 1e-6) / 1e9
-        kstats[name] = {"avg_us": round(us, 3), "algorithmic_bytes": alg[name], "gbps": round(gbps, 1),
-                        "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
-    dominant = max(per, key=per.get)
-    dom_gbps = alg[dominant] / (per[dominant] * 1e-6) / 1e9
-    traffic = measured_traffic(dominant)
+    for name, (ms, n) in timing.items():
+        us = ms * 1e3 / n
+        e = {"avg_us": round(us, 3), "launches_per_step": n / args.steps}
+        if name in alg:
+            gbps = alg[name] / (us * 1e-6) / 1e9
+            e.update({"algorithmic_bytes": alg[name], "gbps": round(gbps, 1),
+                      "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)})
+        kstats[name] = e
+    dominant = max((k for k in kstats if k in alg), key=lambda k: kstats[k]["avg_us"])
+    dom_us = kstats[dominant]["avg_us"]
+    dom_gbps = alg[dominant] / (dom_us * 1e-6) / 1e9
     queries = B * Nq
+    fwd = kstats.get("forward_c256_kernel", {})
     result = {
         "metric": METRIC,
         "value": queries / (step_ms * 1e-3),
@@ -292,19 +396,21 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32" if value.dtype == torch.float32 else "bf16 value, f32 compute",
-        "data": "synthetic (seeded draws with the pages' shapes and distributions; no dataset)",
+        "data": "synthetic (seeded draws with Deformable DETR's encoder shapes and distributions; no dataset)",
         "config": {"workload": w.description, "step": "reference points + locations + softmax + forward + "
-                   "grad_value zero fill + backward", "graph_replay": graph is not None},
+                   "backward", "graph_replay": graph is not None},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic},
+                     "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(dominant), "avg_us": dom_us,
+                     "algorithmic_bytes": alg[dominant]},
         "kernels": kstats,
+        "entry_points_us": {k: round(v, 3) for k, v in per_call.items()},
         "eager_ms_per_step": eager_step_ms,
-        "forward": {"queries_per_s": queries / (per["forward"] * 1e-6),
-                    "effective_gbps": kstats["forward"]["gbps"],
-                    "frac_of_hbm_peak": kstats["forward"]["frac_of_hbm_peak"]},
-        "backward": {"queries_per_s": queries / (per["backward"] * 1e-6),
-                     "effective_gbps": kstats["backward"]["gbps"],
-                     "frac_of_hbm_peak": kstats["backward"]["frac_of_hbm_peak"]},
+        "forward": {"queries_per_s": queries / (fwd["avg_us"] * 1e-6) if fwd else None,
+                    "effective_gbps": fwd.get("gbps"), "frac_of_hbm_peak": fwd.get("frac_of_hbm_peak"),
+                    "traffic": measured_traffic("forward_c256_kernel")},
+        "backward": {"queries_per_s": queries / (per_call["msda_backward"] * 1e-6),
+                     "note": "the whole msda_backward call, all its kernels"},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.workload)

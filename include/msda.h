@@ -54,7 +54,7 @@ extern "C" {
 #define MSDA_API
 #endif
 
-#define MSDA_ABI_VERSION 2
+#define MSDA_ABI_VERSION 3
 #define MSDA_MAX_LEVELS 16
 
 typedef enum {
@@ -156,9 +156,12 @@ MSDA_API int msda_backward_workspace_size(const msda_shape *shape, size_t *bytes
  *                          in time must use different workspaces.
  * At an integer pixel coordinate the location gradient is the right
  * derivative (the cell [floor(x), floor(x)+1] is used).
- * grad_value is accumulated without float atomics on the tiled fast path
- * (value and gradient rows 16-byte aligned, M*D == 256 and compiled (L, K));
- * other sizes use float atomics, whose summation order varies run to run. */
+ * On the tiled fast path (value and gradient rows 16-byte aligned,
+ * M*D == 256 and compiled (L, K)) grad_value is gathered per pixel tile; only
+ * the tiles of the densest levels, whose sample lists are split over several
+ * workgroups, merge their partial sums with float atomics. Other sizes scatter
+ * with float atomics. Where float atomics are used the summation order, and so
+ * the last bits of grad_value, vary from run to run. */
 MSDA_API int msda_backward(const msda_shape *shape, const void *value, msda_dtype value_dtype,
                   const float *sampling_locations, const float *attention_weights,
                   const float *grad_output, float *grad_value,
@@ -173,6 +176,28 @@ MSDA_API const char *msda_last_error(void);
 
 /* MSDA_ABI_VERSION of the built library. */
 MSDA_API int msda_abi_version(void);
+
+/* Per-kernel timing, a profiling aid for the caller's benchmark (not part of
+ * the op). While enabled (on != 0), every kernel this library launches on a
+ * stream that is not being captured into a graph is bracketed by two HIP
+ * events recorded on that stream; the elapsed time between them is added to
+ * the kernel's entry. Enabling adds a little launch overhead; it is off by
+ * default. Host only, thread safe. Returns MSDA_OK. */
+MSDA_API int msda_timing_enable(int on);
+
+/* Drops all timing entries and unread event pairs (waits for the latter). */
+MSDA_API int msda_timing_reset(void);
+
+/* Waits for the recorded event pairs and folds them into the entries, then
+ * reports entry `index` (0 .. count-1, in order of first launch): *name is a
+ * static string, the kernel's name as the compiler and profilers show it
+ * (without template arguments), valid for the life of the process;
+ * *total_ms the summed elapsed time and *launches the number of launches.
+ * Any output pointer may be NULL. *count, if given, receives the number of
+ * entries; index -1 reports only that. Another index out of range:
+ * MSDA_E_DIM (with *count still set). A HIP error while waiting: MSDA_E_HIP. */
+MSDA_API int msda_timing_read(int index, int *count, const char **name, double *total_ms,
+                              int64_t *launches);
 
 #ifdef __cplusplus
 }

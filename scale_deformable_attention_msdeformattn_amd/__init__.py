@@ -7,15 +7,17 @@ that ABI. Entry points (same names as the C ABI):
     msda_reference_points, msda_sampling_locations, msda_attention_softmax,
     msda_forward, msda_backward
 
-plus ``MSDeformAttnFunction`` (autograd over forward/backward) and
+and the per-kernel timing aid msda_timing_enable / msda_timing_read /
+msda_timing_reset, plus ``MSDeformAttnFunction`` (autograd over forward/backward) and
 ``ms_deform_attn`` (location formation + softmax + core in one call).
 """
 from ._binding import (MSDAError, declared_symbols, level_start_index_host, load, msda_attention_softmax,
-                       msda_backward, msda_forward, msda_reference_points, msda_sampling_locations)
+                       msda_backward, msda_forward, msda_reference_points, msda_sampling_locations,
+                       msda_timing_enable, msda_timing_read, msda_timing_reset)
 from .autograd import MSDeformAttnFunction, ms_deform_attn
 
 __all__ = [
     "MSDAError", "MSDeformAttnFunction", "declared_symbols", "level_start_index_host", "load",
     "ms_deform_attn", "msda_attention_softmax", "msda_backward", "msda_forward", "msda_reference_points",
-    "msda_sampling_locations",
+    "msda_sampling_locations", "msda_timing_enable", "msda_timing_read", "msda_timing_reset",
 ]

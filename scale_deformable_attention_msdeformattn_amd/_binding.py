@@ -96,6 +96,13 @@ def load():
     lib.msda_backward.restype = ctypes.c_int
     lib.msda_backward.argtypes = [_shp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                                   ctypes.c_uint, _vp]
+    lib.msda_timing_enable.restype = ctypes.c_int
+    lib.msda_timing_enable.argtypes = [ctypes.c_int]
+    lib.msda_timing_reset.restype = ctypes.c_int
+    lib.msda_timing_reset.argtypes = []
+    lib.msda_timing_read.restype = ctypes.c_int
+    lib.msda_timing_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_char_p),
+                                     ctypes.POINTER(ctypes.c_double), _i64p]
     _lib = lib
     return lib
 
@@ -306,3 +313,29 @@ def raw_call(name: str, *args):
     """Call an entry point with raw ctypes arguments and return its status
     (used by the boundary tests; no checks, no exceptions)."""
     return getattr(load(), name)(*args)
+
+
+def msda_timing_enable(on: bool = True) -> None:
+    """Bracket every kernel launch of the library with a HIP event pair on its
+    stream (not while the stream is captured)."""
+    _check(load().msda_timing_enable(1 if on else 0), "msda_timing_enable")
+
+
+def msda_timing_reset() -> None:
+    _check(load().msda_timing_reset(), "msda_timing_reset")
+
+
+def msda_timing_read() -> dict:
+    """{kernel name: (total milliseconds, launches)} of the timed launches so far."""
+    lib = load()
+    n = ctypes.c_int(0)
+    _check(lib.msda_timing_read(-1, ctypes.byref(n), None, None, None), "msda_timing_read")
+    out = {}
+    for i in range(n.value):
+        name = ctypes.c_char_p()
+        ms = ctypes.c_double()
+        cnt = ctypes.c_int64()
+        _check(lib.msda_timing_read(i, None, ctypes.byref(name), ctypes.byref(ms), ctypes.byref(cnt)),
+               "msda_timing_read")
+        out[name.value.decode()] = (ms.value, cnt.value)
+    return out

@@ -9,8 +9,10 @@
 //
 // grad_value is a scatter: every sample adds to four pixels. On gfx950 float
 // atomics (global and LDS alike) sustain only a small fraction of the
-// required rate, so the fast path has no atomics on floats at all. It turns
-// the scatter into a gather owned by pixel tiles:
+// required rate, so the fast path turns the scatter into a gather owned by
+// pixel tiles (float atomics remain only where the records of one dense tile
+// are split over several workgroups, one add per pixel and channel per
+// workgroup):
 //
 //  1. bin_count   : each workgroup takes a fixed range of queries and counts,
 //                   in an LDS histogram (integer LDS atomics), how many of its
@@ -787,30 +789,47 @@ hipError_t launch_fast(const Geometry &g, const TilePlan &tp, const void *value,
     const int nwg = g.B * tp.wpb;
     const int nkeys = g.B * nkb;
     const size_t hist_bytes = (size_t)nkb * 4;
-    hipLaunchKernelGGL(clear_totals_kernel, dim3((nkeys + kBlock - 1) / kBlock), dim3(kBlock), 0, st, nkeys,
-                       ws.totals);
-    hipLaunchKernelGGL((bin_count_kernel<M, L, K>), dim3(nwg), dim3(kBinThreads), hist_bytes, st, g, tp,
-                       reinterpret_cast<const float2 *>(loc), ws.counts, ws.totals);
-    hipLaunchKernelGGL(scan_bases_kernel, dim3(1), dim3(1024), 0, st, nkeys, ws.totals, ws.bases);
+    {
+        KernelScope ks_("clear_totals_kernel", st);
+        hipLaunchKernelGGL(clear_totals_kernel, dim3((nkeys + kBlock - 1) / kBlock), dim3(kBlock), 0, st, nkeys,
+                           ws.totals);
+    }
+    {
+        KernelScope ks_("bin_count_kernel", st);
+        hipLaunchKernelGGL((bin_count_kernel<M, L, K>), dim3(nwg), dim3(kBinThreads), hist_bytes, st, g, tp,
+                           reinterpret_cast<const float2 *>(loc), ws.counts, ws.totals);
+    }
+    {
+        KernelScope ks_("scan_bases_kernel", st);
+        hipLaunchKernelGGL(scan_bases_kernel, dim3(1), dim3(1024), 0, st, nkeys, ws.totals, ws.bases);
+    }
     const uint32_t grid = round_up8((uint32_t)nwg);
-    hipLaunchKernelGGL((backward_c256_kernel<VT, M, L, K>), dim3(grid), dim3(MainWaves<M, L, K>::kValue * kWave),
-                       hist_bytes, st, g, tp,
-                       static_cast<const VT *>(value), reinterpret_cast<const float2 *>(loc), attn,
-                       reinterpret_cast<const float4 *>(go), reinterpret_cast<float2 *>(gl), ga, ws.counts,
-                       ws.bases, ws.records, grid);
+    {
+        KernelScope ks_("backward_c256_kernel", st);
+        hipLaunchKernelGGL((backward_c256_kernel<VT, M, L, K>), dim3(grid), dim3(MainWaves<M, L, K>::kValue * kWave),
+                           hist_bytes, st, g, tp,
+                           static_cast<const VT *>(value), reinterpret_cast<const float2 *>(loc), attn,
+                           reinterpret_cast<const float4 *>(go), reinterpret_cast<float2 *>(gl), ga, ws.counts,
+                           ws.bases, ws.records, grid);
+    }
     constexpr int LG = 256 / M / 4;
     if (!accumulate) {
         int64_t n = 0;
         for (int l = 0; l < g.L; ++l)
             if (tp.nchunk[l] > 1) n += (int64_t)g.B * g.lv.H[l] * g.lv.W[l] * g.M * g.D / 4;
-        if (n > 0)
+        if (n > 0) {
+            KernelScope ks_("zero_split_levels_kernel", st);
             hipLaunchKernelGGL(zero_split_levels_kernel, dim3((unsigned)((n + kBlock - 1) / kBlock)), dim3(kBlock), 0,
                                st, g, tp, reinterpret_cast<float4 *>(gv));
+        }
     }
     const uint32_t items = (uint32_t)(g.B * g.M * tp.ipb);
-    hipLaunchKernelGGL((tile_accum_kernel<LG>), dim3(round_up8(items)), dim3(kBlock), 0, st, g, tp,
-                       reinterpret_cast<const float2 *>(loc), attn, reinterpret_cast<const float4 *>(go),
-                       reinterpret_cast<float4 *>(gv), ws.records, ws.bases, ws.totals, accumulate ? 1 : 0);
+    {
+        KernelScope ks_("tile_accum_kernel", st);
+        hipLaunchKernelGGL((tile_accum_kernel<LG>), dim3(round_up8(items)), dim3(kBlock), 0, st, g, tp,
+                           reinterpret_cast<const float2 *>(loc), attn, reinterpret_cast<const float4 *>(go),
+                           reinterpret_cast<float4 *>(gv), ws.records, ws.bases, ws.totals, accumulate ? 1 : 0);
+    }
     return hipGetLastError();
 }
 
@@ -857,9 +876,12 @@ hipError_t launch_typed(const Geometry &g, const TilePlan *tpp, const void *valu
         if (e != hipSuccess) return e;
     }
     const int64_t n = g.queries() * g.M;
-    hipLaunchKernelGGL((backward_generic_kernel<VT>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, g,
-                       static_cast<const VT *>(value), reinterpret_cast<const float2 *>(loc), attn, go, gv,
-                       reinterpret_cast<float2 *>(gl), ga);
+    {
+        KernelScope ks_("backward_generic_kernel", st);
+        hipLaunchKernelGGL((backward_generic_kernel<VT>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, g,
+                           static_cast<const VT *>(value), reinterpret_cast<const float2 *>(loc), attn, go, gv,
+                           reinterpret_cast<float2 *>(gl), ga);
+    }
     return hipGetLastError();
 }
 

@@ -195,9 +195,12 @@ hipError_t launch_c256(const Geometry &g, const void *value, const float *loc, c
 {
     const uint32_t tiles = (uint32_t)((g.queries() + kWaves - 1) / kWaves);
     const uint32_t grid = round_up8(tiles);
-    hipLaunchKernelGGL((forward_c256_kernel<VT, M, L, K>), dim3(grid), dim3(kBlock), 0, st, g,
-                       static_cast<const VT *>(value), reinterpret_cast<const float2 *>(loc), attn,
-                       reinterpret_cast<float4 *>(out), grid);
+    {
+        KernelScope ks_("forward_c256_kernel", st);
+        hipLaunchKernelGGL((forward_c256_kernel<VT, M, L, K>), dim3(grid), dim3(kBlock), 0, st, g,
+                           static_cast<const VT *>(value), reinterpret_cast<const float2 *>(loc), attn,
+                           reinterpret_cast<float4 *>(out), grid);
+    }
     return hipGetLastError();
 }
 
@@ -222,9 +225,12 @@ hipError_t launch_typed(const Geometry &g, const void *value, const float *loc, 
         if (g.L == 4 && g.K == 1) return launch_c256<VT, 8, 4, 1>(g, value, loc, attn, out, st);
     }
     const int64_t n = g.queries() * g.M * g.D;
-    hipLaunchKernelGGL((forward_generic_kernel<VT>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                       g, static_cast<const VT *>(value), reinterpret_cast<const float2 *>(loc), attn,
-                       out);
+    {
+        KernelScope ks_("forward_generic_kernel", st);
+        hipLaunchKernelGGL((forward_generic_kernel<VT>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                           g, static_cast<const VT *>(value), reinterpret_cast<const float2 *>(loc), attn,
+                           out);
+    }
     return hipGetLastError();
 }
 

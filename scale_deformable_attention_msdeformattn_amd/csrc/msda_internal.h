@@ -54,6 +54,22 @@ bool backward_uses_workspace(const Geometry &g, const void *value, msda_dtype vt
                              const float *gv);
 size_t backward_workspace_bytes(const Geometry &g);
 
+// Brackets the launches made during its lifetime with a timing event pair on
+// `st` while msda_timing_enable is on (and `st` is not being captured).
+// `name` must be a string literal.
+class KernelScope {
+  public:
+    KernelScope(const char *name, hipStream_t st);
+    ~KernelScope();
+    KernelScope(const KernelScope &) = delete;
+    KernelScope &operator=(const KernelScope &) = delete;
+
+  private:
+    const char *name_;
+    hipStream_t st_;
+    hipEvent_t start_;
+};
+
 // Launchers (each returns a hipError_t from the launch).
 hipError_t launch_reference_points(const Geometry &g, const float *valid_ratios,
                                    const float *query_ref, float *ref_out, hipStream_t st);

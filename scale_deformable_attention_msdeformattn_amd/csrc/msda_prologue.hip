@@ -181,8 +181,11 @@ inline unsigned blocks_for(int64_t n) { return (unsigned)((n + kBlock - 1) / kBl
 hipError_t launch_reference_points(const Geometry &g, const float *vr, const float *u, float *ref,
                                    hipStream_t st)
 {
-    hipLaunchKernelGGL(reference_points_kernel, dim3(blocks_for(g.queries())), dim3(kBlock), 0, st,
-                       g, vr, u, ref);
+    {
+        KernelScope ks_("reference_points_kernel", st);
+        hipLaunchKernelGGL(reference_points_kernel, dim3(blocks_for(g.queries())), dim3(kBlock), 0, st,
+                           g, vr, u, ref);
+    }
     return hipGetLastError();
 }
 
@@ -194,15 +197,20 @@ hipError_t launch_sampling_locations(const Geometry &g, const float *ref, const 
     const auto d = reinterpret_cast<float2 *>(loc);
     const bool a16 = (reinterpret_cast<uintptr_t>(off) % 16) == 0 && (reinterpret_cast<uintptr_t>(loc) % 16) == 0;
     const unsigned rows = blocks_for(g.queries() * g.M * g.L);
-    if (g.K == 4 && a16)
+    if (g.K == 4 && a16) {
+        KernelScope ks_("sampling_locations_kernel", st);
         hipLaunchKernelGGL(sampling_locations_kernel<4>, dim3(rows), dim3(kBlock), 0, st, g, r, o, d);
-    else if (g.K == 2 && a16)
+    } else if (g.K == 2 && a16) {
+        KernelScope ks_("sampling_locations_kernel", st);
         hipLaunchKernelGGL(sampling_locations_kernel<2>, dim3(rows), dim3(kBlock), 0, st, g, r, o, d);
-    else if (g.K == 8 && a16)
+    } else if (g.K == 8 && a16) {
+        KernelScope ks_("sampling_locations_kernel", st);
         hipLaunchKernelGGL(sampling_locations_kernel<8>, dim3(rows), dim3(kBlock), 0, st, g, r, o, d);
-    else
+    } else {
+        KernelScope ks_("sampling_locations_any_kernel", st);
         hipLaunchKernelGGL(sampling_locations_any_kernel, dim3(blocks_for(g.samples())), dim3(kBlock), 0, st, g, r,
                            o, d);
+    }
     return hipGetLastError();
 }
 
@@ -213,16 +221,22 @@ hipError_t launch_softmax(const Geometry &g, const float *logits, float *w, hipS
     const bool a16 = (reinterpret_cast<uintptr_t>(logits) % 16) == 0 && (reinterpret_cast<uintptr_t>(w) % 16) == 0;
     const auto x4 = reinterpret_cast<const float4 *>(logits);
     const auto y4 = reinterpret_cast<float4 *>(w);
-    if (a16 && n == 16)
+    if (a16 && n == 16) {
+        KernelScope ks_("softmax_vec_kernel", st);
         hipLaunchKernelGGL(softmax_vec_kernel<16>, dim3(blocks_for(rows)), dim3(kBlock), 0, st, rows, x4, y4);
-    else if (a16 && n == 32)
+    } else if (a16 && n == 32) {
+        KernelScope ks_("softmax_vec_kernel", st);
         hipLaunchKernelGGL(softmax_vec_kernel<32>, dim3(blocks_for(rows)), dim3(kBlock), 0, st, rows, x4, y4);
-    else if (a16 && n == 8)
+    } else if (a16 && n == 8) {
+        KernelScope ks_("softmax_vec_kernel", st);
         hipLaunchKernelGGL(softmax_vec_kernel<8>, dim3(blocks_for(rows)), dim3(kBlock), 0, st, rows, x4, y4);
-    else if (a16 && n == 4)
+    } else if (a16 && n == 4) {
+        KernelScope ks_("softmax_vec_kernel", st);
         hipLaunchKernelGGL(softmax_vec_kernel<4>, dim3(blocks_for(rows)), dim3(kBlock), 0, st, rows, x4, y4);
-    else
+    } else {
+        KernelScope ks_("softmax_kernel", st);
         hipLaunchKernelGGL(softmax_kernel, dim3(blocks_for(rows)), dim3(kBlock), 0, st, rows, n, logits, w);
+    }
     return hipGetLastError();
 }
 
@@ -231,7 +245,10 @@ hipError_t launch_zero_fill(float *p, int64_t n, hipStream_t st)
     int64_t blocks = (n / 4 + kBlock - 1) / kBlock;
     if (blocks > 4096) blocks = 4096;
     if (blocks < 1) blocks = 1;
-    hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, st, p, n);
+    {
+        KernelScope ks_("zero_fill_kernel", st);
+        hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, st, p, n);
+    }
     return hipGetLastError();
 }
 

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.msda_abi_version() == 2
+    assert lib.msda_abi_version() == 3
     assert lib.msda_status_string(0) == b"ok"
     for code in range(-8, 0):
         assert lib.msda_status_string(code) not in (b"", b"unknown status")
@@ -189,3 +189,15 @@ def test_backward_workspace_size_and_check(lib):
     # sizes without a fast path need none
     assert B.msda_backward_workspace_size(_shape(M=3, D=5)) == 0
     assert lib.msda_backward_workspace_size(sh.ptr, None) == B.MSDA_E_NULL
+
+
+def test_timing_entry_points_without_launches(lib):
+    """The timing aid works on the host alone: no launches, no entries."""
+    assert lib.msda_timing_reset() == 0
+    assert lib.msda_timing_enable(1) == 0
+    assert lib.msda_timing_enable(0) == 0
+    n = ctypes.c_int(-5)
+    assert lib.msda_timing_read(-1, ctypes.byref(n), None, None, None) == 0
+    assert n.value == 0
+    assert lib.msda_timing_read(0, ctypes.byref(n), None, None, None) == -2  # MSDA_E_DIM
+    assert B.msda_timing_read() == {}
