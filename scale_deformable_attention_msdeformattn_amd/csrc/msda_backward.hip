@@ -124,76 +124,56 @@ __global__ void __launch_bounds__(kBlock) clear_totals_kernel(int nkeys, uint32_
 }
 
 // Workgroup w takes queries [q0, q1) of batch b. One thread per (query, head,
-// level) block of K samples: it counts, per distinct tile, how many of the
-// block's samples touch the tile, and adds that into an LDS histogram (one
-// add per distinct tile, so the K samples of a block do not contend). Then
-// every non-zero (w, tile) count reserves its range of the tile's record list
-// with one global atomic add; the returned offset is stored at
+// sparse level) block of K samples: every sample adds one to the LDS
+// histogram entry of each distinct tile its in-map corners fall in. Then
+// every non-zero (w, tile) count reserves its range of the tile's record
+// list with one global atomic add; the returned offset is stored at
 // offsets[w][tile] (entries with a zero count are never read).
 template <int M, int L, int K>
 __global__ void __launch_bounds__(kBinThreads)
 bin_count_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, uint32_t *__restrict__ offsets,
                  uint32_t *__restrict__ totals)
 {
-    constexpr int LK = L * K;
-    constexpr int NB = M * L;  // blocks per query
     extern __shared__ uint32_t s_hist[];  // [M * tpb]
     __shared__ LevelRec s_lv[L];
+    __shared__ int s_sparse[L];            // the levels that keep records
     const int nkeys = M * tp.tpb;
     for (int i = threadIdx.x; i < nkeys; i += kBinThreads) s_hist[i] = 0;
     if (threadIdx.x < L) {
         const int l = threadIdx.x;
         s_lv[l] = LevelRec{(float)g.lv.W[l], (float)g.lv.H[l], g.lv.W[l], g.lv.start[l]};
     }
+    int nsl = 0;
+#pragma unroll
+    for (int l = 0; l < L; ++l)
+        if (!((tp.dense_mask >> l) & 1)) {
+            if (threadIdx.x == 0) s_sparse[nsl] = l;
+            ++nsl;
+        }
     __syncthreads();
     const int w = blockIdx.x;
     const int b = w / tp.wpb;
     const int q0 = (w - b * tp.wpb) * tp.qpw;
     const int q1 = min(q0 + tp.qpw, g.Nq);
-    const int64_t blk0 = ((int64_t)b * g.Nq + q0) * NB;  // first (query, head, level) block
-    const int nblk = (q1 - q0) * NB;
+    const int per_q = M * nsl;
+    const int nblk = (q1 - q0) * per_q;
     for (int i = threadIdx.x; i < nblk; i += kBinThreads) {
-        const int m = (i / L) % M;
-        const int l = i % L;
+        const int qi = i / per_q, rem = i - qi * per_q;
+        const int m = rem / nsl;
+        const int l = s_sparse[rem - m * nsl];
         const LevelRec lv = s_lv[l];
         const int H = (int)lv.Hf;
-        const float2 *u = loc + (blk0 + i) * K;
-        int tiles[K][4];
+        const float2 *u = loc + ((((int64_t)b * g.Nq + q0 + qi) * M + m) * L + l) * K;
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             int cx, cy;
             float fx, fy;
-            const bool in = sample_cell(u[k], lv.Wf, lv.Hf, cx, cy, fx, fy);
+            if (!sample_cell(u[k], lv.Wf, lv.Hf, cx, cy, fx, fy)) continue;
             const SampleTiles st = sample_tiles(tp, l, lv.W, H, cx, cy);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) tiles[k][j] = in ? st.t[j] : -1;
+            for (int j = 0; j < 4; ++j)
+                if (st.t[j] >= 0) atomicAdd(&s_hist[m * tp.tpb + st.t[j]], 1u);
         }
-        // one add per distinct tile: a (k, j) entry adds only if no earlier
-        // entry of the block holds the same tile; it adds the number of
-        // samples of the block holding that tile
-#pragma unroll
-        for (int k = 0; k < K; ++k)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int t = tiles[k][j];
-                if (t < 0) continue;
-                bool first = true;
-#pragma unroll
-                for (int k2 = 0; k2 < K; ++k2)
-#pragma unroll
-                    for (int j2 = 0; j2 < 4; ++j2)
-                        if ((k2 < k || (k2 == k && j2 < j)) && tiles[k2][j2] == t) first = false;
-                if (!first) continue;
-                uint32_t cnt = 0;
-#pragma unroll
-                for (int k2 = 0; k2 < K; ++k2) {
-                    bool has = false;
-#pragma unroll
-                    for (int j2 = 0; j2 < 4; ++j2) has |= tiles[k2][j2] == t;
-                    cnt += has ? 1u : 0u;
-                }
-                atomicAdd(&s_hist[m * tp.tpb + t], cnt);
-            }
     }
     __syncthreads();
     uint32_t *row = offsets + (int64_t)w * nkeys;
@@ -331,7 +311,7 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
                 o.w = (int)((y1ok & x1ok) ? o10 + RB : kOutOfRange);
                 s_off[wave][p] = o;
                 s_geo[wave][p] = make_float4(fx, fy, a, 0.0f);
-                if (in) {
+                if (in && !((tp.dense_mask >> l) & 1)) {
                     const SampleTiles st = sample_tiles(tp, l, lv.W, H, cx, cy);
                     const uint32_t sidx = (uint32_t)(gq * NS + s);
 #pragma unroll
@@ -668,15 +648,15 @@ tile_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, const
     }
 }
 
-// Zero the grad_value rows of the levels whose tiles are shared by several
-// workgroups (their partials are added with atomics). One thread per float4.
+// Zero the grad_value rows of the levels whose partial sums are added with
+// atomics (split tiles, split dense levels). One thread per float4.
 __global__ void __launch_bounds__(kBlock)
 zero_split_levels_kernel(Geometry g, TilePlan tp, float4 *__restrict__ grad_value)
 {
     const int64_t row4 = (int64_t)g.M * g.D / 4;  // float4s per value row
     int64_t t = (int64_t)blockIdx.x * kBlock + threadIdx.x;
     for (int l = 0; l < g.L; ++l) {
-        if (tp.nchunk[l] <= 1) continue;
+        if (!level_uses_atomics(tp, l)) continue;
         const int64_t n = (int64_t)g.lv.H[l] * g.lv.W[l] * row4;
         if (t < (int64_t)g.B * n) {
             const int64_t b = t / n, r = t - b * n;
@@ -684,6 +664,224 @@ zero_split_levels_kernel(Geometry g, TilePlan tp, float4 *__restrict__ grad_valu
             return;
         }
         t -= (int64_t)g.B * n;
+    }
+}
+
+// ------------------------------------------------------------- 5. dense_accum
+
+// Dense levels: many samples per pixel, few pixels. Binning them into tiles
+// would write each sample's record up to four times; instead one workgroup
+// per (b, m, level, pixel part, query split) reads its queries' samples of
+// the level directly (contiguous per query) together with their grad_output
+// rows, and, sub-chunk after sub-chunk:
+//  - ranks each (sample, corner) pair whose pixel lies in its part within
+//    the pixel's LDS count (integer LDS atomics),
+//  - scans the counts and writes every pair's weight A*w_c and query slot,
+//    sorted by pixel,
+//  - lets each lane group sum weight * G over the pairs of the pixels it
+//    owns, in registers.
+// The next sub-chunk's loads are issued before the current one is sorted and
+// stay in flight across the LDS-only barriers. The split partials meet in
+// grad_value with one float atomic add per pixel and channel.
+constexpr int kDensePix = 256;             // pixels per part at most
+constexpr int kDenseSub = 512;             // samples per sub-chunk at most
+constexpr int kDenseQ = 128;               // queries per sub-chunk at most
+constexpr int kDenseBatch = 4;             // pairs in flight per lane group
+constexpr double kDenseMinPerPix = 24.0;   // samples per pixel (per batch and head) that make a level dense
+constexpr int kDenseMaxParts = 8;          // pixel parts of a dense level at most
+constexpr double kDenseItemSamples = 4096; // samples per dense work item (sets the query splits)
+constexpr int kDenseMaxSplit = 64;
+
+template <int LG>
+__global__ void __launch_bounds__(kBlock)
+dense_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, const float *__restrict__ attn,
+                   const float4 *__restrict__ grad_out, float4 *__restrict__ grad_value, int accumulate)
+{
+    constexpr int NG = kBlock / LG;                  // lane groups
+    constexpr int PPG = kDensePix / NG;              // pixel slots per lane group
+    constexpr int kPer = kDenseSub / kBlock;         // samples per thread per sub-chunk
+    constexpr int kGRows = kDenseQ * LG / kBlock;    // float4 of G staged per thread
+    static_assert(kDensePix % NG == 0 && kDenseSub % kBlock == 0 && (kDenseQ * LG) % kBlock == 0,
+                  "dense tiling");
+    __shared__ float4 s_g[kDenseQ * LG];       // G rows of the sub-chunk's queries
+    __shared__ uint2 s_pair[4 * kDenseSub];    // (bits(A * w_c), query slot), sorted by pixel
+    __shared__ uint32_t s_cnt[kDensePix];
+    __shared__ uint32_t s_start[kDensePix + 1];
+
+    const int item = (int)xcd_tile(blockIdx.x, gridDim.x);
+    if (item >= g.B * g.M * tp.dipb) return;
+    const int bm = item / tp.dipb;
+    const int b = bm / g.M, m = bm - (bm / g.M) * g.M;
+    const int r_in = item - bm * tp.dipb;
+    int l = 0;
+    int parts = 1, splits = 1, dib = 0, W = 1, H = 1, lstart = 0;
+#pragma unroll
+    for (int i = 0; i < MSDA_MAX_LEVELS; ++i)
+        if (i < g.L && ((tp.dense_mask >> i) & 1) && r_in >= tp.dibase[i]) l = i;
+#pragma unroll
+    for (int i = 0; i < MSDA_MAX_LEVELS; ++i)
+        if (i == l) {
+            parts = tp.dparts[i];
+            splits = tp.dsplit[i];
+            dib = tp.dibase[i];
+            W = g.lv.W[i];
+            H = g.lv.H[i];
+            lstart = g.lv.start[i];
+        }
+    const int r = r_in - dib;
+    const int part = r / splits, split = r - (r / splits) * splits;
+    const int npix_l = H * W;
+    const int p0 = (int)((int64_t)npix_l * part / parts);
+    const int npix = (int)((int64_t)npix_l * (part + 1) / parts) - p0;
+    const int qa0 = (int)((int64_t)g.Nq * split / splits);
+    const int qa1 = (int)((int64_t)g.Nq * (split + 1) / splits);
+    const float Wf = (float)W, Hf = (float)H;
+    const int K = g.K;
+    const int QS = min(kDenseQ, kDenseSub / K);  // queries per sub-chunk
+    const int64_t LKs = (int64_t)g.L * K;
+    const int grp = threadIdx.x / LG;
+    const int lig = threadIdx.x % LG;
+
+    for (int i = threadIdx.x; i < kDensePix; i += kBlock) s_cnt[i] = 0;
+
+    // loads of one sub-chunk (starting at query qa), held in registers
+    float2 u[kPer];
+    float a[kPer];
+    float4 gst[kGRows];
+    auto fetch = [&](int qa) {
+        const int ns = min(QS, qa1 - qa) * K;
+#pragma unroll
+        for (int t = 0; t < kPer; ++t) {
+            const int i = threadIdx.x + t * kBlock;
+            const int qi = i / K, k = i - (i / K) * K;
+            const int64_t sidx = (((int64_t)b * g.Nq + qa + qi) * g.M + m) * LKs + (int64_t)l * K + k;
+            u[t] = i < ns ? loc[sidx] : make_float2(-1e30f, -1e30f);
+            a[t] = i < ns ? attn[sidx] : 0.0f;
+        }
+        const int nrow = min(QS, qa1 - qa) * LG;  // float4 of G to stage
+#pragma unroll
+        for (int t = 0; t < kGRows; ++t) {
+            const int i = threadIdx.x + t * kBlock;
+            const int qi = i / LG, c = i - (i / LG) * LG;
+            gst[t] = i < nrow ? grad_out[(((int64_t)b * g.Nq + qa + qi) * g.M + m) * LG + c]
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    };
+
+    float4 acc[PPG];
+#pragma unroll
+    for (int j = 0; j < PPG; ++j) acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+
+    if (qa0 < qa1) fetch(qa0);
+    for (int qa = qa0; qa < qa1; qa += QS) {
+        lds_barrier();  // s_cnt cleared; the previous sub-chunk is done with s_g and s_pair
+#pragma unroll
+        for (int t = 0; t < kGRows; ++t) s_g[threadIdx.x + t * kBlock] = gst[t];
+        // rank this part's pairs within their pixel's count
+        int pix[kPer][4];
+        uint32_t rank[kPer][4];
+        float wpair[kPer][4];
+#pragma unroll
+        for (int t = 0; t < kPer; ++t) {
+            int cx, cy;
+            float fx, fy;
+            const bool in = sample_cell(u[t], Wf, Hf, cx, cy, fx, fy);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int px = cx + (c & 1), py = cy + (c >> 1);
+                const int p = py * W + px - p0;
+                wpair[t][c] = a[t] * ((c & 1) ? fx : 1.0f - fx) * ((c & 2) ? fy : 1.0f - fy);
+                pix[t][c] = -1;
+                if (in && px >= 0 && px < W && py >= 0 && py < H && p >= 0 && p < npix) {
+                    pix[t][c] = p;
+                    rank[t][c] = atomicAdd(&s_cnt[p], 1u);
+                }
+            }
+        }
+        if (qa + QS < qa1) fetch(qa + QS);  // in flight until the next sub-chunk is staged
+        lds_barrier();
+        // exclusive scan of the (at most kDensePix) pixel counts, one wave
+        if (threadIdx.x < kWave) {
+            constexpr int E = kDensePix / kWave;
+            uint32_t v[E];
+            uint32_t sum = 0;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                v[e] = s_cnt[threadIdx.x * E + e];
+                sum += v[e];
+            }
+            uint32_t incl = sum;
+#pragma unroll
+            for (int o = 1; o < kWave; o <<= 1) {
+                const uint32_t t = __shfl_up(incl, o, kWave);
+                if ((int)threadIdx.x >= o) incl += t;
+            }
+            uint32_t run = incl - sum;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                s_start[threadIdx.x * E + e] = run;
+                run += v[e];
+            }
+            if (threadIdx.x == kWave - 1) s_start[kDensePix] = incl;
+        }
+        lds_barrier();
+#pragma unroll
+        for (int t = 0; t < kPer; ++t) {
+            const uint32_t qi = (uint32_t)((threadIdx.x + t * kBlock) / K);
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (pix[t][c] >= 0)
+                    s_pair[s_start[pix[t][c]] + rank[t][c]] = make_uint2(__float_as_uint(wpair[t][c]), qi);
+        }
+        for (int i = threadIdx.x; i < kDensePix; i += kBlock) s_cnt[i] = 0;  // for the next sub-chunk
+        lds_barrier();
+        // each lane group sums over the pairs of its pixels grp, grp + NG, ...
+#pragma unroll
+        for (int j = 0; j < PPG; ++j) {
+            const int pl = grp + j * NG;
+            if (pl >= npix) break;
+            const uint32_t e1 = s_start[pl + 1];
+            for (uint32_t e0 = s_start[pl]; e0 < e1; e0 += kDenseBatch) {
+                uint2 pr[kDenseBatch];
+                float4 gv[kDenseBatch];
+#pragma unroll
+                for (int v = 0; v < kDenseBatch; ++v) pr[v] = e0 + v < e1 ? s_pair[e0 + v] : make_uint2(0u, 0u);
+#pragma unroll
+                for (int v = 0; v < kDenseBatch; ++v) gv[v] = s_g[pr[v].y * LG + lig];
+#pragma unroll
+                for (int v = 0; v < kDenseBatch; ++v) {
+                    const float w = __uint_as_float(pr[v].x);
+                    acc[j].x = __builtin_fmaf(w, gv[v].x, acc[j].x);
+                    acc[j].y = __builtin_fmaf(w, gv[v].y, acc[j].y);
+                    acc[j].z = __builtin_fmaf(w, gv[v].z, acc[j].z);
+                    acc[j].w = __builtin_fmaf(w, gv[v].w, acc[j].w);
+                }
+            }
+        }
+    }
+    // write the part's pixels: one writer per pixel unless the queries are split
+#pragma unroll
+    for (int j = 0; j < PPG; ++j) {
+        const int pl = grp + j * NG;
+        if (pl >= npix) break;
+        float4 *dst = grad_value + (((int64_t)b * g.S + lstart + p0 + pl) * g.M + m) * LG + lig;
+        float4 v = acc[j];
+        if (splits > 1) {
+            float *d = reinterpret_cast<float *>(dst);
+            atomicAdd(d + 0, v.x);
+            atomicAdd(d + 1, v.y);
+            atomicAdd(d + 2, v.z);
+            atomicAdd(d + 3, v.w);
+        } else {
+            if (accumulate) {
+                const float4 o = *dst;
+                v.x += o.x;
+                v.y += o.y;
+                v.z += o.z;
+                v.w += o.w;
+            }
+            *dst = v;
+        }
     }
 }
 
@@ -789,17 +987,17 @@ hipError_t launch_fast(const Geometry &g, const TilePlan &tp, const void *value,
     const int nwg = g.B * tp.wpb;
     const int nkeys = g.B * nkb;
     const size_t hist_bytes = (size_t)nkb * 4;
-    {
+    if (nkeys > 0) {
         KernelScope ks_("clear_totals_kernel", st);
         hipLaunchKernelGGL(clear_totals_kernel, dim3((nkeys + kBlock - 1) / kBlock), dim3(kBlock), 0, st, nkeys,
                            ws.totals);
     }
-    {
+    if (nkeys > 0) {
         KernelScope ks_("bin_count_kernel", st);
         hipLaunchKernelGGL((bin_count_kernel<M, L, K>), dim3(nwg), dim3(kBinThreads), hist_bytes, st, g, tp,
                            reinterpret_cast<const float2 *>(loc), ws.counts, ws.totals);
     }
-    {
+    if (nkeys > 0) {
         KernelScope ks_("scan_bases_kernel", st);
         hipLaunchKernelGGL(scan_bases_kernel, dim3(1), dim3(1024), 0, st, nkeys, ws.totals, ws.bases);
     }
@@ -816,15 +1014,22 @@ hipError_t launch_fast(const Geometry &g, const TilePlan &tp, const void *value,
     if (!accumulate) {
         int64_t n = 0;
         for (int l = 0; l < g.L; ++l)
-            if (tp.nchunk[l] > 1) n += (int64_t)g.B * g.lv.H[l] * g.lv.W[l] * g.M * g.D / 4;
+            if (level_uses_atomics(tp, l)) n += (int64_t)g.B * g.lv.H[l] * g.lv.W[l] * g.M * g.D / 4;
         if (n > 0) {
             KernelScope ks_("zero_split_levels_kernel", st);
             hipLaunchKernelGGL(zero_split_levels_kernel, dim3((unsigned)((n + kBlock - 1) / kBlock)), dim3(kBlock), 0,
                                st, g, tp, reinterpret_cast<float4 *>(gv));
         }
     }
+    if (tp.dipb > 0) {
+        const uint32_t ditems = (uint32_t)(g.B * g.M * tp.dipb);
+        KernelScope ks_("dense_accum_kernel", st);
+        hipLaunchKernelGGL((dense_accum_kernel<LG>), dim3(round_up8(ditems)), dim3(kBlock), 0, st, g, tp,
+                           reinterpret_cast<const float2 *>(loc), attn, reinterpret_cast<const float4 *>(go),
+                           reinterpret_cast<float4 *>(gv), accumulate ? 1 : 0);
+    }
     const uint32_t items = (uint32_t)(g.B * g.M * tp.ipb);
-    {
+    if (items > 0) {
         KernelScope ks_("tile_accum_kernel", st);
         hipLaunchKernelGGL((tile_accum_kernel<LG>), dim3(round_up8(items)), dim3(kBlock), 0, st, g, tp,
                            reinterpret_cast<const float2 *>(loc), attn, reinterpret_cast<const float4 *>(go),
@@ -897,10 +1102,25 @@ bool make_tile_plan(const Geometry &g, TilePlan &tp)
     const double target = 0.75 * kChunk;
     // every (cell, split) task needs a slot: cells <= kTaskSlots * lane groups
     const int max_cells = std::min(kTileCells, kTaskSlots * (kBlock / (g.D / 4)));
-    int base = 0, ibase = 0;
+    int base = 0, ibase = 0, dibase = 0;
+    tp.dense_mask = 0;
     for (int l = 0; l < g.L; ++l) {
         const int H = g.lv.H[l], W = g.lv.W[l];
         const double per_cell = (double)g.Nq * g.K / ((double)H * W);
+        tp.dparts[l] = tp.dsplit[l] = 1;
+        tp.dibase[l] = dibase;
+        if (per_cell >= kDenseMinPerPix && H * W <= kDenseMaxParts * kDensePix) {
+            // dense level: no tiles; (pixel part, query split) items
+            tp.dense_mask |= 1 << l;
+            tp.dparts[l] = (H * W + kDensePix - 1) / kDensePix;
+            const double s = std::ceil((double)g.Nq * g.K / kDenseItemSamples);
+            tp.dsplit[l] = (int)std::min<double>(kDenseMaxSplit, std::max(1.0, s));
+            dibase += tp.dparts[l] * tp.dsplit[l];
+            tp.th[l] = tp.tw[l] = tp.ntw[l] = tp.nchunk[l] = 1;
+            tp.tbase[l] = base;
+            tp.ibase[l] = ibase;
+            continue;
+        }
         int bt = 1, bw = 1, barea = 0, bcells = 1 << 30;
         for (int th = 1; th <= std::min(H, kTilePix); ++th)
             for (int tw = 1; tw <= std::min(W, kTilePix / th); ++tw) {
@@ -937,10 +1157,13 @@ bool make_tile_plan(const Geometry &g, TilePlan &tp)
         tp.ibase[l] = ibase;
         ibase += ntiles * nch;
     }
-    for (int l = g.L; l < MSDA_MAX_LEVELS; ++l)
+    for (int l = g.L; l < MSDA_MAX_LEVELS; ++l) {
         tp.th[l] = tp.tw[l] = tp.ntw[l] = tp.nchunk[l] = 1, tp.tbase[l] = base, tp.ibase[l] = ibase;
+        tp.dparts[l] = tp.dsplit[l] = 1, tp.dibase[l] = dibase;
+    }
     tp.tpb = base;
     tp.ipb = ibase;
+    tp.dipb = dibase;
     tp.qpw = kQueriesPerGroup;
     tp.wpb = (g.Nq + tp.qpw - 1) / tp.qpw;
     // the per-workgroup histogram / cursors live in LDS; record indices are 32-bit

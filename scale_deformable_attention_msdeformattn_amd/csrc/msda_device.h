@@ -78,6 +78,17 @@ __device__ __forceinline__ bool sample_in_range(float u, float v, float Wf, floa
     return (x > -2.0f) & (x < Wf + 1.0f) & (y > -2.0f) & (y < Hf + 1.0f);
 }
 
+// Workgroup barrier that orders LDS accesses only. Unlike __syncthreads it
+// does not wait for the wave's outstanding global loads, so loads issued
+// before it (a prefetch) stay in flight across it. Use it only where the
+// threads exchange data through LDS.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // DPP lane moves (VALU, no LDS traffic): within quads, lanes swapped by
 // xor 1 and xor 2; within half-rows of 8, lane i <-> 7-i; within rows of 16,
 // lane i <-> 15-i.

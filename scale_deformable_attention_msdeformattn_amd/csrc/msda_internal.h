@@ -44,7 +44,22 @@ struct TilePlan {
     int32_t tpb;  // tiles per (batch, head)
     int32_t qpw;  // queries per workgroup
     int32_t wpb;  // workgroups per batch
+    // Dense levels (bit l of dense_mask) have no tiles and no records: their
+    // grad_value is accumulated from the samples directly, per (pixel part,
+    // query split) work item.
+    int32_t dense_mask;
+    int32_t dparts[MSDA_MAX_LEVELS];  // pixel parts of a dense level
+    int32_t dsplit[MSDA_MAX_LEVELS];  // query splits of a dense level
+    int32_t dibase[MSDA_MAX_LEVELS];  // first dense item of the level within (batch, head)
+    int32_t dipb;                     // dense items per (batch, head)
 };
+
+// Whether level l's grad_value rows are summed with float atomics (they must
+// then be zeroed first unless the call accumulates).
+__host__ __device__ inline bool level_uses_atomics(const TilePlan &tp, int l)
+{
+    return ((tp.dense_mask >> l) & 1) ? tp.dsplit[l] > 1 : tp.nchunk[l] > 1;
+}
 
 // Whether the backward takes the tiled fast path for this call (it then needs
 // backward_workspace_bytes(g) bytes of workspace), and that size (0 when the
