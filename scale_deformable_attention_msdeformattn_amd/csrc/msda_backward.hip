@@ -228,10 +228,12 @@ scan_bases_kernel(int nkeys, const uint32_t *__restrict__ totals, uint32_t *__re
 
 // --------------------------------------------------------------------- 3. main
 
-// Waves per workgroup of the main kernel: as many as fit about 104 KB of LDS.
+// Waves per workgroup of the main kernel: as many (16, 8 or 4) as fit 56 KB of
+// per-wave LDS staging, so that several workgroups share a CU.
 template <int M, int L, int K> struct MainWaves {
-    static constexpr int kPerWave = 3 * M * (L * K + 1) * 16;
-    static constexpr int kValue = 104 * 1024 / kPerWave >= 16 ? 16 : 104 * 1024 / kPerWave >= 8 ? 8 : 4;
+    static constexpr int kPerWave = 2 * M * (L * K + 1) * 16;
+    static constexpr int kBudget = 56 * 1024;
+    static constexpr int kValue = kBudget / kPerWave >= 16 ? 16 : kBudget / kPerWave >= 8 ? 8 : 4;
 };
 
 template <typename VT, int M, int L, int K>
@@ -255,8 +257,10 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
     extern __shared__ uint32_t s_cursor[];  // [M * tpb]
     __shared__ LevelRec s_lv[L];
     __shared__ int4 s_off[MW][M * PAD];
-    __shared__ float4 s_geo[MW][M * PAD];   // (fx, fy, A, -)
-    __shared__ float4 s_res[MW][M * PAD];   // (grad_attn, grad_x, grad_y, -)
+    // (fx, fy, A, -) per sample; each entry is overwritten in place by its
+    // (grad_attn, grad_x, grad_y, -) once the wave has read it (a wave's LDS
+    // accesses execute in program order)
+    __shared__ float4 s_geo[MW][M * PAD];
 
     const int lane = threadIdx.x % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -325,7 +329,7 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
         const float4 G = grad_out[gq * (C / 4) + lane];
         const int4 *offs = &s_off[wave][m * PAD];
         const float4 *geo = &s_geo[wave][m * PAD];
-        float4 *res = &s_res[wave][m * PAD];
+        float4 *res = &s_geo[wave][m * PAD];
 #pragma unroll
         for (int l = 0; l < L; ++l) {
             const float Wf = (float)g.lv.W[l], Hf = (float)g.lv.H[l];
@@ -356,7 +360,7 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
         for (int s0 = 0; s0 < NS; s0 += kWave) {
             const int s = s0 + lane;
             if (NS % kWave == 0 || s < NS) {
-                const float4 r = s_res[wave][s + s / LK];
+                const float4 r = s_geo[wave][s + s / LK];
                 grad_attn[gq * NS + s] = r.x;
                 grad_loc[gq * NS + s] = make_float2(r.y, r.z);
             }
@@ -437,6 +441,11 @@ tile_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, const
     const uint32_t nsamples = (uint32_t)g.samples();
     const int grp = threadIdx.x / LG;
     const int lig = threadIdx.x % LG;
+    // grad_output rows through a buffer resource: 32-bit offsets, and an
+    // out-of-range offset reads zeros (the host keeps grad_output < 2 GB)
+    const __amdgpu_buffer_rsrc_t grs = make_rsrc(grad_out, (uint32_t)((uint64_t)g.queries() * g.M * LG * 16));
+    const uint32_t grow_bytes = (uint32_t)g.M * LG * 16;  // one query's row, all heads
+    const uint32_t gbase = ((uint32_t)m * LG + lig) * 16;
     uint32_t rbeg = bases[key];
     uint32_t rtot = totals[key];
 
@@ -493,7 +502,7 @@ tile_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, const
         // reduce over the lane groups: slots [group * kDirectPix + p]
 #pragma unroll
         for (int p = 0; p < kDirectPix; ++p) s_part[grp * kDirectPix + p][lig] = acc[p];
-        __syncthreads();
+        lds_barrier();
         if (grp < npix) {
             float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
             for (int q = 0; q < NG; ++q) {
@@ -533,7 +542,7 @@ tile_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, const
     for (uint32_t c0r = 0; c0r < rtot; c0r += kChunk) {
         const int n = (int)min((uint32_t)kChunk, rtot - c0r);
         for (int i = threadIdx.x; i < ncells; i += kBlock) s_cur[i] = 0;
-        __syncthreads();
+        lds_barrier();
         // this chunk's records: geometry and cell; count per cell
         for (int i = threadIdx.x; i < n; i += kBlock) {
             const uint32_t sidx = records[rbeg + c0r + i];
@@ -552,7 +561,7 @@ tile_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, const
             s_cell[i] = cell < 0 ? (uint8_t)0xff : (uint8_t)cell;
             if (cell >= 0) atomicAdd(&s_cur[cell], 1u);
         }
-        __syncthreads();
+        lds_barrier();
         // exclusive scan of the (at most kTileCells = 2 * kWave) cell counts, one wave
         if (threadIdx.x < kWave) {
             const int i0 = 2 * threadIdx.x;
@@ -569,10 +578,10 @@ tile_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, const
             if (i0 + 1 < ncells) s_start[i0 + 1] = s_cur[i0 + 1] = ex + a;
             if (threadIdx.x == kWave - 1) s_start[ncells] = incl;
         }
-        __syncthreads();
+        lds_barrier();
         for (int i = threadIdx.x; i < n; i += kBlock)
             if (s_cell[i] != 0xff) s_entry[atomicAdd(&s_cur[s_cell[i]], 1u)] = (uint16_t)i;
-        __syncthreads();
+        lds_barrier();
         // (cell, split) tasks; each adds its four corner sums into its own
         // (pixel, role, split) slots, which no other task touches
         for (int t = 0; t < kTaskSlots; ++t) {
@@ -584,17 +593,18 @@ tile_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, const
             for (int r = 0; r < 4; ++r) acc[r] = make_float4(0.f, 0.f, 0.f, 0.f);
             const uint32_t e_end = s_start[cell + 1];
             for (uint32_t e0 = s_start[cell] + split; e0 < e_end; e0 += S * kBatch) {
+                // branch-free batch: entries past the cell's end re-read its
+                // last entry and load a zero G row (out-of-range offset)
                 float4 pay[kBatch], gv[kBatch];
+                uint32_t ent[kBatch];
+#pragma unroll
+                for (int j = 0; j < kBatch; ++j) ent[j] = s_entry[min(e0 + j * S, e_end - 1)];
+#pragma unroll
+                for (int j = 0; j < kBatch; ++j) pay[j] = s_pay[ent[j]];
 #pragma unroll
                 for (int j = 0; j < kBatch; ++j) {
-                    const uint32_t e = e0 + j * S;
-                    pay[j] = e < e_end ? s_pay[s_entry[e]] : make_float4(0.f, 0.f, 0.f, 0.f);
-                }
-#pragma unroll
-                for (int j = 0; j < kBatch; ++j) {
-                    const uint32_t e = e0 + j * S;
-                    const uint32_t bq = __float_as_uint(pay[j].w);
-                    gv[j] = e < e_end ? grad_out[((int64_t)bq * g.M + m) * LG + lig] : make_float4(0.f, 0.f, 0.f, 0.f);
+                    const uint32_t off = __float_as_uint(pay[j].w) * grow_bytes + gbase;
+                    gv[j] = load_f32x4(grs, e0 + j * S < e_end ? off : kOutOfRange);
                 }
 #pragma unroll
                 for (int j = 0; j < kBatch; ++j) {
@@ -624,8 +634,9 @@ tile_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, const
                 }
             }
         }
-        __syncthreads();  // LDS is reused by the next chunk
+        lds_barrier();  // LDS is reused by the next chunk
     }
+    if (rtot == 0) lds_barrier();  // orders the zeroing of s_part before the sums below
     for (int pix = grp; pix < npix; pix += NG) {
         float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
         for (int i = 0; i < 4 * S; ++i) {
@@ -695,7 +706,8 @@ constexpr int kDenseMaxSplit = 64;
 template <int LG>
 __global__ void __launch_bounds__(kBlock)
 dense_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, const float *__restrict__ attn,
-                   const float4 *__restrict__ grad_out, float4 *__restrict__ grad_value, int accumulate)
+                   const float4 *__restrict__ grad_out, float4 *__restrict__ grad_value,
+                   float4 *__restrict__ partials, int accumulate)
 {
     constexpr int NG = kBlock / LG;                  // lane groups
     constexpr int PPG = kDensePix / NG;              // pixel slots per lane group
@@ -859,20 +871,17 @@ dense_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, cons
             }
         }
     }
-    // write the part's pixels: one writer per pixel unless the queries are split
+    // one query split: write the part's pixels; several: park the sums in the
+    // item's workspace slot for dense_reduce
 #pragma unroll
     for (int j = 0; j < PPG; ++j) {
         const int pl = grp + j * NG;
         if (pl >= npix) break;
-        float4 *dst = grad_value + (((int64_t)b * g.S + lstart + p0 + pl) * g.M + m) * LG + lig;
         float4 v = acc[j];
         if (splits > 1) {
-            float *d = reinterpret_cast<float *>(dst);
-            atomicAdd(d + 0, v.x);
-            atomicAdd(d + 1, v.y);
-            atomicAdd(d + 2, v.z);
-            atomicAdd(d + 3, v.w);
+            partials[((int64_t)item * kDensePix + pl) * LG + lig] = v;
         } else {
+            float4 *dst = grad_value + (((int64_t)b * g.S + lstart + p0 + pl) * g.M + m) * LG + lig;
             if (accumulate) {
                 const float4 o = *dst;
                 v.x += o.x;
@@ -882,6 +891,54 @@ dense_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, cons
             }
             *dst = v;
         }
+    }
+}
+
+// Sum the query splits of the dense levels, in split order, into grad_value.
+// One thread per (batch, pixel, head, float4 of channels) of the split levels.
+template <int LG>
+__global__ void __launch_bounds__(kBlock)
+dense_reduce_kernel(Geometry g, TilePlan tp, const float4 *__restrict__ partials, float4 *__restrict__ grad_value,
+                    int accumulate)
+{
+    int64_t t = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    for (int l = 0; l < g.L; ++l) {
+        if (!((tp.dense_mask >> l) & 1) || tp.dsplit[l] <= 1) continue;
+        const int npix_l = g.lv.H[l] * g.lv.W[l];
+        const int64_t n = (int64_t)g.B * npix_l * g.M * LG;
+        if (t >= n) {
+            t -= n;
+            continue;
+        }
+        const int c = (int)(t % LG);
+        const int m = (int)((t / LG) % g.M);
+        const int p = (int)((t / ((int64_t)LG * g.M)) % npix_l);
+        const int b = (int)(t / ((int64_t)LG * g.M * npix_l));
+        const int parts = tp.dparts[l], splits = tp.dsplit[l];
+        // the part holding pixel p: parts start at floor(npix_l * k / parts)
+        int part = (int)((int64_t)p * parts / npix_l);
+        while (part + 1 < parts && (int)((int64_t)npix_l * (part + 1) / parts) <= p) ++part;
+        while (part > 0 && (int)((int64_t)npix_l * part / parts) > p) --part;
+        const int pl = p - (int)((int64_t)npix_l * part / parts);
+        const int64_t item0 = (int64_t)(b * g.M + m) * tp.dipb + tp.dibase[l] + (int64_t)part * splits;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int s = 0; s < splits; ++s) {
+            const float4 x = partials[((item0 + s) * kDensePix + pl) * LG + c];
+            v.x += x.x;
+            v.y += x.y;
+            v.z += x.z;
+            v.w += x.w;
+        }
+        float4 *dst = grad_value + (((int64_t)b * g.S + g.lv.start[l] + p) * g.M + m) * LG + c;
+        if (accumulate) {
+            const float4 o = *dst;
+            v.x += o.x;
+            v.y += o.y;
+            v.z += o.z;
+            v.w += o.w;
+        }
+        *dst = v;
+        return;
     }
 }
 
@@ -952,6 +1009,7 @@ backward_generic_kernel(Geometry g, const VT *__restrict__ value, const float2 *
 
 struct Workspace {
     uint32_t *counts, *totals, *bases, *records;
+    float4 *partials;  // per dense work item: kDensePix pixels x D channels
 };
 
 inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
@@ -972,6 +1030,7 @@ size_t layout(const Geometry &g, const TilePlan &tp, char *base, Workspace *ws)
     w.totals = take(nkeys * 4);
     w.bases = take(nkeys * 4);
     w.records = take(nrec * 4);
+    w.partials = reinterpret_cast<float4 *>(take((size_t)g.B * g.M * tp.dipb * kDensePix * g.D * 4));
     if (ws) *ws = w;
     return off;
 }
@@ -1023,10 +1082,21 @@ hipError_t launch_fast(const Geometry &g, const TilePlan &tp, const void *value,
     }
     if (tp.dipb > 0) {
         const uint32_t ditems = (uint32_t)(g.B * g.M * tp.dipb);
-        KernelScope ks_("dense_accum_kernel", st);
-        hipLaunchKernelGGL((dense_accum_kernel<LG>), dim3(round_up8(ditems)), dim3(kBlock), 0, st, g, tp,
-                           reinterpret_cast<const float2 *>(loc), attn, reinterpret_cast<const float4 *>(go),
-                           reinterpret_cast<float4 *>(gv), accumulate ? 1 : 0);
+        {
+            KernelScope ks_("dense_accum_kernel", st);
+            hipLaunchKernelGGL((dense_accum_kernel<LG>), dim3(round_up8(ditems)), dim3(kBlock), 0, st, g, tp,
+                               reinterpret_cast<const float2 *>(loc), attn, reinterpret_cast<const float4 *>(go),
+                               reinterpret_cast<float4 *>(gv), ws.partials, accumulate ? 1 : 0);
+        }
+        int64_t nred = 0;
+        for (int l = 0; l < g.L; ++l)
+            if (((tp.dense_mask >> l) & 1) && tp.dsplit[l] > 1)
+                nred += (int64_t)g.B * g.lv.H[l] * g.lv.W[l] * g.M * LG;
+        if (nred > 0) {
+            KernelScope ks_("dense_reduce_kernel", st);
+            hipLaunchKernelGGL((dense_reduce_kernel<LG>), dim3((unsigned)((nred + kBlock - 1) / kBlock)), dim3(kBlock), 0,
+                               st, g, tp, ws.partials, reinterpret_cast<float4 *>(gv), accumulate ? 1 : 0);
+        }
     }
     const uint32_t items = (uint32_t)(g.B * g.M * tp.ipb);
     if (items > 0) {
@@ -1169,6 +1239,8 @@ bool make_tile_plan(const Geometry &g, TilePlan &tp)
     // the per-workgroup histogram / cursors live in LDS; record indices are 32-bit
     if ((size_t)g.M * tp.tpb * 4 > 64 * 1024) return false;
     if ((uint64_t)g.samples() * 4 >= (1ull << 32)) return false;
+    // grad_output is read through 32-bit buffer offsets below the out-of-range marker
+    if ((uint64_t)g.queries() * g.M * g.D * 4 >= (uint64_t)kOutOfRange) return false;
     return true;
 }
 

@@ -55,10 +55,11 @@ struct TilePlan {
 };
 
 // Whether level l's grad_value rows are summed with float atomics (they must
-// then be zeroed first unless the call accumulates).
+// then be zeroed first unless the call accumulates): the split tiles of the
+// direct mode. Dense levels sum their query splits in a second pass.
 __host__ __device__ inline bool level_uses_atomics(const TilePlan &tp, int l)
 {
-    return ((tp.dense_mask >> l) & 1) ? tp.dsplit[l] > 1 : tp.nchunk[l] > 1;
+    return !((tp.dense_mask >> l) & 1) && tp.nchunk[l] > 1;
 }
 
 // Whether the backward takes the tiled fast path for this call (it then needs
