@@ -85,28 +85,47 @@ def unique_value_bytes(loc, shapes, B, M, row_bytes):
     return int(touched.sum().item()) * row_bytes
 
 
-def algorithmic_bytes(B, M, D, Nq, S, L, K, vbytes):
-    """Bytes each kernel must move at the least (read + write, fp32 unless
-    noted), per launch. `vbytes` = the distinct value rows the samples touch.
-    Scratch-only kernels of the backward (binning, scans, clears) count the
-    op's own arrays they read, not their workspace traffic."""
+def dense_levels(shapes, Nq, K):
+    """The levels the backward treats as dense (no tile records): at least 24
+    samples per pixel per batch and head, and at most 8 x 256 pixels. This
+    mirrors the library's tile planner so that each backward kernel is
+    charged for the levels it handles."""
+    return [l for l, (H, W) in enumerate(shapes) if Nq * K >= 24 * H * W and H * W <= 8 * 256]
+
+
+def algorithmic_bytes(B, M, D, Nq, shapes, K, vbytes):
+    """Bytes each kernel must move at the least (read + write, fp32), per
+    launch. `vbytes` = the distinct value rows the samples touch. Kernels that
+    only touch workspace (clears, scans, the dense split sums) count the op's
+    own arrays they read or write, and scratch-only ones count 0."""
     f32 = 4
+    L = len(shapes)
+    S = sum(H * W for H, W in shapes)
     samples = B * Nq * M * L * K
-    rows = B * Nq * M * D * f32          # output / grad_output
-    grad_value = B * S * M * D * f32
+    per_level = B * Nq * M * K              # samples of one level
+    rows = B * Nq * M * D * f32             # output / grad_output
+    dense = dense_levels(shapes, Nq, K)
+    dense_pix = sum(shapes[l][0] * shapes[l][1] for l in dense)
+    sparse_samples = per_level * (L - len(dense))
+    dense_samples = per_level * len(dense)
+    gv_row = B * M * D * f32                 # grad_value bytes per pixel
     return {
         "reference_points_kernel": B * L * 2 * f32 + B * Nq * L * 2 * f32,
         "sampling_locations_kernel": B * Nq * L * 2 * f32 + 2 * samples * 2 * f32,
         "softmax_vec_kernel": 2 * samples * f32,
         "forward_c256_kernel": vbytes + samples * 3 * f32 + rows,
-        "zero_fill_kernel": grad_value,
+        "zero_fill_kernel": S * gv_row,
         "clear_totals_kernel": 0,
-        "bin_count_kernel": samples * 2 * f32,
+        "bin_count_kernel": sparse_samples * 2 * f32,
         "scan_bases_kernel": 0,
         # value rows, loc, A, grad_output in; grad_loc, grad_A out
         "backward_c256_kernel": vbytes + samples * 3 * f32 + rows + samples * 3 * f32,
-        # grad_output, loc, A in; grad_value out
-        "tile_accum_kernel": rows + samples * 3 * f32 + grad_value,
+        # sparse levels: grad_output, their loc and A in; their grad_value rows out
+        "tile_accum_kernel": rows + sparse_samples * 3 * f32 + (S - dense_pix) * gv_row,
+        # dense levels: grad_output, their loc and A in (sums parked in workspace)
+        "dense_accum_kernel": rows + dense_samples * 3 * f32,
+        # dense levels: their grad_value rows out
+        "dense_reduce_kernel": dense_pix * gv_row,
     }
 
 
@@ -171,7 +190,7 @@ def ingest_counters(d, copy_mib, workload):
 
     fetch_scale = copy_kib / copy_avg("copy_fetch", "FETCH_SIZE")
     write_scale = copy_kib / copy_avg("copy_write", "WRITE_SIZE")
-    names = list(algorithmic_bytes(1, 1, 1, 1, 1, 1, 1, 0))
+    names = list(algorithmic_bytes(1, 1, 1, 1, [(1, 1)], 1, 0))
     kernels = {}
     for counter, sub in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
         for full, v in _counter_rows(os.path.join(d, sub), counter):
@@ -305,7 +324,7 @@ def main():
     torch.cuda.synchronize()
 
     vbytes = unique_value_bytes(state["loc"], shapes.to(dev), B, M, D * elem)
-    alg = algorithmic_bytes(B, M, D, Nq, S, L, K, vbytes)
+    alg = algorithmic_bytes(B, M, D, Nq, [tuple(int(v) for v in hw) for hw in shapes.tolist()], K, vbytes)
 
     # ---- timed region 1: whole steps (graph replay unless --eager) ----
     graph = None

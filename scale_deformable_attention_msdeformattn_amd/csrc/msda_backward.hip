@@ -49,7 +49,7 @@ constexpr int kQueriesPerGroup = 64;     // queries per workgroup of bin_count a
 constexpr int kChunk = 1024;             // records per LDS chunk in tile_accum
 constexpr int kTilePix = 32;             // pixels per tile
 constexpr int kTileCells = 2 * kWave;    // cells per tile (the tile plus one row and column of halo)
-constexpr int kTaskSlots = 4;            // (cell, split) tasks per lane group in tile_accum
+constexpr int kTaskSlots = 1;            // (cell, split) tasks per lane group in tile_accum
 constexpr int kBatch = 8;                // records in flight per task
 constexpr int kDirectPix = 4;            // tiles this small skip the per-cell sort
 constexpr int kDirectRecords = 768;      // records per workgroup in direct mode
@@ -712,9 +712,8 @@ dense_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, cons
     constexpr int NG = kBlock / LG;                  // lane groups
     constexpr int PPG = kDensePix / NG;              // pixel slots per lane group
     constexpr int kPer = kDenseSub / kBlock;         // samples per thread per sub-chunk
-    constexpr int kGRows = kDenseQ * LG / kBlock;    // float4 of G staged per thread
-    static_assert(kDensePix % NG == 0 && kDenseSub % kBlock == 0 && (kDenseQ * LG) % kBlock == 0,
-                  "dense tiling");
+    constexpr int kGRows = (kDenseQ * LG + kBlock - 1) / kBlock;  // float4 of G staged per thread
+    static_assert(kDensePix % NG == 0 && kDenseSub % kBlock == 0, "dense tiling");
     __shared__ float4 s_g[kDenseQ * LG];       // G rows of the sub-chunk's queries
     __shared__ uint2 s_pair[4 * kDenseSub];    // (bits(A * w_c), query slot), sorted by pixel
     __shared__ uint32_t s_cnt[kDensePix];
@@ -788,7 +787,8 @@ dense_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, cons
     for (int qa = qa0; qa < qa1; qa += QS) {
         lds_barrier();  // s_cnt cleared; the previous sub-chunk is done with s_g and s_pair
 #pragma unroll
-        for (int t = 0; t < kGRows; ++t) s_g[threadIdx.x + t * kBlock] = gst[t];
+        for (int t = 0; t < kGRows; ++t)
+            if ((kDenseQ * LG) % kBlock == 0 || threadIdx.x + t * kBlock < kDenseQ * LG) s_g[threadIdx.x + t * kBlock] = gst[t];
         // rank this part's pairs within their pixel's count
         int pix[kPer][4];
         uint32_t rank[kPer][4];
