@@ -60,6 +60,11 @@ def _bind(lib):
                                                    ctypes.c_int, _i64p, _f64p, _f64p, _f64p]
     lib.msda_oracle_softmax.restype = None
     lib.msda_oracle_softmax.argtypes = [ctypes.c_int64, ctypes.c_int, _f64p, _f64p]
+    lib.msda_oracle_softmax_backward.restype = None
+    lib.msda_oracle_softmax_backward.argtypes = [ctypes.c_int64, ctypes.c_int, _f64p, _f64p, _f64p]
+    lib.msda_oracle_sampling_locations_backward.restype = None
+    lib.msda_oracle_sampling_locations_backward.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                                            ctypes.c_int, _i64p, _f64p, _f64p, _f64p]
     lib.msda_oracle_forward.restype = None
     lib.msda_oracle_forward.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                                         ctypes.c_int, ctypes.c_int, _i64p, _i64p, _f64p, _f64p, _f64p,
@@ -149,6 +154,29 @@ def softmax(logits, n):
     out = np.empty_like(flat)
     _load().msda_oracle_softmax(flat.shape[0], n, _p(flat, _f64p), _p(out, _f64p))
     return out.reshape(shape)
+
+
+def softmax_backward(attn, grad_attn, n):
+    """grad_logits for A = softmax(logits) over trailing groups of n entries."""
+    a = _f64(attn)
+    g = _f64(grad_attn)
+    assert a.shape == g.shape
+    fa, fg = a.reshape(-1, n), g.reshape(-1, n)
+    out = np.empty_like(fa)
+    _load().msda_oracle_softmax_backward(fa.shape[0], n, _p(fa, _f64p), _p(fg, _f64p), _p(out, _f64p))
+    return out.reshape(a.shape)
+
+
+def sampling_locations_backward(spatial_shapes, grad_loc):
+    """(grad_ref [B,Nq,L,2], grad_offset_px [B,Nq,M,L,K,2]) of loc = ref + offset_px / (W_l, H_l)."""
+    shapes = _i64(spatial_shapes).reshape(-1, 2)
+    gl = _f64(grad_loc)
+    B, Nq, M, L, K, _ = gl.shape
+    gref = np.empty((B, Nq, L, 2), dtype=np.float64)
+    goff = np.empty_like(gl)
+    _load().msda_oracle_sampling_locations_backward(B, Nq, M, L, K, _p(shapes, _i64p), _p(gl, _f64p),
+                                                    _p(gref, _f64p), _p(goff, _f64p))
+    return gref, goff
 
 
 def forward(value, spatial_shapes, level_start_index, sampling_locations, attention_weights,

@@ -134,6 +134,50 @@ void msda_oracle_softmax(int64_t rows, int n, const double *logits, double *out)
     }
 }
 
+/* Backward of the L*K softmax ([P4] "Insight 2" normalisation): with
+ * A = softmax(x) over one row, dA_i/dx_j = A_i (delta_ij - A_j), so
+ * grad_x_i = A_i (grad_A_i - sum_j A_j grad_A_j). */
+void msda_oracle_softmax_backward(int64_t rows, int n, const double *attn, const double *grad_attn,
+                                  double *grad_logits)
+{
+    for (int64_t r = 0; r < rows; ++r) {
+        const double *a = attn + r * n;
+        const double *ga = grad_attn + r * n;
+        double dot = 0.0;
+        for (int j = 0; j < n; ++j) dot += a[j] * ga[j];
+        for (int i = 0; i < n; ++i) grad_logits[r * n + i] = a[i] * (ga[i] - dot);
+    }
+}
+
+/* Backward of the location formation ([P2] "encoder", [P4] "Key code"):
+ * loc = ref[b,q,l] + offset_px / (W_l, H_l), so grad_offset_px = grad_loc /
+ * (W_l, H_l) and grad_ref[b,q,l] = sum over heads and points of grad_loc.
+ * grad_ref may be NULL. */
+void msda_oracle_sampling_locations_backward(int B, int64_t Nq, int M, int L, int K,
+                                             const int64_t *shapes, const double *grad_loc,
+                                             double *grad_ref, double *grad_offset_px)
+{
+    if (grad_ref)
+        for (int64_t i = 0; i < (int64_t)B * Nq * L * 2; ++i) grad_ref[i] = 0.0;
+    for (int b = 0; b < B; ++b)
+        for (int64_t q = 0; q < Nq; ++q)
+            for (int m = 0; m < M; ++m)
+                for (int l = 0; l < L; ++l) {
+                    const double H = (double)shapes[2 * l + 0];
+                    const double W = (double)shapes[2 * l + 1];
+                    for (int k = 0; k < K; ++k) {
+                        const int64_t idx = ((((b * Nq + q) * M + m) * L + l) * K + k) * 2;
+                        grad_offset_px[idx + 0] = grad_loc[idx + 0] / W;
+                        grad_offset_px[idx + 1] = grad_loc[idx + 1] / H;
+                        if (grad_ref) {
+                            double *gr = grad_ref + ((b * Nq + q) * L + l) * 2;
+                            gr[0] += grad_loc[idx + 0];
+                            gr[1] += grad_loc[idx + 1];
+                        }
+                    }
+                }
+}
+
 /* One bilinear sample's geometry on a level of size H x W: the pixel
  * coordinates of the top-left corner of its cell and the fractional parts.
  * Returns 0 if the location is non-finite or so far out that no corner can be

@@ -58,6 +58,17 @@ void msda_oracle_sampling_locations(int B, int64_t Nq, int M, int L, int K,
  * levels and points, so n = L*K). */
 void msda_oracle_softmax(int64_t rows, int n, const double *logits, double *out);
 
+/* Backward of msda_oracle_softmax ([P4] "Insight 2"): grad_logits[r,i] =
+ * A[r,i] * (grad_A[r,i] - sum_j A[r,j] grad_A[r,j]). */
+void msda_oracle_softmax_backward(int64_t rows, int n, const double *attn, const double *grad_attn,
+                                  double *grad_logits);
+
+/* Backward of msda_oracle_sampling_locations: grad_offset_px = grad_loc /
+ * (W_l, H_l); grad_ref [B,Nq,L,2] (may be NULL) = sum over m, k of grad_loc. */
+void msda_oracle_sampling_locations_backward(int B, int64_t Nq, int M, int L, int K,
+                                             const int64_t *shapes, const double *grad_loc,
+                                             double *grad_ref, double *grad_offset_px);
+
 /* Forward ([P4] "Insight 2" equation, bracketed sum; [P2] "encoder" core:
  * bilinear sampling, zero padding, align_corners=False):
  * out[b,q,m*D+d] = sum_{l,k} A[b,q,m,l,k] * bilinear(value_l[b,:,:,m,d], loc).

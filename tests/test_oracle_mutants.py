@@ -10,6 +10,7 @@ import oracle
 from oracle import build as obuild
 from tests import test_oracle_backward as tb
 from tests import test_oracle_forward as tf
+from tests import test_oracle_fused_grads as tg
 from tests import test_oracle_prologue as tp
 
 
@@ -37,6 +38,13 @@ def _prologue_pins():
     tp.test_softmax_matches_scipy_and_sums_to_one_over_levels_and_points()
 
 
+def _fused_grad_pins():
+    tg.test_softmax_backward_matches_explicit_jacobian()
+    tg.test_softmax_backward_central_differences()
+    tg.test_locations_backward_central_differences()
+    tg.test_locations_backward_scales_by_level_size()
+
+
 MUTANTS = [
     # (name, text in msda_oracle.c, replacement, pins expected to catch it)
     ("swapped_x_weights", "(dx ? fx : 1.0 - fx)", "(dx ? 1.0 - fx : fx)", _forward_pins),
@@ -58,6 +66,11 @@ MUTANTS = [
     ("lsi_inclusive", "lsi_out[l] = start;\n        start += shapes[2 * l + 0] * shapes[2 * l + 1];",
      "start += shapes[2 * l + 0] * shapes[2 * l + 1];\n        lsi_out[l] = start;", _prologue_pins),
     ("softmax_no_normalise", "for (int i = 0; i < n; ++i) y[i] /= sum;", "", _prologue_pins),
+    ("softmax_grad_drops_mean", "a[i] * (ga[i] - dot)", "a[i] * ga[i]", _fused_grad_pins),
+    ("softmax_grad_wrong_factor", "a[i] * (ga[i] - dot)", "(ga[i] - dot)", _fused_grad_pins),
+    ("offset_grad_swapped_normaliser", "grad_offset_px[idx + 0] = grad_loc[idx + 0] / W;",
+     "grad_offset_px[idx + 0] = grad_loc[idx + 0] / H;", _fused_grad_pins),
+    ("ref_grad_one_term", "gr[0] += grad_loc[idx + 0];", "gr[0] = grad_loc[idx + 0];", _fused_grad_pins),
 ]
 
 
