@@ -96,6 +96,11 @@ def load():
     lib.msda_backward.restype = ctypes.c_int
     lib.msda_backward.argtypes = [_shp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                                   ctypes.c_uint, _vp]
+    lib.msda_forward_fused.restype = ctypes.c_int
+    lib.msda_forward_fused.argtypes = [_shp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+    lib.msda_backward_fused.restype = ctypes.c_int
+    lib.msda_backward_fused.argtypes = [_shp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                        ctypes.c_size_t, ctypes.c_uint, _vp]
     lib.msda_timing_enable.restype = ctypes.c_int
     lib.msda_timing_enable.argtypes = [ctypes.c_int]
     lib.msda_timing_reset.restype = ctypes.c_int
@@ -300,6 +305,73 @@ def msda_backward(value: torch.Tensor, spatial_shapes, level_start_index, sampli
     _check(load().msda_backward(sh.ptr, _p(value), vt, _p(loc), _p(attn), _p(go), _p(grad_value), _p(gl),
                                 _p(ga), _p(ws), nbytes, flags, _stream(go)), "msda_backward")
     return grad_value, gl, ga
+
+
+def msda_forward_fused(value: torch.Tensor, spatial_shapes, level_start_index, reference_points: torch.Tensor,
+                       sampling_offsets: torch.Tensor, attention_logits: torch.Tensor):
+    """Fused forward: locations and the L*K softmax formed inside the core.
+    reference_points [B,Nq,L,2], sampling_offsets [B,Nq,M,L,K,2] (pixels of
+    level l), attention_logits [B,Nq,M,L*K] ->
+    (output [B,Nq,M*D], sampling_locations, attention_weights)."""
+    if value.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"value must be float32 or bfloat16 (got {value.dtype})")
+    value = _dev(value, "value", None)
+    ref = _dev(reference_points, "reference_points")
+    off = _dev(sampling_offsets, "sampling_offsets")
+    logits = _dev(attention_logits, "attention_logits")
+    if value.dim() != 4:
+        raise ValueError("value must be [B, S, M, D]")
+    B, S, M, D = value.shape
+    if off.dim() != 6 or off.shape[0] != B or off.shape[2] != M or off.shape[-1] != 2:
+        raise ValueError(f"sampling_offsets must be [{B}, Nq, {M}, L, K, 2], got {tuple(off.shape)}")
+    _, Nq, _, L, K, _ = off.shape
+    if tuple(ref.shape) != (B, Nq, L, 2):
+        raise ValueError(f"reference_points must be {(B, Nq, L, 2)}, got {tuple(ref.shape)}")
+    if tuple(logits.shape) != (B, Nq, M, L * K):
+        raise ValueError(f"attention_logits must be {(B, Nq, M, L * K)}, got {tuple(logits.shape)}")
+    sh = Shape(spatial_shapes, B, M, D, K, Nq, level_start_index)
+    if sh.levels != L:
+        raise ValueError("spatial_shapes and sampling_offsets disagree on the level count")
+    sh.c.num_value = S
+    vt = MSDA_BF16 if value.dtype == torch.bfloat16 else MSDA_F32
+    out = torch.empty(B, Nq, M * D, dtype=torch.float32, device=value.device)
+    loc = torch.empty_like(off)
+    attn = torch.empty(B, Nq, M, L, K, dtype=torch.float32, device=value.device)
+    _check(load().msda_forward_fused(sh.ptr, _p(value), vt, _p(ref), _p(off), _p(logits), _p(out), _p(loc),
+                                     _p(attn), _stream(out)), "msda_forward_fused")
+    return out, loc, attn
+
+
+def msda_backward_fused(value: torch.Tensor, spatial_shapes, level_start_index, sampling_locations: torch.Tensor,
+                        attention_weights: torch.Tensor, grad_output: torch.Tensor,
+                        grad_value: Optional[torch.Tensor] = None, reference_grad: bool = True):
+    """Backward of msda_forward_fused, from the locations and weights it
+    returned -> (grad_value [B,S,M,D], grad_sampling_offsets [B,Nq,M,L,K,2],
+    grad_attention_logits [B,Nq,M,L*K], grad_reference_points [B,Nq,L,2] or
+    None). If grad_value is given it is accumulated into."""
+    value, loc, attn, sh, vt = _core_shape(value, spatial_shapes, level_start_index, sampling_locations,
+                                           attention_weights)
+    B, S, M, D = value.shape
+    _, Nq, _, L, K, _ = loc.shape
+    go = _dev(grad_output, "grad_output")
+    if tuple(go.shape) != (B, Nq, M * D):
+        raise ValueError(f"grad_output must be {(B, Nq, M * D)}, got {tuple(go.shape)}")
+    flags = 0
+    if grad_value is None:
+        grad_value = torch.empty(B, S, M, D, dtype=torch.float32, device=value.device)
+    else:
+        if grad_value.dtype != torch.float32 or tuple(grad_value.shape) != (B, S, M, D) or \
+                not grad_value.is_contiguous():
+            raise ValueError("grad_value to accumulate into must be a contiguous fp32 [B,S,M,D] tensor")
+        flags = MSDA_BWD_ACCUMULATE
+    goff = torch.empty_like(loc)
+    glog = torch.empty(B, Nq, M, L * K, dtype=torch.float32, device=value.device)
+    gref = torch.empty(B, Nq, L, 2, dtype=torch.float32, device=value.device) if reference_grad else None
+    nbytes = msda_backward_workspace_size(sh)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=value.device)
+    _check(load().msda_backward_fused(sh.ptr, _p(value), vt, _p(loc), _p(attn), _p(go), _p(grad_value), _p(goff),
+                                      _p(glog), _p(gref), _p(ws), nbytes, flags, _stream(go)), "msda_backward_fused")
+    return grad_value, goff, glog, gref
 
 
 def msda_backward_workspace_size(shape: "Shape") -> int:

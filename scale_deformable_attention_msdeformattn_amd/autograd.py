@@ -28,6 +28,32 @@ class MSDeformAttnFunction(torch.autograd.Function):
         return gv, None, None, gl, ga
 
 
+class MSDeformAttnFusedFunction(torch.autograd.Function):
+    """value, reference points, pixel offsets and logits -> output, with the
+    location formation and the L*K softmax inside the core; gradients for all
+    four tensor inputs."""
+
+    @staticmethod
+    def forward(ctx, value, spatial_shapes, level_start_index, reference_points, sampling_offsets,
+                attention_logits):
+        out, loc, attn = B.msda_forward_fused(value, spatial_shapes, level_start_index, reference_points,
+                                              sampling_offsets, attention_logits)
+        ctx.save_for_backward(value, loc, attn)
+        ctx.shapes = spatial_shapes
+        ctx.lsi = level_start_index
+        return out
+
+    @staticmethod
+    def backward(ctx, grad_output):
+        value, loc, attn = ctx.saved_tensors
+        gv, goff, glog, gref = B.msda_backward_fused(value, ctx.shapes, ctx.lsi, loc, attn,
+                                                     grad_output.contiguous(),
+                                                     reference_grad=ctx.needs_input_grad[3])
+        if value.dtype != torch.float32:
+            gv = gv.to(value.dtype)
+        return gv, None, None, gref, goff, glog
+
+
 def ms_deform_attn(value, spatial_shapes, reference_points, offsets_px, logits, points):
     """Location formation + L*K softmax + core forward, all in the HIP library
     (no autograd through the first two steps)."""

@@ -244,4 +244,63 @@ int msda_backward(const msda_shape *shape, const void *value, msda_dtype value_d
                     "backward");
 }
 
+int msda_forward_fused(const msda_shape *shape, const void *value, msda_dtype value_dtype,
+                       const float *reference_points, const float *sampling_offsets, const float *attention_logits,
+                       float *output, float *sampling_locations_out, float *attention_weights_out, void *stream)
+{
+    msda::Geometry g;
+    if (int st = make_geometry(shape, g)) return st;
+    if (g.B == 0 || g.Nq == 0) return ok();
+    if (value_dtype != MSDA_F32 && value_dtype != MSDA_BF16) return fail(MSDA_E_UNSUPPORTED, "value dtype %d", (int)value_dtype);
+    if (!value || !reference_points || !sampling_offsets || !attention_logits || !output || !sampling_locations_out ||
+        !attention_weights_out)
+        return fail(MSDA_E_NULL, "NULL tensor");
+    if (!aligned(value, value_dtype == MSDA_F32 ? 4 : 2) || !aligned(reference_points, 8) ||
+        !aligned(sampling_offsets, 8) || !aligned(attention_logits, 4) || !aligned(output, 4) ||
+        !aligned(sampling_locations_out, 8) || !aligned(attention_weights_out, 4))
+        return fail(MSDA_E_ALIGN, "value needs element alignment, (x, y) tensors 8 bytes, the others 4 bytes");
+    msda::FusedInputs fi{reinterpret_cast<const float2 *>(reference_points),
+                         reinterpret_cast<const float2 *>(sampling_offsets), attention_logits,
+                         reinterpret_cast<float2 *>(sampling_locations_out), attention_weights_out};
+    return launched(msda::launch_forward_fused(g, value, value_dtype, fi, output, (hipStream_t)stream),
+                    "forward_fused");
+}
+
+int msda_backward_fused(const msda_shape *shape, const void *value, msda_dtype value_dtype,
+                        const float *sampling_locations, const float *attention_weights, const float *grad_output,
+                        float *grad_value, float *grad_sampling_offsets, float *grad_attention_logits,
+                        float *grad_reference_points, void *workspace, size_t workspace_bytes, unsigned flags,
+                        void *stream)
+{
+    msda::Geometry g;
+    if (int st = make_geometry(shape, g)) return st;
+    if (flags & ~MSDA_BWD_ACCUMULATE) return fail(MSDA_E_UNSUPPORTED, "unknown flags 0x%x", flags);
+    const bool accumulate = (flags & MSDA_BWD_ACCUMULATE) != 0;
+    if (g.B == 0) return ok();
+    if (g.Nq == 0) {  // no queries: grad_value is all zeros (or left as is when accumulating)
+        if (accumulate) return ok();
+        if (!grad_value) return fail(MSDA_E_NULL, "grad_value is NULL");
+        if (!aligned(grad_value, 4)) return fail(MSDA_E_ALIGN, "grad_value needs 4-byte alignment");
+        return launched(msda::launch_zero_fill(grad_value, (int64_t)g.B * g.S * g.M * g.D, (hipStream_t)stream),
+                        "zero_fill");
+    }
+    if (int st = check_core(g, value, value_dtype, sampling_locations, attention_weights)) return st;
+    if (!grad_output || !grad_value || !grad_sampling_offsets || !grad_attention_logits)
+        return fail(MSDA_E_NULL, "NULL gradient tensor");
+    if (!aligned(grad_output, 4) || !aligned(grad_value, 4) || !aligned(grad_sampling_offsets, 8) ||
+        !aligned(grad_attention_logits, 4) || (grad_reference_points && !aligned(grad_reference_points, 8)))
+        return fail(MSDA_E_ALIGN, "gradient tensors need 4-byte ((x, y) tensors 8-byte) alignment");
+    if (msda::backward_uses_workspace(g, value, value_dtype, grad_output, grad_value)) {
+        const size_t need = msda::backward_workspace_bytes(g);
+        if (!workspace || workspace_bytes < need)
+            return fail(MSDA_E_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
+                        need);
+        if (!aligned(workspace, 256)) return fail(MSDA_E_ALIGN, "workspace needs 256-byte alignment");
+    }
+    return launched(msda::launch_backward_fused(g, value, value_dtype, sampling_locations, attention_weights,
+                                                grad_output, grad_value, grad_sampling_offsets, grad_attention_logits,
+                                                grad_reference_points, workspace, accumulate, (hipStream_t)stream),
+                    "backward_fused");
+}
+
 }  // extern "C"

@@ -236,13 +236,18 @@ template <int M, int L, int K> struct MainWaves {
     static constexpr int kValue = kBudget / kPerWave >= 16 ? 16 : kBudget / kPerWave >= 8 ? 8 : 4;
 };
 
-template <typename VT, int M, int L, int K>
+// FUSED: the gradients go one step further back, to the inputs of the fused
+// forward: grad_loc becomes the gradient of the pixel offsets (divided by
+// (W_l, H_l)), grad_attn that of the logits (through the L*K softmax, across
+// the LK adjacent lanes of one head), and grad_ref (if not null) sums grad_loc
+// over heads and points.
+template <typename VT, int M, int L, int K, bool FUSED>
 __global__ void __launch_bounds__((MainWaves<M, L, K>::kValue * kWave))
 backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, const float2 *__restrict__ loc,
                      const float *__restrict__ attn, const float4 *__restrict__ grad_out,
                      float2 *__restrict__ grad_loc, float *__restrict__ grad_attn,
                      const uint32_t *__restrict__ offsets, const uint32_t *__restrict__ bases,
-                     uint32_t *__restrict__ records, uint32_t grid)
+                     uint32_t *__restrict__ records, uint32_t grid, float2 *__restrict__ grad_ref)
 {
     constexpr int C = 256;
     constexpr int D = C / M;
@@ -352,7 +357,7 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
                 ga = group_sum<LPH>(ga);
                 gx = group_sum<LPH>(gx);
                 gy = group_sum<LPH>(gy);
-                if (lane % LPH == 0) res[i] = make_float4(ga, a * Wf * gx, a * Hf * gy, 0.0f);
+                if (lane % LPH == 0) res[i] = make_float4(ga, a * Wf * gx, a * Hf * gy, FUSED ? a : 0.0f);
             }
         }
         wave_lds_sync();
@@ -361,8 +366,32 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
             const int s = s0 + lane;
             if (NS % kWave == 0 || s < NS) {
                 const float4 r = s_geo[wave][s + s / LK];
-                grad_attn[gq * NS + s] = r.x;
-                grad_loc[gq * NS + s] = make_float2(r.y, r.z);
+                if constexpr (FUSED) {
+                    // grad_logit = A * (grad_A - sum over the head's L*K samples of A * grad_A)
+                    float t = r.w * r.x;
+#pragma unroll
+                    for (int w = 1; w < LK; w <<= 1) t += __shfl_xor(t, w, kWave);
+                    const LevelRec lv = s_lv[(s / K) % L];
+                    grad_attn[gq * NS + s] = r.w * (r.x - t);
+                    grad_loc[gq * NS + s] = make_float2(r.y / lv.Wf, r.z / lv.Hf);
+                } else {
+                    grad_attn[gq * NS + s] = r.x;
+                    grad_loc[gq * NS + s] = make_float2(r.y, r.z);
+                }
+            }
+        }
+        if constexpr (FUSED) {
+            if (grad_ref && lane < L) {
+                float sx = 0.0f, sy = 0.0f;
+#pragma unroll
+                for (int mm = 0; mm < M; ++mm)
+#pragma unroll
+                    for (int k = 0; k < K; ++k) {
+                        const float4 r = s_geo[wave][mm * PAD + lane * K + k];
+                        sx += r.y;
+                        sy += r.z;
+                    }
+                grad_ref[gq * L + lane] = make_float2(sx, sy);
             }
         }
         wave_lds_sync();
@@ -1035,10 +1064,10 @@ size_t layout(const Geometry &g, const TilePlan &tp, char *base, Workspace *ws)
     return off;
 }
 
-template <typename VT, int M, int L, int K>
+template <typename VT, int M, int L, int K, bool FUSED>
 hipError_t launch_fast(const Geometry &g, const TilePlan &tp, const void *value, const float *loc,
-                       const float *attn, const float *go, float *gv, float *gl, float *ga, void *wsp,
-                       bool accumulate, hipStream_t st)
+                       const float *attn, const float *go, float *gv, float *gl, float *ga, float *gref,
+                       void *wsp, bool accumulate, hipStream_t st)
 {
     Workspace ws;
     layout(g, tp, static_cast<char *>(wsp), &ws);
@@ -1062,12 +1091,12 @@ hipError_t launch_fast(const Geometry &g, const TilePlan &tp, const void *value,
     }
     const uint32_t grid = round_up8((uint32_t)nwg);
     {
-        KernelScope ks_("backward_c256_kernel", st);
-        hipLaunchKernelGGL((backward_c256_kernel<VT, M, L, K>), dim3(grid), dim3(MainWaves<M, L, K>::kValue * kWave),
-                           hist_bytes, st, g, tp,
+        KernelScope ks_(FUSED ? "backward_fused_c256_kernel" : "backward_c256_kernel", st);
+        hipLaunchKernelGGL((backward_c256_kernel<VT, M, L, K, FUSED>), dim3(grid),
+                           dim3(MainWaves<M, L, K>::kValue * kWave), hist_bytes, st, g, tp,
                            static_cast<const VT *>(value), reinterpret_cast<const float2 *>(loc), attn,
                            reinterpret_cast<const float4 *>(go), reinterpret_cast<float2 *>(gl), ga, ws.counts,
-                           ws.bases, ws.records, grid);
+                           ws.bases, ws.records, grid, reinterpret_cast<float2 *>(gref));
     }
     constexpr int LG = 256 / M / 4;
     if (!accumulate) {
@@ -1128,36 +1157,91 @@ Fast fast_kind(const Geometry &g)
     return Fast::None;
 }
 
+// The fused gradients for shapes without an in-kernel form: in place, one
+// thread per (b, q): grad_attn -> grad_logits through the L*K softmax,
+// grad_loc -> grad_offset_px, and grad_ref = sum of grad_loc over (m, k).
+__global__ void __launch_bounds__(256)
+fused_grads_kernel(Geometry g, const float *__restrict__ attn, float *__restrict__ grad_attn,
+                   float2 *__restrict__ grad_loc, float2 *__restrict__ grad_ref)
+{
+    const int64_t bq = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (bq >= g.queries()) return;
+    const int LK = g.L * g.K;
+    for (int m = 0; m < g.M; ++m) {
+        const int64_t row = (bq * g.M + m) * LK;
+        float dot = 0.0f;
+        for (int i = 0; i < LK; ++i) dot += attn[row + i] * grad_attn[row + i];
+        for (int i = 0; i < LK; ++i) grad_attn[row + i] = attn[row + i] * (grad_attn[row + i] - dot);
+    }
+    for (int l = 0; l < g.L; ++l) {
+        int W = 1, H = 1;
+#pragma unroll
+        for (int i = 0; i < MSDA_MAX_LEVELS; ++i)
+            if (i == l) {
+                W = g.lv.W[i];
+                H = g.lv.H[i];
+            }
+        float sx = 0.0f, sy = 0.0f;
+        for (int m = 0; m < g.M; ++m)
+            for (int k = 0; k < g.K; ++k) {
+                const int64_t s = ((bq * g.M + m) * g.L + l) * g.K + k;
+                const float2 v = grad_loc[s];
+                sx += v.x;
+                sy += v.y;
+                grad_loc[s] = make_float2(v.x / (float)W, v.y / (float)H);
+            }
+        if (grad_ref) grad_ref[bq * g.L + l] = make_float2(sx, sy);
+    }
+}
+
 template <typename VT>
 hipError_t launch_typed(const Geometry &g, const TilePlan *tpp, const void *value, const float *loc,
-                        const float *attn, const float *go, float *gv, float *gl, float *ga, void *ws,
-                        bool accumulate, hipStream_t st)
+                        const float *attn, const float *go, float *gv, float *gl, float *ga, float *gref,
+                        void *ws, bool accumulate, bool fused, hipStream_t st)
 {
-#define MSDA_FAST(M_, L_, K_) \
-    launch_fast<VT, M_, L_, K_>(g, *tpp, value, loc, attn, go, gv, gl, ga, ws, accumulate, st)
+    // fused gradients inside the main kernel where the L*K softmax fits the
+    // wave's lanes; otherwise the plain gradients, converted afterwards
+    const bool in_kernel = fused && fused_forward_supported(g);
+    hipError_t e = hipSuccess;
+    bool done = false;
+#define MSDA_FAST(M_, L_, K_)                                                                                    \
+    e = in_kernel ? launch_fast<VT, M_, L_, K_, true>(g, *tpp, value, loc, attn, go, gv, gl, ga, gref, ws,       \
+                                                      accumulate, st)                                            \
+                  : launch_fast<VT, M_, L_, K_, false>(g, *tpp, value, loc, attn, go, gv, gl, ga, nullptr, ws,   \
+                                                       accumulate, st);                                          \
+    done = true;
     switch (tpp ? fast_kind(g) : Fast::None) {
-    case Fast::M8L4K4: return MSDA_FAST(8, 4, 4);
-    case Fast::M4L4K4: return MSDA_FAST(4, 4, 4);
-    case Fast::M16L4K4: return MSDA_FAST(16, 4, 4);
-    case Fast::M8L1K4: return MSDA_FAST(8, 1, 4);
-    case Fast::M8L4K8: return MSDA_FAST(8, 4, 8);
-    case Fast::M8L3K4: return MSDA_FAST(8, 3, 4);
-    case Fast::M8L4K1: return MSDA_FAST(8, 4, 1);
+    case Fast::M8L4K4: MSDA_FAST(8, 4, 4) break;
+    case Fast::M4L4K4: MSDA_FAST(4, 4, 4) break;
+    case Fast::M16L4K4: MSDA_FAST(16, 4, 4) break;
+    case Fast::M8L1K4: MSDA_FAST(8, 1, 4) break;
+    case Fast::M8L4K8: MSDA_FAST(8, 4, 8) break;
+    case Fast::M8L3K4: MSDA_FAST(8, 3, 4) break;
+    case Fast::M8L4K1: MSDA_FAST(8, 4, 1) break;
     case Fast::None: break;
     }
 #undef MSDA_FAST
-    if (!accumulate) {
-        hipError_t e = launch_zero_fill(gv, (int64_t)g.B * g.S * g.M * g.D, st);
-        if (e != hipSuccess) return e;
-    }
-    const int64_t n = g.queries() * g.M;
-    {
+    if (e != hipSuccess) return e;
+    if (!done) {
+        if (!accumulate) {
+            e = launch_zero_fill(gv, (int64_t)g.B * g.S * g.M * g.D, st);
+            if (e != hipSuccess) return e;
+        }
+        const int64_t n = g.queries() * g.M;
         KernelScope ks_("backward_generic_kernel", st);
         hipLaunchKernelGGL((backward_generic_kernel<VT>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, g,
                            static_cast<const VT *>(value), reinterpret_cast<const float2 *>(loc), attn, go, gv,
                            reinterpret_cast<float2 *>(gl), ga);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
-    return hipGetLastError();
+    if (fused && !(done && in_kernel)) {
+        KernelScope ks_("fused_grads_kernel", st);
+        hipLaunchKernelGGL(fused_grads_kernel, dim3((unsigned)((g.queries() + 255) / 256)), dim3(256), 0, st, g,
+                           attn, ga, reinterpret_cast<float2 *>(gl), reinterpret_cast<float2 *>(gref));
+        e = hipGetLastError();
+    }
+    return e;
 }
 
 }  // namespace
@@ -1266,8 +1350,21 @@ hipError_t launch_backward(const Geometry &g, const void *value, msda_dtype vt, 
 {
     TilePlan tp;
     const TilePlan *tpp = backward_uses_workspace(g, value, vt, go, gv) && make_tile_plan(g, tp) ? &tp : nullptr;
-    if (vt == MSDA_BF16) return launch_typed<uint16_t>(g, tpp, value, loc, attn, go, gv, gl, ga, ws, accumulate, st);
-    return launch_typed<float>(g, tpp, value, loc, attn, go, gv, gl, ga, ws, accumulate, st);
+    if (vt == MSDA_BF16)
+        return launch_typed<uint16_t>(g, tpp, value, loc, attn, go, gv, gl, ga, nullptr, ws, accumulate, false, st);
+    return launch_typed<float>(g, tpp, value, loc, attn, go, gv, gl, ga, nullptr, ws, accumulate, false, st);
+}
+
+hipError_t launch_backward_fused(const Geometry &g, const void *value, msda_dtype vt, const float *loc,
+                                 const float *attn, const float *go, float *gv, float *goff, float *glogits,
+                                 float *gref, void *ws, bool accumulate, hipStream_t st)
+{
+    TilePlan tp;
+    const TilePlan *tpp = backward_uses_workspace(g, value, vt, go, gv) && make_tile_plan(g, tp) ? &tp : nullptr;
+    if (vt == MSDA_BF16)
+        return launch_typed<uint16_t>(g, tpp, value, loc, attn, go, gv, goff, glogits, gref, ws, accumulate, true,
+                                      st);
+    return launch_typed<float>(g, tpp, value, loc, attn, go, gv, goff, glogits, gref, ws, accumulate, true, st);
 }
 
 }  // namespace msda

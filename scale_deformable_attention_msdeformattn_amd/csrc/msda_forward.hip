@@ -34,10 +34,13 @@ struct LevelRec {  // one level, as read by lane-varying level index from LDS
     int32_t W, start;
 };
 
-template <typename VT, int M, int L, int K>
+// Fused form: the sampling locations and the L*K softmax are formed in phase
+// 1 from the reference points, pixel offsets and logits (and written out for
+// the backward) instead of being read.
+template <typename VT, int M, int L, int K, bool FUSED>
 __global__ void __launch_bounds__(kBlock)
 forward_c256_kernel(Geometry g, const VT *__restrict__ value, const float2 *__restrict__ loc,
-                    const float *__restrict__ attn, float4 *__restrict__ out, uint32_t grid)
+                    const float *__restrict__ attn, float4 *__restrict__ out, uint32_t grid, FusedInputs fi)
 {
     constexpr int C = 256;
     constexpr int D = C / M;
@@ -73,8 +76,30 @@ forward_c256_kernel(Geometry g, const VT *__restrict__ value, const float2 *__re
             if (NS % kWave == 0 || s < NS) {
                 const int l = (s / K) % L;
                 const LevelRec lv = s_lv[l];
-                float2 u = loc[gq * NS + s];
-                const float a = attn[gq * NS + s];
+                float2 u;
+                float a;
+                if constexpr (FUSED) {
+                    // loc = ref + offset_px / (W_l, H_l); A = softmax over the
+                    // L*K consecutive samples of this head (LK divides 64, so a
+                    // head's samples sit in LK adjacent lanes of this pass)
+                    const float2 r = fi.ref[gq * L + l];
+                    const float2 o = fi.off[gq * NS + s];
+                    u = make_float2(r.x + o.x / lv.Wf, r.y + o.y / lv.Hf);
+                    const float x = fi.logits[gq * NS + s];
+                    float mx = x;
+#pragma unroll
+                    for (int w = 1; w < LK; w <<= 1) mx = fmaxf(mx, __shfl_xor(mx, w, kWave));
+                    const float e = expf(x - mx);
+                    float sum = e;
+#pragma unroll
+                    for (int w = 1; w < LK; w <<= 1) sum += __shfl_xor(sum, w, kWave);
+                    a = e / sum;
+                    fi.loc_out[gq * NS + s] = u;
+                    fi.attn_out[gq * NS + s] = a;
+                } else {
+                    u = loc[gq * NS + s];
+                    a = attn[gq * NS + s];
+                }
                 const bool in = sample_in_range(u.x, u.y, lv.Wf, lv.Hf);
                 u.x = in ? u.x : 0.0f;
                 u.y = in ? u.y : 0.0f;
@@ -191,38 +216,60 @@ forward_generic_kernel(Geometry g, const VT *__restrict__ value, const float2 *_
 
 template <typename VT, int M, int L, int K>
 hipError_t launch_c256(const Geometry &g, const void *value, const float *loc, const float *attn,
-                       float *out, hipStream_t st)
+                       float *out, const FusedInputs *fi, hipStream_t st)
 {
     const uint32_t tiles = (uint32_t)((g.queries() + kWaves - 1) / kWaves);
     const uint32_t grid = round_up8(tiles);
-    {
+    if (fi) {
+        if constexpr ((L * K) <= kWave && (kWave % (L * K)) == 0) {
+            KernelScope ks_("forward_fused_c256_kernel", st);
+            hipLaunchKernelGGL((forward_c256_kernel<VT, M, L, K, true>), dim3(grid), dim3(kBlock), 0, st, g,
+                               static_cast<const VT *>(value), nullptr, nullptr, reinterpret_cast<float4 *>(out),
+                               grid, *fi);
+        } else {
+            return hipErrorInvalidValue;  // callers check fused_forward_supported first
+        }
+    } else {
         KernelScope ks_("forward_c256_kernel", st);
-        hipLaunchKernelGGL((forward_c256_kernel<VT, M, L, K>), dim3(grid), dim3(kBlock), 0, st, g,
+        hipLaunchKernelGGL((forward_c256_kernel<VT, M, L, K, false>), dim3(grid), dim3(kBlock), 0, st, g,
                            static_cast<const VT *>(value), reinterpret_cast<const float2 *>(loc), attn,
-                           reinterpret_cast<float4 *>(out), grid);
+                           reinterpret_cast<float4 *>(out), grid, FusedInputs{});
     }
     return hipGetLastError();
 }
 
 template <typename VT>
 hipError_t launch_typed(const Geometry &g, const void *value, const float *loc, const float *attn,
-                        float *out, hipStream_t st)
+                        float *out, const FusedInputs *fi, hipStream_t st)
 {
     const bool c256 = g.M * g.D == 256 && (reinterpret_cast<uintptr_t>(value) % (4 * sizeof(VT))) == 0 &&
                       (reinterpret_cast<uintptr_t>(out) % 16) == 0;
-    if (c256 && g.L == 4 && g.K == 4) {
+    // a fused launch needs a compiled shape whose L*K divides the wave
+    const bool ok = c256 && (!fi || fused_forward_supported(g));
+    if (ok && g.L == 4 && g.K == 4) {
         switch (g.M) {
-        case 8: return launch_c256<VT, 8, 4, 4>(g, value, loc, attn, out, st);
-        case 4: return launch_c256<VT, 4, 4, 4>(g, value, loc, attn, out, st);
-        case 16: return launch_c256<VT, 16, 4, 4>(g, value, loc, attn, out, st);
+        case 8: return launch_c256<VT, 8, 4, 4>(g, value, loc, attn, out, fi, st);
+        case 4: return launch_c256<VT, 4, 4, 4>(g, value, loc, attn, out, fi, st);
+        case 16: return launch_c256<VT, 16, 4, 4>(g, value, loc, attn, out, fi, st);
         default: break;
         }
     }
-    if (c256 && g.M == 8) {
-        if (g.L == 1 && g.K == 4) return launch_c256<VT, 8, 1, 4>(g, value, loc, attn, out, st);
-        if (g.L == 4 && g.K == 8) return launch_c256<VT, 8, 4, 8>(g, value, loc, attn, out, st);
-        if (g.L == 3 && g.K == 4) return launch_c256<VT, 8, 3, 4>(g, value, loc, attn, out, st);
-        if (g.L == 4 && g.K == 1) return launch_c256<VT, 8, 4, 1>(g, value, loc, attn, out, st);
+    if (ok && g.M == 8) {
+        if (g.L == 1 && g.K == 4) return launch_c256<VT, 8, 1, 4>(g, value, loc, attn, out, fi, st);
+        if (g.L == 4 && g.K == 8) return launch_c256<VT, 8, 4, 8>(g, value, loc, attn, out, fi, st);
+        if (g.L == 3 && g.K == 4) return launch_c256<VT, 8, 3, 4>(g, value, loc, attn, out, fi, st);
+        if (g.L == 4 && g.K == 1) return launch_c256<VT, 8, 4, 1>(g, value, loc, attn, out, fi, st);
+    }
+    if (fi) {
+        // no fused kernel for this shape: the three steps, through the caller's
+        // loc / attention output buffers
+        hipError_t e = launch_sampling_locations(g, reinterpret_cast<const float *>(fi->ref),
+                                                 reinterpret_cast<const float *>(fi->off),
+                                                 reinterpret_cast<float *>(fi->loc_out), st);
+        if (e == hipSuccess) e = launch_softmax(g, fi->logits, fi->attn_out, st);
+        if (e != hipSuccess) return e;
+        return launch_typed<VT>(g, value, reinterpret_cast<const float *>(fi->loc_out), fi->attn_out, out,
+                                nullptr, st);
     }
     const int64_t n = g.queries() * g.M * g.D;
     {
@@ -239,8 +286,15 @@ hipError_t launch_typed(const Geometry &g, const void *value, const float *loc, 
 hipError_t launch_forward(const Geometry &g, const void *value, msda_dtype vt, const float *loc,
                           const float *attn, float *out, hipStream_t st)
 {
-    if (vt == MSDA_BF16) return launch_typed<uint16_t>(g, value, loc, attn, out, st);
-    return launch_typed<float>(g, value, loc, attn, out, st);
+    if (vt == MSDA_BF16) return launch_typed<uint16_t>(g, value, loc, attn, out, nullptr, st);
+    return launch_typed<float>(g, value, loc, attn, out, nullptr, st);
+}
+
+hipError_t launch_forward_fused(const Geometry &g, const void *value, msda_dtype vt, const FusedInputs &fi,
+                                float *out, hipStream_t st)
+{
+    if (vt == MSDA_BF16) return launch_typed<uint16_t>(g, value, nullptr, nullptr, out, &fi, st);
+    return launch_typed<float>(g, value, nullptr, nullptr, out, &fi, st);
 }
 
 }  // namespace msda

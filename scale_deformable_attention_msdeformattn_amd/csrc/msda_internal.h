@@ -86,6 +86,24 @@ class KernelScope {
     hipEvent_t start_;
 };
 
+// Inputs and side outputs of the fused forward: reference points [B,Nq,L,2],
+// pixel offsets [B,Nq,M,L,K,2] and logits [B,Nq,M,L*K] in; the sampling
+// locations and attention weights it forms out (for the backward).
+struct FusedInputs {
+    const float2 *ref;
+    const float2 *off;
+    const float *logits;
+    float2 *loc_out;
+    float *attn_out;
+};
+
+// The fused kernels form the L*K softmax across adjacent lanes of a wave.
+inline bool fused_forward_supported(const Geometry &g)
+{
+    const int lk = g.L * g.K;
+    return lk <= 64 && (64 % lk) == 0;
+}
+
 // Launchers (each returns a hipError_t from the launch).
 hipError_t launch_reference_points(const Geometry &g, const float *valid_ratios,
                                    const float *query_ref, float *ref_out, hipStream_t st);
@@ -94,6 +112,8 @@ hipError_t launch_sampling_locations(const Geometry &g, const float *ref, const 
 hipError_t launch_softmax(const Geometry &g, const float *logits, float *w, hipStream_t st);
 hipError_t launch_forward(const Geometry &g, const void *value, msda_dtype vt, const float *loc,
                           const float *attn, float *out, hipStream_t st);
+hipError_t launch_forward_fused(const Geometry &g, const void *value, msda_dtype vt, const FusedInputs &fi,
+                                float *out, hipStream_t st);
 hipError_t launch_zero_fill(float *p, int64_t n, hipStream_t st);
 // grad_value is fully overwritten unless `accumulate`. `workspace` must hold
 // backward_workspace_bytes(g) bytes when backward_uses_workspace(...) holds.
@@ -101,5 +121,11 @@ hipError_t launch_backward(const Geometry &g, const void *value, msda_dtype vt, 
                            const float *attn, const float *grad_out, float *grad_value,
                            float *grad_loc, float *grad_attn, void *workspace, bool accumulate,
                            hipStream_t st);
+// The same, carried back to the fused forward's inputs: grad_offset_px,
+// grad_logits and (if not null) grad_ref instead of grad_loc and grad_attn.
+hipError_t launch_backward_fused(const Geometry &g, const void *value, msda_dtype vt, const float *loc,
+                                 const float *attn, const float *grad_out, float *grad_value,
+                                 float *grad_offset_px, float *grad_logits, float *grad_ref, void *workspace,
+                                 bool accumulate, hipStream_t st);
 
 }  // namespace msda

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.msda_abi_version() == 3
+    assert lib.msda_abi_version() == 4
     assert lib.msda_status_string(0) == b"ok"
     for code in range(-8, 0):
         assert lib.msda_status_string(code) not in (b"", b"unknown status")
@@ -91,6 +91,28 @@ def test_null_arguments(lib):
     assert lib.msda_sampling_locations(_shape().ptr, FAKE, None, FAKE, None) == B.MSDA_E_NULL
     assert lib.msda_attention_softmax(_shape().ptr, None, FAKE, None) == B.MSDA_E_NULL
     assert b"NULL" in lib.msda_last_error()
+
+
+@cpu_only
+def test_fused_entry_points_validate_on_the_host(lib):
+    ptrs = [FAKE] * 6   # ref, offsets, logits, output, loc_out, attn_out
+    for i in range(6):
+        p = list(ptrs)
+        p[i] = None
+        assert lib.msda_forward_fused(_shape().ptr, FAKE, B.MSDA_F32, *p, None) == B.MSDA_E_NULL, i
+    assert lib.msda_forward_fused(_shape().ptr, FAKE, 7, *ptrs, None) == B.MSDA_E_UNSUPPORTED
+    odd = ctypes.c_void_p(0x10004)   # 4-byte aligned, not 8: (x, y) tensors need 8
+    assert lib.msda_forward_fused(_shape().ptr, FAKE, B.MSDA_F32, odd, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                  None) == B.MSDA_E_ALIGN
+    for i in range(3):   # grad_offsets, grad_logits required; grad_ref optional
+        g = [FAKE, FAKE, FAKE, FAKE]   # grad_value, grad_offsets, grad_logits, grad_ref
+        g[i] = None
+        assert lib.msda_backward_fused(_shape().ptr, FAKE, B.MSDA_F32, FAKE, FAKE, FAKE, *g, None, 0, 0,
+                                       None) == B.MSDA_E_NULL, i
+    assert lib.msda_backward_fused(_shape().ptr, FAKE, B.MSDA_F32, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                   None, 0, 0x4, None) == B.MSDA_E_UNSUPPORTED
+    assert lib.msda_backward_fused(_shape().ptr, FAKE, B.MSDA_F32, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                   None, 0, 0, None) == B.MSDA_E_WORKSPACE
 
 
 @cpu_only
