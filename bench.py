@@ -319,6 +319,16 @@ def main():
         for _, f in calls:
             f()
 
+    # the fused path: reference points -> fused forward (locations and softmax
+    # formed in the core, written out for the backward) -> fused backward
+    # (gradients carried to the offsets, logits and reference points)
+    logits_flat = logits.reshape(B, Nq, M, L * K)
+
+    def fused_step():
+        ref = msda.msda_reference_points(shapes, valid_ratios=vr)
+        out, loc, A = msda.msda_forward_fused(value, shapes, lsi, ref, off, logits_flat)
+        state["fused"] = (out, msda.msda_backward_fused(value, shapes, lsi, loc, A, G))
+
     for _ in range(max(1, args.warmup)):
         step()
     torch.cuda.synchronize()
@@ -362,6 +372,40 @@ def main():
     t1.record(stream)
     torch.cuda.synchronize()
     step_ms = t0.elapsed_time(t1) / args.steps
+
+    # ---- timed region 1b: the fused step, graph replay like region 1 ----
+    fused_ms = None
+    try:
+        for _ in range(2):
+            fused_step()
+        torch.cuda.synchronize()
+        s2 = torch.cuda.Stream(dev)
+        s2.wait_stream(stream)
+        with torch.cuda.stream(s2):
+            fused_step()
+        stream.wait_stream(s2)
+        torch.cuda.synchronize()
+        eager_fused = state["fused"][0].clone()
+        fgraph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(fgraph):
+            fused_step()
+        fgraph.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(state["fused"][0], eager_fused):
+            raise RuntimeError("fused graph replay differs from eager")
+        for _ in range(args.warmup):
+            fgraph.replay()
+        torch.cuda.synchronize()
+        f0 = torch.cuda.Event(enable_timing=True)
+        f1 = torch.cuda.Event(enable_timing=True)
+        f0.record(stream)
+        for _ in range(args.steps):
+            fgraph.replay()
+        f1.record(stream)
+        torch.cuda.synchronize()
+        fused_ms = f0.elapsed_time(f1) / args.steps
+    except Exception as e:  # report, do not hide
+        print(f"[bench] fused step not timed ({e})", file=sys.stderr)
 
     # ---- timed region 2: per entry point, events between the calls of eager
     # steps on the same stream ----
@@ -430,6 +474,10 @@ def main():
                     "traffic": measured_traffic("forward_c256_kernel")},
         "backward": {"queries_per_s": queries / (per_call["msda_backward"] * 1e-6),
                      "note": "the whole msda_backward call, all its kernels"},
+        "fused_step": None if fused_ms is None else {
+            "ms_per_step": fused_ms, "queries_per_s": queries / (fused_ms * 1e-3),
+            "step": "reference points + msda_forward_fused + msda_backward_fused (gradients to value, offsets, "
+                    "logits and reference points)"},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.workload)
