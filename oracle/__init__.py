@@ -65,6 +65,13 @@ def _bind(lib):
     lib.msda_oracle_sampling_locations_backward.restype = None
     lib.msda_oracle_sampling_locations_backward.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                                                             ctypes.c_int, _i64p, _f64p, _f64p, _f64p]
+    lib.msda_oracle_sampling_locations_box.restype = None
+    lib.msda_oracle_sampling_locations_box.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                                       ctypes.c_int, _f64p, _f64p, _f64p]
+    lib.msda_oracle_sampling_locations_box_backward.restype = None
+    lib.msda_oracle_sampling_locations_box_backward.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                                                                ctypes.c_int, ctypes.c_int, _f64p, _f64p, _f64p,
+                                                                _f64p, _f64p]
     lib.msda_oracle_forward.restype = None
     lib.msda_oracle_forward.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                                         ctypes.c_int, ctypes.c_int, _i64p, _i64p, _f64p, _f64p, _f64p,
@@ -176,6 +183,30 @@ def sampling_locations_backward(spatial_shapes, grad_loc):
     goff = np.empty_like(gl)
     _load().msda_oracle_sampling_locations_backward(B, Nq, M, L, K, _p(shapes, _i64p), _p(gl, _f64p),
                                                     _p(gref, _f64p), _p(goff, _f64p))
+    return gref, goff
+
+
+def sampling_locations_box(ref, offset):
+    """loc = ref[..., :2] + offset / K * ref[..., 2:] * 0.5; ref [B,Nq,L,4], offsets [B,Nq,M,L,K,2]."""
+    ref = _f64(ref)
+    off = _f64(offset)
+    B, Nq, M, L, K, _ = off.shape
+    assert ref.shape == (B, Nq, L, 4)
+    out = np.empty_like(off)
+    _load().msda_oracle_sampling_locations_box(B, Nq, M, L, K, _p(ref, _f64p), _p(off, _f64p), _p(out, _f64p))
+    return out
+
+
+def sampling_locations_box_backward(ref, offset, grad_loc):
+    """(grad_ref [B,Nq,L,4], grad_offset [B,Nq,M,L,K,2]) of sampling_locations_box."""
+    ref = _f64(ref)
+    off = _f64(offset)
+    gl = _f64(grad_loc)
+    B, Nq, M, L, K, _ = off.shape
+    gref = np.empty((B, Nq, L, 4), dtype=np.float64)
+    goff = np.empty_like(off)
+    _load().msda_oracle_sampling_locations_box_backward(B, Nq, M, L, K, _p(ref, _f64p), _p(off, _f64p),
+                                                        _p(gl, _f64p), _p(gref, _f64p), _p(goff, _f64p))
     return gref, goff
 
 

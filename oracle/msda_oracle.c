@@ -134,6 +134,56 @@ void msda_oracle_softmax(int64_t rows, int n, const double *logits, double *out)
     }
 }
 
+/* Sampling locations from 4-d box references (cx, cy, w, h) per query and
+ * level, the iterative-refinement form of the walkthrough page's MSDeformAttn
+ * source ("encoder" section, the reference_points.shape[-1] == 4 branch): the
+ * offsets are taken relative to the box size,
+ *   loc = ref[b,q,l,0:2] + offset / K * ref[b,q,l,2:4] * 0.5. */
+void msda_oracle_sampling_locations_box(int B, int64_t Nq, int M, int L, int K, const double *ref,
+                                        const double *offset, double *loc)
+{
+    for (int b = 0; b < B; ++b)
+        for (int64_t q = 0; q < Nq; ++q)
+            for (int m = 0; m < M; ++m)
+                for (int l = 0; l < L; ++l) {
+                    const double *r = ref + ((b * Nq + q) * L + l) * 4;
+                    for (int k = 0; k < K; ++k) {
+                        const int64_t idx = ((((b * Nq + q) * M + m) * L + l) * K + k) * 2;
+                        loc[idx + 0] = r[0] + offset[idx + 0] / (double)K * r[2] * 0.5;
+                        loc[idx + 1] = r[1] + offset[idx + 1] / (double)K * r[3] * 0.5;
+                    }
+                }
+}
+
+/* Its backward: grad_offset = grad_loc * ref_wh * 0.5 / K;
+ * grad_ref[0:2] = sum over m, k of grad_loc, grad_ref[2:4] = sum over m, k of
+ * grad_loc * offset * 0.5 / K. grad_ref [B,Nq,L,4] may be NULL. */
+void msda_oracle_sampling_locations_box_backward(int B, int64_t Nq, int M, int L, int K, const double *ref,
+                                                 const double *offset, const double *grad_loc, double *grad_ref,
+                                                 double *grad_offset)
+{
+    if (grad_ref)
+        for (int64_t i = 0; i < (int64_t)B * Nq * L * 4; ++i) grad_ref[i] = 0.0;
+    for (int b = 0; b < B; ++b)
+        for (int64_t q = 0; q < Nq; ++q)
+            for (int m = 0; m < M; ++m)
+                for (int l = 0; l < L; ++l) {
+                    const double *r = ref + ((b * Nq + q) * L + l) * 4;
+                    for (int k = 0; k < K; ++k) {
+                        const int64_t idx = ((((b * Nq + q) * M + m) * L + l) * K + k) * 2;
+                        grad_offset[idx + 0] = grad_loc[idx + 0] * r[2] * 0.5 / (double)K;
+                        grad_offset[idx + 1] = grad_loc[idx + 1] * r[3] * 0.5 / (double)K;
+                        if (grad_ref) {
+                            double *gr = grad_ref + ((b * Nq + q) * L + l) * 4;
+                            gr[0] += grad_loc[idx + 0];
+                            gr[1] += grad_loc[idx + 1];
+                            gr[2] += grad_loc[idx + 0] * offset[idx + 0] * 0.5 / (double)K;
+                            gr[3] += grad_loc[idx + 1] * offset[idx + 1] * 0.5 / (double)K;
+                        }
+                    }
+                }
+}
+
 /* Backward of the L*K softmax ([P4] "Insight 2" normalisation): with
  * A = softmax(x) over one row, dA_i/dx_j = A_i (delta_ij - A_j), so
  * grad_x_i = A_i (grad_A_i - sum_j A_j grad_A_j). */

@@ -58,6 +58,15 @@ void msda_oracle_sampling_locations(int B, int64_t Nq, int M, int L, int K,
  * levels and points, so n = L*K). */
 void msda_oracle_softmax(int64_t rows, int n, const double *logits, double *out);
 
+/* Locations from 4-d box references [B,Nq,L,4] = (cx, cy, w, h) ([P2]
+ * MSDeformAttn source, the 4-d reference branch): loc = ref_xy + offset / K *
+ * ref_wh * 0.5, and its backward (grad_ref [B,Nq,L,4] may be NULL). */
+void msda_oracle_sampling_locations_box(int B, int64_t Nq, int M, int L, int K, const double *ref,
+                                        const double *offset, double *loc);
+void msda_oracle_sampling_locations_box_backward(int B, int64_t Nq, int M, int L, int K, const double *ref,
+                                                 const double *offset, const double *grad_loc, double *grad_ref,
+                                                 double *grad_offset);
+
 /* Backward of msda_oracle_softmax ([P4] "Insight 2"): grad_logits[r,i] =
  * A[r,i] * (grad_A[r,i] - sum_j A[r,j] grad_A[r,j]). */
 void msda_oracle_softmax_backward(int64_t rows, int n, const double *attn, const double *grad_attn,

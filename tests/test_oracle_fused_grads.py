@@ -98,3 +98,52 @@ def test_locations_backward_scales_by_level_size():
     gref, goff = oracle.sampling_locations_backward(shapes, gl)
     np.testing.assert_allclose(goff.reshape(2), [1 / 7, 1 / 5], rtol=0, atol=1e-16)
     np.testing.assert_allclose(gref.reshape(2), [1.0, 1.0], rtol=0, atol=0)
+
+
+def test_box_locations_reduce_to_pixel_offsets():
+    """With one level and a box of size (2K/W, 2K/H), offset / K * wh * 0.5 is
+    offset / (W, H): the 4-d form must equal the 2-d form."""
+    rng = np.random.default_rng(7)
+    H, W, K = 6, 9, 3
+    B, Nq, M = 2, 4, 2
+    xy = rng.uniform(size=(B, Nq, 1, 2))
+    box = np.concatenate([xy, np.broadcast_to([2.0 * K / W, 2.0 * K / H], (B, Nq, 1, 2))], axis=-1)
+    off = rng.normal(size=(B, Nq, M, 1, K, 2))
+    np.testing.assert_allclose(oracle.sampling_locations_box(box, off),
+                               oracle.sampling_locations([[H, W]], xy, off), rtol=0, atol=1e-15)
+
+
+def test_box_locations_worked_value():
+    """cx = 0.5, w = 0.2, K = 4, offset 2.0: 0.5 + 2/4 * 0.2 * 0.5 = 0.55."""
+    ref = np.array([0.5, 0.25, 0.2, 0.4]).reshape(1, 1, 1, 4)
+    off = np.array([2.0, -1.0]).reshape(1, 1, 1, 1, 1, 2)
+    off = np.repeat(off, 4, axis=4)
+    loc = oracle.sampling_locations_box(ref, off)
+    np.testing.assert_allclose(loc[0, 0, 0, 0, 0], [0.55, 0.25 - 1.0 / 4 * 0.4 * 0.5], rtol=0, atol=1e-15)
+
+
+def test_box_locations_backward_central_differences():
+    rng = np.random.default_rng(8)
+    B, Nq, M, L, K = 2, 3, 2, 2, 3
+    ref = np.concatenate([rng.uniform(size=(B, Nq, L, 2)), rng.uniform(0.05, 0.5, size=(B, Nq, L, 2))], axis=-1)
+    off = rng.normal(size=(B, Nq, M, L, K, 2))
+    gl = rng.normal(size=(B, Nq, M, L, K, 2))
+    gref, goff = oracle.sampling_locations_box_backward(ref, off, gl)
+
+    def f(r, o):
+        return float((oracle.sampling_locations_box(r, o) * gl).sum())
+
+    h = 1e-4
+    for arr, got in ((off, goff), (ref, gref)):
+        num = np.zeros_like(arr)
+        it = np.nditer(arr, flags=["multi_index"])
+        for _ in it:
+            i = it.multi_index
+            p_, m_ = arr.copy(), arr.copy()
+            p_[i] += h
+            m_[i] -= h
+            if arr is off:
+                num[i] = (f(ref, p_) - f(ref, m_)) / (2 * h)
+            else:
+                num[i] = (f(p_, off) - f(m_, off)) / (2 * h)
+        np.testing.assert_allclose(got, num, rtol=1e-7, atol=1e-10)

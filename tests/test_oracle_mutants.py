@@ -43,6 +43,9 @@ def _fused_grad_pins():
     tg.test_softmax_backward_central_differences()
     tg.test_locations_backward_central_differences()
     tg.test_locations_backward_scales_by_level_size()
+    tg.test_box_locations_reduce_to_pixel_offsets()
+    tg.test_box_locations_worked_value()
+    tg.test_box_locations_backward_central_differences()
 
 
 MUTANTS = [
@@ -70,7 +73,14 @@ MUTANTS = [
     ("softmax_grad_wrong_factor", "a[i] * (ga[i] - dot)", "(ga[i] - dot)", _fused_grad_pins),
     ("offset_grad_swapped_normaliser", "grad_offset_px[idx + 0] = grad_loc[idx + 0] / W;",
      "grad_offset_px[idx + 0] = grad_loc[idx + 0] / H;", _fused_grad_pins),
-    ("ref_grad_one_term", "gr[0] += grad_loc[idx + 0];", "gr[0] = grad_loc[idx + 0];", _fused_grad_pins),
+    ("ref_grad_one_term", "gr[0] += grad_loc[idx + 0];\n                            gr[1] += grad_loc[idx + 1];\n                        }",
+     "gr[0] = grad_loc[idx + 0];\n                            gr[1] += grad_loc[idx + 1];\n                        }", _fused_grad_pins),
+    ("box_wh_swapped", "offset[idx + 0] / (double)K * r[2] * 0.5", "offset[idx + 0] / (double)K * r[3] * 0.5",
+     _fused_grad_pins),
+    ("box_no_half", "offset[idx + 1] / (double)K * r[3] * 0.5", "offset[idx + 1] / (double)K * r[3]",
+     _fused_grad_pins),
+    ("box_grad_wh_term", "gr[2] += grad_loc[idx + 0] * offset[idx + 0] * 0.5 / (double)K;",
+     "gr[2] += grad_loc[idx + 0] * offset[idx + 0] / (double)K;", _fused_grad_pins),
 ]
 
 
