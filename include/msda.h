@@ -54,7 +54,7 @@ extern "C" {
 #define MSDA_API
 #endif
 
-#define MSDA_ABI_VERSION 4
+#define MSDA_ABI_VERSION 5
 #define MSDA_MAX_LEVELS 16
 
 typedef enum {
@@ -170,32 +170,43 @@ MSDA_API int msda_backward(const msda_shape *shape, const void *value, msda_dtyp
 
 /* Fused forward (the adjacent steps formed inside the core): for every sample
  *   loc = reference_points[b,q,l] + sampling_offsets[b,q,m,l,k] / (W_l, H_l)
+ *         (reference_dims 2: points, offsets in pixels of level l), or
+ *   loc = ref[b,q,l,0:2] + sampling_offsets / K * ref[b,q,l,2:4] * 0.5
+ *         (reference_dims 4: boxes (cx, cy, w, h), the iterative-refinement
+ *          branch of the module source)
  *   A[b,q,m,:] = softmax over the L*K logits attention_logits[b,q,m,:]
  * and then output as msda_forward (walkthrough page, "encoder" and the
  * MSDeformAttn module source; paper notes, "Insight 2" and "Key code").
- *  reference_points        [B,Nq,L,2]     fp32 (x, y), normalised
- *  sampling_offsets        [B,Nq,M,L,K,2] fp32 (x, y) in pixels of level l
+ *  reference_points        [B,Nq,L,reference_dims] fp32, normalised
+ *  sampling_offsets        [B,Nq,M,L,K,2] fp32 (x, y)
  *  attention_logits        [B,Nq,M,L*K]   fp32
  *  output                  [B,Nq,M*D]     fp32, fully overwritten
  *  sampling_locations_out  [B,Nq,M,L,K,2] fp32, fully overwritten (for the
  *  attention_weights_out   [B,Nq,M,L,K]   fp32   backward; never NULL)
  * Shapes whose L*K does not divide 64 run the three steps one after the other
- * through the two side outputs. Same status codes as msda_forward. */
+ * through the two side outputs. reference_dims other than 2 or 4:
+ * MSDA_E_UNSUPPORTED; otherwise the status codes of msda_forward. */
 MSDA_API int msda_forward_fused(const msda_shape *shape, const void *value, msda_dtype value_dtype,
-                                const float *reference_points, const float *sampling_offsets,
+                                const float *reference_points, int reference_dims, const float *sampling_offsets,
                                 const float *attention_logits, float *output, float *sampling_locations_out,
                                 float *attention_weights_out, void *stream);
 
 /* Backward of msda_forward_fused, given the locations and weights it wrote:
  * grad_value as msda_backward, and, by the chain rule through the two fused
  * steps,
- *   grad_sampling_offsets[b,q,m,l,k] = grad_loc / (W_l, H_l)
- *   grad_attention_logits[b,q,m,i]   = A_i * (grad_A_i - sum_j A_j grad_A_j)
- *   grad_reference_points[b,q,l]     = sum over m, k of grad_loc (if not NULL)
- * Shapes [B,Nq,M,L,K,2], [B,Nq,M,L*K] and [B,Nq,L,2], fp32, fully
- * overwritten. Workspace, flags and status codes as msda_backward. */
+ *   grad_sampling_offsets = grad_loc / (W_l, H_l)            (points)
+ *                         = grad_loc * ref_wh * 0.5 / K       (boxes)
+ *   grad_attention_logits[b,q,m,i] = A_i * (grad_A_i - sum_j A_j grad_A_j)
+ *   grad_reference_points[b,q,l]   = sum over m, k of grad_loc, and for boxes
+ *                                    sum of grad_loc * offset * 0.5 / K for
+ *                                    (w, h)  (if not NULL)
+ * reference_points and sampling_offsets are read for boxes only (NULL allowed
+ * for points). Shapes [B,Nq,M,L,K,2], [B,Nq,M,L*K], [B,Nq,L,reference_dims],
+ * fp32, fully overwritten. Workspace, flags and status codes as
+ * msda_backward. */
 MSDA_API int msda_backward_fused(const msda_shape *shape, const void *value, msda_dtype value_dtype,
                                  const float *sampling_locations, const float *attention_weights,
+                                 const float *reference_points, const float *sampling_offsets, int reference_dims,
                                  const float *grad_output, float *grad_value, float *grad_sampling_offsets,
                                  float *grad_attention_logits, float *grad_reference_points, void *workspace,
                                  size_t workspace_bytes, unsigned flags, void *stream);

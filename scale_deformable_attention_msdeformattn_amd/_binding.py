@@ -97,10 +97,10 @@ def load():
     lib.msda_backward.argtypes = [_shp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                                   ctypes.c_uint, _vp]
     lib.msda_forward_fused.restype = ctypes.c_int
-    lib.msda_forward_fused.argtypes = [_shp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+    lib.msda_forward_fused.argtypes = [_shp, _vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp]
     lib.msda_backward_fused.restype = ctypes.c_int
-    lib.msda_backward_fused.argtypes = [_shp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                                        ctypes.c_size_t, ctypes.c_uint, _vp]
+    lib.msda_backward_fused.argtypes = [_shp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp,
+                                        _vp, _vp, _vp, ctypes.c_size_t, ctypes.c_uint, _vp]
     lib.msda_timing_enable.restype = ctypes.c_int
     lib.msda_timing_enable.argtypes = [ctypes.c_int]
     lib.msda_timing_reset.restype = ctypes.c_int
@@ -310,8 +310,9 @@ def msda_backward(value: torch.Tensor, spatial_shapes, level_start_index, sampli
 def msda_forward_fused(value: torch.Tensor, spatial_shapes, level_start_index, reference_points: torch.Tensor,
                        sampling_offsets: torch.Tensor, attention_logits: torch.Tensor):
     """Fused forward: locations and the L*K softmax formed inside the core.
-    reference_points [B,Nq,L,2], sampling_offsets [B,Nq,M,L,K,2] (pixels of
-    level l), attention_logits [B,Nq,M,L*K] ->
+    reference_points [B,Nq,L,2] (offsets in pixels of level l) or boxes
+    [B,Nq,L,4] (offsets relative to the box size), sampling_offsets
+    [B,Nq,M,L,K,2], attention_logits [B,Nq,M,L*K] ->
     (output [B,Nq,M*D], sampling_locations, attention_weights)."""
     if value.dtype not in (torch.float32, torch.bfloat16):
         raise ValueError(f"value must be float32 or bfloat16 (got {value.dtype})")
@@ -325,8 +326,8 @@ def msda_forward_fused(value: torch.Tensor, spatial_shapes, level_start_index, r
     if off.dim() != 6 or off.shape[0] != B or off.shape[2] != M or off.shape[-1] != 2:
         raise ValueError(f"sampling_offsets must be [{B}, Nq, {M}, L, K, 2], got {tuple(off.shape)}")
     _, Nq, _, L, K, _ = off.shape
-    if tuple(ref.shape) != (B, Nq, L, 2):
-        raise ValueError(f"reference_points must be {(B, Nq, L, 2)}, got {tuple(ref.shape)}")
+    if ref.dim() != 4 or tuple(ref.shape[:3]) != (B, Nq, L) or ref.shape[3] not in (2, 4):
+        raise ValueError(f"reference_points must be [{B}, {Nq}, {L}, 2 or 4], got {tuple(ref.shape)}")
     if tuple(logits.shape) != (B, Nq, M, L * K):
         raise ValueError(f"attention_logits must be {(B, Nq, M, L * K)}, got {tuple(logits.shape)}")
     sh = Shape(spatial_shapes, B, M, D, K, Nq, level_start_index)
@@ -337,18 +338,21 @@ def msda_forward_fused(value: torch.Tensor, spatial_shapes, level_start_index, r
     out = torch.empty(B, Nq, M * D, dtype=torch.float32, device=value.device)
     loc = torch.empty_like(off)
     attn = torch.empty(B, Nq, M, L, K, dtype=torch.float32, device=value.device)
-    _check(load().msda_forward_fused(sh.ptr, _p(value), vt, _p(ref), _p(off), _p(logits), _p(out), _p(loc),
-                                     _p(attn), _stream(out)), "msda_forward_fused")
+    _check(load().msda_forward_fused(sh.ptr, _p(value), vt, _p(ref), int(ref.shape[3]), _p(off), _p(logits),
+                                     _p(out), _p(loc), _p(attn), _stream(out)), "msda_forward_fused")
     return out, loc, attn
 
 
 def msda_backward_fused(value: torch.Tensor, spatial_shapes, level_start_index, sampling_locations: torch.Tensor,
                         attention_weights: torch.Tensor, grad_output: torch.Tensor,
-                        grad_value: Optional[torch.Tensor] = None, reference_grad: bool = True):
+                        grad_value: Optional[torch.Tensor] = None, reference_grad: bool = True,
+                        box_references: Optional[torch.Tensor] = None,
+                        sampling_offsets: Optional[torch.Tensor] = None):
     """Backward of msda_forward_fused, from the locations and weights it
     returned -> (grad_value [B,S,M,D], grad_sampling_offsets [B,Nq,M,L,K,2],
-    grad_attention_logits [B,Nq,M,L*K], grad_reference_points [B,Nq,L,2] or
-    None). If grad_value is given it is accumulated into."""
+    grad_attention_logits [B,Nq,M,L*K], grad_reference_points [B,Nq,L,2|4]
+    or None). For 4-d box references pass the boxes and the offsets of the
+    forward. If grad_value is given it is accumulated into."""
     value, loc, attn, sh, vt = _core_shape(value, spatial_shapes, level_start_index, sampling_locations,
                                            attention_weights)
     B, S, M, D = value.shape
@@ -364,13 +368,22 @@ def msda_backward_fused(value: torch.Tensor, spatial_shapes, level_start_index, 
                 not grad_value.is_contiguous():
             raise ValueError("grad_value to accumulate into must be a contiguous fp32 [B,S,M,D] tensor")
         flags = MSDA_BWD_ACCUMULATE
+    dims = 2
+    box = off = None
+    if box_references is not None:
+        dims = 4
+        box = _dev(box_references, "box_references")
+        off = _dev(sampling_offsets, "sampling_offsets")
+        if tuple(box.shape) != (B, Nq, L, 4) or tuple(off.shape) != tuple(loc.shape):
+            raise ValueError("box_references must be [B,Nq,L,4] and sampling_offsets [B,Nq,M,L,K,2]")
     goff = torch.empty_like(loc)
     glog = torch.empty(B, Nq, M, L * K, dtype=torch.float32, device=value.device)
-    gref = torch.empty(B, Nq, L, 2, dtype=torch.float32, device=value.device) if reference_grad else None
+    gref = torch.empty(B, Nq, L, dims, dtype=torch.float32, device=value.device) if reference_grad else None
     nbytes = msda_backward_workspace_size(sh)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=value.device)
-    _check(load().msda_backward_fused(sh.ptr, _p(value), vt, _p(loc), _p(attn), _p(go), _p(grad_value), _p(goff),
-                                      _p(glog), _p(gref), _p(ws), nbytes, flags, _stream(go)), "msda_backward_fused")
+    _check(load().msda_backward_fused(sh.ptr, _p(value), vt, _p(loc), _p(attn), _p(box), _p(off), dims, _p(go),
+                                      _p(grad_value), _p(goff), _p(glog), _p(gref), _p(ws), nbytes, flags,
+                                      _stream(go)), "msda_backward_fused")
     return grad_value, goff, glog, gref
 
 

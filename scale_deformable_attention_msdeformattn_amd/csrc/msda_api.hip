@@ -245,35 +245,41 @@ int msda_backward(const msda_shape *shape, const void *value, msda_dtype value_d
 }
 
 int msda_forward_fused(const msda_shape *shape, const void *value, msda_dtype value_dtype,
-                       const float *reference_points, const float *sampling_offsets, const float *attention_logits,
-                       float *output, float *sampling_locations_out, float *attention_weights_out, void *stream)
+                       const float *reference_points, int reference_dims, const float *sampling_offsets,
+                       const float *attention_logits, float *output, float *sampling_locations_out,
+                       float *attention_weights_out, void *stream)
 {
     msda::Geometry g;
     if (int st = make_geometry(shape, g)) return st;
+    if (reference_dims != 2 && reference_dims != 4)
+        return fail(MSDA_E_UNSUPPORTED, "reference_dims %d (2 or 4)", reference_dims);
     if (g.B == 0 || g.Nq == 0) return ok();
     if (value_dtype != MSDA_F32 && value_dtype != MSDA_BF16) return fail(MSDA_E_UNSUPPORTED, "value dtype %d", (int)value_dtype);
     if (!value || !reference_points || !sampling_offsets || !attention_logits || !output || !sampling_locations_out ||
         !attention_weights_out)
         return fail(MSDA_E_NULL, "NULL tensor");
-    if (!aligned(value, value_dtype == MSDA_F32 ? 4 : 2) || !aligned(reference_points, 8) ||
+    if (!aligned(value, value_dtype == MSDA_F32 ? 4 : 2) || !aligned(reference_points, 4 * reference_dims) ||
         !aligned(sampling_offsets, 8) || !aligned(attention_logits, 4) || !aligned(output, 4) ||
         !aligned(sampling_locations_out, 8) || !aligned(attention_weights_out, 4))
-        return fail(MSDA_E_ALIGN, "value needs element alignment, (x, y) tensors 8 bytes, the others 4 bytes");
-    msda::FusedInputs fi{reinterpret_cast<const float2 *>(reference_points),
-                         reinterpret_cast<const float2 *>(sampling_offsets), attention_logits,
+        return fail(MSDA_E_ALIGN, "value needs element alignment, (x, y) tensors 8 bytes, boxes 16, the others 4");
+    msda::FusedInputs fi{reference_points, reference_dims, reinterpret_cast<const float2 *>(sampling_offsets),
+                         attention_logits,
                          reinterpret_cast<float2 *>(sampling_locations_out), attention_weights_out};
     return launched(msda::launch_forward_fused(g, value, value_dtype, fi, output, (hipStream_t)stream),
                     "forward_fused");
 }
 
 int msda_backward_fused(const msda_shape *shape, const void *value, msda_dtype value_dtype,
-                        const float *sampling_locations, const float *attention_weights, const float *grad_output,
-                        float *grad_value, float *grad_sampling_offsets, float *grad_attention_logits,
-                        float *grad_reference_points, void *workspace, size_t workspace_bytes, unsigned flags,
-                        void *stream)
+                        const float *sampling_locations, const float *attention_weights,
+                        const float *reference_points, const float *sampling_offsets, int reference_dims,
+                        const float *grad_output, float *grad_value, float *grad_sampling_offsets,
+                        float *grad_attention_logits, float *grad_reference_points, void *workspace,
+                        size_t workspace_bytes, unsigned flags, void *stream)
 {
     msda::Geometry g;
     if (int st = make_geometry(shape, g)) return st;
+    if (reference_dims != 2 && reference_dims != 4)
+        return fail(MSDA_E_UNSUPPORTED, "reference_dims %d (2 or 4)", reference_dims);
     if (flags & ~MSDA_BWD_ACCUMULATE) return fail(MSDA_E_UNSUPPORTED, "unknown flags 0x%x", flags);
     const bool accumulate = (flags & MSDA_BWD_ACCUMULATE) != 0;
     if (g.B == 0) return ok();
@@ -287,9 +293,13 @@ int msda_backward_fused(const msda_shape *shape, const void *value, msda_dtype v
     if (int st = check_core(g, value, value_dtype, sampling_locations, attention_weights)) return st;
     if (!grad_output || !grad_value || !grad_sampling_offsets || !grad_attention_logits)
         return fail(MSDA_E_NULL, "NULL gradient tensor");
+    if (reference_dims == 4 && (!reference_points || !sampling_offsets))
+        return fail(MSDA_E_NULL, "box references need reference_points and sampling_offsets");
     if (!aligned(grad_output, 4) || !aligned(grad_value, 4) || !aligned(grad_sampling_offsets, 8) ||
-        !aligned(grad_attention_logits, 4) || (grad_reference_points && !aligned(grad_reference_points, 8)))
-        return fail(MSDA_E_ALIGN, "gradient tensors need 4-byte ((x, y) tensors 8-byte) alignment");
+        !aligned(grad_attention_logits, 4) ||
+        (grad_reference_points && !aligned(grad_reference_points, 4 * reference_dims)) ||
+        (reference_dims == 4 && (!aligned(reference_points, 16) || !aligned(sampling_offsets, 8))))
+        return fail(MSDA_E_ALIGN, "gradient tensors need 4-byte ((x, y) 8-byte, boxes 16-byte) alignment");
     if (msda::backward_uses_workspace(g, value, value_dtype, grad_output, grad_value)) {
         const size_t need = msda::backward_workspace_bytes(g);
         if (!workspace || workspace_bytes < need)
@@ -297,9 +307,11 @@ int msda_backward_fused(const msda_shape *shape, const void *value, msda_dtype v
                         need);
         if (!aligned(workspace, 256)) return fail(MSDA_E_ALIGN, "workspace needs 256-byte alignment");
     }
+    const msda::FusedGrads fg{reference_points, reinterpret_cast<const float2 *>(sampling_offsets), reference_dims,
+                              grad_reference_points};
     return launched(msda::launch_backward_fused(g, value, value_dtype, sampling_locations, attention_weights,
                                                 grad_output, grad_value, grad_sampling_offsets, grad_attention_logits,
-                                                grad_reference_points, workspace, accumulate, (hipStream_t)stream),
+                                                fg, workspace, accumulate, (hipStream_t)stream),
                     "backward_fused");
 }
 

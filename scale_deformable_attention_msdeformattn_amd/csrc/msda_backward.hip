@@ -237,17 +237,18 @@ template <int M, int L, int K> struct MainWaves {
 };
 
 // FUSED: the gradients go one step further back, to the inputs of the fused
-// forward: grad_loc becomes the gradient of the pixel offsets (divided by
-// (W_l, H_l)), grad_attn that of the logits (through the L*K softmax, across
-// the LK adjacent lanes of one head), and grad_ref (if not null) sums grad_loc
-// over heads and points.
+// forward: grad_loc becomes the gradient of the offsets (divided by (W_l, H_l),
+// or times ref_wh / (2K) for box references), grad_attn that of the logits
+// (through the L*K softmax, across the LK adjacent lanes of one head), and
+// grad_ref (if not null) sums grad_loc over heads and points (box references:
+// also grad_loc * offset / (2K) for the box size).
 template <typename VT, int M, int L, int K, bool FUSED>
 __global__ void __launch_bounds__((MainWaves<M, L, K>::kValue * kWave))
 backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, const float2 *__restrict__ loc,
                      const float *__restrict__ attn, const float4 *__restrict__ grad_out,
                      float2 *__restrict__ grad_loc, float *__restrict__ grad_attn,
                      const uint32_t *__restrict__ offsets, const uint32_t *__restrict__ bases,
-                     uint32_t *__restrict__ records, uint32_t grid, float2 *__restrict__ grad_ref)
+                     uint32_t *__restrict__ records, uint32_t grid, FusedGrads fg)
 {
     constexpr int C = 256;
     constexpr int D = C / M;
@@ -371,9 +372,15 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
                     float t = r.w * r.x;
 #pragma unroll
                     for (int w = 1; w < LK; w <<= 1) t += __shfl_xor(t, w, kWave);
-                    const LevelRec lv = s_lv[(s / K) % L];
+                    const int l = (s / K) % L;
                     grad_attn[gq * NS + s] = r.w * (r.x - t);
-                    grad_loc[gq * NS + s] = make_float2(r.y / lv.Wf, r.z / lv.Hf);
+                    if (fg.ref_dims == 4) {
+                        const float4 bx = reinterpret_cast<const float4 *>(fg.ref)[gq * L + l];
+                        grad_loc[gq * NS + s] = make_float2(r.y * (bx.z * 0.5f / (float)K), r.z * (bx.w * 0.5f / (float)K));
+                    } else {
+                        const LevelRec lv = s_lv[l];
+                        grad_loc[gq * NS + s] = make_float2(r.y / lv.Wf, r.z / lv.Hf);
+                    }
                 } else {
                     grad_attn[gq * NS + s] = r.x;
                     grad_loc[gq * NS + s] = make_float2(r.y, r.z);
@@ -381,8 +388,8 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
             }
         }
         if constexpr (FUSED) {
-            if (grad_ref && lane < L) {
-                float sx = 0.0f, sy = 0.0f;
+            if (fg.grad_ref && lane < L) {
+                float sx = 0.0f, sy = 0.0f, sw = 0.0f, sh = 0.0f;
 #pragma unroll
                 for (int mm = 0; mm < M; ++mm)
 #pragma unroll
@@ -390,8 +397,16 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
                         const float4 r = s_geo[wave][mm * PAD + lane * K + k];
                         sx += r.y;
                         sy += r.z;
+                        if (fg.ref_dims == 4) {
+                            const float2 o = fg.off[gq * NS + mm * LK + lane * K + k];
+                            sw += r.y * o.x * 0.5f / (float)K;
+                            sh += r.z * o.y * 0.5f / (float)K;
+                        }
                     }
-                grad_ref[gq * L + lane] = make_float2(sx, sy);
+                if (fg.ref_dims == 4)
+                    reinterpret_cast<float4 *>(fg.grad_ref)[gq * L + lane] = make_float4(sx, sy, sw, sh);
+                else
+                    reinterpret_cast<float2 *>(fg.grad_ref)[gq * L + lane] = make_float2(sx, sy);
             }
         }
         wave_lds_sync();
@@ -1066,7 +1081,7 @@ size_t layout(const Geometry &g, const TilePlan &tp, char *base, Workspace *ws)
 
 template <typename VT, int M, int L, int K, bool FUSED>
 hipError_t launch_fast(const Geometry &g, const TilePlan &tp, const void *value, const float *loc,
-                       const float *attn, const float *go, float *gv, float *gl, float *ga, float *gref,
+                       const float *attn, const float *go, float *gv, float *gl, float *ga, const FusedGrads &fg,
                        void *wsp, bool accumulate, hipStream_t st)
 {
     Workspace ws;
@@ -1096,7 +1111,7 @@ hipError_t launch_fast(const Geometry &g, const TilePlan &tp, const void *value,
                            dim3(MainWaves<M, L, K>::kValue * kWave), hist_bytes, st, g, tp,
                            static_cast<const VT *>(value), reinterpret_cast<const float2 *>(loc), attn,
                            reinterpret_cast<const float4 *>(go), reinterpret_cast<float2 *>(gl), ga, ws.counts,
-                           ws.bases, ws.records, grid, reinterpret_cast<float2 *>(gref));
+                           ws.bases, ws.records, grid, fg);
     }
     constexpr int LG = 256 / M / 4;
     if (!accumulate) {
@@ -1159,14 +1174,15 @@ Fast fast_kind(const Geometry &g)
 
 // The fused gradients for shapes without an in-kernel form: in place, one
 // thread per (b, q): grad_attn -> grad_logits through the L*K softmax,
-// grad_loc -> grad_offset_px, and grad_ref = sum of grad_loc over (m, k).
+// grad_loc -> grad_offsets, and grad_ref from the sums of grad_loc over (m, k).
 __global__ void __launch_bounds__(256)
 fused_grads_kernel(Geometry g, const float *__restrict__ attn, float *__restrict__ grad_attn,
-                   float2 *__restrict__ grad_loc, float2 *__restrict__ grad_ref)
+                   float2 *__restrict__ grad_loc, FusedGrads fg)
 {
     const int64_t bq = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (bq >= g.queries()) return;
     const int LK = g.L * g.K;
+    const float Kf = (float)g.K;
     for (int m = 0; m < g.M; ++m) {
         const int64_t row = (bq * g.M + m) * LK;
         float dot = 0.0f;
@@ -1181,34 +1197,49 @@ fused_grads_kernel(Geometry g, const float *__restrict__ attn, float *__restrict
                 W = g.lv.W[i];
                 H = g.lv.H[i];
             }
-        float sx = 0.0f, sy = 0.0f;
+        float4 bx = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (fg.ref_dims == 4) bx = reinterpret_cast<const float4 *>(fg.ref)[bq * g.L + l];
+        float sx = 0.0f, sy = 0.0f, sw = 0.0f, sh = 0.0f;
         for (int m = 0; m < g.M; ++m)
             for (int k = 0; k < g.K; ++k) {
                 const int64_t s = ((bq * g.M + m) * g.L + l) * g.K + k;
                 const float2 v = grad_loc[s];
                 sx += v.x;
                 sy += v.y;
-                grad_loc[s] = make_float2(v.x / (float)W, v.y / (float)H);
+                if (fg.ref_dims == 4) {
+                    const float2 o = fg.off[s];
+                    sw += v.x * o.x * 0.5f / Kf;
+                    sh += v.y * o.y * 0.5f / Kf;
+                    grad_loc[s] = make_float2(v.x * (bx.z * 0.5f / Kf), v.y * (bx.w * 0.5f / Kf));
+                } else {
+                    grad_loc[s] = make_float2(v.x / (float)W, v.y / (float)H);
+                }
             }
-        if (grad_ref) grad_ref[bq * g.L + l] = make_float2(sx, sy);
+        if (fg.grad_ref) {
+            if (fg.ref_dims == 4)
+                reinterpret_cast<float4 *>(fg.grad_ref)[bq * g.L + l] = make_float4(sx, sy, sw, sh);
+            else
+                reinterpret_cast<float2 *>(fg.grad_ref)[bq * g.L + l] = make_float2(sx, sy);
+        }
     }
 }
 
 template <typename VT>
 hipError_t launch_typed(const Geometry &g, const TilePlan *tpp, const void *value, const float *loc,
-                        const float *attn, const float *go, float *gv, float *gl, float *ga, float *gref,
-                        void *ws, bool accumulate, bool fused, hipStream_t st)
+                        const float *attn, const float *go, float *gv, float *gl, float *ga, const FusedGrads *fg,
+                        void *ws, bool accumulate, hipStream_t st)
 {
     // fused gradients inside the main kernel where the L*K softmax fits the
     // wave's lanes; otherwise the plain gradients, converted afterwards
+    const bool fused = fg != nullptr;
     const bool in_kernel = fused && fused_forward_supported(g);
     hipError_t e = hipSuccess;
     bool done = false;
 #define MSDA_FAST(M_, L_, K_)                                                                                    \
-    e = in_kernel ? launch_fast<VT, M_, L_, K_, true>(g, *tpp, value, loc, attn, go, gv, gl, ga, gref, ws,       \
+    e = in_kernel ? launch_fast<VT, M_, L_, K_, true>(g, *tpp, value, loc, attn, go, gv, gl, ga, *fg, ws,        \
                                                       accumulate, st)                                            \
-                  : launch_fast<VT, M_, L_, K_, false>(g, *tpp, value, loc, attn, go, gv, gl, ga, nullptr, ws,   \
-                                                       accumulate, st);                                          \
+                  : launch_fast<VT, M_, L_, K_, false>(g, *tpp, value, loc, attn, go, gv, gl, ga, FusedGrads{},  \
+                                                       ws, accumulate, st);                                      \
     done = true;
     switch (tpp ? fast_kind(g) : Fast::None) {
     case Fast::M8L4K4: MSDA_FAST(8, 4, 4) break;
@@ -1238,7 +1269,7 @@ hipError_t launch_typed(const Geometry &g, const TilePlan *tpp, const void *valu
     if (fused && !(done && in_kernel)) {
         KernelScope ks_("fused_grads_kernel", st);
         hipLaunchKernelGGL(fused_grads_kernel, dim3((unsigned)((g.queries() + 255) / 256)), dim3(256), 0, st, g,
-                           attn, ga, reinterpret_cast<float2 *>(gl), reinterpret_cast<float2 *>(gref));
+                           attn, ga, reinterpret_cast<float2 *>(gl), *fg);
         e = hipGetLastError();
     }
     return e;
@@ -1351,20 +1382,19 @@ hipError_t launch_backward(const Geometry &g, const void *value, msda_dtype vt, 
     TilePlan tp;
     const TilePlan *tpp = backward_uses_workspace(g, value, vt, go, gv) && make_tile_plan(g, tp) ? &tp : nullptr;
     if (vt == MSDA_BF16)
-        return launch_typed<uint16_t>(g, tpp, value, loc, attn, go, gv, gl, ga, nullptr, ws, accumulate, false, st);
-    return launch_typed<float>(g, tpp, value, loc, attn, go, gv, gl, ga, nullptr, ws, accumulate, false, st);
+        return launch_typed<uint16_t>(g, tpp, value, loc, attn, go, gv, gl, ga, nullptr, ws, accumulate, st);
+    return launch_typed<float>(g, tpp, value, loc, attn, go, gv, gl, ga, nullptr, ws, accumulate, st);
 }
 
 hipError_t launch_backward_fused(const Geometry &g, const void *value, msda_dtype vt, const float *loc,
                                  const float *attn, const float *go, float *gv, float *goff, float *glogits,
-                                 float *gref, void *ws, bool accumulate, hipStream_t st)
+                                 const FusedGrads &fg, void *ws, bool accumulate, hipStream_t st)
 {
     TilePlan tp;
     const TilePlan *tpp = backward_uses_workspace(g, value, vt, go, gv) && make_tile_plan(g, tp) ? &tp : nullptr;
     if (vt == MSDA_BF16)
-        return launch_typed<uint16_t>(g, tpp, value, loc, attn, go, gv, goff, glogits, gref, ws, accumulate, true,
-                                      st);
-    return launch_typed<float>(g, tpp, value, loc, attn, go, gv, goff, glogits, gref, ws, accumulate, true, st);
+        return launch_typed<uint16_t>(g, tpp, value, loc, attn, go, gv, goff, glogits, &fg, ws, accumulate, st);
+    return launch_typed<float>(g, tpp, value, loc, attn, go, gv, goff, glogits, &fg, ws, accumulate, st);
 }
 
 }  // namespace msda

@@ -79,12 +79,11 @@ forward_c256_kernel(Geometry g, const VT *__restrict__ value, const float2 *__re
                 float2 u;
                 float a;
                 if constexpr (FUSED) {
-                    // loc = ref + offset_px / (W_l, H_l); A = softmax over the
+                    // loc = ref + offset_px / (W_l, H_l) (or, from a box,
+                    // ref_xy + offset / K * ref_wh / 2); A = softmax over the
                     // L*K consecutive samples of this head (LK divides 64, so a
                     // head's samples sit in LK adjacent lanes of this pass)
-                    const float2 r = fi.ref[gq * L + l];
-                    const float2 o = fi.off[gq * NS + s];
-                    u = make_float2(r.x + o.x / lv.Wf, r.y + o.y / lv.Hf);
+                    u = fused_location(fi.ref, fi.ref_dims, gq * L + l, fi.off[gq * NS + s], lv.Wf, lv.Hf, (float)K);
                     const float x = fi.logits[gq * NS + s];
                     float mx = x;
 #pragma unroll
@@ -263,9 +262,11 @@ hipError_t launch_typed(const Geometry &g, const void *value, const float *loc, 
     if (fi) {
         // no fused kernel for this shape: the three steps, through the caller's
         // loc / attention output buffers
-        hipError_t e = launch_sampling_locations(g, reinterpret_cast<const float *>(fi->ref),
-                                                 reinterpret_cast<const float *>(fi->off),
-                                                 reinterpret_cast<float *>(fi->loc_out), st);
+        hipError_t e = fi->ref_dims == 4
+                           ? launch_sampling_locations_box(g, fi->ref, reinterpret_cast<const float *>(fi->off),
+                                                           reinterpret_cast<float *>(fi->loc_out), st)
+                           : launch_sampling_locations(g, fi->ref, reinterpret_cast<const float *>(fi->off),
+                                                       reinterpret_cast<float *>(fi->loc_out), st);
         if (e == hipSuccess) e = launch_softmax(g, fi->logits, fi->attn_out, st);
         if (e != hipSuccess) return e;
         return launch_typed<VT>(g, value, reinterpret_cast<const float *>(fi->loc_out), fi->attn_out, out,

@@ -86,15 +86,38 @@ class KernelScope {
     hipEvent_t start_;
 };
 
-// Inputs and side outputs of the fused forward: reference points [B,Nq,L,2],
-// pixel offsets [B,Nq,M,L,K,2] and logits [B,Nq,M,L*K] in; the sampling
-// locations and attention weights it forms out (for the backward).
+// Inputs and side outputs of the fused forward: reference points [B,Nq,L,2]
+// (or 4-d boxes [B,Nq,L,4]), offsets [B,Nq,M,L,K,2] and logits [B,Nq,M,L*K]
+// in; the sampling locations and attention weights it forms out (for the
+// backward).
 struct FusedInputs {
-    const float2 *ref;
+    const float *ref;
+    int ref_dims;  // 2: offsets in pixels of level l; 4: relative to the box size
     const float2 *off;
     const float *logits;
     float2 *loc_out;
     float *attn_out;
+};
+
+// One sample's location from its reference and offset.
+__host__ __device__ inline float2 fused_location(const float *ref, int ref_dims, int64_t ref_row, float2 o,
+                                                 float Wf, float Hf, float Kf)
+{
+    if (ref_dims == 4) {
+        const float4 r = reinterpret_cast<const float4 *>(ref)[ref_row];
+        return make_float2(r.x + o.x / Kf * r.z * 0.5f, r.y + o.y / Kf * r.w * 0.5f);
+    }
+    const float2 r = reinterpret_cast<const float2 *>(ref)[ref_row];
+    return make_float2(r.x + o.x / Wf, r.y + o.y / Hf);
+}
+
+// What the fused backward needs besides the plain one: the references and
+// offsets (4-d boxes only) and the optional reference gradient [B,Nq,L,dims].
+struct FusedGrads {
+    const float *ref;
+    const float2 *off;
+    int ref_dims;
+    float *grad_ref;
 };
 
 // The fused kernels form the L*K softmax across adjacent lanes of a wave.
@@ -121,11 +144,14 @@ hipError_t launch_backward(const Geometry &g, const void *value, msda_dtype vt, 
                            const float *attn, const float *grad_out, float *grad_value,
                            float *grad_loc, float *grad_attn, void *workspace, bool accumulate,
                            hipStream_t st);
-// The same, carried back to the fused forward's inputs: grad_offset_px,
-// grad_logits and (if not null) grad_ref instead of grad_loc and grad_attn.
+// The same, carried back to the fused forward's inputs: grad_offsets,
+// grad_logits and (if fg.grad_ref is not null) grad_ref instead of grad_loc
+// and grad_attn.
 hipError_t launch_backward_fused(const Geometry &g, const void *value, msda_dtype vt, const float *loc,
                                  const float *attn, const float *grad_out, float *grad_value,
-                                 float *grad_offset_px, float *grad_logits, float *grad_ref, void *workspace,
+                                 float *grad_offsets, float *grad_logits, const FusedGrads &fg, void *workspace,
                                  bool accumulate, hipStream_t st);
+hipError_t launch_sampling_locations_box(const Geometry &g, const float *ref, const float *off, float *loc,
+                                         hipStream_t st);
 
 }  // namespace msda

@@ -112,6 +112,21 @@ sampling_locations_any_kernel(Geometry g, const float2 *__restrict__ ref, const 
     loc[s] = make_float2(r.x + v.x / (float)W, r.y + v.y / (float)H);
 }
 
+// Locations from 4-d box references (cx, cy, w, h): ref_xy + offset / K *
+// ref_wh / 2 (the 4-d reference branch of the module source on the
+// walkthrough page). One thread per sample.
+__global__ void __launch_bounds__(kBlock)
+sampling_locations_box_kernel(Geometry g, const float *__restrict__ ref, const float2 *__restrict__ off,
+                              float2 *__restrict__ loc)
+{
+    const int64_t s = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (s >= g.samples()) return;
+    const int64_t row = s / g.K;  // (b, q, m, l)
+    const int l = (int)(row % g.L);
+    const int64_t bq = row / ((int64_t)g.L * g.M);
+    loc[s] = fused_location(ref, 4, bq * g.L + l, off[s], 1.0f, 1.0f, (float)g.K);
+}
+
 // Softmax over the L*K logits of one (b, q, m) (paper notes, "Insight 2": the
 // weights of a query and head sum to 1 over all levels and points). One
 // thread per row; rows of N (a multiple of 4) use 16-byte loads and stores.
@@ -210,6 +225,17 @@ hipError_t launch_sampling_locations(const Geometry &g, const float *ref, const 
         KernelScope ks_("sampling_locations_any_kernel", st);
         hipLaunchKernelGGL(sampling_locations_any_kernel, dim3(blocks_for(g.samples())), dim3(kBlock), 0, st, g, r,
                            o, d);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_sampling_locations_box(const Geometry &g, const float *ref, const float *off, float *loc,
+                                         hipStream_t st)
+{
+    {
+        KernelScope ks_("sampling_locations_box_kernel", st);
+        hipLaunchKernelGGL(sampling_locations_box_kernel, dim3(blocks_for(g.samples())), dim3(kBlock), 0, st, g, ref,
+                           reinterpret_cast<const float2 *>(off), reinterpret_cast<float2 *>(loc));
     }
     return hipGetLastError();
 }

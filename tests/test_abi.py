@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.msda_abi_version() == 4
+    assert lib.msda_abi_version() == 5
     assert lib.msda_status_string(0) == b"ok"
     for code in range(-8, 0):
         assert lib.msda_status_string(code) not in (b"", b"unknown status")
@@ -99,20 +99,27 @@ def test_fused_entry_points_validate_on_the_host(lib):
     for i in range(6):
         p = list(ptrs)
         p[i] = None
-        assert lib.msda_forward_fused(_shape().ptr, FAKE, B.MSDA_F32, *p, None) == B.MSDA_E_NULL, i
-    assert lib.msda_forward_fused(_shape().ptr, FAKE, 7, *ptrs, None) == B.MSDA_E_UNSUPPORTED
+        assert lib.msda_forward_fused(_shape().ptr, FAKE, B.MSDA_F32, p[0], 2, *p[1:], None) == B.MSDA_E_NULL, i
+    assert lib.msda_forward_fused(_shape().ptr, FAKE, 7, FAKE, 2, *ptrs[1:], None) == B.MSDA_E_UNSUPPORTED
+    assert lib.msda_forward_fused(_shape().ptr, FAKE, B.MSDA_F32, FAKE, 3, *ptrs[1:], None) == B.MSDA_E_UNSUPPORTED
     odd = ctypes.c_void_p(0x10004)   # 4-byte aligned, not 8: (x, y) tensors need 8
-    assert lib.msda_forward_fused(_shape().ptr, FAKE, B.MSDA_F32, odd, FAKE, FAKE, FAKE, FAKE, FAKE,
+    assert lib.msda_forward_fused(_shape().ptr, FAKE, B.MSDA_F32, odd, 2, FAKE, FAKE, FAKE, FAKE, FAKE,
                                   None) == B.MSDA_E_ALIGN
-    for i in range(3):   # grad_offsets, grad_logits required; grad_ref optional
-        g = [FAKE, FAKE, FAKE, FAKE]   # grad_value, grad_offsets, grad_logits, grad_ref
+    box8 = ctypes.c_void_p(0x10008)  # 8-byte aligned, not 16: boxes need 16
+    assert lib.msda_forward_fused(_shape().ptr, FAKE, B.MSDA_F32, box8, 4, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                  None) == B.MSDA_E_ALIGN
+
+    def bwd(g, ref=None, off=None, dims=2, flags=0):
+        return lib.msda_backward_fused(_shape().ptr, FAKE, B.MSDA_F32, FAKE, FAKE, ref, off, dims, FAKE, *g, None, 0,
+                                       flags, None)
+    for i in range(3):   # grad_value, grad_offsets, grad_logits required; grad_ref optional
+        g = [FAKE, FAKE, FAKE, FAKE]
         g[i] = None
-        assert lib.msda_backward_fused(_shape().ptr, FAKE, B.MSDA_F32, FAKE, FAKE, FAKE, *g, None, 0, 0,
-                                       None) == B.MSDA_E_NULL, i
-    assert lib.msda_backward_fused(_shape().ptr, FAKE, B.MSDA_F32, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
-                                   None, 0, 0x4, None) == B.MSDA_E_UNSUPPORTED
-    assert lib.msda_backward_fused(_shape().ptr, FAKE, B.MSDA_F32, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
-                                   None, 0, 0, None) == B.MSDA_E_WORKSPACE
+        assert bwd(g) == B.MSDA_E_NULL, i
+    assert bwd([FAKE] * 3 + [None], dims=4) == B.MSDA_E_NULL        # boxes need references and offsets
+    assert bwd([FAKE] * 3 + [None], dims=5) == B.MSDA_E_UNSUPPORTED
+    assert bwd([FAKE] * 3 + [None], flags=0x4) == B.MSDA_E_UNSUPPORTED
+    assert bwd([FAKE] * 3 + [None]) == B.MSDA_E_WORKSPACE
 
 
 @cpu_only

@@ -36,13 +36,23 @@ def fused_case(ci):
     return ref32, d.offsets_px, logits
 
 
-def check_fused(ci, vtol, name):
-    w = ci.draws.workload
+def box_case(ci, seed=11):
+    """4-d references: the point as (cx, cy), box sizes drawn in [0.05, 0.5]."""
     ref32, off, logits = fused_case(ci)
+    g = torch.Generator().manual_seed(seed)
+    wh = 0.05 + 0.45 * torch.rand(ref32.shape, generator=g)
+    return torch.cat([ref32, wh], dim=-1), off, logits
+
+
+def check_fused(ci, vtol, name, box=False):
+    w = ci.draws.workload
+    ref32, off, logits = box_case(ci) if box else fused_case(ci)
     out, loc, A = msda.msda_forward_fused(dev(ci.value), ci.shapes, ci.lsi, dev(ref32), dev(off), dev(logits))
     torch.cuda.synchronize()
     loc, A = loc.cpu(), A.cpu()
-    tolerance_check(loc, oracle.sampling_locations(ci.shapes, ref32, off), PRO_TOL, f"fused loc {name}")
+    want_loc = (oracle.sampling_locations_box(ref32, off) if box
+                else oracle.sampling_locations(ci.shapes, ref32, off))
+    tolerance_check(loc, want_loc, PRO_TOL, f"fused loc {name}")
     tolerance_check(A, oracle.softmax(logits, w.levels * w.points).reshape(A.shape), PRO_TOL, f"fused A {name}")
     tolerance_check(out.cpu(), oracle.forward(ci.value, ci.shapes, ci.lsi, loc, A), vtol, f"fused out {name}")
     # the core is the same code as msda_forward: identical output at the same locations and weights
@@ -52,10 +62,15 @@ def check_fused(ci, vtol, name):
     if ci.grad_output is None:
         return
     G = ci.grad_output
-    gv, goff, glog, gref = msda.msda_backward_fused(dev(ci.value), ci.shapes, ci.lsi, dev(loc), dev(A), dev(G))
+    gv, goff, glog, gref = msda.msda_backward_fused(dev(ci.value), ci.shapes, ci.lsi, dev(loc), dev(A), dev(G),
+                                                    box_references=dev(ref32) if box else None,
+                                                    sampling_offsets=dev(off) if box else None)
     torch.cuda.synchronize()
     rgv, rgl, rga = oracle.backward(ci.value, ci.shapes, ci.lsi, loc, A, G)
-    rgref, rgoff = oracle.sampling_locations_backward(ci.shapes, rgl)
+    if box:
+        rgref, rgoff = oracle.sampling_locations_box_backward(ref32, off, rgl)
+    else:
+        rgref, rgoff = oracle.sampling_locations_backward(ci.shapes, rgl)
     LK = w.levels * w.points
     rglog = oracle.softmax_backward(A, rga, LK).reshape(glog.shape)
     tolerance_check(gv.cpu(), rgv, BWD_TOL, f"fused grad_value {name}")
@@ -67,8 +82,12 @@ def check_fused(ci, vtol, name):
     extra = BWD_TOL * a * (2.0 + ga + ga.max(axis=-1, keepdims=True))
     err = np.abs(glog.cpu().numpy() - rglog)
     assert np.all(err <= BWD_TOL * (1 + np.abs(rglog)) + extra), f"fused grad_logits {name}"
-    # grad_ref sums M*K grad_loc entries, each within 1e-4 (1+|entry|)
-    span = (BWD_TOL * (1 + np.abs(rgl))).sum(axis=(2, 4))          # [B,Nq,L,2]
+    # grad_ref sums M*K grad_loc entries (for box sizes times |offset| / (2K)),
+    # each entry within 1e-4 (1+|entry|)
+    e = BWD_TOL * (1 + np.abs(rgl))                                   # [B,Nq,M,L,K,2]
+    span = e.sum(axis=(2, 4))                                         # [B,Nq,L,2]
+    if box:
+        span = np.concatenate([span, (e * np.abs(off.numpy()) * 0.5 / w.points).sum(axis=(2, 4))], axis=-1)
     err = np.abs(gref.cpu().numpy() - rgref)
     assert np.all(err <= span + BWD_TOL * (1 + np.abs(rgref))), f"fused grad_ref {name}"
 
@@ -86,6 +105,18 @@ def test_fused_shapes(gpu_lib, geom):
     wl = workloads.custom(name="geom", offset_sigma_px=2.5, random_valid_ratios=True, backward=True, **geom)
     print(f"[fused shape] {geom}", flush=True)
     check_fused(build(wl, seed=5), FWD_TOL, str(geom))
+
+
+@pytest.mark.parametrize("name", ["tiny", "encoder_backward"])
+def test_fused_box_references(gpu_lib, name):
+    print(f"[fused box] {name}", flush=True)
+    check_fused(build(name), FWD_TOL, name, box=True)
+
+
+@pytest.mark.parametrize("geom", [GEOMS[0], GEOMS[5], GEOMS[7]], ids=["fast", "lk12", "generic"])
+def test_fused_box_shapes(gpu_lib, geom):
+    wl = workloads.custom(name="geom", offset_sigma_px=2.5, random_valid_ratios=True, backward=True, **geom)
+    check_fused(build(wl, seed=6), FWD_TOL, str(geom), box=True)
 
 
 def test_fused_bf16_value(gpu_lib):
