@@ -50,6 +50,8 @@ def parse():
     p.add_argument("--workload", default="encoder_backward",
                    help="workload name (the step always runs fwd+bwd)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-encoder-stack", action="store_true",
+                   help="skip the 6-layer encoder stack measurement (projections + FFN around the core)")
     p.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP graph replay")
     p.add_argument("--copy-mib", type=int, default=0,
                    help="only run a plain copy of this many MiB, 5 times (counter calibration)")
@@ -228,6 +230,50 @@ def copy_calibration(mib):
     print(json.dumps({"copy_mib": mib, "dispatches": 5}))
 
 
+def encoder_stack(msda, shapes, lsi, vr, B, S, M, L, K, dev, args, n_layers=6):
+    """Six Deformable-DETR encoder layers (MSDeformAttn with its four
+    projections + FFN 1024 + layer norms, random init) forward and backward at
+    the workload's shapes, fp32: time per step (eager, HIP events) and the
+    share of it spent in libmsda's kernels."""
+    import torch
+    from scale_deformable_attention_msdeformattn_amd.layer import Encoder
+    torch.manual_seed(0)
+    enc = Encoder(n_layers=n_layers, d_model=256, d_ffn=1024, n_levels=L, n_heads=M, n_points=K).to(dev)
+    src = torch.randn(B, S, 256, device=dev, requires_grad=True)
+    pos = torch.randn(B, S, 256, device=dev)
+    ref = msda.msda_reference_points(shapes, valid_ratios=vr)
+    R = torch.randn(B, S, 256, device=dev)
+
+    def step():
+        enc.zero_grad(set_to_none=True)
+        src.grad = None
+        (enc(src, pos, ref, shapes, lsi) * R).sum().backward()
+
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    steps = max(3, min(args.steps, 10))
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    msda.msda_timing_reset()
+    msda.msda_timing_enable(True)
+    step()
+    torch.cuda.synchronize()
+    msda.msda_timing_enable(False)
+    core_ms = sum(v[0] for v in msda.msda_timing_read().values())
+    msda.msda_timing_reset()
+    return {"layers": n_layers, "ms_per_step": ms, "queries_per_s": B * S / (ms * 1e-3),
+            "core_ms_per_step": core_ms, "core_share": core_ms / ms,
+            "note": "fwd+bwd of the stack; core = libmsda kernels (fused forward/backward), the rest torch "
+                    "GEMMs (fp32), layer norms and elementwise ops"}
+
+
 def cpu_baseline(wl_name, min_seconds=10.0):
     """The fp64 oracle, as it stands (single-threaded C), on the same step:
     reference points, locations, softmax, forward and backward of the whole
@@ -329,6 +375,16 @@ def main():
         out, loc, A = msda.msda_forward_fused(value, shapes, lsi, ref, off, logits_flat)
         state["fused"] = (out, msda.msda_backward_fused(value, shapes, lsi, loc, A, G))
 
+    # the same with 4-d box references (cx, cy, w, h): the encoder points with
+    # a fixed box of 8 level-0 pixels, offsets relative to the box size
+    box_ref = torch.cat([msda.msda_reference_points(shapes, valid_ratios=vr),
+                         torch.full((B, Nq, L, 2), 8.0 / float(shapes[0, 1]), device=dev)], dim=-1).contiguous()
+
+    def box_step():
+        out, loc, A = msda.msda_forward_fused(value, shapes, lsi, box_ref, off, logits_flat)
+        state["box"] = (out, msda.msda_backward_fused(value, shapes, lsi, loc, A, G, box_references=box_ref,
+                                                      sampling_offsets=off))
+
     for _ in range(max(1, args.warmup)):
         step()
     torch.cuda.synchronize()
@@ -373,39 +429,43 @@ def main():
     torch.cuda.synchronize()
     step_ms = t0.elapsed_time(t1) / args.steps
 
-    # ---- timed region 1b: the fused step, graph replay like region 1 ----
-    fused_ms = None
-    try:
-        for _ in range(2):
-            fused_step()
-        torch.cuda.synchronize()
-        s2 = torch.cuda.Stream(dev)
-        s2.wait_stream(stream)
-        with torch.cuda.stream(s2):
-            fused_step()
-        stream.wait_stream(s2)
-        torch.cuda.synchronize()
-        eager_fused = state["fused"][0].clone()
-        fgraph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(fgraph):
-            fused_step()
-        fgraph.replay()
-        torch.cuda.synchronize()
-        if not torch.equal(state["fused"][0], eager_fused):
-            raise RuntimeError("fused graph replay differs from eager")
-        for _ in range(args.warmup):
-            fgraph.replay()
-        torch.cuda.synchronize()
-        f0 = torch.cuda.Event(enable_timing=True)
-        f1 = torch.cuda.Event(enable_timing=True)
-        f0.record(stream)
-        for _ in range(args.steps):
-            fgraph.replay()
-        f1.record(stream)
-        torch.cuda.synchronize()
-        fused_ms = f0.elapsed_time(f1) / args.steps
-    except Exception as e:  # report, do not hide
-        print(f"[bench] fused step not timed ({e})", file=sys.stderr)
+    # ---- timed region 1b: the fused steps, graph replay like region 1 ----
+    def graph_time(fn, key):
+        try:
+            for _ in range(2):
+                fn()
+            torch.cuda.synchronize()
+            s2 = torch.cuda.Stream(dev)
+            s2.wait_stream(stream)
+            with torch.cuda.stream(s2):
+                fn()
+            stream.wait_stream(s2)
+            torch.cuda.synchronize()
+            eager = state[key][0].clone()
+            g2 = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g2):
+                fn()
+            g2.replay()
+            torch.cuda.synchronize()
+            if not torch.equal(state[key][0], eager):
+                raise RuntimeError(f"{key} graph replay differs from eager")
+            for _ in range(args.warmup):
+                g2.replay()
+            torch.cuda.synchronize()
+            f0 = torch.cuda.Event(enable_timing=True)
+            f1 = torch.cuda.Event(enable_timing=True)
+            f0.record(stream)
+            for _ in range(args.steps):
+                g2.replay()
+            f1.record(stream)
+            torch.cuda.synchronize()
+            return f0.elapsed_time(f1) / args.steps
+        except Exception as e:  # report, do not hide
+            print(f"[bench] {key} step not timed ({e})", file=sys.stderr)
+            return None
+
+    fused_ms = graph_time(fused_step, "fused")
+    box_ms = graph_time(box_step, "box")
 
     # ---- timed region 2: per entry point, events between the calls of eager
     # steps on the same stream ----
@@ -478,7 +538,13 @@ def main():
             "ms_per_step": fused_ms, "queries_per_s": queries / (fused_ms * 1e-3),
             "step": "reference points + msda_forward_fused + msda_backward_fused (gradients to value, offsets, "
                     "logits and reference points)"},
+        "fused_box_step": None if box_ms is None else {
+            "ms_per_step": box_ms, "queries_per_s": queries / (box_ms * 1e-3),
+            "step": "msda_forward_fused + msda_backward_fused with 4-d box references (gradients to value, "
+                    "offsets, logits and boxes)"},
     }
+    if not args.no_encoder_stack:
+        result["encoder_stack"] = encoder_stack(msda, shapes, lsi, vr, B, S, M, L, K, dev, args)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.workload)
     print(json.dumps(result), flush=True)

@@ -1,0 +1,111 @@
+"""The MSDeformAttn layer workload (projections around the fused core) on the
+GPU against the oracle chain with fp64 projections. The projections are
+library GEMMs (fp32 on the GPU); the bounds below add their rounding to the
+core's tolerances."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from scale_deformable_attention_msdeformattn_amd.layer import Encoder, MSDeformAttnLayer
+from tests.core_inputs import tolerance_check
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = np.array([[9, 13], [5, 7], [3, 4], [1, 2]], dtype=np.int64)
+
+
+def _case(seed=0, d=64, M=8, K=4, B=2, Nq=23):
+    torch.manual_seed(seed)
+    L = len(SHAPES)
+    layer = MSDeformAttnLayer(d, L, M, K)
+    with torch.no_grad():  # away from the zero init so that offsets and weights vary per query
+        layer.sampling_offsets.weight.normal_(0, 0.05)
+        layer.attention_weights.weight.normal_(0, 0.1)
+    S = int((SHAPES[:, 0] * SHAPES[:, 1]).sum())
+    x = torch.randn(B, S, d)
+    q = torch.randn(B, Nq, d)
+    ref = torch.rand(B, Nq, L, 2)
+    lsi, _ = oracle.level_start_index(SHAPES)
+    return layer, x, q, ref, lsi
+
+
+def _np(t):
+    return t.detach().cpu().double().numpy()
+
+
+def _oracle_chain(layer, x, q, ref, lsi, core_in=None):
+    """fp64 projections + oracle core. core_in = (value, offsets, logits) fp32
+    tensors to feed the core instead of the fp64 projections."""
+    M, L, K = layer.n_heads, layer.n_levels, layer.n_points
+    B, S, d = x.shape
+    Nq = q.shape[1]
+    W = {n: (_np(m.weight), _np(m.bias)) for n, m in
+         (("v", layer.value_proj), ("o", layer.sampling_offsets), ("a", layer.attention_weights),
+          ("out", layer.output_proj))}
+    if core_in is None:
+        value = (_np(x) @ W["v"][0].T + W["v"][1]).reshape(B, S, M, d // M)
+        off = (_np(q) @ W["o"][0].T + W["o"][1]).reshape(B, Nq, M, L, K, 2)
+        logits = (_np(q) @ W["a"][0].T + W["a"][1]).reshape(B, Nq, M, L * K)
+    else:
+        value, off, logits = (_np(t) for t in core_in)
+    loc = oracle.sampling_locations(SHAPES, _np(ref), off)
+    A = oracle.softmax(logits, L * K).reshape(B, Nq, M, L, K)
+    core = oracle.forward(value, SHAPES, lsi, loc, A)
+    out = core @ W["out"][0].T + W["out"][1]
+    return dict(value=value, off=off, logits=logits, loc=loc, A=A, core=core, out=out, W=W)
+
+
+def test_layer_forward_matches_oracle_chain(gpu_lib):
+    layer, x, q, ref, lsi = _case()
+    got = layer.cuda()(q.cuda(), ref.cuda(), x.cuda(), SHAPES, lsi).detach().cpu()
+    want = _oracle_chain(layer.cpu(), x, q, ref, lsi)
+    # fp32 GEMMs (inner size d) move the offsets by ~1e-6 pixels and the core
+    # output through its location slope; 1e-4 covers both at these sizes
+    tolerance_check(got, want["out"], 1e-4, "layer output")
+
+
+def test_layer_backward_matches_oracle_chain(gpu_lib):
+    """Gradients of <R, layer(...)> w.r.t. the input, the query and the
+    reference points, against the oracle's chain evaluated at the GPU's own
+    projection outputs (so that the core sees identical inputs)."""
+    layer, x, q, ref, lsi = _case(seed=1)
+    M, L, K = layer.n_heads, layer.n_levels, layer.n_points
+    layer = layer.cuda()
+    xg, qg, rg = (t.cuda().requires_grad_(True) for t in (x, q, ref))
+    out = layer(qg, rg, xg, SHAPES, lsi)
+    R = torch.randn(out.shape, device="cuda")
+    out.backward(R)
+    with torch.no_grad():
+        B, S, d = x.shape
+        Nq = q.shape[1]
+        value = layer.value_proj(xg).view(B, S, M, d // M)
+        off = layer.sampling_offsets(qg).view(B, Nq, M, L, K, 2)
+        logits = layer.attention_weights(qg).view(B, Nq, M, L * K)
+    c = _oracle_chain(layer.cpu(), x, q, ref, lsi, core_in=(value, off, logits))
+    g_core = _np(R) @ c["W"]["out"][0]
+    gv, gl, ga = oracle.backward(c["value"], SHAPES, lsi, c["loc"], c["A"], g_core)
+    g_ref, g_off = oracle.sampling_locations_backward(SHAPES, gl)
+    g_logits = oracle.softmax_backward(c["A"], ga, L * K)
+    g_x = gv.reshape(B, S, d) @ c["W"]["v"][0]
+    g_q = g_off.reshape(B, Nq, -1) @ c["W"]["o"][0] + g_logits.reshape(B, Nq, -1) @ c["W"]["a"][0]
+    tolerance_check(xg.grad.cpu(), g_x, 1e-3, "layer grad input")
+    tolerance_check(qg.grad.cpu(), g_q, 1e-3, "layer grad query")
+    tolerance_check(rg.grad.cpu(), g_ref, 1e-3 * M * K, "layer grad reference points")
+
+
+def test_encoder_stack_runs_and_trains(gpu_lib):
+    """Two encoder layers forward and backward on a small pyramid: finite,
+    with gradients reaching every parameter."""
+    torch.manual_seed(3)
+    enc = Encoder(n_layers=2, d_model=64, d_ffn=128, n_levels=len(SHAPES), n_heads=8, n_points=4).cuda()
+    S = int((SHAPES[:, 0] * SHAPES[:, 1]).sum())
+    lsi, _ = oracle.level_start_index(SHAPES)
+    src = torch.randn(2, S, 64, device="cuda", requires_grad=True)
+    pos = torch.randn(2, S, 64, device="cuda")
+    ref = torch.rand(2, S, len(SHAPES), 2, device="cuda")
+    out = enc(src, pos, ref, SHAPES, lsi)
+    out.square().mean().backward()
+    assert torch.isfinite(out).all() and torch.isfinite(src.grad).all()
+    for n, p in enc.named_parameters():
+        assert p.grad is not None and torch.isfinite(p.grad).all(), n
