@@ -45,7 +45,7 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kBlock = kWaves * kWave;
-constexpr int kQueriesPerGroup = 64;     // queries per workgroup of bin_count and main
+constexpr int kQueriesPerGroup = 32;     // queries per workgroup of bin_count and main
 constexpr int kChunk = 1024;             // records per LDS chunk in tile_accum
 constexpr int kTilePix = 32;             // pixels per tile
 constexpr int kTileCells = 2 * kWave;    // cells per tile (the tile plus one row and column of halo)
@@ -114,7 +114,7 @@ __device__ __forceinline__ bool sample_cell(float2 u, float Wf, float Hf, int &c
 
 // ---------------------------------------------------------------- 1. bin_count
 
-constexpr int kBinThreads = 1024;
+constexpr int kBinThreads = 512;
 
 // Clear the per-tile record totals before bin_count adds into them.
 __global__ void __launch_bounds__(kBlock) clear_totals_kernel(int nkeys, uint32_t *__restrict__ totals)
@@ -739,25 +739,26 @@ zero_split_levels_kernel(Geometry g, TilePlan tp, float4 *__restrict__ grad_valu
 // stay in flight across the LDS-only barriers. The split partials meet in
 // grad_value with one float atomic add per pixel and channel.
 constexpr int kDensePix = 256;             // pixels per part at most
-constexpr int kDenseSub = 512;             // samples per sub-chunk at most
-constexpr int kDenseQ = 128;               // queries per sub-chunk at most
+constexpr int kDenseSub = 1024;             // samples per sub-chunk at most
+constexpr int kDenseQ = 256;               // queries per sub-chunk at most
 constexpr int kDenseBatch = 4;             // pairs in flight per lane group
+constexpr int kDenseThreads = 512;         // threads per dense workgroup
 constexpr double kDenseMinPerPix = 24.0;   // samples per pixel (per batch and head) that make a level dense
 constexpr int kDenseMaxParts = 8;          // pixel parts of a dense level at most
-constexpr double kDenseItemSamples = 4096; // samples per dense work item (sets the query splits)
+constexpr double kDenseItemSamples = 3072; // samples per dense work item (sets the query splits)
 constexpr int kDenseMaxSplit = 64;
 
 template <int LG>
-__global__ void __launch_bounds__(kBlock)
+__global__ void __launch_bounds__(kDenseThreads)
 dense_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, const float *__restrict__ attn,
                    const float4 *__restrict__ grad_out, float4 *__restrict__ grad_value,
                    float4 *__restrict__ partials, int accumulate)
 {
-    constexpr int NG = kBlock / LG;                  // lane groups
+    constexpr int NG = kDenseThreads / LG;                  // lane groups
     constexpr int PPG = kDensePix / NG;              // pixel slots per lane group
-    constexpr int kPer = kDenseSub / kBlock;         // samples per thread per sub-chunk
-    constexpr int kGRows = (kDenseQ * LG + kBlock - 1) / kBlock;  // float4 of G staged per thread
-    static_assert(kDensePix % NG == 0 && kDenseSub % kBlock == 0, "dense tiling");
+    constexpr int kPer = kDenseSub / kDenseThreads;         // samples per thread per sub-chunk
+    constexpr int kGRows = (kDenseQ * LG + kDenseThreads - 1) / kDenseThreads;  // float4 of G staged per thread
+    static_assert(kDensePix % NG == 0 && kDenseSub % kDenseThreads == 0, "dense tiling");
     __shared__ float4 s_g[kDenseQ * LG];       // G rows of the sub-chunk's queries
     __shared__ uint2 s_pair[4 * kDenseSub];    // (bits(A * w_c), query slot), sorted by pixel
     __shared__ uint32_t s_cnt[kDensePix];
@@ -797,7 +798,7 @@ dense_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, cons
     const int grp = threadIdx.x / LG;
     const int lig = threadIdx.x % LG;
 
-    for (int i = threadIdx.x; i < kDensePix; i += kBlock) s_cnt[i] = 0;
+    for (int i = threadIdx.x; i < kDensePix; i += kDenseThreads) s_cnt[i] = 0;
 
     // loads of one sub-chunk (starting at query qa), held in registers
     float2 u[kPer];
@@ -807,7 +808,7 @@ dense_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, cons
         const int ns = min(QS, qa1 - qa) * K;
 #pragma unroll
         for (int t = 0; t < kPer; ++t) {
-            const int i = threadIdx.x + t * kBlock;
+            const int i = threadIdx.x + t * kDenseThreads;
             const int qi = i / K, k = i - (i / K) * K;
             const int64_t sidx = (((int64_t)b * g.Nq + qa + qi) * g.M + m) * LKs + (int64_t)l * K + k;
             u[t] = i < ns ? loc[sidx] : make_float2(-1e30f, -1e30f);
@@ -816,7 +817,7 @@ dense_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, cons
         const int nrow = min(QS, qa1 - qa) * LG;  // float4 of G to stage
 #pragma unroll
         for (int t = 0; t < kGRows; ++t) {
-            const int i = threadIdx.x + t * kBlock;
+            const int i = threadIdx.x + t * kDenseThreads;
             const int qi = i / LG, c = i - (i / LG) * LG;
             gst[t] = i < nrow ? grad_out[(((int64_t)b * g.Nq + qa + qi) * g.M + m) * LG + c]
                               : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -832,7 +833,7 @@ dense_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, cons
         lds_barrier();  // s_cnt cleared; the previous sub-chunk is done with s_g and s_pair
 #pragma unroll
         for (int t = 0; t < kGRows; ++t)
-            if ((kDenseQ * LG) % kBlock == 0 || threadIdx.x + t * kBlock < kDenseQ * LG) s_g[threadIdx.x + t * kBlock] = gst[t];
+            if ((kDenseQ * LG) % kDenseThreads == 0 || threadIdx.x + t * kDenseThreads < kDenseQ * LG) s_g[threadIdx.x + t * kDenseThreads] = gst[t];
         // rank this part's pairs within their pixel's count
         int pix[kPer][4];
         uint32_t rank[kPer][4];
@@ -883,13 +884,13 @@ dense_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, cons
         lds_barrier();
 #pragma unroll
         for (int t = 0; t < kPer; ++t) {
-            const uint32_t qi = (uint32_t)((threadIdx.x + t * kBlock) / K);
+            const uint32_t qi = (uint32_t)((threadIdx.x + t * kDenseThreads) / K);
 #pragma unroll
             for (int c = 0; c < 4; ++c)
                 if (pix[t][c] >= 0)
                     s_pair[s_start[pix[t][c]] + rank[t][c]] = make_uint2(__float_as_uint(wpair[t][c]), qi);
         }
-        for (int i = threadIdx.x; i < kDensePix; i += kBlock) s_cnt[i] = 0;  // for the next sub-chunk
+        for (int i = threadIdx.x; i < kDensePix; i += kDenseThreads) s_cnt[i] = 0;  // for the next sub-chunk
         lds_barrier();
         // each lane group sums over the pairs of its pixels grp, grp + NG, ...
 #pragma unroll
@@ -1128,7 +1129,7 @@ hipError_t launch_fast(const Geometry &g, const TilePlan &tp, const void *value,
         const uint32_t ditems = (uint32_t)(g.B * g.M * tp.dipb);
         {
             KernelScope ks_("dense_accum_kernel", st);
-            hipLaunchKernelGGL((dense_accum_kernel<LG>), dim3(round_up8(ditems)), dim3(kBlock), 0, st, g, tp,
+            hipLaunchKernelGGL((dense_accum_kernel<LG>), dim3(round_up8(ditems)), dim3(kDenseThreads), 0, st, g, tp,
                                reinterpret_cast<const float2 *>(loc), attn, reinterpret_cast<const float4 *>(go),
                                reinterpret_cast<float4 *>(gv), ws.partials, accumulate ? 1 : 0);
         }
