@@ -492,6 +492,14 @@ def main():
     msda.msda_timing_enable(False)
     timing = msda.msda_timing_read()
     msda.msda_timing_reset()
+    # the fused step's kernels, in a session of their own
+    msda.msda_timing_enable(True)
+    for _ in range(args.steps):
+        fused_step()
+    torch.cuda.synchronize()
+    msda.msda_timing_enable(False)
+    timing_fused = msda.msda_timing_read()
+    msda.msda_timing_reset()
 
     kstats = {}
     for name, (ms, n) in timing.items():
@@ -536,6 +544,7 @@ def main():
                      "note": "the whole msda_backward call, all its kernels"},
         "fused_step": None if fused_ms is None else {
             "ms_per_step": fused_ms, "queries_per_s": queries / (fused_ms * 1e-3),
+            "kernels_avg_us": {k: round(v[0] * 1e3 / v[1], 3) for k, v in timing_fused.items()},
             "step": "reference points + msda_forward_fused + msda_backward_fused (gradients to value, offsets, "
                     "logits and reference points)"},
         "fused_box_step": None if box_ms is None else {

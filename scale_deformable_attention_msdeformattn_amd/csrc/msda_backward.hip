@@ -362,6 +362,9 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
             }
         }
         wave_lds_sync();
+        // fused: grad_ref sums over the heads and points of each level, kept in
+        // the lanes of the pass's first head (lane l*K holds level l)
+        float4 ref_acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int s0 = 0; s0 < NS; s0 += kWave) {
             const int s = s0 + lane;
@@ -369,9 +372,7 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
                 const float4 r = s_geo[wave][s + s / LK];
                 if constexpr (FUSED) {
                     // grad_logit = A * (grad_A - sum over the head's L*K samples of A * grad_A)
-                    float t = r.w * r.x;
-#pragma unroll
-                    for (int w = 1; w < LK; w <<= 1) t += __shfl_xor(t, w, kWave);
+                    const float t = group_sum<LK>(r.w * r.x);
                     const int l = (s / K) % L;
                     grad_attn[gq * NS + s] = r.w * (r.x - t);
                     if (fg.ref_dims == 4) {
@@ -381,6 +382,37 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
                         const LevelRec lv = s_lv[l];
                         grad_loc[gq * NS + s] = make_float2(r.y / lv.Wf, r.z / lv.Hf);
                     }
+                    if (fg.grad_ref) {
+                        // (x, y) from grad_loc; for boxes (w, h) from grad_loc * offset / (2K)
+                        float4 p = make_float4(r.y, r.z, 0.f, 0.f);
+                        if (fg.ref_dims == 4) {
+                            const float2 o = fg.off[gq * NS + s];
+                            p.z = r.y * o.x * 0.5f / (float)K;
+                            p.w = r.z * o.y * 0.5f / (float)K;
+                        }
+                        // over the K points (adjacent lanes), then over the
+                        // heads of this pass (lanes LK apart); levels stay apart
+                        p.x = group_sum<K>(p.x);
+                        p.y = group_sum<K>(p.y);
+                        if (fg.ref_dims == 4) {
+                            p.z = group_sum<K>(p.z);
+                            p.w = group_sum<K>(p.w);
+                        }
+                        constexpr int kSpan = NS < kWave ? NS : kWave;  // lanes of one pass
+#pragma unroll
+                        for (int w = LK; w < kSpan; w <<= 1) {
+                            p.x += __shfl_xor(p.x, w, kWave);
+                            p.y += __shfl_xor(p.y, w, kWave);
+                            if (fg.ref_dims == 4) {
+                                p.z += __shfl_xor(p.z, w, kWave);
+                                p.w += __shfl_xor(p.w, w, kWave);
+                            }
+                        }
+                        ref_acc.x += p.x;
+                        ref_acc.y += p.y;
+                        ref_acc.z += p.z;
+                        ref_acc.w += p.w;
+                    }
                 } else {
                     grad_attn[gq * NS + s] = r.x;
                     grad_loc[gq * NS + s] = make_float2(r.y, r.z);
@@ -388,25 +420,12 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
             }
         }
         if constexpr (FUSED) {
-            if (fg.grad_ref && lane < L) {
-                float sx = 0.0f, sy = 0.0f, sw = 0.0f, sh = 0.0f;
-#pragma unroll
-                for (int mm = 0; mm < M; ++mm)
-#pragma unroll
-                    for (int k = 0; k < K; ++k) {
-                        const float4 r = s_geo[wave][mm * PAD + lane * K + k];
-                        sx += r.y;
-                        sy += r.z;
-                        if (fg.ref_dims == 4) {
-                            const float2 o = fg.off[gq * NS + mm * LK + lane * K + k];
-                            sw += r.y * o.x * 0.5f / (float)K;
-                            sh += r.z * o.y * 0.5f / (float)K;
-                        }
-                    }
+            if (fg.grad_ref && lane < LK && lane % K == 0) {
+                const int l = lane / K;
                 if (fg.ref_dims == 4)
-                    reinterpret_cast<float4 *>(fg.grad_ref)[gq * L + lane] = make_float4(sx, sy, sw, sh);
+                    reinterpret_cast<float4 *>(fg.grad_ref)[gq * L + l] = ref_acc;
                 else
-                    reinterpret_cast<float2 *>(fg.grad_ref)[gq * L + lane] = make_float2(sx, sy);
+                    reinterpret_cast<float2 *>(fg.grad_ref)[gq * L + l] = make_float2(ref_acc.x, ref_acc.y);
             }
         }
         wave_lds_sync();

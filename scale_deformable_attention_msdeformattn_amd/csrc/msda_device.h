@@ -116,6 +116,18 @@ template <int N> __device__ __forceinline__ float group_sum(float v)
     return v;
 }
 
+// The same butterfly for the maximum.
+template <int N> __device__ __forceinline__ float group_max(float v)
+{
+    if constexpr (N >= 2) v = fmaxf(v, dpp_move<kDppQuadXor1>(v));
+    if constexpr (N >= 4) v = fmaxf(v, dpp_move<kDppQuadXor2>(v));
+    if constexpr (N >= 8) v = fmaxf(v, dpp_move<kDppHalfRowMirror>(v));
+    if constexpr (N >= 16) v = fmaxf(v, dpp_move<kDppRowMirror>(v));
+#pragma unroll
+    for (int o = 16; o < N; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
 // Map a workgroup id to a logical tile so that each of the 8 XCDs (which
 // receive workgroups round-robin and have private L2 caches) processes one
 // contiguous range of tiles. `n` is the grid size and must be a multiple of 8

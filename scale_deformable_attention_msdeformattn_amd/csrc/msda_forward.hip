@@ -85,14 +85,9 @@ forward_c256_kernel(Geometry g, const VT *__restrict__ value, const float2 *__re
                     // head's samples sit in LK adjacent lanes of this pass)
                     u = fused_location(fi.ref, fi.ref_dims, gq * L + l, fi.off[gq * NS + s], lv.Wf, lv.Hf, (float)K);
                     const float x = fi.logits[gq * NS + s];
-                    float mx = x;
-#pragma unroll
-                    for (int w = 1; w < LK; w <<= 1) mx = fmaxf(mx, __shfl_xor(mx, w, kWave));
+                    const float mx = group_max<LK>(x);
                     const float e = expf(x - mx);
-                    float sum = e;
-#pragma unroll
-                    for (int w = 1; w < LK; w <<= 1) sum += __shfl_xor(sum, w, kWave);
-                    a = e / sum;
+                    a = e / group_sum<LK>(e);
                     fi.loc_out[gq * NS + s] = u;
                     fi.attn_out[gq * NS + s] = a;
                 } else {
