@@ -98,7 +98,7 @@ def dense_levels(shapes, Nq, K):
 def algorithmic_bytes(B, M, D, Nq, shapes, K, vbytes):
     """Bytes each kernel must move at the least (read + write, fp32), per
     launch. `vbytes` = the distinct value rows the samples touch. Kernels that
-    only touch workspace (clears, scans, the dense split sums) count the op's
+    only touch workspace (clears) count the op's
     own arrays they read or write, and scratch-only ones count 0."""
     f32 = 4
     L = len(shapes)
@@ -108,6 +108,8 @@ def algorithmic_bytes(B, M, D, Nq, shapes, K, vbytes):
     rows = B * Nq * M * D * f32             # output / grad_output
     dense = dense_levels(shapes, Nq, K)
     dense_pix = sum(shapes[l][0] * shapes[l][1] for l in dense)
+    # a dense level is split over queries when it has over 3072 samples
+    split_pix = sum(shapes[l][0] * shapes[l][1] for l in dense if Nq * K > 3072)
     sparse_samples = per_level * (L - len(dense))
     dense_samples = per_level * len(dense)
     gv_row = B * M * D * f32                 # grad_value bytes per pixel
@@ -119,15 +121,14 @@ def algorithmic_bytes(B, M, D, Nq, shapes, K, vbytes):
         "zero_fill_kernel": S * gv_row,
         "clear_totals_kernel": 0,
         "bin_count_kernel": sparse_samples * 2 * f32,
-        "scan_bases_kernel": 0,
         # value rows, loc, A, grad_output in; grad_loc, grad_A out
         "backward_c256_kernel": vbytes + samples * 3 * f32 + rows + samples * 3 * f32,
-        # sparse levels: grad_output, their loc and A in; their grad_value rows out
-        "tile_accum_kernel": rows + sparse_samples * 3 * f32 + (S - dense_pix) * gv_row,
-        # dense levels: grad_output, their loc and A in (sums parked in workspace)
-        "dense_accum_kernel": rows + dense_samples * 3 * f32,
-        # dense levels: their grad_value rows out
-        "dense_reduce_kernel": dense_pix * gv_row,
+        # sparse levels: grad_output, their loc and A in, their grad_value rows
+        # out; the sums of split dense levels ride along as extra items
+        "tile_accum_kernel": rows + sparse_samples * 3 * f32 + (S - dense_pix + split_pix) * gv_row,
+        # dense levels: grad_output, their loc and A in; grad_value rows out
+        # for levels with one query split (the others park sums in workspace)
+        "dense_accum_kernel": rows + dense_samples * 3 * f32 + (dense_pix - split_pix) * gv_row,
     }
 
 

@@ -16,19 +16,23 @@
 //
 //  1. bin_count   : each workgroup takes a fixed range of queries and counts,
 //                   in an LDS histogram (integer LDS atomics), how many of its
-//                   samples touch each pixel tile of each (head, level); each
-//                   non-zero count reserves the workgroup's range inside the
-//                   tile's record list with one global atomic add.
-//  2. scan_bases  : exclusive prefix of the tile totals (record base offsets).
-//  3. main        : one wavefront per query (as the forward) computes
+//                   samples touch each pixel tile of each (head, sparse level);
+//                   each non-zero count reserves the workgroup's range inside
+//                   the tile's record list with one global atomic add.
+//  2. main        : one wavefront per query (as the forward) computes
 //                   grad_attn and grad_loc, and writes each sample's index into
 //                   the record list of every tile it touches (positions from
-//                   an LDS cursor per tile: no global atomics).
-//  4. tile_accum  : one workgroup per tile sorts its records by cell in LDS,
+//                   an LDS cursor per tile: no global atomics). Each workgroup
+//                   first scans its batch's tile totals into the list bases.
+//  3. tile_accum  : one workgroup per tile sorts its records by cell in LDS,
 //                   then every pixel of the tile gathers A*w*G over the samples
 //                   of its four neighbouring cells in registers and is written
 //                   once with a plain store. Every pixel of grad_value belongs
 //                   to exactly one tile, so no zero fill is needed.
+//  4. dense_accum : the dense levels (few pixels, many samples each) skip the
+//                   records: workgroups read the samples of a query range
+//                   directly and sort their (sample, corner) pairs by pixel in
+//                   LDS; the query splits are added in a fixed order.
 //
 // Tiles are sized on the host from the expected sample density so that one
 // tile's records fit one LDS chunk; denser tiles take several chunks in turn,
@@ -184,49 +188,7 @@ bin_count_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, uint32
     }
 }
 
-// --------------------------------------------------------------- 2. scan_bases
-
-// One workgroup: exclusive prefix of the key totals (staged through LDS in
-// slices of kScanSlice keys).
-constexpr int kScanSlice = 8192;
-__global__ void __launch_bounds__(1024)
-scan_bases_kernel(int nkeys, const uint32_t *__restrict__ totals, uint32_t *__restrict__ bases)
-{
-    __shared__ uint32_t s_v[kScanSlice];
-    __shared__ uint32_t s_part[1024];
-    constexpr int per = kScanSlice / 1024;
-    uint32_t carry = 0;
-    for (int k0 = 0; k0 < nkeys; k0 += kScanSlice) {
-        for (int i = threadIdx.x; i < kScanSlice; i += 1024) s_v[i] = k0 + i < nkeys ? totals[k0 + i] : 0u;
-        __syncthreads();
-        uint32_t sum = 0;
-#pragma unroll
-        for (int j = 0; j < per; ++j) sum += s_v[threadIdx.x * per + j];
-        s_part[threadIdx.x] = sum;
-        __syncthreads();
-        for (int o = 1; o < 1024; o <<= 1) {
-            const uint32_t t = threadIdx.x >= (unsigned)o ? s_part[threadIdx.x - o] : 0u;
-            __syncthreads();
-            s_part[threadIdx.x] += t;
-            __syncthreads();
-        }
-        uint32_t run = carry + s_part[threadIdx.x] - sum;
-#pragma unroll
-        for (int j = 0; j < per; ++j) {
-            const int i = threadIdx.x * per + j;
-            const uint32_t v = s_v[i];
-            s_v[i] = run;
-            run += v;
-        }
-        carry += s_part[1023];
-        __syncthreads();
-        for (int i = threadIdx.x; i < kScanSlice; i += 1024)
-            if (k0 + i < nkeys) bases[k0 + i] = s_v[i];
-        __syncthreads();
-    }
-}
-
-// --------------------------------------------------------------------- 3. main
+// --------------------------------------------------------------------- 2. main
 
 // Waves per workgroup of the main kernel: as many (16, 8 or 4) as fit 56 KB of
 // per-wave LDS staging, so that several workgroups share a CU.
@@ -247,8 +209,8 @@ __global__ void __launch_bounds__((MainWaves<M, L, K>::kValue * kWave))
 backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, const float2 *__restrict__ loc,
                      const float *__restrict__ attn, const float4 *__restrict__ grad_out,
                      float2 *__restrict__ grad_loc, float *__restrict__ grad_attn,
-                     const uint32_t *__restrict__ offsets, const uint32_t *__restrict__ bases,
-                     uint32_t *__restrict__ records, uint32_t grid, FusedGrads fg)
+                     const uint32_t *__restrict__ offsets, const uint32_t *__restrict__ totals,
+                     uint32_t *__restrict__ bases, uint32_t *__restrict__ records, uint32_t grid, FusedGrads fg)
 {
     constexpr int C = 256;
     constexpr int D = C / M;
@@ -281,9 +243,42 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
         s_lv[l] = LevelRec{(float)g.lv.W[l], (float)g.lv.H[l], g.lv.W[l], g.lv.start[l]};
     }
     if (wg_active) {
+        // The record ranges of batch b's tiles: batch b owns records from
+        // b * 4 * (its samples) on (a sample lands in at most 4 tiles), tile i
+        // from there plus the exclusive prefix of the tile totals. Every
+        // workgroup of the batch scans the totals itself; its first one
+        // publishes the bases for tile_accum.
+        __shared__ uint32_t s_wsum[MW];
+        const uint32_t *tot = totals + (int64_t)b * nkeys;
+        for (int i = threadIdx.x; i < nkeys; i += NT) s_cursor[i] = tot[i];
+        __syncthreads();
+        const int per = (nkeys + NT - 1) / NT;
+        const int i0 = min((int)threadIdx.x * per, nkeys), i1 = min(i0 + per, nkeys);
+        uint32_t sum = 0;
+        for (int i = i0; i < i1; ++i) sum += s_cursor[i];
+        uint32_t incl = sum;  // inclusive scan over the wave
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const uint32_t t = __shfl_up(incl, o, kWave);
+            if (lane >= o) incl += t;
+        }
+        if (lane == kWave - 1) s_wsum[wave] = incl;
+        __syncthreads();
+        uint32_t run = (uint32_t)b * 4u * (uint32_t)(g.Nq * NS) + incl - sum;
+        for (int v = 0; v < wave; ++v) run += s_wsum[v];
+        for (int i = i0; i < i1; ++i) {
+            const uint32_t c = s_cursor[i];
+            s_cursor[i] = run;
+            run += c;
+        }
+        __syncthreads();
         const uint32_t *off = offsets + (int64_t)w * nkeys;
-        const uint32_t *bs = bases + (int64_t)b * nkeys;
-        for (int i = threadIdx.x; i < nkeys; i += NT) s_cursor[i] = bs[i] + off[i];
+        const bool publish = (w % tp.wpb) == 0;
+        for (int i = threadIdx.x; i < nkeys; i += NT) {
+            const uint32_t base = s_cursor[i];
+            if (publish) bases[(int64_t)b * nkeys + i] = base;
+            s_cursor[i] = base + off[i];
+        }
     }
     __syncthreads();
     if (!wg_active) return;
@@ -432,7 +427,12 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
     }
 }
 
-// --------------------------------------------------------------- 4. tile_accum
+// --------------------------------------------------------------- 3. tile_accum
+
+// defined with the dense levels below; tile_accum runs it for its extra items
+template <int LG>
+__device__ void dense_reduce_one(const Geometry &g, const TilePlan &tp, const float4 *__restrict__ partials,
+                                 float4 *__restrict__ grad_value, int accumulate, int64_t t);
 
 // One workgroup per tile (b, m, level, tile). Its records are counting-sorted
 // by cell in LDS; then each lane group (LG lanes, 4 channels each, D = 4*LG)
@@ -446,7 +446,8 @@ __global__ void __launch_bounds__(kBlock)
 tile_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, const float *__restrict__ attn,
                   const float4 *__restrict__ grad_out, float4 *__restrict__ grad_value,
                   const uint32_t *__restrict__ records, const uint32_t *__restrict__ bases,
-                  const uint32_t *__restrict__ totals, int accumulate)
+                  const uint32_t *__restrict__ totals, int accumulate, const float4 *__restrict__ partials,
+                  int reduce_blocks)
 {
     constexpr int NG = kBlock / LG;
     // (pixel, role, split) slots in use: npix*4 when cells >= NG, else at most 4*NG
@@ -459,13 +460,17 @@ tile_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, const
     __shared__ uint16_t s_entry[kChunk];
     __shared__ float4 s_part[kPartSlots][LG];
 
-    // consecutive keys (same batch and head, neighbouring tiles) read G rows of
-    // neighbouring queries: give each XCD (private L2) a contiguous key range
     // work item (b, m, level, tile, chunk); consecutive items (same batch and
     // head, neighbouring tiles) read G rows of neighbouring queries, so each
     // XCD (private L2) gets a contiguous item range
     const int item = (int)xcd_tile(blockIdx.x, gridDim.x);
-    if (item >= g.B * g.M * tp.ipb) return;
+    if (item >= g.B * g.M * tp.ipb) {
+        // the items after the tiles add up the dense levels' query splits
+        const int r = item - g.B * g.M * tp.ipb;
+        if (r < reduce_blocks)
+            dense_reduce_one<LG>(g, tp, partials, grad_value, accumulate, (int64_t)r * kBlock + threadIdx.x);
+        return;
+    }
     const int bm = item / tp.ipb;
     const int b = bm / g.M, m = bm - (bm / g.M) * g.M;
     const int r_in = item - bm * tp.ipb;
@@ -741,7 +746,7 @@ zero_split_levels_kernel(Geometry g, TilePlan tp, float4 *__restrict__ grad_valu
     }
 }
 
-// ------------------------------------------------------------- 5. dense_accum
+// ------------------------------------------------------------- 4. dense_accum
 
 // Dense levels: many samples per pixel, few pixels. Binning them into tiles
 // would write each sample's record up to four times; instead one workgroup
@@ -771,7 +776,7 @@ template <int LG>
 __global__ void __launch_bounds__(kDenseThreads)
 dense_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, const float *__restrict__ attn,
                    const float4 *__restrict__ grad_out, float4 *__restrict__ grad_value,
-                   float4 *__restrict__ partials, int accumulate)
+                   float4 *__restrict__ partials, int accumulate, uint32_t *__restrict__ totals, int nkeys)
 {
     constexpr int NG = kDenseThreads / LG;                  // lane groups
     constexpr int PPG = kDensePix / NG;              // pixel slots per lane group
@@ -783,6 +788,9 @@ dense_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, cons
     __shared__ uint32_t s_cnt[kDensePix];
     __shared__ uint32_t s_start[kDensePix + 1];
 
+    // this kernel runs first in the backward: it also clears the tile
+    // totals that bin_count adds into
+    for (int i = blockIdx.x * kDenseThreads + threadIdx.x; i < nkeys; i += gridDim.x * kDenseThreads) totals[i] = 0;
     const int item = (int)xcd_tile(blockIdx.x, gridDim.x);
     if (item >= g.B * g.M * tp.dipb) return;
     const int bm = item / tp.dipb;
@@ -959,13 +967,11 @@ dense_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, cons
 }
 
 // Sum the query splits of the dense levels, in split order, into grad_value.
-// One thread per (batch, pixel, head, float4 of channels) of the split levels.
+// Thread t of (batch, pixel, head, float4 of channels) over the split levels.
 template <int LG>
-__global__ void __launch_bounds__(kBlock)
-dense_reduce_kernel(Geometry g, TilePlan tp, const float4 *__restrict__ partials, float4 *__restrict__ grad_value,
-                    int accumulate)
+__device__ void dense_reduce_one(const Geometry &g, const TilePlan &tp, const float4 *__restrict__ partials,
+                                 float4 *__restrict__ grad_value, int accumulate, int64_t t)
 {
-    int64_t t = (int64_t)blockIdx.x * kBlock + threadIdx.x;
     for (int l = 0; l < g.L; ++l) {
         if (!((tp.dense_mask >> l) & 1) || tp.dsplit[l] <= 1) continue;
         const int npix_l = g.lv.H[l] * g.lv.W[l];
@@ -1110,7 +1116,16 @@ hipError_t launch_fast(const Geometry &g, const TilePlan &tp, const void *value,
     const int nwg = g.B * tp.wpb;
     const int nkeys = g.B * nkb;
     const size_t hist_bytes = (size_t)nkb * 4;
-    if (nkeys > 0) {
+    constexpr int LG = 256 / M / 4;
+    // dense levels first: they need no binning, and the kernel also clears
+    // the tile totals
+    if (tp.dipb > 0) {
+        const uint32_t ditems = (uint32_t)(g.B * g.M * tp.dipb);
+        KernelScope ks_("dense_accum_kernel", st);
+        hipLaunchKernelGGL((dense_accum_kernel<LG>), dim3(round_up8(ditems)), dim3(kDenseThreads), 0, st, g, tp,
+                           reinterpret_cast<const float2 *>(loc), attn, reinterpret_cast<const float4 *>(go),
+                           reinterpret_cast<float4 *>(gv), ws.partials, accumulate ? 1 : 0, ws.totals, nkeys);
+    } else if (nkeys > 0) {
         KernelScope ks_("clear_totals_kernel", st);
         hipLaunchKernelGGL(clear_totals_kernel, dim3((nkeys + kBlock - 1) / kBlock), dim3(kBlock), 0, st, nkeys,
                            ws.totals);
@@ -1120,10 +1135,6 @@ hipError_t launch_fast(const Geometry &g, const TilePlan &tp, const void *value,
         hipLaunchKernelGGL((bin_count_kernel<M, L, K>), dim3(nwg), dim3(kBinThreads), hist_bytes, st, g, tp,
                            reinterpret_cast<const float2 *>(loc), ws.counts, ws.totals);
     }
-    if (nkeys > 0) {
-        KernelScope ks_("scan_bases_kernel", st);
-        hipLaunchKernelGGL(scan_bases_kernel, dim3(1), dim3(1024), 0, st, nkeys, ws.totals, ws.bases);
-    }
     const uint32_t grid = round_up8((uint32_t)nwg);
     {
         KernelScope ks_(FUSED ? "backward_fused_c256_kernel" : "backward_c256_kernel", st);
@@ -1131,9 +1142,8 @@ hipError_t launch_fast(const Geometry &g, const TilePlan &tp, const void *value,
                            dim3(MainWaves<M, L, K>::kValue * kWave), hist_bytes, st, g, tp,
                            static_cast<const VT *>(value), reinterpret_cast<const float2 *>(loc), attn,
                            reinterpret_cast<const float4 *>(go), reinterpret_cast<float2 *>(gl), ga, ws.counts,
-                           ws.bases, ws.records, grid, fg);
+                           ws.totals, ws.bases, ws.records, grid, fg);
     }
-    constexpr int LG = 256 / M / 4;
     if (!accumulate) {
         int64_t n = 0;
         for (int l = 0; l < g.L; ++l)
@@ -1144,30 +1154,19 @@ hipError_t launch_fast(const Geometry &g, const TilePlan &tp, const void *value,
                                st, g, tp, reinterpret_cast<float4 *>(gv));
         }
     }
-    if (tp.dipb > 0) {
-        const uint32_t ditems = (uint32_t)(g.B * g.M * tp.dipb);
-        {
-            KernelScope ks_("dense_accum_kernel", st);
-            hipLaunchKernelGGL((dense_accum_kernel<LG>), dim3(round_up8(ditems)), dim3(kDenseThreads), 0, st, g, tp,
-                               reinterpret_cast<const float2 *>(loc), attn, reinterpret_cast<const float4 *>(go),
-                               reinterpret_cast<float4 *>(gv), ws.partials, accumulate ? 1 : 0);
-        }
-        int64_t nred = 0;
-        for (int l = 0; l < g.L; ++l)
-            if (((tp.dense_mask >> l) & 1) && tp.dsplit[l] > 1)
-                nred += (int64_t)g.B * g.lv.H[l] * g.lv.W[l] * g.M * LG;
-        if (nred > 0) {
-            KernelScope ks_("dense_reduce_kernel", st);
-            hipLaunchKernelGGL((dense_reduce_kernel<LG>), dim3((unsigned)((nred + kBlock - 1) / kBlock)), dim3(kBlock), 0,
-                               st, g, tp, ws.partials, reinterpret_cast<float4 *>(gv), accumulate ? 1 : 0);
-        }
-    }
-    const uint32_t items = (uint32_t)(g.B * g.M * tp.ipb);
+    // the sparse tiles, then (as extra items of the same launch) the sums of
+    // the dense levels' query splits
+    int64_t nred = 0;
+    for (int l = 0; l < g.L; ++l)
+        if (((tp.dense_mask >> l) & 1) && tp.dsplit[l] > 1) nred += (int64_t)g.B * g.lv.H[l] * g.lv.W[l] * g.M * LG;
+    const int reduce_blocks = (int)((nred + kBlock - 1) / kBlock);
+    const uint32_t items = (uint32_t)(g.B * g.M * tp.ipb) + (uint32_t)reduce_blocks;
     if (items > 0) {
         KernelScope ks_("tile_accum_kernel", st);
         hipLaunchKernelGGL((tile_accum_kernel<LG>), dim3(round_up8(items)), dim3(kBlock), 0, st, g, tp,
                            reinterpret_cast<const float2 *>(loc), attn, reinterpret_cast<const float4 *>(go),
-                           reinterpret_cast<float4 *>(gv), ws.records, ws.bases, ws.totals, accumulate ? 1 : 0);
+                           reinterpret_cast<float4 *>(gv), ws.records, ws.bases, ws.totals, accumulate ? 1 : 0,
+                           ws.partials, reduce_blocks);
     }
     return hipGetLastError();
 }
