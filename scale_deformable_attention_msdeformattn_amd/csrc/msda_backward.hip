@@ -53,8 +53,8 @@ constexpr int kQueriesPerGroup = 32;     // queries per workgroup of bin_count a
 constexpr int kChunk = 1024;             // records per LDS chunk in tile_accum
 constexpr int kTilePix = 32;             // pixels per tile
 constexpr int kTileCells = 2 * kWave;    // cells per tile (the tile plus one row and column of halo)
-constexpr int kTaskSlots = 1;            // (cell, split) tasks per lane group in tile_accum
-constexpr int kBatch = 8;                // records in flight per task
+constexpr int kTaskSlots = 2;            // (cell, split) tasks per lane group in tile_accum
+constexpr int kBatch = 6;                // records in flight per task
 constexpr int kDirectPix = 4;            // tiles this small skip the per-cell sort
 constexpr int kDirectRecords = 768;      // records per workgroup in direct mode
 constexpr int kMaxSplit = 64;            // workgroups sharing one direct-mode tile
@@ -86,11 +86,14 @@ struct SampleTiles {
 
 __device__ __forceinline__ SampleTiles sample_tiles(const TilePlan &tp, int l, int W, int H, int cx, int cy)
 {
-    const int th = tp.th[l], tw = tp.tw[l], ntw = tp.ntw[l], base = tp.tbase[l];
+    const int ntw = tp.ntw[l], base = tp.tbase[l];
+    const float iw = tp.tinv_w[l], ih = tp.tinv_h[l];
     const bool x0 = cx >= 0 && cx < W, x1 = cx + 1 >= 0 && cx + 1 < W;
     const bool y0 = cy >= 0 && cy < H, y1 = cy + 1 >= 0 && cy + 1 < H;
-    const int tx0 = x0 ? cx / tw : -1, tx1 = x1 ? (cx + 1) / tw : -1;
-    const int ty0 = y0 ? cy / th : -1, ty1 = y1 ? (cy + 1) / th : -1;
+    // c / t for in-map c (0 <= c < W or H < 2^20) by the float reciprocal
+    const float fcx = (float)cx + 0.5f, fcy = (float)cy + 0.5f;
+    const int tx0 = x0 ? (int)(fcx * iw) : -1, tx1 = x1 ? (int)((fcx + 1.0f) * iw) : -1;
+    const int ty0 = y0 ? (int)(fcy * ih) : -1, ty1 = y1 ? (int)((fcy + 1.0f) * ih) : -1;
     // tile rows: ty0, and ty1 when it differs; tile columns likewise. The four
     // combinations are distinct; slot (i, j) is fixed so nothing is indexed
     // dynamically.
@@ -182,9 +185,22 @@ bin_count_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, uint32
     __syncthreads();
     uint32_t *row = offsets + (int64_t)w * nkeys;
     uint32_t *tot = totals + (int64_t)b * nkeys;
-    for (int i = threadIdx.x; i < nkeys; i += kBinThreads) {
-        const uint32_t c = s_hist[i];
-        if (c) row[i] = atomicAdd(&tot[i], c);
+    // kKeysInFlight atomics per thread are issued before any result is
+    // stored, so their round trips overlap instead of running one by one
+    constexpr int kKeysInFlight = 8;
+    for (int i0 = threadIdx.x; i0 < nkeys; i0 += kBinThreads * kKeysInFlight) {
+        uint32_t r[kKeysInFlight];
+#pragma unroll
+        for (int j = 0; j < kKeysInFlight; ++j) {
+            const int i = i0 + j * kBinThreads;
+            const uint32_t c = i < nkeys ? s_hist[i] : 0u;
+            r[j] = c ? atomicAdd(&tot[i], c) : 0u;
+        }
+#pragma unroll
+        for (int j = 0; j < kKeysInFlight; ++j) {
+            const int i = i0 + j * kBinThreads;
+            if (i < nkeys && s_hist[i]) row[i] = r[j];
+        }
     }
 }
 
@@ -455,9 +471,10 @@ tile_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, const
     constexpr int kPartSlots = kPartSlots0 > kDirectPix * NG ? kPartSlots0 : kDirectPix * NG;
     __shared__ uint32_t s_start[kTileCells + 1];
     __shared__ uint32_t s_cur[kTileCells];
-    __shared__ float4 s_pay[kChunk];       // (fx, fy, A, bits(b*Nq+q))
-    __shared__ uint8_t s_cell[kChunk];
-    __shared__ uint16_t s_entry[kChunk];
+    // a chunk's records sorted by cell: the four corner weights A*w_c, and
+    // the byte offset of the query's grad_output row
+    __shared__ float4 s_w[kChunk];
+    __shared__ uint32_t s_q[kChunk];
     __shared__ float4 s_part[kPartSlots][LG];
 
     // work item (b, m, level, tile, chunk); consecutive items (same batch and
@@ -611,24 +628,34 @@ tile_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, const
         const int n = (int)min((uint32_t)kChunk, rtot - c0r);
         for (int i = threadIdx.x; i < ncells; i += kBlock) s_cur[i] = 0;
         lds_barrier();
-        // this chunk's records: geometry and cell; count per cell
-        for (int i = threadIdx.x; i < n; i += kBlock) {
-            const uint32_t sidx = records[rbeg + c0r + i];
+        // this chunk's records: cell, corner weights and G row offset, kept
+        // in registers (kChunk / kBlock per thread, loads all in flight)
+        // until their sorted slots are known; count per cell
+        constexpr int RPT = kChunk / kBlock;
+        static_assert(kChunk % kBlock == 0, "a chunk is whole records per thread");
+        float4 rw[RPT];
+        uint32_t rq[RPT];
+        int rc[RPT];
+#pragma unroll
+        for (int k = 0; k < RPT; ++k) {
+            const int i = threadIdx.x + k * kBlock;
+            const uint32_t sidx = i < n ? records[rbeg + c0r + i] : nsamples;
             // the main kernel wrote each record for this tile with the same
             // cell computation; the checks only keep a corrupt record from
             // addressing outside loc/attn or the cell table
-            int cell = -1;
-            if (sidx < nsamples) {
-                int cx, cy;
-                float fx, fy;
-                sample_cell(loc[sidx], Wf, Hf, cx, cy, fx, fy);
-                s_pay[i] = make_float4(fx, fy, attn[sidx], __uint_as_float(sidx / (uint32_t)NS));
-                const int ry = cy - r0 + 1, rx = cx - c0 + 1;
-                if (ry >= 0 && ry <= ph && rx >= 0 && rx < cw) cell = ry * cw + rx;
-            }
-            s_cell[i] = cell < 0 ? (uint8_t)0xff : (uint8_t)cell;
-            if (cell >= 0) atomicAdd(&s_cur[cell], 1u);
+            int cx, cy;
+            float fx, fy;
+            sample_cell(sidx < nsamples ? loc[sidx] : make_float2(0.f, 0.f), Wf, Hf, cx, cy, fx, fy);
+            const float a = sidx < nsamples ? attn[sidx] : 0.0f;
+            const float ay0 = a * (1.0f - fy), ay1 = a * fy;
+            rw[k] = make_float4(ay0 * (1.0f - fx), ay0 * fx, ay1 * (1.0f - fx), ay1 * fx);
+            rq[k] = (sidx / (uint32_t)NS) * grow_bytes;
+            const int ry = cy - r0 + 1, rx = cx - c0 + 1;
+            rc[k] = (sidx < nsamples && ry >= 0 && ry <= ph && rx >= 0 && rx < cw) ? ry * cw + rx : -1;
         }
+#pragma unroll
+        for (int k = 0; k < RPT; ++k)
+            if (rc[k] >= 0) atomicAdd(&s_cur[rc[k]], 1u);
         lds_barrier();
         // exclusive scan of the (at most kTileCells = 2 * kWave) cell counts, one wave
         if (threadIdx.x < kWave) {
@@ -647,8 +674,13 @@ tile_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, const
             if (threadIdx.x == kWave - 1) s_start[ncells] = incl;
         }
         lds_barrier();
-        for (int i = threadIdx.x; i < n; i += kBlock)
-            if (s_cell[i] != 0xff) s_entry[atomicAdd(&s_cur[s_cell[i]], 1u)] = (uint16_t)i;
+#pragma unroll
+        for (int k = 0; k < RPT; ++k)
+            if (rc[k] >= 0) {
+                const uint32_t pos = atomicAdd(&s_cur[rc[k]], 1u);
+                s_w[pos] = rw[k];
+                s_q[pos] = rq[k];
+            }
         lds_barrier();
         // (cell, split) tasks; each adds its four corner sums into its own
         // (pixel, role, split) slots, which no other task touches
@@ -663,28 +695,23 @@ tile_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, const
             for (uint32_t e0 = s_start[cell] + split; e0 < e_end; e0 += S * kBatch) {
                 // branch-free batch: entries past the cell's end re-read its
                 // last entry and load a zero G row (out-of-range offset)
-                float4 pay[kBatch], gv[kBatch];
-                uint32_t ent[kBatch];
-#pragma unroll
-                for (int j = 0; j < kBatch; ++j) ent[j] = s_entry[min(e0 + j * S, e_end - 1)];
-#pragma unroll
-                for (int j = 0; j < kBatch; ++j) pay[j] = s_pay[ent[j]];
+                float4 w[kBatch], gv[kBatch];
 #pragma unroll
                 for (int j = 0; j < kBatch; ++j) {
-                    const uint32_t off = __float_as_uint(pay[j].w) * grow_bytes + gbase;
+                    const uint32_t e = min(e0 + j * S, e_end - 1);
+                    w[j] = s_w[e];
+                    const uint32_t off = s_q[e] + gbase;
                     gv[j] = load_f32x4(grs, e0 + j * S < e_end ? off : kOutOfRange);
                 }
 #pragma unroll
                 for (int j = 0; j < kBatch; ++j) {
-                    const float fx = pay[j].x, fy = pay[j].y, a = pay[j].z;
-                    const float ay0 = a * (1.0f - fy), ay1 = a * fy;
-                    const float w[4] = {ay0 * (1.0f - fx), ay0 * fx, ay1 * (1.0f - fx), ay1 * fx};
+                    const float wr[4] = {w[j].x, w[j].y, w[j].z, w[j].w};
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        acc[r].x = __builtin_fmaf(w[r], gv[j].x, acc[r].x);
-                        acc[r].y = __builtin_fmaf(w[r], gv[j].y, acc[r].y);
-                        acc[r].z = __builtin_fmaf(w[r], gv[j].z, acc[r].z);
-                        acc[r].w = __builtin_fmaf(w[r], gv[j].w, acc[r].w);
+                        acc[r].x = __builtin_fmaf(wr[r], gv[j].x, acc[r].x);
+                        acc[r].y = __builtin_fmaf(wr[r], gv[j].y, acc[r].y);
+                        acc[r].z = __builtin_fmaf(wr[r], gv[j].z, acc[r].z);
+                        acc[r].w = __builtin_fmaf(wr[r], gv[j].w, acc[r].w);
                     }
                 }
             }
@@ -1310,6 +1337,8 @@ bool make_tile_plan(const Geometry &g, TilePlan &tp)
     tp.dense_mask = 0;
     for (int l = 0; l < g.L; ++l) {
         const int H = g.lv.H[l], W = g.lv.W[l];
+        // tile indices come from float reciprocals, exact below 2^20
+        if (H >= (1 << 20) || W >= (1 << 20)) return false;
         const double per_cell = (double)g.Nq * g.K / ((double)H * W);
         tp.dparts[l] = tp.dsplit[l] = 1;
         tp.dibase[l] = dibase;
@@ -1321,6 +1350,7 @@ bool make_tile_plan(const Geometry &g, TilePlan &tp)
             tp.dsplit[l] = (int)std::min<double>(kDenseMaxSplit, std::max(1.0, s));
             dibase += tp.dparts[l] * tp.dsplit[l];
             tp.th[l] = tp.tw[l] = tp.ntw[l] = tp.nchunk[l] = 1;
+            tp.tinv_h[l] = tp.tinv_w[l] = 1.0f;
             tp.tbase[l] = base;
             tp.ibase[l] = ibase;
             continue;
@@ -1346,6 +1376,8 @@ bool make_tile_plan(const Geometry &g, TilePlan &tp)
         }
         tp.th[l] = bt;
         tp.tw[l] = bw;
+        tp.tinv_h[l] = 1.0f / (float)bt;
+        tp.tinv_w[l] = 1.0f / (float)bw;
         tp.ntw[l] = (W + bw - 1) / bw;
         tp.tbase[l] = base;
         const int ntiles = ((H + bt - 1) / bt) * tp.ntw[l];
@@ -1363,6 +1395,7 @@ bool make_tile_plan(const Geometry &g, TilePlan &tp)
     }
     for (int l = g.L; l < MSDA_MAX_LEVELS; ++l) {
         tp.th[l] = tp.tw[l] = tp.ntw[l] = tp.nchunk[l] = 1, tp.tbase[l] = base, tp.ibase[l] = ibase;
+        tp.tinv_h[l] = tp.tinv_w[l] = 1.0f;
         tp.dparts[l] = tp.dsplit[l] = 1, tp.dibase[l] = dibase;
     }
     tp.tpb = base;

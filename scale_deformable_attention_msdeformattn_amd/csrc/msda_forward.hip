@@ -48,11 +48,14 @@ forward_c256_kernel(Geometry g, const VT *__restrict__ value, const float2 *__re
     constexpr int LK = L * K;
     constexpr int NS = M * LK;               // samples per query
     constexpr uint32_t RB = C * sizeof(VT);  // bytes per value row (one pixel, all heads)
+    // per-head stride of the LDS records: one record of padding, so that the
+    // heads' records read together in phase 2 fall in different banks
+    constexpr int PAD = LK + 1;
     static_assert(D % 4 == 0 && LPH >= 1 && LPH <= kWave, "C=256 path needs 4 | D");
 
     __shared__ LevelRec s_lv[L];
-    __shared__ int4 s_off[kWaves][NS];
-    __shared__ float4 s_w[kWaves][NS];
+    __shared__ int4 s_off[kWaves][M * PAD];
+    __shared__ float4 s_w[kWaves][M * PAD];
 
     const int lane = threadIdx.x % kWave;
     // wave-uniform by construction; readfirstlane lets the compiler keep the
@@ -113,8 +116,9 @@ forward_c256_kernel(Geometry g, const VT *__restrict__ value, const float2 *__re
                 o.z = (int)((y1ok & x0ok) ? o10 : kOutOfRange);
                 o.w = (int)((y1ok & x1ok) ? o10 + RB : kOutOfRange);
                 const float wy0 = a * (1.0f - fy), wy1 = a * fy;
-                s_off[wave][s] = o;
-                s_w[wave][s] = make_float4(wy0 * (1.0f - fx), wy0 * fx, wy1 * (1.0f - fx), wy1 * fx);
+                const int p = s + s / LK;
+                s_off[wave][p] = o;
+                s_w[wave][p] = make_float4(wy0 * (1.0f - fx), wy0 * fx, wy1 * (1.0f - fx), wy1 * fx);
             }
         }
     }
@@ -127,8 +131,8 @@ forward_c256_kernel(Geometry g, const VT *__restrict__ value, const float2 *__re
         make_rsrc(value + (int64_t)b * g.S * C, (uint32_t)g.S * RB);
     const uint32_t lane_off = (uint32_t)lane * 4u * sizeof(VT);
     const int m = lane / LPH;
-    const int4 *offs = &s_off[wave][m * LK];
-    const float4 *ws = &s_w[wave][m * LK];
+    const int4 *offs = &s_off[wave][m * PAD];
+    const float4 *ws = &s_w[wave][m * PAD];
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int i = 0; i < LK; ++i) {

@@ -52,6 +52,10 @@ struct TilePlan {
     int32_t dsplit[MSDA_MAX_LEVELS];  // query splits of a dense level
     int32_t dibase[MSDA_MAX_LEVELS];  // first dense item of the level within (batch, head)
     int32_t dipb;                     // dense items per (batch, head)
+    // 1/tw and 1/th as floats: floor((c + 0.5) * (1/t)) is c / t exactly for
+    // 0 <= c < 2^20 and t <= 128 (checked exhaustively), without a division
+    float tinv_w[MSDA_MAX_LEVELS];
+    float tinv_h[MSDA_MAX_LEVELS];
 };
 
 // Whether level l's grad_value rows are summed with float atomics (they must
