@@ -174,10 +174,17 @@ def _counter_rows(d, counter):
 
 
 def _short_kernel_name(full):
-    """'void ns::(anonymous namespace)::name<T, 8>(args)' -> 'name'."""
+    """'void ns::(anonymous namespace)::name<T, 8>(args)' -> 'name'. The fused
+    instantiations of the c256 kernels (last template argument true) get the
+    names the library's own timing uses for them, forward_fused_c256_kernel
+    and backward_fused_c256_kernel, so their counters are kept apart."""
     head = full.replace("(anonymous namespace)", "")
-    head = head.split("<")[0].split("(")[0]
-    return head.split("::")[-1].split()[-1] if head.strip() else head
+    tmpl = head.split("(")[0]
+    name = tmpl.split("<")[0]
+    name = name.split("::")[-1].split()[-1] if name.strip() else name
+    if name in ("forward_c256_kernel", "backward_c256_kernel") and tmpl.rstrip().endswith("true>"):
+        name = name.replace("_c256", "_fused_c256")
+    return name
 
 
 def ingest_counters(d, copy_mib, workload):

@@ -14,6 +14,10 @@
 // are split over several workgroups, one add per pixel and channel per
 // workgroup):
 //
+//  0. dense_accum : the dense levels (few pixels, many samples each) skip the
+//                   records: workgroups read the samples of a query range
+//                   directly and sort their (sample, corner) pairs by pixel in
+//                   LDS. It runs first and also clears the tile totals.
 //  1. bin_count   : each workgroup takes a fixed range of queries and counts,
 //                   in an LDS histogram (integer LDS atomics), how many of its
 //                   samples touch each pixel tile of each (head, sparse level);
@@ -24,15 +28,14 @@
 //                   the record list of every tile it touches (positions from
 //                   an LDS cursor per tile: no global atomics). Each workgroup
 //                   first scans its batch's tile totals into the list bases.
-//  3. tile_accum  : one workgroup per tile sorts its records by cell in LDS,
-//                   then every pixel of the tile gathers A*w*G over the samples
-//                   of its four neighbouring cells in registers and is written
-//                   once with a plain store. Every pixel of grad_value belongs
-//                   to exactly one tile, so no zero fill is needed.
-//  4. dense_accum : the dense levels (few pixels, many samples each) skip the
-//                   records: workgroups read the samples of a query range
-//                   directly and sort their (sample, corner) pairs by pixel in
-//                   LDS; the query splits are added in a fixed order.
+//  3. tile_accum  : one workgroup per tile sorts its records by cell in LDS
+//                   (with each record's four corner weights and G row offset),
+//                   then each lane group takes a cell and sums A*w_c*G into
+//                   the slots of the cell's four corner pixels; every pixel
+//                   adds its slots and is written once with a plain store.
+//                   Every pixel of a sparse level belongs to exactly one tile,
+//                   so no zero fill is needed. Extra work items of the same
+//                   launch add the dense levels' query splits in a fixed order.
 //
 // Tiles are sized on the host from the expected sample density so that one
 // tile's records fit one LDS chunk; denser tiles take several chunks in turn,
