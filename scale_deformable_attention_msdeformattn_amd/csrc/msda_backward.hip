@@ -87,10 +87,22 @@ struct SampleTiles {
     int t[4];
 };
 
-__device__ __forceinline__ SampleTiles sample_tiles(const TilePlan &tp, int l, int W, int H, int cx, int cy)
+// One level's tiling, staged in LDS: a lane-varying level index into the
+// kernel-argument TilePlan would turn into a memory load per lane.
+struct TileLevel {
+    float iw, ih;     // 1/tw, 1/th
+    int32_t ntw, base;
+};
+
+__device__ __forceinline__ TileLevel tile_level(const TilePlan &tp, int l)
 {
-    const int ntw = tp.ntw[l], base = tp.tbase[l];
-    const float iw = tp.tinv_w[l], ih = tp.tinv_h[l];
+    return TileLevel{tp.tinv_w[l], tp.tinv_h[l], tp.ntw[l], tp.tbase[l]};
+}
+
+__device__ __forceinline__ SampleTiles sample_tiles(const TileLevel &tl, int W, int H, int cx, int cy)
+{
+    const int ntw = tl.ntw, base = tl.base;
+    const float iw = tl.iw, ih = tl.ih;
     const bool x0 = cx >= 0 && cx < W, x1 = cx + 1 >= 0 && cx + 1 < W;
     const bool y0 = cy >= 0 && cy < H, y1 = cy + 1 >= 0 && cy + 1 < H;
     // c / t for in-map c (0 <= c < W or H < 2^20) by the float reciprocal
@@ -146,12 +158,14 @@ bin_count_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, uint32
 {
     extern __shared__ uint32_t s_hist[];  // [M * tpb]
     __shared__ LevelRec s_lv[L];
+    __shared__ TileLevel s_tl[L];
     __shared__ int s_sparse[L];            // the levels that keep records
     const int nkeys = M * tp.tpb;
     for (int i = threadIdx.x; i < nkeys; i += kBinThreads) s_hist[i] = 0;
     if (threadIdx.x < L) {
         const int l = threadIdx.x;
         s_lv[l] = LevelRec{(float)g.lv.W[l], (float)g.lv.H[l], g.lv.W[l], g.lv.start[l]};
+        s_tl[l] = tile_level(tp, l);
     }
     int nsl = 0;
 #pragma unroll
@@ -179,7 +193,7 @@ bin_count_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, uint32
             int cx, cy;
             float fx, fy;
             if (!sample_cell(u[k], lv.Wf, lv.Hf, cx, cy, fx, fy)) continue;
-            const SampleTiles st = sample_tiles(tp, l, lv.W, H, cx, cy);
+            const SampleTiles st = sample_tiles(s_tl[l], lv.W, H, cx, cy);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 if (st.t[j] >= 0) atomicAdd(&s_hist[m * tp.tpb + st.t[j]], 1u);
@@ -243,6 +257,7 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
 
     extern __shared__ uint32_t s_cursor[];  // [M * tpb]
     __shared__ LevelRec s_lv[L];
+    __shared__ TileLevel s_tl[L];
     __shared__ int4 s_off[MW][M * PAD];
     // (fx, fy, A, -) per sample; each entry is overwritten in place by its
     // (grad_attn, grad_x, grad_y, -) once the wave has read it (a wave's LDS
@@ -260,6 +275,7 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
     if (threadIdx.x < L) {
         const int l = threadIdx.x;
         s_lv[l] = LevelRec{(float)g.lv.W[l], (float)g.lv.H[l], g.lv.W[l], g.lv.start[l]};
+        s_tl[l] = tile_level(tp, l);
     }
     if (wg_active) {
         // The record ranges of batch b's tiles: batch b owns records from
@@ -336,7 +352,7 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
                 s_off[wave][p] = o;
                 s_geo[wave][p] = make_float4(fx, fy, a, 0.0f);
                 if (in && !((tp.dense_mask >> l) & 1)) {
-                    const SampleTiles st = sample_tiles(tp, l, lv.W, H, cx, cy);
+                    const SampleTiles st = sample_tiles(s_tl[l], lv.W, H, cx, cy);
                     const uint32_t sidx = (uint32_t)(gq * NS + s);
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
