@@ -51,17 +51,22 @@ reference_points_kernel(Geometry g, const float *__restrict__ vr, const float *_
 }
 
 // loc = ref + offset_px / (W_l, H_l) (walkthrough page, "encoder"; paper
-// notes, "Key code"). One thread per (b, q, m, l): its K (x, y) pairs are
-// contiguous, so consecutive threads read and write consecutive 8K-byte runs.
+// notes, "Key code"). For even K the (x, y) pairs of one (b, q, m, l) are
+// contiguous, so consecutive threads take consecutive pairs of points.
 template <int K>
 __global__ void __launch_bounds__(kBlock)
-sampling_locations_kernel(Geometry g, const float2 *__restrict__ ref, const float2 *__restrict__ off,
-                          float2 *__restrict__ loc)
+sampling_locations_kernel(Geometry g, const float2 *__restrict__ ref, const float4 *__restrict__ off,
+                          float4 *__restrict__ loc)
 {
-    const int64_t t = (int64_t)blockIdx.x * kBlock + threadIdx.x;  // (b, q, m, l)
-    if (t >= (int64_t)g.B * g.Nq * g.M * g.L) return;
-    const int l = (int)(t % g.L);
-    const int64_t bq = t / ((int64_t)g.L * g.M);
+    // one thread per pair of points of one (b, q, m, l): a 16-byte load and
+    // store each; 32-bit index math (the host keeps the pair count < 2^32)
+    constexpr int KP = K / 2;
+    static_assert(K % 2 == 0, "pairs of points");
+    const uint32_t t = blockIdx.x * kBlock + threadIdx.x;
+    if (t >= (uint32_t)(g.queries() * g.M * g.L * KP)) return;
+    const uint32_t row = t / KP;  // (b, q, m, l)
+    const int l = (int)(row % (uint32_t)g.L);
+    const uint32_t bq = row / (uint32_t)(g.L * g.M);
     int W = 1, H = 1;
 #pragma unroll
     for (int i = 0; i < MSDA_MAX_LEVELS; ++i)
@@ -70,24 +75,9 @@ sampling_locations_kernel(Geometry g, const float2 *__restrict__ ref, const floa
             H = g.lv.H[i];
         }
     const float Wf = (float)W, Hf = (float)H;
-    const float2 r = ref[bq * g.L + l];
-    const float2 *o = off + t * K;
-    float2 *out = loc + t * K;
-    if constexpr (K % 2 == 0) {
-        const float4 *o4 = reinterpret_cast<const float4 *>(o);
-        float4 *out4 = reinterpret_cast<float4 *>(out);
-#pragma unroll
-        for (int k = 0; k < K / 2; ++k) {
-            const float4 v = o4[k];
-            out4[k] = make_float4(r.x + v.x / Wf, r.y + v.y / Hf, r.x + v.z / Wf, r.y + v.w / Hf);
-        }
-    } else {
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-            const float2 v = o[k];
-            out[k] = make_float2(r.x + v.x / Wf, r.y + v.y / Hf);
-        }
-    }
+    const float2 r = ref[(int64_t)bq * g.L + l];
+    const float4 v = off[t];
+    loc[t] = make_float4(r.x + v.x / Wf, r.y + v.y / Hf, r.x + v.z / Wf, r.y + v.w / Hf);
 }
 
 // Any K: one thread per sample.
@@ -128,35 +118,25 @@ sampling_locations_box_kernel(Geometry g, const float *__restrict__ ref, const f
 }
 
 // Softmax over the L*K logits of one (b, q, m) (paper notes, "Insight 2": the
-// weights of a query and head sum to 1 over all levels and points). One
-// thread per row; rows of N (a multiple of 4) use 16-byte loads and stores.
+// weights of a query and head sum to 1 over all levels and points). Rows of N
+// (a multiple of 4) take N/4 adjacent lanes, one 16-byte load and store each;
+// the max and the sum go across the row's lanes by DPP butterflies, so that
+// many rows are in flight per wave.
 template <int N>
 __global__ void __launch_bounds__(kBlock)
 softmax_vec_kernel(int64_t rows, const float4 *x, float4 *y)  // y may alias x
 {
-    const int64_t row = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    if (row >= rows) return;
-    float v[N];
-#pragma unroll
-    for (int i = 0; i < N / 4; ++i) {
-        const float4 t = x[row * (N / 4) + i];
-        v[4 * i + 0] = t.x;
-        v[4 * i + 1] = t.y;
-        v[4 * i + 2] = t.z;
-        v[4 * i + 3] = t.w;
-    }
-    float mx = v[0];
-#pragma unroll
-    for (int i = 1; i < N; ++i) mx = fmaxf(mx, v[i]);
-    float sum = 0.0f;
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-        v[i] = expf(v[i] - mx);
-        sum += v[i];
-    }
-#pragma unroll
-    for (int i = 0; i < N / 4; ++i)
-        y[row * (N / 4) + i] = make_float4(v[4 * i] / sum, v[4 * i + 1] / sum, v[4 * i + 2] / sum, v[4 * i + 3] / sum);
+    constexpr int C = N / 4;  // lanes per row (divides 64: rows never straddle a wave)
+    static_assert(N % 4 == 0 && kWave % C == 0, "row lanes");
+    const int64_t t = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    // a row's lanes are all in range or all out of it, so the butterflies
+    // below only ever combine lanes of one live row
+    if (t >= rows * C) return;
+    const float4 v = x[t];
+    const float mx = group_max<C>(fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
+    const float e0 = expf(v.x - mx), e1 = expf(v.y - mx), e2 = expf(v.z - mx), e3 = expf(v.w - mx);
+    const float sum = group_sum<C>((e0 + e1) + (e2 + e3));
+    y[t] = make_float4(e0 / sum, e1 / sum, e2 / sum, e3 / sum);
 }
 
 __global__ void __launch_bounds__(kBlock)
@@ -210,17 +190,21 @@ hipError_t launch_sampling_locations(const Geometry &g, const float *ref, const 
     const auto r = reinterpret_cast<const float2 *>(ref);
     const auto o = reinterpret_cast<const float2 *>(off);
     const auto d = reinterpret_cast<float2 *>(loc);
+    const auto o4 = reinterpret_cast<const float4 *>(off);
+    const auto d4 = reinterpret_cast<float4 *>(loc);
     const bool a16 = (reinterpret_cast<uintptr_t>(off) % 16) == 0 && (reinterpret_cast<uintptr_t>(loc) % 16) == 0;
-    const unsigned rows = blocks_for(g.queries() * g.M * g.L);
-    if (g.K == 4 && a16) {
+    const int64_t pairs = g.samples() / 2;  // float4 = two points
+    const bool vec = a16 && g.K % 2 == 0 && pairs + kBlock < (int64_t(1) << 32);
+    const unsigned blocks = blocks_for(pairs);
+    if (vec && g.K == 4) {
         KernelScope ks_("sampling_locations_kernel", st);
-        hipLaunchKernelGGL(sampling_locations_kernel<4>, dim3(rows), dim3(kBlock), 0, st, g, r, o, d);
-    } else if (g.K == 2 && a16) {
+        hipLaunchKernelGGL(sampling_locations_kernel<4>, dim3(blocks), dim3(kBlock), 0, st, g, r, o4, d4);
+    } else if (vec && g.K == 2) {
         KernelScope ks_("sampling_locations_kernel", st);
-        hipLaunchKernelGGL(sampling_locations_kernel<2>, dim3(rows), dim3(kBlock), 0, st, g, r, o, d);
-    } else if (g.K == 8 && a16) {
+        hipLaunchKernelGGL(sampling_locations_kernel<2>, dim3(blocks), dim3(kBlock), 0, st, g, r, o4, d4);
+    } else if (vec && g.K == 8) {
         KernelScope ks_("sampling_locations_kernel", st);
-        hipLaunchKernelGGL(sampling_locations_kernel<8>, dim3(rows), dim3(kBlock), 0, st, g, r, o, d);
+        hipLaunchKernelGGL(sampling_locations_kernel<8>, dim3(blocks), dim3(kBlock), 0, st, g, r, o4, d4);
     } else {
         KernelScope ks_("sampling_locations_any_kernel", st);
         hipLaunchKernelGGL(sampling_locations_any_kernel, dim3(blocks_for(g.samples())), dim3(kBlock), 0, st, g, r,
@@ -249,16 +233,16 @@ hipError_t launch_softmax(const Geometry &g, const float *logits, float *w, hipS
     const auto y4 = reinterpret_cast<float4 *>(w);
     if (a16 && n == 16) {
         KernelScope ks_("softmax_vec_kernel", st);
-        hipLaunchKernelGGL(softmax_vec_kernel<16>, dim3(blocks_for(rows)), dim3(kBlock), 0, st, rows, x4, y4);
+        hipLaunchKernelGGL(softmax_vec_kernel<16>, dim3(blocks_for(rows * 4)), dim3(kBlock), 0, st, rows, x4, y4);
     } else if (a16 && n == 32) {
         KernelScope ks_("softmax_vec_kernel", st);
-        hipLaunchKernelGGL(softmax_vec_kernel<32>, dim3(blocks_for(rows)), dim3(kBlock), 0, st, rows, x4, y4);
+        hipLaunchKernelGGL(softmax_vec_kernel<32>, dim3(blocks_for(rows * 8)), dim3(kBlock), 0, st, rows, x4, y4);
     } else if (a16 && n == 8) {
         KernelScope ks_("softmax_vec_kernel", st);
-        hipLaunchKernelGGL(softmax_vec_kernel<8>, dim3(blocks_for(rows)), dim3(kBlock), 0, st, rows, x4, y4);
+        hipLaunchKernelGGL(softmax_vec_kernel<8>, dim3(blocks_for(rows * 2)), dim3(kBlock), 0, st, rows, x4, y4);
     } else if (a16 && n == 4) {
         KernelScope ks_("softmax_vec_kernel", st);
-        hipLaunchKernelGGL(softmax_vec_kernel<4>, dim3(blocks_for(rows)), dim3(kBlock), 0, st, rows, x4, y4);
+        hipLaunchKernelGGL(softmax_vec_kernel<4>, dim3(blocks_for(rows * 1)), dim3(kBlock), 0, st, rows, x4, y4);
     } else {
         KernelScope ks_("softmax_kernel", st);
         hipLaunchKernelGGL(softmax_kernel, dim3(blocks_for(rows)), dim3(kBlock), 0, st, rows, n, logits, w);
