@@ -238,7 +238,7 @@ template <int M, int L, int K> struct MainWaves {
 // grad_ref (if not null) sums grad_loc over heads and points (box references:
 // also grad_loc * offset / (2K) for the box size).
 template <typename VT, int M, int L, int K, bool FUSED>
-__global__ void __launch_bounds__((MainWaves<M, L, K>::kValue * kWave))
+__global__ void __launch_bounds__((MainWaves<M, L, K>::kValue * kWave)) __attribute__((amdgpu_waves_per_eu(5, 5)))
 backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, const float2 *__restrict__ loc,
                      const float *__restrict__ attn, const float4 *__restrict__ grad_out,
                      float2 *__restrict__ grad_loc, float *__restrict__ grad_attn,
@@ -366,18 +366,34 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
         const int4 *offs = &s_off[wave][m * PAD];
         const float4 *geo = &s_geo[wave][m * PAD];
         float4 *res = &s_geo[wave][m * PAD];
+        // software-pipelined over the L*K samples: the next sample's four
+        // gathers are issued before this one's arithmetic, so that eight are
+        // in flight (the in-place result writes below would otherwise keep
+        // the compiler from hoisting them)
+        float4 f = geo[0];
+        float4 v00, v01, v10, v11;
+        {
+            const int4 o = offs[0];
+            v00 = ValueTraits<VT>::load4(vr, (uint32_t)o.x + vlane);
+            v01 = ValueTraits<VT>::load4(vr, (uint32_t)o.y + vlane);
+            v10 = ValueTraits<VT>::load4(vr, (uint32_t)o.z + vlane);
+            v11 = ValueTraits<VT>::load4(vr, (uint32_t)o.w + vlane);
+        }
 #pragma unroll
         for (int l = 0; l < L; ++l) {
             const float Wf = (float)g.lv.W[l], Hf = (float)g.lv.H[l];
 #pragma unroll
             for (int k = 0; k < K; ++k) {
                 const int i = l * K + k;
-                const int4 o = offs[i];
-                const float4 f = geo[i];
-                const float4 v00 = ValueTraits<VT>::load4(vr, (uint32_t)o.x + vlane);
-                const float4 v01 = ValueTraits<VT>::load4(vr, (uint32_t)o.y + vlane);
-                const float4 v10 = ValueTraits<VT>::load4(vr, (uint32_t)o.z + vlane);
-                const float4 v11 = ValueTraits<VT>::load4(vr, (uint32_t)o.w + vlane);
+                float4 fn = f, n00 = v00, n01 = v01, n10 = v10, n11 = v11;
+                if (i + 1 < LK) {
+                    const int4 o = offs[i + 1];
+                    fn = geo[i + 1];
+                    n00 = ValueTraits<VT>::load4(vr, (uint32_t)o.x + vlane);
+                    n01 = ValueTraits<VT>::load4(vr, (uint32_t)o.y + vlane);
+                    n10 = ValueTraits<VT>::load4(vr, (uint32_t)o.z + vlane);
+                    n11 = ValueTraits<VT>::load4(vr, (uint32_t)o.w + vlane);
+                }
                 const float d00 = dot4(G, v00), d01 = dot4(G, v01);
                 const float d10 = dot4(G, v10), d11 = dot4(G, v11);
                 const float fx = f.x, fy = f.y, a = f.z;
@@ -388,7 +404,14 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
                 ga = group_sum<LPH>(ga);
                 gx = group_sum<LPH>(gx);
                 gy = group_sum<LPH>(gy);
-                if (lane % LPH == 0) res[i] = make_float4(ga, a * Wf * gx, a * Hf * gy, FUSED ? a : 0.0f);
+                // every lane of the head holds the sums: all write the same
+                // value (no branch, so the loop stays one basic block)
+                res[i] = make_float4(ga, a * Wf * gx, a * Hf * gy, FUSED ? a : 0.0f);
+                f = fn;
+                v00 = n00;
+                v01 = n01;
+                v10 = n10;
+                v11 = n11;
             }
         }
         wave_lds_sync();
