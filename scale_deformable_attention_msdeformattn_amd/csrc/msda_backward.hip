@@ -900,7 +900,7 @@ dense_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, cons
     float2 u[kPer];
     float a[kPer];
     float4 gst[kGRows];
-    auto fetch = [&](int qa) {
+    auto fetch_samples = [&](int qa) {
         const int ns = min(QS, qa1 - qa) * K;
 #pragma unroll
         for (int t = 0; t < kPer; ++t) {
@@ -910,6 +910,8 @@ dense_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, cons
             u[t] = i < ns ? loc[sidx] : make_float2(-1e30f, -1e30f);
             a[t] = i < ns ? attn[sidx] : 0.0f;
         }
+    };
+    auto fetch_g = [&](int qa) {
         const int nrow = min(QS, qa1 - qa) * LG;  // float4 of G to stage
 #pragma unroll
         for (int t = 0; t < kGRows; ++t) {
@@ -924,12 +926,17 @@ dense_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, cons
 #pragma unroll
     for (int j = 0; j < PPG; ++j) acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
 
-    if (qa0 < qa1) fetch(qa0);
+    if (qa0 < qa1) {
+        fetch_samples(qa0);
+        fetch_g(qa0);
+    }
     for (int qa = qa0; qa < qa1; qa += QS) {
         lds_barrier();  // s_cnt cleared; the previous sub-chunk is done with s_g and s_pair
 #pragma unroll
         for (int t = 0; t < kGRows; ++t)
             if ((kDenseQ * LG) % kDenseThreads == 0 || threadIdx.x + t * kDenseThreads < kDenseQ * LG) s_g[threadIdx.x + t * kDenseThreads] = gst[t];
+        // the next sub-chunk's G rows: in flight through this one's ranking
+        if (qa + QS < qa1) fetch_g(qa + QS);
         // rank this part's pairs within their pixel's count
         int pix[kPer][4];
         uint32_t rank[kPer][4];
@@ -951,7 +958,7 @@ dense_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, cons
                 }
             }
         }
-        if (qa + QS < qa1) fetch(qa + QS);  // in flight until the next sub-chunk is staged
+        if (qa + QS < qa1) fetch_samples(qa + QS);  // in flight until the next sub-chunk is ranked
         lds_barrier();
         // exclusive scan of the (at most kDensePix) pixel counts, one wave
         if (threadIdx.x < kWave) {
