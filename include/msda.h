@@ -24,7 +24,10 @@
  *    level_start_index[l] .. +H_l*W_l, row-major (y, x) inside a level.
  *  - Locations are (x, y): x along the width. spatial_shapes is (H, W).
  *  - The caller (PyTorch) allocates and owns all memory; the library allocates
- *    nothing and keeps no state between calls. All entry points are reentrant.
+ *    no device memory and keeps no data between calls. All entry points are
+ *    reentrant. The one resource it keeps: msda_backward creates, on first
+ *    use per device and host thread, one more HIP stream (default priority)
+ *    and two events, kept for the life of the process; see msda_backward.
  *  - Every call validates its arguments on the host BEFORE any device work, so
  *    an error never leaves partial output. On success the work is enqueued on
  *    `stream` (a hipStream_t; NULL = the default stream) and the call returns
@@ -160,8 +163,15 @@ MSDA_API int msda_backward_workspace_size(const msda_shape *shape, size_t *bytes
  * M*D == 256 and compiled (L, K)) grad_value is gathered per pixel tile; only
  * the tiles of the densest levels, whose sample lists are split over several
  * workgroups, merge their partial sums with float atomics. Other sizes scatter
- * with float atomics. Where float atomics are used the summation order, and so
- * the last bits of grad_value, vary from run to run. */
+ * with float atomics. The fast path also orders each pixel's contributions
+ * by integer LDS atomics racing between waves. So the summation order, and
+ * with it the last bits of grad_value, can vary from run to run;
+ * grad_sampling_locations and grad_attention_weights are reproducible.
+ * On the fast path the dense levels' accumulation runs on the library's own
+ * stream, forked from `stream` by an event and joined back into it by another
+ * before the kernels that need it, so the call stays ordered on `stream`
+ * (later work on `stream` sees all of its results) and can be captured into a
+ * HIP graph from `stream`. */
 MSDA_API int msda_backward(const msda_shape *shape, const void *value, msda_dtype value_dtype,
                   const float *sampling_locations, const float *attention_weights,
                   const float *grad_output, float *grad_value,
@@ -202,7 +212,7 @@ MSDA_API int msda_forward_fused(const msda_shape *shape, const void *value, msda
  *                                    (w, h)  (if not NULL)
  * reference_points and sampling_offsets are read for boxes only (NULL allowed
  * for points). Shapes [B,Nq,M,L,K,2], [B,Nq,M,L*K], [B,Nq,L,reference_dims],
- * fp32, fully overwritten. Workspace, flags and status codes as
+ * fp32, fully overwritten. Workspace, flags, stream use and status codes as
  * msda_backward. */
 MSDA_API int msda_backward_fused(const msda_shape *shape, const void *value, msda_dtype value_dtype,
                                  const float *sampling_locations, const float *attention_weights,

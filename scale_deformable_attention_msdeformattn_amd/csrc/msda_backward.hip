@@ -845,7 +845,7 @@ template <int LG>
 __global__ void __launch_bounds__(kDenseThreads)
 dense_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, const float *__restrict__ attn,
                    const float4 *__restrict__ grad_out, float4 *__restrict__ grad_value,
-                   float4 *__restrict__ partials, int accumulate, uint32_t *__restrict__ totals, int nkeys)
+                   float4 *__restrict__ partials, int accumulate)
 {
     constexpr int NG = kDenseThreads / LG;                  // lane groups
     constexpr int PPG = kDensePix / NG;              // pixel slots per lane group
@@ -857,9 +857,6 @@ dense_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, cons
     __shared__ uint32_t s_cnt[kDensePix];
     __shared__ uint32_t s_start[kDensePix + 1];
 
-    // this kernel runs first in the backward: it also clears the tile
-    // totals that bin_count adds into
-    for (int i = blockIdx.x * kDenseThreads + threadIdx.x; i < nkeys; i += gridDim.x * kDenseThreads) totals[i] = 0;
     const int item = (int)xcd_tile(blockIdx.x, gridDim.x);
     if (item >= g.B * g.M * tp.dipb) return;
     const int bm = item / tp.dipb;
@@ -1181,6 +1178,35 @@ size_t layout(const Geometry &g, const TilePlan &tp, char *base, Workspace *ws)
     return off;
 }
 
+// A second stream per device (and host thread) for the dense levels, which
+// need neither the binning nor the main kernel and so overlap them, with its
+// fork and join events. Created on first use at the default priority and
+// kept for the life of the process; thread-local, so host threads never
+// share the events. Under graph capture the side stream joins the capture
+// through the fork event.
+struct SideStream {
+    hipStream_t s;
+    hipEvent_t fork, join;
+};
+
+hipError_t side_stream(SideStream **out)
+{
+    constexpr int kMaxDevices = 64;
+    thread_local SideStream per_device[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    SideStream &ss = per_device[dev];
+    if (!ss.s) {
+        if ((e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming)) != hipSuccess) return e;
+        if ((e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming)) != hipSuccess) return e;
+        if ((e = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking)) != hipSuccess) return e;
+    }
+    *out = &ss;
+    return hipSuccess;
+}
+
 template <typename VT, int M, int L, int K, bool FUSED>
 hipError_t launch_fast(const Geometry &g, const TilePlan &tp, const void *value, const float *loc,
                        const float *attn, const float *go, float *gv, float *gl, float *ga, const FusedGrads &fg,
@@ -1193,15 +1219,27 @@ hipError_t launch_fast(const Geometry &g, const TilePlan &tp, const void *value,
     const int nkeys = g.B * nkb;
     const size_t hist_bytes = (size_t)nkb * 4;
     constexpr int LG = 256 / M / 4;
-    // dense levels first: they need no binning, and the kernel also clears
-    // the tile totals
+    // the dense levels on the side stream: they read only the inputs and
+    // write their own grad_value rows and workspace section, so they run
+    // beside the binning and the main kernel; tile_accum (which adds their
+    // query splits) waits for them
+    SideStream *side = nullptr;
     if (tp.dipb > 0) {
+        hipError_t e = side_stream(&side);
+        if (e == hipSuccess) e = hipEventRecord(side->fork, st);
+        if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
+        if (e != hipSuccess) return e;
         const uint32_t ditems = (uint32_t)(g.B * g.M * tp.dipb);
-        KernelScope ks_("dense_accum_kernel", st);
-        hipLaunchKernelGGL((dense_accum_kernel<LG>), dim3(round_up8(ditems)), dim3(kDenseThreads), 0, st, g, tp,
-                           reinterpret_cast<const float2 *>(loc), attn, reinterpret_cast<const float4 *>(go),
-                           reinterpret_cast<float4 *>(gv), ws.partials, accumulate ? 1 : 0, ws.totals, nkeys);
-    } else if (nkeys > 0) {
+        {
+            KernelScope ks_("dense_accum_kernel", side->s);
+            hipLaunchKernelGGL((dense_accum_kernel<LG>), dim3(round_up8(ditems)), dim3(kDenseThreads), 0, side->s, g,
+                               tp, reinterpret_cast<const float2 *>(loc), attn, reinterpret_cast<const float4 *>(go),
+                               reinterpret_cast<float4 *>(gv), ws.partials, accumulate ? 1 : 0);
+        }
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = hipEventRecord(side->join, side->s)) != hipSuccess) return e;
+    }
+    if (nkeys > 0) {
         KernelScope ks_("clear_totals_kernel", st);
         hipLaunchKernelGGL(clear_totals_kernel, dim3((nkeys + kBlock - 1) / kBlock), dim3(kBlock), 0, st, nkeys,
                            ws.totals);
@@ -1229,6 +1267,10 @@ hipError_t launch_fast(const Geometry &g, const TilePlan &tp, const void *value,
             hipLaunchKernelGGL(zero_split_levels_kernel, dim3((unsigned)((n + kBlock - 1) / kBlock)), dim3(kBlock), 0,
                                st, g, tp, reinterpret_cast<float4 *>(gv));
         }
+    }
+    if (side) {
+        const hipError_t e = hipStreamWaitEvent(st, side->join, 0);
+        if (e != hipSuccess) return e;
     }
     // the sparse tiles, then (as extra items of the same launch) the sums of
     // the dense levels' query splits
