@@ -8,7 +8,9 @@ the eager result each time, not only the first).
 grad_loc and grad_attn are summed in a fixed order and must be equal bit for
 bit. grad_value sums each pixel's contributions in an order set by LDS atomics
 racing between waves, so its last bits may differ from run to run: it is
-compared to a bound on fp32 reordering, far below the parity tolerance."""
+compared within 1e-5 * (1 + |x|), a tenth of the parity tolerance. (On the
+coarsest level a pixel sums about 1600 terms; reordering them moves the
+result by up to about 2e-6 here.)"""
 import pytest
 import torch
 
@@ -54,7 +56,7 @@ def test_backward_graph_replays_equal_eager(gpu_lib):
         torch.cuda.synchronize()
         for name, a, b in zip(("grad_value", "grad_loc", "grad_attn"), out, eager):
             if name == "grad_value":
-                assert torch.allclose(a, b, rtol=1e-5, atol=1e-6), (i, name)
+                assert torch.allclose(a, b, rtol=1e-5, atol=1e-5), (i, name)
             else:
                 assert torch.equal(a, b), (i, name)
         # eager work between the replays, on the same stream
@@ -75,7 +77,7 @@ def test_fused_backward_graph_replays_equal_eager(gpu_lib):
         torch.cuda.synchronize()
         for k, (a, b) in enumerate(zip(out, eager)):
             if k == 0:  # grad_value
-                assert torch.allclose(a, b, rtol=1e-5, atol=1e-6), (i, k)
+                assert torch.allclose(a, b, rtol=1e-5, atol=1e-5), (i, k)
             else:
                 assert torch.equal(a, b), (i, k)
         msda.msda_backward(value, shapes, lsi, loc, A, G)
@@ -99,6 +101,6 @@ def test_backward_on_two_streams_in_turn(gpu_lib):
     with torch.cuda.stream(s2):
         r2 = msda.msda_backward(value, shapes, lsi, loc, A, G2)[0]
     s1.synchronize()
-    assert torch.allclose(r1, want, rtol=1e-5, atol=1e-6)
+    assert torch.allclose(r1, want, rtol=1e-5, atol=1e-5)
     s2.synchronize()
-    assert torch.allclose(r2, want2, rtol=1e-5, atol=1e-6)
+    assert torch.allclose(r2, want2, rtol=1e-5, atol=1e-5)
