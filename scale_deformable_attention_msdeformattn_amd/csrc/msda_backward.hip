@@ -54,6 +54,7 @@ constexpr int kWaves = 4;
 constexpr int kBlock = kWaves * kWave;
 constexpr int kQueriesPerGroup = 32;     // queries per workgroup of bin_count and main
 constexpr int kChunk = 1024;             // records per LDS chunk in tile_accum
+constexpr int kTileTarget = 768;         // expected records per tile the planner aims at
 constexpr int kTilePix = 32;             // pixels per tile
 constexpr int kTileCells = 2 * kWave;    // cells per tile (the tile plus one row and column of halo)
 constexpr int kTaskSlots = 2;            // (cell, split) tasks per lane group in tile_accum
@@ -1421,7 +1422,7 @@ hipError_t launch_typed(const Geometry &g, const TilePlan *tpp, const void *valu
 bool make_tile_plan(const Geometry &g, TilePlan &tp)
 {
     if (fast_kind(g) == Fast::None) return false;
-    const double target = 0.75 * kChunk;
+    const double target = kTileTarget;
     // every (cell, split) task needs a slot: cells <= kTaskSlots * lane groups
     const int max_cells = std::min(kTileCells, kTaskSlots * (kBlock / (g.D / 4)));
     int base = 0, ibase = 0, dibase = 0;
