@@ -53,6 +53,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kBlock = kWaves * kWave;
 constexpr int kQueriesPerGroup = 32;     // queries per workgroup of bin_count and main
+constexpr int kMainAhead = 1;            // samples whose gathers run ahead in the main kernel
 constexpr int kChunk = 1024;             // records per LDS chunk in tile_accum
 constexpr int kTileTarget = 768;         // expected records per tile the planner aims at
 constexpr int kTilePix = 32;             // pixels per tile
@@ -367,34 +368,34 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
         const int4 *offs = &s_off[wave][m * PAD];
         const float4 *geo = &s_geo[wave][m * PAD];
         float4 *res = &s_geo[wave][m * PAD];
-        // software-pipelined over the L*K samples: the next sample's four
-        // gathers are issued before this one's arithmetic, so that eight are
-        // in flight (the in-place result writes below would otherwise keep
-        // the compiler from hoisting them)
-        float4 f = geo[0];
-        float4 v00, v01, v10, v11;
-        {
-            const int4 o = offs[0];
-            v00 = ValueTraits<VT>::load4(vr, (uint32_t)o.x + vlane);
-            v01 = ValueTraits<VT>::load4(vr, (uint32_t)o.y + vlane);
-            v10 = ValueTraits<VT>::load4(vr, (uint32_t)o.z + vlane);
-            v11 = ValueTraits<VT>::load4(vr, (uint32_t)o.w + vlane);
-        }
+        // software-pipelined over the L*K samples: the gathers of the next
+        // kMainAhead samples are in flight during each one's arithmetic (the
+        // in-place result writes below would otherwise keep the compiler from
+        // hoisting them); kMainAhead + 1 register slots, indexed at compile
+        // time (the loops are unrolled)
+        constexpr int NSLOT = kMainAhead + 1;
+        float4 fb[NSLOT], vb[NSLOT][4];
+        auto gather = [&](int i, int slot) {
+            const int4 o = offs[i];
+            fb[slot] = geo[i];
+            vb[slot][0] = ValueTraits<VT>::load4(vr, (uint32_t)o.x + vlane);
+            vb[slot][1] = ValueTraits<VT>::load4(vr, (uint32_t)o.y + vlane);
+            vb[slot][2] = ValueTraits<VT>::load4(vr, (uint32_t)o.z + vlane);
+            vb[slot][3] = ValueTraits<VT>::load4(vr, (uint32_t)o.w + vlane);
+        };
+#pragma unroll
+        for (int i = 0; i < kMainAhead; ++i)
+            if (i < LK) gather(i, i);
 #pragma unroll
         for (int l = 0; l < L; ++l) {
             const float Wf = (float)g.lv.W[l], Hf = (float)g.lv.H[l];
 #pragma unroll
             for (int k = 0; k < K; ++k) {
                 const int i = l * K + k;
-                float4 fn = f, n00 = v00, n01 = v01, n10 = v10, n11 = v11;
-                if (i + 1 < LK) {
-                    const int4 o = offs[i + 1];
-                    fn = geo[i + 1];
-                    n00 = ValueTraits<VT>::load4(vr, (uint32_t)o.x + vlane);
-                    n01 = ValueTraits<VT>::load4(vr, (uint32_t)o.y + vlane);
-                    n10 = ValueTraits<VT>::load4(vr, (uint32_t)o.z + vlane);
-                    n11 = ValueTraits<VT>::load4(vr, (uint32_t)o.w + vlane);
-                }
+                if (i + kMainAhead < LK) gather(i + kMainAhead, (i + kMainAhead) % NSLOT);
+                const int slot = i % NSLOT;
+                const float4 f = fb[slot];
+                const float4 v00 = vb[slot][0], v01 = vb[slot][1], v10 = vb[slot][2], v11 = vb[slot][3];
                 const float d00 = dot4(G, v00), d01 = dot4(G, v01);
                 const float d10 = dot4(G, v10), d11 = dot4(G, v11);
                 const float fx = f.x, fy = f.y, a = f.z;
@@ -408,11 +409,6 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
                 // every lane of the head holds the sums: all write the same
                 // value (no branch, so the loop stays one basic block)
                 res[i] = make_float4(ga, a * Wf * gx, a * Hf * gy, FUSED ? a : 0.0f);
-                f = fn;
-                v00 = n00;
-                v01 = n01;
-                v10 = n10;
-                v11 = n11;
             }
         }
         wave_lds_sync();
