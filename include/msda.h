@@ -57,7 +57,7 @@ extern "C" {
 #define MSDA_API
 #endif
 
-#define MSDA_ABI_VERSION 5
+#define MSDA_ABI_VERSION 6
 #define MSDA_MAX_LEVELS 16
 
 typedef enum {
@@ -143,6 +143,18 @@ MSDA_API int msda_forward(const msda_shape *shape, const void *value, msda_dtype
 /* Bytes of device workspace msda_backward needs for these sizes (0 when the
  * sizes have no tiled fast path; the call then needs none). Host only. */
 MSDA_API int msda_backward_workspace_size(const msda_shape *shape, size_t *bytes);
+
+/* How msda_backward's tiled fast path would treat each level of these sizes
+ * (host only; for diagnostics and tests). Bit l of *dense_levels: level l is
+ * summed from its samples directly (at least 24 samples per pixel, per batch
+ * and head, and at most 2048 pixels). Bit l of *direct_levels: its tiles are
+ * so small (at most 4 pixels) that they skip the per-cell sort. Bit l of
+ * *split_levels: those small tiles share their records among several
+ * workgroups, whose partial sums meet in float atomics. All three are 0 when
+ * the sizes take the generic path (msda_backward_workspace_size reports 0).
+ * Any output pointer may be NULL. */
+MSDA_API int msda_backward_plan(const msda_shape *shape, uint32_t *dense_levels, uint32_t *direct_levels,
+                                uint32_t *split_levels);
 
 /* Backward of the core: the exact derivative of msda_forward given
  * grad_output [B,Nq,M*D] fp32 (the op is trained end to end through autograd:

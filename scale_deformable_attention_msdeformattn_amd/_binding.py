@@ -93,6 +93,8 @@ def load():
     lib.msda_forward.argtypes = [_shp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp]
     lib.msda_backward_workspace_size.restype = ctypes.c_int
     lib.msda_backward_workspace_size.argtypes = [_shp, ctypes.POINTER(ctypes.c_size_t)]
+    lib.msda_backward_plan.restype = ctypes.c_int
+    lib.msda_backward_plan.argtypes = [_shp] + [ctypes.POINTER(ctypes.c_uint32)] * 3
     lib.msda_backward.restype = ctypes.c_int
     lib.msda_backward.argtypes = [_shp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                                   ctypes.c_uint, _vp]
@@ -392,6 +394,17 @@ def msda_backward_workspace_size(shape: "Shape") -> int:
     n = ctypes.c_size_t()
     _check(load().msda_backward_workspace_size(shape.ptr, ctypes.byref(n)), "msda_backward_workspace_size")
     return int(n.value)
+
+
+def msda_backward_plan(shape: "Shape") -> dict:
+    """Which levels the backward's tiled fast path would sum from their samples
+    ('dense'), give tiles too small to sort ('direct'), and split over several
+    workgroups with float atomics ('split'); lists of level indices."""
+    masks = [ctypes.c_uint32() for _ in range(3)]
+    _check(load().msda_backward_plan(shape.ptr, *[ctypes.byref(m) for m in masks]), "msda_backward_plan")
+    levels = shape.levels
+    return {key: [l for l in range(levels) if (m.value >> l) & 1]
+            for key, m in zip(("dense", "direct", "split"), masks)}
 
 
 def raw_call(name: str, *args):

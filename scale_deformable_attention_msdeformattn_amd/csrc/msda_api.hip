@@ -208,6 +208,19 @@ int msda_backward_workspace_size(const msda_shape *shape, size_t *bytes)
     return ok();
 }
 
+int msda_backward_plan(const msda_shape *shape, uint32_t *dense_levels, uint32_t *direct_levels,
+                       uint32_t *split_levels)
+{
+    msda::Geometry g;
+    if (int st = make_geometry(shape, g)) return st;
+    uint32_t d = 0, r = 0, sp = 0;
+    if (g.B > 0 && g.Nq > 0) msda::backward_plan_masks(g, d, r, sp);
+    if (dense_levels) *dense_levels = d;
+    if (direct_levels) *direct_levels = r;
+    if (split_levels) *split_levels = sp;
+    return ok();
+}
+
 int msda_backward(const msda_shape *shape, const void *value, msda_dtype value_dtype,
                   const float *sampling_locations, const float *attention_weights, const float *grad_output,
                   float *grad_value, float *grad_sampling_locations, float *grad_attention_weights,

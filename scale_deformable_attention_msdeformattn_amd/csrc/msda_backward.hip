@@ -1506,6 +1506,20 @@ size_t backward_workspace_bytes(const Geometry &g)
     return layout(g, tp, nullptr, nullptr);
 }
 
+bool backward_plan_masks(const Geometry &g, uint32_t &dense, uint32_t &direct, uint32_t &split)
+{
+    dense = direct = split = 0;
+    TilePlan tp;
+    if (!make_tile_plan(g, tp)) return false;
+    dense = (uint32_t)tp.dense_mask;
+    for (int l = 0; l < g.L; ++l) {
+        if ((dense >> l) & 1) continue;
+        if (tp.th[l] * tp.tw[l] <= kDirectPix) direct |= 1u << l;
+        if (level_uses_atomics(tp, l)) split |= 1u << l;
+    }
+    return true;
+}
+
 bool backward_uses_workspace(const Geometry &g, const void *value, msda_dtype vt, const float *go,
                              const float *gv)
 {

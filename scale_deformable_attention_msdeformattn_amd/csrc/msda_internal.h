@@ -73,6 +73,8 @@ bool make_tile_plan(const Geometry &g, TilePlan &tp);
 bool backward_uses_workspace(const Geometry &g, const void *value, msda_dtype vt, const float *go,
                              const float *gv);
 size_t backward_workspace_bytes(const Geometry &g);
+// The per-level path masks of the tiled fast path (false: generic path).
+bool backward_plan_masks(const Geometry &g, uint32_t &dense, uint32_t &direct, uint32_t &split);
 
 // Brackets the launches made during its lifetime with a timing event pair on
 // `st` while msda_timing_enable is on (and `st` is not being captured).

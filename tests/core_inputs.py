@@ -27,8 +27,14 @@ class CoreInputs:
     grad_output: Optional[torch.Tensor]
 
 
-def build(wl, seed: int = 0, valid_ratios: Optional[torch.Tensor] = None) -> CoreInputs:
+def build(wl, seed: int = 0, valid_ratios: Optional[torch.Tensor] = None,
+          query_ref: Optional[torch.Tensor] = None) -> CoreInputs:
+    """query_ref (decoder workloads only) replaces the drawn [B,Nq,2] inputs u,
+    to place the queries where a test needs them."""
     d = workloads.draw(wl, seed)
+    if query_ref is not None:
+        assert d.query_ref is not None and query_ref.shape == d.query_ref.shape
+        d.query_ref = query_ref
     w = d.workload
     shapes = d.spatial_shapes.numpy()
     lsi, S = oracle.level_start_index(shapes)

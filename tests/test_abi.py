@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.msda_abi_version() == 5
+    assert lib.msda_abi_version() == 6
     assert lib.msda_status_string(0) == b"ok"
     for code in range(-8, 0):
         assert lib.msda_status_string(code) not in (b"", b"unknown status")
@@ -230,3 +230,23 @@ def test_timing_entry_points_without_launches(lib):
     assert n.value == 0
     assert lib.msda_timing_read(0, ctypes.byref(n), None, None, None) == -2  # MSDA_E_DIM
     assert B.msda_timing_read() == {}
+
+
+@cpu_only
+def test_backward_plan_per_level(lib):
+    """The planner's choice of path per level, from the sizes alone (host
+    only). The GPU tests of each path rely on these shapes taking it."""
+    # the encoder pyramid: the two coarse levels are dense, the fine ones sorted tiles
+    assert B.msda_backward_plan(_shape()) == {"dense": [2, 3], "direct": [], "split": []}
+    # one 46x46 level (over 2048 pixels, so never dense) at about 94 samples per
+    # pixel: 2x2 tiles without the sort, their ~850 records split over two workgroups
+    assert B.msda_backward_plan(_shape(B_=1, shapes=((46, 46),), Nq=50000)) == \
+        {"dense": [], "direct": [0], "split": [0]}
+    # ... at about 80 samples per pixel: 2x2 tiles, one workgroup each
+    assert B.msda_backward_plan(_shape(B_=1, shapes=((46, 46),), Nq=42320)) == \
+        {"dense": [], "direct": [0], "split": []}
+    # sizes off the fast path (M*D != 256): no plan
+    assert B.msda_backward_plan(_shape(M=3, D=5)) == {"dense": [], "direct": [], "split": []}
+    # empty calls have no plan either, and NULL outputs are allowed
+    assert B.msda_backward_plan(_shape(B_=0)) == {"dense": [], "direct": [], "split": []}
+    assert lib.msda_backward_plan(_shape().ptr, None, None, None) == B.MSDA_OK
