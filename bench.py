@@ -61,13 +61,15 @@ def parse():
 
 
 def unique_value_bytes(loc, shapes, B, M, row_bytes):
-    """Bytes of the distinct value rows (b, s, m) -- D channels each -- that
+    """(Bytes of the distinct value rows (b, s, m) -- D channels each -- that
     at least one in-map corner touches: what an ideal kernel must read of
-    value."""
+    value; and the number of in-map corner reads, each one such row, that the
+    forward's gathers serve from the caches.)"""
     import torch
     touched = torch.zeros(B, int((shapes[:, 0] * shapes[:, 1]).sum()), M, dtype=torch.bool, device=loc.device)
     _, Nq, _, L, K, _ = loc.shape
     start = 0
+    corners = 0
     for l in range(L):
         H, W = int(shapes[l, 0]), int(shapes[l, 1])
         x = loc[:, :, :, l, :, 0].double() * W - 0.5
@@ -79,12 +81,13 @@ def unique_value_bytes(loc, shapes, B, M, row_bytes):
                 xi = x0 + dx
                 yi = y0 + dy
                 ok = (xi >= 0) & (xi < W) & (yi >= 0) & (yi < H)
+                corners += int(ok.sum().item())
                 row = (start + yi.clamp(0, H - 1) * W + xi.clamp(0, W - 1)).long()
                 bidx = torch.arange(B, device=loc.device).view(B, 1, 1, 1).expand_as(row)
                 midx = torch.arange(M, device=loc.device).view(1, 1, M, 1).expand_as(row)
                 touched[bidx[ok], row[ok], midx[ok]] = True
         start += H * W
-    return int(touched.sum().item()) * row_bytes
+    return int(touched.sum().item()) * row_bytes, corners
 
 
 def dense_levels(shapes, Nq, K):
@@ -397,7 +400,7 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    vbytes = unique_value_bytes(state["loc"], shapes.to(dev), B, M, D * elem)
+    vbytes, corner_reads = unique_value_bytes(state["loc"], shapes.to(dev), B, M, D * elem)
     alg = algorithmic_bytes(B, M, D, Nq, [tuple(int(v) for v in hw) for hw in shapes.tolist()], K, vbytes)
 
     # ---- timed region 1: whole steps (graph replay unless --eager) ----
@@ -547,7 +550,13 @@ def main():
         "eager_ms_per_step": eager_step_ms,
         "forward": {"queries_per_s": queries / (fwd["avg_us"] * 1e-6) if fwd else None,
                     "effective_gbps": fwd.get("gbps"), "frac_of_hbm_peak": fwd.get("frac_of_hbm_peak"),
-                    "traffic": measured_traffic("forward_c256_kernel")},
+                    "traffic": measured_traffic("forward_c256_kernel"),
+                    "gather": None if not fwd else {
+                        "corner_reads": corner_reads, "bytes": corner_reads * D * elem,
+                        "tbps": round(corner_reads * D * elem / (fwd["avg_us"] * 1e-6) / 1e12, 2),
+                        "note": "in-map corner reads of one head's value row each, served by L1/L2: the rate "
+                                "that bounds the forward (we measured 50-58 B/clk/CU for 16-byte lane gathers on "
+                                "this path, 31-36 TB/s on 256 CUs at 2.4 GHz)"}},
         "backward": {"queries_per_s": queries / (per_call["msda_backward"] * 1e-6),
                      "note": "the whole msda_backward call, all its kernels"},
         "fused_step": None if fused_ms is None else {
