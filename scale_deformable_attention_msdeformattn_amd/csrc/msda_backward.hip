@@ -17,7 +17,7 @@
 //  0. dense_accum : the dense levels (few pixels, many samples each) skip the
 //                   records: workgroups read the samples of a query range
 //                   directly and sort their (sample, corner) pairs by pixel in
-//                   LDS. It runs first and also clears the tile totals.
+//                   LDS. It runs on a second stream, beside steps 1 and 2.
 //  1. bin_count   : each workgroup takes a fixed range of queries and counts,
 //                   in an LDS histogram (integer LDS atomics), how many of its
 //                   samples touch each pixel tile of each (head, sparse level);
