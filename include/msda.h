@@ -57,7 +57,7 @@ extern "C" {
 #define MSDA_API
 #endif
 
-#define MSDA_ABI_VERSION 6
+#define MSDA_ABI_VERSION 7
 #define MSDA_MAX_LEVELS 16
 
 typedef enum {
@@ -93,6 +93,9 @@ typedef struct {
 
 /* Flag for msda_backward: add into grad_value instead of overwriting it. */
 #define MSDA_BWD_ACCUMULATE 1u
+/* Flag for msda_backward: the workspace already holds the binning of these
+ * sampling_locations, made by msda_backward_prepare (see there). */
+#define MSDA_BWD_PREPARED 2u
 
 /* Host helper: level_start_index as the exclusive prefix sum of H_l*W_l
  * (walkthrough page, "transformer" section: the start of each level in the
@@ -143,6 +146,25 @@ MSDA_API int msda_forward(const msda_shape *shape, const void *value, msda_dtype
 /* Bytes of device workspace msda_backward needs for these sizes (0 when the
  * sizes have no tiled fast path; the call then needs none). Host only. */
 MSDA_API int msda_backward_workspace_size(const msda_shape *shape, size_t *bytes);
+
+/* The part of the backward that depends on the sampling locations alone:
+ * on the tiled fast path, the binning of the sparse levels' samples into
+ * their pixel tiles (counts per tile and per range of queries), written into
+ * `workspace` on `stream`. It needs no grad_output, so a caller can run it
+ * as soon as the locations exist, for instance on a second stream beside the
+ * forward, and pass MSDA_BWD_PREPARED to the msda_backward or
+ * msda_backward_fused call that uses the same sizes, the same
+ * sampling_locations (unchanged in between) and the same workspace; that call
+ * then skips the binning. Ordering the two calls (one stream, or an event) is
+ * the caller's part, as for any input. A backward told PREPARED over a
+ * workspace that was not prepared for its locations returns wrong gradients
+ * (its record writes and reads stay inside the workspace). Nothing to do, and
+ * MSDA_OK, when the sizes have no fast path (msda_backward_workspace_size is
+ * 0) or are empty. Errors: MSDA_E_NULL (locations or workspace),
+ * MSDA_E_WORKSPACE (too small), MSDA_E_ALIGN (locations 8 bytes, workspace
+ * 256 bytes). */
+MSDA_API int msda_backward_prepare(const msda_shape *shape, const float *sampling_locations, void *workspace,
+                                   size_t workspace_bytes, void *stream);
 
 /* How msda_backward's tiled fast path would treat each level of these sizes
  * (host only; for diagnostics and tests). Bit l of *dense_levels: level l is

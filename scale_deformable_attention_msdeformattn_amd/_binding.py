@@ -29,6 +29,7 @@ MSDA_E_WORKSPACE = -8
 MSDA_F32 = 0
 MSDA_BF16 = 1
 MSDA_BWD_ACCUMULATE = 1
+MSDA_BWD_PREPARED = 2
 MSDA_MAX_LEVELS = 16
 
 
@@ -93,6 +94,8 @@ def load():
     lib.msda_forward.argtypes = [_shp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp]
     lib.msda_backward_workspace_size.restype = ctypes.c_int
     lib.msda_backward_workspace_size.argtypes = [_shp, ctypes.POINTER(ctypes.c_size_t)]
+    lib.msda_backward_prepare.restype = ctypes.c_int
+    lib.msda_backward_prepare.argtypes = [_shp, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.msda_backward_plan.restype = ctypes.c_int
     lib.msda_backward_plan.argtypes = [_shp] + [ctypes.POINTER(ctypes.c_uint32)] * 3
     lib.msda_backward.restype = ctypes.c_int
@@ -281,11 +284,48 @@ def msda_forward(value: torch.Tensor, spatial_shapes, level_start_index, samplin
     return out
 
 
+def _workspace(sh, device, prepared):
+    """(workspace tensor, bytes, extra flags): a fresh one, or the prepared
+    one from msda_backward_prepare for the same sizes."""
+    nbytes = msda_backward_workspace_size(sh)
+    if prepared is None:
+        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device), nbytes, 0
+    if prepared.dtype != torch.uint8 or prepared.device != device or prepared.numel() < max(nbytes, 1):
+        raise ValueError("prepared workspace is not one from msda_backward_prepare for these sizes")
+    return prepared, nbytes, MSDA_BWD_PREPARED
+
+
+def msda_backward_prepare(value: torch.Tensor, spatial_shapes, level_start_index,
+                          sampling_locations: torch.Tensor) -> torch.Tensor:
+    """The backward's binning of these locations (it needs no grad_output),
+    enqueued on the current stream into a new workspace, which is returned.
+    Pass it as `prepared=` to msda_backward or msda_backward_fused with the
+    same sizes and unchanged sampling_locations, ordered after this call on
+    the device (same stream, or a wait), to skip that part of the backward.
+    value only gives the sizes and dtype."""
+    value = _dev(value, "value", None)
+    loc = _dev(sampling_locations, "sampling_locations")
+    if value.dim() != 4 or loc.dim() != 6 or loc.shape[0] != value.shape[0] or loc.shape[2] != value.shape[2]:
+        raise ValueError("value must be [B,S,M,D] and sampling_locations [B,Nq,M,L,K,2]")
+    B, S, M, D = value.shape
+    _, Nq, _, L, K, _ = loc.shape
+    sh = Shape(spatial_shapes, B, M, D, K, Nq, level_start_index)
+    if sh.levels != L:
+        raise ValueError("spatial_shapes and sampling_locations disagree on the level count")
+    sh.c.num_value = S
+    nbytes = msda_backward_workspace_size(sh)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=value.device)
+    _check(load().msda_backward_prepare(sh.ptr, _p(loc), _p(ws), nbytes, _stream(loc)), "msda_backward_prepare")
+    return ws
+
+
 def msda_backward(value: torch.Tensor, spatial_shapes, level_start_index, sampling_locations: torch.Tensor,
                   attention_weights: torch.Tensor, grad_output: torch.Tensor,
-                  grad_value: Optional[torch.Tensor] = None):
+                  grad_value: Optional[torch.Tensor] = None, prepared: Optional[torch.Tensor] = None):
     """Core backward -> (grad_value [B,S,M,D] fp32, grad_sampling_locations, grad_attention_weights).
-    If grad_value is given it is accumulated into (MSDA_BWD_ACCUMULATE)."""
+    If grad_value is given it is accumulated into (MSDA_BWD_ACCUMULATE).
+    prepared: the workspace msda_backward_prepare returned for these
+    sampling_locations (MSDA_BWD_PREPARED)."""
     value, loc, attn, sh, vt = _core_shape(value, spatial_shapes, level_start_index, sampling_locations,
                                            attention_weights)
     B, S, M, D = value.shape
@@ -302,8 +342,8 @@ def msda_backward(value: torch.Tensor, spatial_shapes, level_start_index, sampli
         flags = MSDA_BWD_ACCUMULATE
     gl = torch.empty_like(loc)
     ga = torch.empty_like(attn)
-    nbytes = msda_backward_workspace_size(sh)
-    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=value.device)
+    ws, nbytes, extra = _workspace(sh, value.device, prepared)
+    flags |= extra
     _check(load().msda_backward(sh.ptr, _p(value), vt, _p(loc), _p(attn), _p(go), _p(grad_value), _p(gl),
                                 _p(ga), _p(ws), nbytes, flags, _stream(go)), "msda_backward")
     return grad_value, gl, ga
@@ -349,12 +389,13 @@ def msda_backward_fused(value: torch.Tensor, spatial_shapes, level_start_index, 
                         attention_weights: torch.Tensor, grad_output: torch.Tensor,
                         grad_value: Optional[torch.Tensor] = None, reference_grad: bool = True,
                         box_references: Optional[torch.Tensor] = None,
-                        sampling_offsets: Optional[torch.Tensor] = None):
+                        sampling_offsets: Optional[torch.Tensor] = None, prepared: Optional[torch.Tensor] = None):
     """Backward of msda_forward_fused, from the locations and weights it
     returned -> (grad_value [B,S,M,D], grad_sampling_offsets [B,Nq,M,L,K,2],
     grad_attention_logits [B,Nq,M,L*K], grad_reference_points [B,Nq,L,2|4]
     or None). For 4-d box references pass the boxes and the offsets of the
-    forward. If grad_value is given it is accumulated into."""
+    forward. If grad_value is given it is accumulated into. prepared: as for
+    msda_backward."""
     value, loc, attn, sh, vt = _core_shape(value, spatial_shapes, level_start_index, sampling_locations,
                                            attention_weights)
     B, S, M, D = value.shape
@@ -381,8 +422,8 @@ def msda_backward_fused(value: torch.Tensor, spatial_shapes, level_start_index, 
     goff = torch.empty_like(loc)
     glog = torch.empty(B, Nq, M, L * K, dtype=torch.float32, device=value.device)
     gref = torch.empty(B, Nq, L, dims, dtype=torch.float32, device=value.device) if reference_grad else None
-    nbytes = msda_backward_workspace_size(sh)
-    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=value.device)
+    ws, nbytes, extra = _workspace(sh, value.device, prepared)
+    flags |= extra
     _check(load().msda_backward_fused(sh.ptr, _p(value), vt, _p(loc), _p(attn), _p(box), _p(off), dims, _p(go),
                                       _p(grad_value), _p(goff), _p(glog), _p(gref), _p(ws), nbytes, flags,
                                       _stream(go)), "msda_backward_fused")

@@ -274,6 +274,7 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
     const int q0 = wg_active ? (int)(w - b * tp.wpb) * tp.qpw : 0;
     const int q1 = wg_active ? min(q0 + tp.qpw, g.Nq) : 0;
     const int nkeys = M * tp.tpb;
+    const uint32_t rcap = (uint32_t)g.B * 4u * (uint32_t)(g.Nq * NS);  // record slots
     if (threadIdx.x < L) {
         const int l = threadIdx.x;
         s_lv[l] = LevelRec{(float)g.lv.W[l], (float)g.lv.H[l], g.lv.W[l], g.lv.start[l]};
@@ -358,7 +359,13 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
                     const uint32_t sidx = (uint32_t)(gq * NS + s);
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
-                        if (st.t[j] >= 0) records[atomicAdd(&s_cursor[sm * tp.tpb + st.t[j]], 1u)] = sidx;
+                        if (st.t[j] >= 0) {
+                            // the bound only matters for a workspace that was
+                            // not binned for these locations (a misused
+                            // prepared flag): wrong sums then, never a stray write
+                            const uint32_t pos = atomicAdd(&s_cursor[sm * tp.tpb + st.t[j]], 1u);
+                            if (pos < rcap) records[pos] = sidx;
+                        }
                 }
             }
         }
@@ -572,6 +579,11 @@ tile_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, const
     const uint32_t gbase = ((uint32_t)m * LG + lig) * 16;
     uint32_t rbeg = bases[key];
     uint32_t rtot = totals[key];
+    {
+        // keep the range inside the record array whatever the workspace holds
+        const uint32_t rcap = (uint32_t)(4 * g.samples());
+        rtot = rbeg < rcap ? min(rtot, rcap - rbeg) : 0u;
+    }
 
     if (npix <= kDirectPix) {
         if (nch > 1) {  // this workgroup's share of the tile's records
@@ -1204,10 +1216,33 @@ hipError_t side_stream(SideStream **out)
     return hipSuccess;
 }
 
+// The binning of the sparse levels' samples into their tiles' record lists:
+// it depends on the locations only, so a caller may run it ahead
+// (msda_backward_prepare) and let the backward skip it.
+template <int M, int L, int K>
+hipError_t launch_binning(const Geometry &g, const TilePlan &tp, const float *loc, const Workspace &ws,
+                          hipStream_t st)
+{
+    const int nkb = M * tp.tpb;
+    const int nkeys = g.B * nkb;
+    if (nkeys == 0) return hipSuccess;
+    {
+        KernelScope ks_("clear_totals_kernel", st);
+        hipLaunchKernelGGL(clear_totals_kernel, dim3((nkeys + kBlock - 1) / kBlock), dim3(kBlock), 0, st, nkeys,
+                           ws.totals);
+    }
+    {
+        KernelScope ks_("bin_count_kernel", st);
+        hipLaunchKernelGGL((bin_count_kernel<M, L, K>), dim3(g.B * tp.wpb), dim3(kBinThreads), (size_t)nkb * 4, st,
+                           g, tp, reinterpret_cast<const float2 *>(loc), ws.counts, ws.totals);
+    }
+    return hipGetLastError();
+}
+
 template <typename VT, int M, int L, int K, bool FUSED>
 hipError_t launch_fast(const Geometry &g, const TilePlan &tp, const void *value, const float *loc,
                        const float *attn, const float *go, float *gv, float *gl, float *ga, const FusedGrads &fg,
-                       void *wsp, bool accumulate, hipStream_t st)
+                       void *wsp, bool accumulate, bool prepared, hipStream_t st)
 {
     Workspace ws;
     layout(g, tp, static_cast<char *>(wsp), &ws);
@@ -1236,15 +1271,9 @@ hipError_t launch_fast(const Geometry &g, const TilePlan &tp, const void *value,
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if ((e = hipEventRecord(side->join, side->s)) != hipSuccess) return e;
     }
-    if (nkeys > 0) {
-        KernelScope ks_("clear_totals_kernel", st);
-        hipLaunchKernelGGL(clear_totals_kernel, dim3((nkeys + kBlock - 1) / kBlock), dim3(kBlock), 0, st, nkeys,
-                           ws.totals);
-    }
-    if (nkeys > 0) {
-        KernelScope ks_("bin_count_kernel", st);
-        hipLaunchKernelGGL((bin_count_kernel<M, L, K>), dim3(nwg), dim3(kBinThreads), hist_bytes, st, g, tp,
-                           reinterpret_cast<const float2 *>(loc), ws.counts, ws.totals);
+    if (!prepared) {
+        const hipError_t e = launch_binning<M, L, K>(g, tp, loc, ws, st);
+        if (e != hipSuccess) return e;
     }
     const uint32_t grid = round_up8((uint32_t)nwg);
     {
@@ -1361,7 +1390,7 @@ fused_grads_kernel(Geometry g, const float *__restrict__ attn, float *__restrict
 template <typename VT>
 hipError_t launch_typed(const Geometry &g, const TilePlan *tpp, const void *value, const float *loc,
                         const float *attn, const float *go, float *gv, float *gl, float *ga, const FusedGrads *fg,
-                        void *ws, bool accumulate, hipStream_t st)
+                        void *ws, bool accumulate, bool prepared, hipStream_t st)
 {
     // fused gradients inside the main kernel where the L*K softmax fits the
     // wave's lanes; otherwise the plain gradients, converted afterwards
@@ -1371,9 +1400,9 @@ hipError_t launch_typed(const Geometry &g, const TilePlan *tpp, const void *valu
     bool done = false;
 #define MSDA_FAST(M_, L_, K_)                                                                                    \
     e = in_kernel ? launch_fast<VT, M_, L_, K_, true>(g, *tpp, value, loc, attn, go, gv, gl, ga, *fg, ws,        \
-                                                      accumulate, st)                                            \
+                                                      accumulate, prepared, st)                                  \
                   : launch_fast<VT, M_, L_, K_, false>(g, *tpp, value, loc, attn, go, gv, gl, ga, FusedGrads{},  \
-                                                       ws, accumulate, st);                                      \
+                                                       ws, accumulate, prepared, st);                            \
     done = true;
     switch (tpp ? fast_kind(g) : Fast::None) {
     case Fast::M8L4K4: MSDA_FAST(8, 4, 4) break;
@@ -1531,24 +1560,45 @@ bool backward_uses_workspace(const Geometry &g, const void *value, msda_dtype vt
 
 hipError_t launch_backward(const Geometry &g, const void *value, msda_dtype vt, const float *loc,
                            const float *attn, const float *go, float *gv, float *gl, float *ga, void *ws,
-                           bool accumulate, hipStream_t st)
+                           bool accumulate, bool prepared, hipStream_t st)
 {
     TilePlan tp;
     const TilePlan *tpp = backward_uses_workspace(g, value, vt, go, gv) && make_tile_plan(g, tp) ? &tp : nullptr;
     if (vt == MSDA_BF16)
-        return launch_typed<uint16_t>(g, tpp, value, loc, attn, go, gv, gl, ga, nullptr, ws, accumulate, st);
-    return launch_typed<float>(g, tpp, value, loc, attn, go, gv, gl, ga, nullptr, ws, accumulate, st);
+        return launch_typed<uint16_t>(g, tpp, value, loc, attn, go, gv, gl, ga, nullptr, ws, accumulate, prepared,
+                                      st);
+    return launch_typed<float>(g, tpp, value, loc, attn, go, gv, gl, ga, nullptr, ws, accumulate, prepared, st);
 }
 
 hipError_t launch_backward_fused(const Geometry &g, const void *value, msda_dtype vt, const float *loc,
                                  const float *attn, const float *go, float *gv, float *goff, float *glogits,
-                                 const FusedGrads &fg, void *ws, bool accumulate, hipStream_t st)
+                                 const FusedGrads &fg, void *ws, bool accumulate, bool prepared, hipStream_t st)
 {
     TilePlan tp;
     const TilePlan *tpp = backward_uses_workspace(g, value, vt, go, gv) && make_tile_plan(g, tp) ? &tp : nullptr;
     if (vt == MSDA_BF16)
-        return launch_typed<uint16_t>(g, tpp, value, loc, attn, go, gv, goff, glogits, &fg, ws, accumulate, st);
-    return launch_typed<float>(g, tpp, value, loc, attn, go, gv, goff, glogits, &fg, ws, accumulate, st);
+        return launch_typed<uint16_t>(g, tpp, value, loc, attn, go, gv, goff, glogits, &fg, ws, accumulate, prepared,
+                                      st);
+    return launch_typed<float>(g, tpp, value, loc, attn, go, gv, goff, glogits, &fg, ws, accumulate, prepared, st);
+}
+
+hipError_t launch_backward_prepare(const Geometry &g, const float *loc, void *wsp, hipStream_t st)
+{
+    TilePlan tp;
+    if (!make_tile_plan(g, tp)) return hipSuccess;  // no fast path: nothing to prepare
+    Workspace ws;
+    layout(g, tp, static_cast<char *>(wsp), &ws);
+    switch (fast_kind(g)) {
+    case Fast::M8L4K4: return launch_binning<8, 4, 4>(g, tp, loc, ws, st);
+    case Fast::M4L4K4: return launch_binning<4, 4, 4>(g, tp, loc, ws, st);
+    case Fast::M16L4K4: return launch_binning<16, 4, 4>(g, tp, loc, ws, st);
+    case Fast::M8L1K4: return launch_binning<8, 1, 4>(g, tp, loc, ws, st);
+    case Fast::M8L4K8: return launch_binning<8, 4, 8>(g, tp, loc, ws, st);
+    case Fast::M8L3K4: return launch_binning<8, 3, 4>(g, tp, loc, ws, st);
+    case Fast::M8L4K1: return launch_binning<8, 4, 1>(g, tp, loc, ws, st);
+    case Fast::None: break;
+    }
+    return hipSuccess;
 }
 
 }  // namespace msda

@@ -146,17 +146,22 @@ hipError_t launch_forward_fused(const Geometry &g, const void *value, msda_dtype
 hipError_t launch_zero_fill(float *p, int64_t n, hipStream_t st);
 // grad_value is fully overwritten unless `accumulate`. `workspace` must hold
 // backward_workspace_bytes(g) bytes when backward_uses_workspace(...) holds.
+// `prepared`: the workspace already holds the binning of these locations
+// (launch_backward_prepare), which is then skipped.
 hipError_t launch_backward(const Geometry &g, const void *value, msda_dtype vt, const float *loc,
                            const float *attn, const float *grad_out, float *grad_value,
                            float *grad_loc, float *grad_attn, void *workspace, bool accumulate,
-                           hipStream_t st);
+                           bool prepared, hipStream_t st);
+// The binning part of the backward (it needs only the locations), into the
+// workspace; nothing when the sizes have no fast path.
+hipError_t launch_backward_prepare(const Geometry &g, const float *loc, void *workspace, hipStream_t st);
 // The same, carried back to the fused forward's inputs: grad_offsets,
 // grad_logits and (if fg.grad_ref is not null) grad_ref instead of grad_loc
 // and grad_attn.
 hipError_t launch_backward_fused(const Geometry &g, const void *value, msda_dtype vt, const float *loc,
                                  const float *attn, const float *grad_out, float *grad_value,
                                  float *grad_offsets, float *grad_logits, const FusedGrads &fg, void *workspace,
-                                 bool accumulate, hipStream_t st);
+                                 bool accumulate, bool prepared, hipStream_t st);
 hipError_t launch_sampling_locations_box(const Geometry &g, const float *ref, const float *off, float *loc,
                                          hipStream_t st);
 

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.msda_abi_version() == 6
+    assert lib.msda_abi_version() == 7
     assert lib.msda_status_string(0) == b"ok"
     for code in range(-8, 0):
         assert lib.msda_status_string(code) not in (b"", b"unknown status")
@@ -157,7 +157,7 @@ def test_unsupported(lib):
     assert _fwd(lib, _shape(), dtype=7) == B.MSDA_E_UNSUPPORTED
     many_levels = tuple((2, 2) for _ in range(17))
     assert _fwd(lib, _shape(shapes=many_levels)) == B.MSDA_E_UNSUPPORTED
-    assert _bwd(lib, _shape(), flags=2) == B.MSDA_E_UNSUPPORTED
+    assert _bwd(lib, _shape(), flags=4) == B.MSDA_E_UNSUPPORTED
 
 
 @cpu_only
@@ -250,3 +250,21 @@ def test_backward_plan_per_level(lib):
     # empty calls have no plan either, and NULL outputs are allowed
     assert B.msda_backward_plan(_shape(B_=0)) == {"dense": [], "direct": [], "split": []}
     assert lib.msda_backward_plan(_shape().ptr, None, None, None) == B.MSDA_OK
+
+
+@cpu_only
+def test_backward_prepare_validates_on_the_host(lib):
+    """msda_backward_prepare refuses bad arguments before any device work, and
+    is a no-op for sizes without a fast path or empty sizes."""
+    sh = _shape()
+    n = B.msda_backward_workspace_size(sh)
+    f = lib.msda_backward_prepare
+    assert f(sh.ptr, None, FAKE, n, None) == B.MSDA_E_NULL
+    assert f(sh.ptr, MISALIGNED, FAKE, n, None) == B.MSDA_E_ALIGN
+    assert f(sh.ptr, FAKE, None, n, None) == B.MSDA_E_WORKSPACE
+    assert f(sh.ptr, FAKE, FAKE, n - 1, None) == B.MSDA_E_WORKSPACE
+    assert f(sh.ptr, FAKE, ctypes.c_void_p(0x10010), n, None) == B.MSDA_E_ALIGN
+    assert f(_shape(M=3, D=5).ptr, None, None, 0, None) == B.MSDA_OK
+    assert f(_shape(B_=0).ptr, None, None, 0, None) == B.MSDA_OK
+    # the backward accepts the prepared flag (and still validates the rest)
+    assert _bwd(lib, sh, flags=B.MSDA_BWD_PREPARED) == B.MSDA_E_WORKSPACE
