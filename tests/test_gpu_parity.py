@@ -93,6 +93,17 @@ def test_backward_workloads(gpu_lib, name):
     check_backward(build(name), name=name, repeats=2)
 
 
+def test_backward_bf16_large(gpu_lib):
+    """The backward at the large-batch bf16 shape (B=8, S=Nq=22223): 22.8M
+    samples, so the 32-bit record and row offsets run at four times the
+    encoder's range; every element against the oracle."""
+    wl = workloads.custom(name="bf16_large_backward", batch=8, heads=8, channels=32, points=4,
+                          spatial_shapes=workloads.WORKLOADS["encoder_bf16_large"].spatial_shapes,
+                          num_query=None, offset_sigma_px=2.0, value_dtype=torch.bfloat16, backward=True)
+    print("[backward parity] bf16 large", flush=True)
+    check_backward(build(wl), name="bf16 large")
+
+
 # ------------------------------------------------- shapes: fast path and generic
 
 GEOMS = [
