@@ -10,8 +10,8 @@
 // grad_value is a scatter: every sample adds to four pixels. On gfx950 float
 // atomics (global and LDS alike) sustain only a small fraction of the
 // required rate, so the fast path turns the scatter into a gather owned by
-// pixel tiles (float atomics remain only where the records of one dense tile
-// are split over several workgroups, one add per pixel and channel per
+// pixel tiles (float atomics remain only where the records of one crowded
+// tile are split over several workgroups, one add per pixel and channel per
 // workgroup):
 //
 //  0. dense_accum : the dense levels (few pixels, many samples each) skip the
@@ -805,8 +805,8 @@ tile_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, const
     }
 }
 
-// Zero the grad_value rows of the levels whose partial sums are added with
-// atomics (split tiles, split dense levels). One thread per float4.
+// Zero the grad_value rows of the sparse levels whose split tiles add their
+// partial sums with atomics. One thread per float4.
 __global__ void __launch_bounds__(kBlock)
 zero_split_levels_kernel(Geometry g, TilePlan tp, float4 *__restrict__ grad_value)
 {
@@ -838,8 +838,9 @@ zero_split_levels_kernel(Geometry g, TilePlan tp, float4 *__restrict__ grad_valu
 //  - lets each lane group sum weight * G over the pairs of the pixels it
 //    owns, in registers.
 // The next sub-chunk's loads are issued before the current one is sorted and
-// stay in flight across the LDS-only barriers. The split partials meet in
-// grad_value with one float atomic add per pixel and channel.
+// stay in flight across the LDS-only barriers. A level whose queries are split
+// over several items parks each item's sums in the workspace; extra items of
+// tile_accum add them up in split order and write every pixel once.
 constexpr int kDensePix = 256;             // pixels per part at most
 constexpr int kDenseSub = 1024;             // samples per sub-chunk at most
 constexpr int kDenseQ = 256;               // queries per sub-chunk at most
@@ -1026,7 +1027,7 @@ dense_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, cons
         }
     }
     // one query split: write the part's pixels; several: park the sums in the
-    // item's workspace slot for dense_reduce
+    // item's workspace slot, which tile_accum's extra items add up
 #pragma unroll
     for (int j = 0; j < PPG; ++j) {
         const int pl = grp + j * NG;
