@@ -233,6 +233,10 @@ template <int M, int L, int K> struct MainWaves {
     static constexpr int kValue = kBudget / kPerWave >= 16 ? 16 : kBudget / kPerWave >= 8 ? 8 : 4;
 };
 
+// Four waves per SIMD: with the eight-wave workgroups of the usual shapes a
+// fifth would not admit another workgroup, and the 128-register budget this
+// allows keeps every instantiation free of spills.
+//
 // FUSED: the gradients go one step further back, to the inputs of the fused
 // forward: grad_loc becomes the gradient of the offsets (divided by (W_l, H_l),
 // or times ref_wh / (2K) for box references), grad_attn that of the logits
@@ -240,7 +244,7 @@ template <int M, int L, int K> struct MainWaves {
 // grad_ref (if not null) sums grad_loc over heads and points (box references:
 // also grad_loc * offset / (2K) for the box size).
 template <typename VT, int M, int L, int K, bool FUSED>
-__global__ void __launch_bounds__((MainWaves<M, L, K>::kValue * kWave)) __attribute__((amdgpu_waves_per_eu(5, 5)))
+__global__ void __launch_bounds__((MainWaves<M, L, K>::kValue * kWave)) __attribute__((amdgpu_waves_per_eu(4, 4)))
 backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, const float2 *__restrict__ loc,
                      const float *__restrict__ attn, const float4 *__restrict__ grad_out,
                      float2 *__restrict__ grad_loc, float *__restrict__ grad_attn,
@@ -257,11 +261,11 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
     constexpr int MW = MainWaves<M, L, K>::kValue;
     constexpr int NT = MW * kWave;
 
-    extern __shared__ uint32_t s_cursor[];  // [M * tpb]
+    extern __shared__ uint32_t s_cursor[];  // [M * tpb + kWave]; then one slot per lane for its idle adds
     __shared__ LevelRec s_lv[L];
     __shared__ TileLevel s_tl[L];
     __shared__ int4 s_off[MW][M * PAD];
-    // (fx, fy, A, -) per sample; each entry is overwritten in place by its
+    // (fx, fy, A*W_l, A*H_l) per sample; each entry is overwritten in place by its
     // (grad_attn, grad_x, grad_y, -) once the wave has read it (a wave's LDS
     // accesses execute in program order)
     __shared__ float4 s_geo[MW][M * PAD];
@@ -325,16 +329,28 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
     const uint32_t vlane = (uint32_t)lane * 4u * sizeof(VT);
     const int m = lane / LPH;
 
+    constexpr int NP = (NS + kWave - 1) / kWave;  // samples per lane and query
+
     for (int q = q0 + wave; q < q1; q += MW) {
         const int64_t gq = (int64_t)b * g.Nq + q;
+        // the lane index, opaque to the compiler within each query: what phase
+        // 1 derives from it (sample, level, LDS slots) is recomputed per query
+        // instead of being held in registers across the loop
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
         // ---- phase 1: per-sample geometry, one sample per lane per pass ----
+        // record keys (head * tiles + tile) of the sparse-level samples, or
+        // the lane's idle slot
+        int keys[NP][4];
 #pragma unroll
-        for (int s0 = 0; s0 < NS; s0 += kWave) {
-            const int s = s0 + lane;
+        for (int p = 0; p < NP; ++p) {
+            const int s = p * kWave + ln;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) keys[p][j] = nkeys + ln;
             if (NS % kWave == 0 || s < NS) {
                 const int sm = s / LK;
                 const int l = (s / K) % L;
-                const int p = s + s / LK;
+                const int pp = s + s / LK;
                 const LevelRec lv = s_lv[l];
                 int cx, cy;
                 float fx, fy;
@@ -352,20 +368,13 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
                 o.y = (int)((y0ok & x1ok) ? o00 + RB : kOutOfRange);
                 o.z = (int)((y1ok & x0ok) ? o10 : kOutOfRange);
                 o.w = (int)((y1ok & x1ok) ? o10 + RB : kOutOfRange);
-                s_off[wave][p] = o;
-                s_geo[wave][p] = make_float4(fx, fy, a, 0.0f);
+                s_off[wave][pp] = o;
+                s_geo[wave][pp] = make_float4(fx, fy, a * lv.Wf, a * lv.Hf);
                 if (in && !((tp.dense_mask >> l) & 1)) {
                     const SampleTiles st = sample_tiles(s_tl[l], lv.W, H, cx, cy);
-                    const uint32_t sidx = (uint32_t)(gq * NS + s);
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
-                        if (st.t[j] >= 0) {
-                            // the bound only matters for a workspace that was
-                            // not binned for these locations (a misused
-                            // prepared flag): wrong sums then, never a stray write
-                            const uint32_t pos = atomicAdd(&s_cursor[sm * tp.tpb + st.t[j]], 1u);
-                            if (pos < rcap) records[pos] = sidx;
-                        }
+                        if (st.t[j] >= 0) keys[p][j] = sm * tp.tpb + st.t[j];
                 }
             }
         }
@@ -393,9 +402,24 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
 #pragma unroll
         for (int i = 0; i < kMainAhead; ++i)
             if (i < LK) gather(i, i);
+        // the records, after the first gathers (a wait on a load also waits on
+        // every store issued before it): a position per key from the LDS
+        // cursor, all adds in flight at once
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const uint32_t sidx = (uint32_t)(gq * NS + p * kWave + ln);
+            uint32_t pos[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) pos[j] = atomicAdd(&s_cursor[keys[p][j]], 1u);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                // the bound only matters for a workspace that was not binned
+                // for these locations (a misused prepared flag): wrong sums
+                // then, never a stray write
+                if (keys[p][j] < nkeys && pos[j] < rcap) records[pos[j]] = sidx;
+        }
 #pragma unroll
         for (int l = 0; l < L; ++l) {
-            const float Wf = (float)g.lv.W[l], Hf = (float)g.lv.H[l];
 #pragma unroll
             for (int k = 0; k < K; ++k) {
                 const int i = l * K + k;
@@ -405,7 +429,7 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
                 const float4 v00 = vb[slot][0], v01 = vb[slot][1], v10 = vb[slot][2], v11 = vb[slot][3];
                 const float d00 = dot4(G, v00), d01 = dot4(G, v01);
                 const float d10 = dot4(G, v10), d11 = dot4(G, v11);
-                const float fx = f.x, fy = f.y, a = f.z;
+                const float fx = f.x, fy = f.y;
                 const float hx = 1.0f - fx, hy = 1.0f - fy;
                 float ga = hy * (hx * d00 + fx * d01) + fy * (hx * d10 + fx * d11);
                 float gx = hy * (d01 - d00) + fy * (d11 - d10);
@@ -415,7 +439,7 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
                 gy = group_sum<LPH>(gy);
                 // every lane of the head holds the sums: all write the same
                 // value (no branch, so the loop stays one basic block)
-                res[i] = make_float4(ga, a * Wf * gx, a * Hf * gy, FUSED ? a : 0.0f);
+                res[i] = make_float4(ga, f.z * gx, f.w * gy, 0.0f);
             }
         }
         wave_lds_sync();
@@ -424,14 +448,15 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
         float4 ref_acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int s0 = 0; s0 < NS; s0 += kWave) {
-            const int s = s0 + lane;
+            const int s = s0 + ln;
             if (NS % kWave == 0 || s < NS) {
                 const float4 r = s_geo[wave][s + s / LK];
                 if constexpr (FUSED) {
                     // grad_logit = A * (grad_A - sum over the head's L*K samples of A * grad_A)
-                    const float t = group_sum<LK>(r.w * r.x);
+                    const float a = attn[gq * NS + s];
+                    const float t = group_sum<LK>(a * r.x);
                     const int l = (s / K) % L;
-                    grad_attn[gq * NS + s] = r.w * (r.x - t);
+                    grad_attn[gq * NS + s] = a * (r.x - t);
                     if (fg.ref_dims == 4) {
                         const float4 bx = reinterpret_cast<const float4 *>(fg.ref)[gq * L + l];
                         grad_loc[gq * NS + s] = make_float2(r.y * (bx.z * 0.5f / (float)K), r.z * (bx.w * 0.5f / (float)K));
@@ -1250,7 +1275,7 @@ hipError_t launch_fast(const Geometry &g, const TilePlan &tp, const void *value,
     const int nkb = M * tp.tpb;
     const int nwg = g.B * tp.wpb;
     const int nkeys = g.B * nkb;
-    const size_t hist_bytes = (size_t)nkb * 4;
+    const size_t hist_bytes = (size_t)(nkb + kWave) * 4;  // + a slot per lane for its idle adds
     constexpr int LG = 256 / M / 4;
     // the dense levels on the side stream: they read only the inputs and
     // write their own grad_value rows and workspace section, so they run
@@ -1522,7 +1547,7 @@ bool make_tile_plan(const Geometry &g, TilePlan &tp)
     tp.qpw = kQueriesPerGroup;
     tp.wpb = (g.Nq + tp.qpw - 1) / tp.qpw;
     // the per-workgroup histogram / cursors live in LDS; record indices are 32-bit
-    if ((size_t)g.M * tp.tpb * 4 > 64 * 1024) return false;
+    if (((size_t)g.M * tp.tpb + kWave) * 4 > 64 * 1024) return false;  // the main kernel's LDS cursors
     if ((uint64_t)g.samples() * 4 >= (1ull << 32)) return false;
     // grad_output is read through 32-bit buffer offsets below the out-of-range marker
     if ((uint64_t)g.queries() * g.M * g.D * 4 >= (uint64_t)kOutOfRange) return false;
