@@ -121,6 +121,8 @@ def algorithmic_bytes(B, M, D, Nq, shapes, K, vbytes):
         "sampling_locations_kernel": B * Nq * L * 2 * f32 + 2 * samples * 2 * f32,
         "softmax_vec_kernel": 2 * samples * f32,
         "forward_c256_kernel": vbytes + samples * 3 * f32 + rows,
+        # the same op with the coarse levels staged in LDS (same algorithmic bytes)
+        "forward_staged_kernel": vbytes + samples * 3 * f32 + rows,
         "zero_fill_kernel": S * gv_row,
         "clear_totals_kernel": 0,
         "bin_count_kernel": sparse_samples * 2 * f32,
@@ -178,15 +180,18 @@ def _counter_rows(d, counter):
 
 def _short_kernel_name(full):
     """'void ns::(anonymous namespace)::name<T, 8>(args)' -> 'name'. The fused
-    instantiations of the c256 kernels (last template argument true) get the
-    names the library's own timing uses for them, forward_fused_c256_kernel
-    and backward_fused_c256_kernel, so their counters are kept apart."""
+    instantiations of the c256 and staged kernels (last template argument
+    true) get the names the library's own timing uses for them,
+    forward_fused_c256_kernel, backward_fused_c256_kernel and
+    forward_fused_staged_kernel, so their counters are kept apart."""
     head = full.replace("(anonymous namespace)", "")
     tmpl = head.split("(")[0]
     name = tmpl.split("<")[0]
     name = name.split("::")[-1].split()[-1] if name.strip() else name
     if name in ("forward_c256_kernel", "backward_c256_kernel") and tmpl.rstrip().endswith("true>"):
         name = name.replace("_c256", "_fused_c256")
+    if name == "forward_staged_kernel" and tmpl.rstrip().endswith("true>"):
+        name = "forward_fused_staged_kernel"
     return name
 
 
@@ -525,7 +530,9 @@ def main():
     dom_us = kstats[dominant]["avg_us"]
     dom_gbps = alg[dominant] / (dom_us * 1e-6) / 1e9
     queries = B * Nq
-    fwd = kstats.get("forward_c256_kernel", {})
+    # the forward kernel this shape takes (coarse levels staged in LDS, or one wave per query)
+    fwd_name = next((k for k in ("forward_staged_kernel", "forward_c256_kernel") if k in kstats), None)
+    fwd = kstats.get(fwd_name, {}) if fwd_name else {}
     result = {
         "metric": METRIC,
         "value": queries / (step_ms * 1e-3),
@@ -548,15 +555,15 @@ def main():
         "kernels": kstats,
         "entry_points_us": {k: round(v, 3) for k, v in per_call.items()},
         "eager_ms_per_step": eager_step_ms,
-        "forward": {"queries_per_s": queries / (fwd["avg_us"] * 1e-6) if fwd else None,
+        "forward": {"kernel": fwd_name, "queries_per_s": queries / (fwd["avg_us"] * 1e-6) if fwd else None,
                     "effective_gbps": fwd.get("gbps"), "frac_of_hbm_peak": fwd.get("frac_of_hbm_peak"),
-                    "traffic": measured_traffic("forward_c256_kernel"),
+                    "traffic": measured_traffic(fwd_name) if fwd_name else None,
                     "gather": None if not fwd else {
                         "corner_reads": corner_reads, "bytes": corner_reads * D * elem,
                         "tbps": round(corner_reads * D * elem / (fwd["avg_us"] * 1e-6) / 1e12, 2),
-                        "note": "in-map corner reads of one head's value row each, served by L1/L2: the rate "
-                                "that bounds the forward (we measured 50-58 B/clk/CU for 16-byte lane gathers on "
-                                "this path, 31-36 TB/s on 256 CUs at 2.4 GHz)"}},
+                        "note": "in-map corner reads of one head's value row each; the fine levels' are served by "
+                                "L1/L2 (we measured 50-58 B/clk/CU for 16-byte lane gathers on that path, 31-36 TB/s "
+                                "on 256 CUs at 2.4 GHz), the coarse levels' from LDS when they are staged"}},
         "backward": {"queries_per_s": queries / (per_call["msda_backward"] * 1e-6),
                      "note": "the whole msda_backward call, all its kernels"},
         "fused_step": None if fused_ms is None else {

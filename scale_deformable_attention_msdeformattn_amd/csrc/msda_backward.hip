@@ -74,15 +74,6 @@ __device__ __forceinline__ float dot4(const float4 &a, const float4 &b)
     return __builtin_fmaf(a.w, b.w, __builtin_fmaf(a.z, b.z, __builtin_fmaf(a.y, b.y, a.x * b.x)));
 }
 
-// Orders this wave's LDS writes before its later LDS reads of other lanes'
-// data (one wavefront's LDS instructions execute in order).
-__device__ __forceinline__ void wave_lds_sync()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // The pixel tiles (of one head and level) that a sample's in-map corners fall
 // in: up to four distinct ids, -1 for none. (cx, cy) is the sample's cell.
 struct SampleTiles {

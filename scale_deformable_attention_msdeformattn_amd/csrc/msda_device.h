@@ -128,6 +128,15 @@ template <int N> __device__ __forceinline__ float group_max(float v)
     return v;
 }
 
+// Orders this wave's LDS writes before its later LDS reads of other lanes'
+// data (one wavefront's LDS instructions execute in order).
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Map a workgroup id to a logical tile so that each of the 8 XCDs (which
 // receive workgroups round-robin and have private L2 caches) processes one
 // contiguous range of tiles. `n` is the grid size and must be a multiple of 8

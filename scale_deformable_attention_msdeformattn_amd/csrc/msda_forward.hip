@@ -20,6 +20,8 @@
 //           corners with bounds-checked buffer loads (off-map corners read 0)
 //           and accumulate in fp32.
 // Generic path (any M, D): one thread per output element.
+#include <algorithm>
+
 #include "msda_device.h"
 #include "msda_internal.h"
 
@@ -162,6 +164,219 @@ forward_c256_kernel(Geometry g, const VT *__restrict__ value, const float2 *__re
     out[gq * (C / 4) + lane] = acc;
 }
 
+// Staged path: the forward above spends most of its time on the cache-side
+// gather path (64 wave-wide 16-byte gathers per query). The coarse levels are
+// small and read by every query, so here each workgroup takes one (batch,
+// head) and a range of its queries, copies that head's rows of the coarse
+// levels (levels LS..L-1) into LDS once, and serves their corners from LDS;
+// the fine levels are gathered from memory as above. A wave holds QPW queries
+// of the head side by side (LPH lanes of 4 channels each), so phase 1 forms
+// QPW*L*K sample records per pass and phase 2 walks the (l, k) samples of all
+// QPW queries at once. The fused form forms the locations and the L*K softmax
+// in phase 1, as the per-query kernel does (a query-head's samples sit in L*K
+// adjacent lanes of a pass).
+constexpr int kStagedWaves = 16;
+constexpr int kStageRowPad = 0;           // chunks of padding after each staged row (padding did not pay)
+constexpr int kStagedThreads = kStagedWaves * kWave;
+constexpr int kStagedTargetWGs = 512;     // two rounds of one workgroup per CU (the staging fills most of its LDS)
+constexpr int kStagedMinQueries = 1024;   // fewer queries per (batch, head) do not repay the staging
+constexpr size_t kLdsPerWG = 160 * 1024;  // gfx950
+
+struct StagePlan {
+    int32_t nqr;  // query ranges (workgroups) per (batch, head)
+    int32_t qpr;  // queries per range
+};
+
+template <typename VT> struct StageChunk;  // four channels of one staged row
+template <> struct StageChunk<float> {
+    using type = float4;
+    __device__ static float4 zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+    __device__ static float4 widen(const float4 &v) { return v; }
+};
+template <> struct StageChunk<uint16_t> {
+    using type = uint2;
+    __device__ static uint2 zero() { return make_uint2(0u, 0u); }
+    __device__ static float4 widen(const uint2 &v)
+    {
+        return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                           __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
+    }
+};
+
+template <typename VT, int M, int L, int K, int LS, bool FUSED>
+__global__ void __launch_bounds__(kStagedThreads)
+forward_staged_kernel(Geometry g, const VT *__restrict__ value, const float2 *__restrict__ loc,
+                      const float *__restrict__ attn, float4 *__restrict__ out, StagePlan sp, uint32_t grid,
+                      FusedInputs fi)
+{
+    constexpr int C = 256;
+    constexpr int D = C / M;
+    constexpr int LPH = D / 4;         // lanes (4 channels each) per query
+    constexpr int QPW = kWave / LPH;   // queries side by side in a wave
+    constexpr int RS = LPH + kStageRowPad;  // staged row stride in chunks
+    constexpr int LK = L * K;
+    constexpr int PAD = LK + 1;
+    constexpr uint32_t RB = C * sizeof(VT);
+    static_assert(0 < LS && LS < L, "some levels from memory, some from LDS");
+    static_assert(!FUSED || (kWave % LK == 0 && (QPW * LK) % kWave == 0), "softmax groups within a pass");
+    using Chunk = typename StageChunk<VT>::type;
+
+    extern __shared__ __align__(16) unsigned char s_raw[];
+    Chunk *s_stage = reinterpret_cast<Chunk *>(s_raw);  // [(rows + 1) * RS], the last row zeros
+    __shared__ LevelRec s_lv[L];
+    __shared__ int4 s_off[kStagedWaves][QPW * PAD];
+    __shared__ float4 s_w[kStagedWaves][QPW * PAD];
+
+    const int lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint32_t wg = xcd_tile(blockIdx.x, grid);
+    if (wg >= (uint32_t)(g.B * M * sp.nqr)) return;  // whole workgroup: before any barrier
+    const int bm = (int)(wg / sp.nqr), r = (int)(wg - (uint32_t)bm * sp.nqr);
+    const int b = bm / M, m = bm - (bm / M) * M;
+    const int q0 = r * sp.qpr, q1 = min(q0 + sp.qpr, g.Nq);
+    if (threadIdx.x < L) {
+        const int l = threadIdx.x;
+        s_lv[l] = LevelRec{(float)g.lv.W[l], (float)g.lv.H[l], g.lv.W[l], g.lv.start[l]};
+    }
+    // head m's rows of the staged levels (pixels start[LS] .. S-1), then a zero
+    // row that off-map corners read
+    const int srow0 = g.lv.start[LS];
+    const int nrows = g.S - srow0;
+    {
+        // kStageBatch loads in flight per thread before their LDS stores
+        constexpr int kStageBatch = 8;
+        const Chunk *src = reinterpret_cast<const Chunk *>(value + ((int64_t)b * g.S + srow0) * C + m * D);
+        const int n = nrows * LPH;
+        for (int i0 = threadIdx.x; i0 < n; i0 += kStagedThreads * kStageBatch) {
+            Chunk v[kStageBatch];
+#pragma unroll
+            for (int k = 0; k < kStageBatch; ++k) {
+                const int i = i0 + k * kStagedThreads;
+                v[k] = i < n ? src[(int64_t)(i / LPH) * (C / 4) + i % LPH] : StageChunk<VT>::zero();
+            }
+#pragma unroll
+            for (int k = 0; k < kStageBatch; ++k) {
+                const int i = i0 + k * kStagedThreads;
+                if (i < n) s_stage[(i / LPH) * RS + i % LPH] = v[k];
+            }
+        }
+        if (threadIdx.x < LPH) s_stage[nrows * RS + threadIdx.x] = StageChunk<VT>::zero();
+    }
+    __syncthreads();
+
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(value + (int64_t)b * g.S * C, (uint32_t)g.S * RB);
+    const int jq = lane / LPH, c = lane - (lane / LPH) * LPH;
+    const uint32_t lane_off = (uint32_t)(m * D + c * 4) * sizeof(VT);
+    const int zero_row = nrows * RS;
+    for (int qb = q0 + wave * QPW; qb < q1; qb += kStagedWaves * QPW) {
+        // ---- phase 1: the QPW*L*K samples of this pass, one per lane ----
+#pragma unroll
+        for (int t0 = 0; t0 < QPW * LK; t0 += kWave) {
+            const int t = t0 + lane;
+            if ((QPW * LK) % kWave == 0 || t < QPW * LK) {
+                const int j = t / LK, i = t - (t / LK) * LK;
+                const int l = i / K;
+                const bool staged = l >= LS;
+                const int q = qb + j;
+                int4 o = staged ? make_int4(zero_row, zero_row, zero_row, zero_row)
+                                : make_int4((int)kOutOfRange, (int)kOutOfRange, (int)kOutOfRange, (int)kOutOfRange);
+                float4 w = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (q < q1) {  // the same for the L*K lanes of a query
+                    const int64_t si = (((int64_t)b * g.Nq + q) * M + m) * LK + i;
+                    const LevelRec lv = s_lv[l];
+                    float2 u;
+                    float a;
+                    if constexpr (FUSED) {
+                        u = fused_location(fi.ref, fi.ref_dims, ((int64_t)b * g.Nq + q) * L + l, fi.off[si], lv.Wf,
+                                           lv.Hf, (float)K);
+                        const float x = fi.logits[si];
+                        const float mx = group_max<LK>(x);
+                        const float e = expf(x - mx);
+                        a = e / group_sum<LK>(e);
+                        fi.loc_out[si] = u;
+                        fi.attn_out[si] = a;
+                    } else {
+                        u = loc[si];
+                        a = attn[si];
+                    }
+                    const bool in = sample_in_range(u.x, u.y, lv.Wf, lv.Hf);
+                    u.x = in ? u.x : 0.0f;
+                    u.y = in ? u.y : 0.0f;
+                    float cx, fx, cy, fy;
+                    cell_1d(u.x, lv.Wf, cx, fx);
+                    cell_1d(u.y, lv.Hf, cy, fy);
+                    const bool x0ok = (cx >= 0.0f) & (cx < lv.Wf);
+                    const bool x1ok = (cx >= -1.0f) & (cx + 1.0f < lv.Wf);
+                    const bool y0ok = in & (cy >= 0.0f) & (cy < lv.Hf);
+                    const bool y1ok = in & (cy >= -1.0f) & (cy + 1.0f < lv.Hf);
+                    const int row = lv.start + (int)cy * lv.W + (int)cx;
+                    if (staged) {
+                        // chunk index of the corner's row in LDS
+                        const int r00 = (row - srow0) * RS, r10 = r00 + lv.W * RS;
+                        o.x = (y0ok & x0ok) ? r00 : zero_row;
+                        o.y = (y0ok & x1ok) ? r00 + RS : zero_row;
+                        o.z = (y1ok & x0ok) ? r10 : zero_row;
+                        o.w = (y1ok & x1ok) ? r10 + RS : zero_row;
+                    } else {
+                        const uint32_t o00 = (uint32_t)row * RB, o10 = o00 + (uint32_t)lv.W * RB;
+                        o.x = (int)((y0ok & x0ok) ? o00 : kOutOfRange);
+                        o.y = (int)((y0ok & x1ok) ? o00 + RB : kOutOfRange);
+                        o.z = (int)((y1ok & x0ok) ? o10 : kOutOfRange);
+                        o.w = (int)((y1ok & x1ok) ? o10 + RB : kOutOfRange);
+                    }
+                    const float wy0 = a * (1.0f - fy), wy1 = a * fy;
+                    w = make_float4(wy0 * (1.0f - fx), wy0 * fx, wy1 * (1.0f - fx), wy1 * fx);
+                }
+                s_off[wave][j * PAD + i] = o;
+                s_w[wave][j * PAD + i] = w;
+            }
+        }
+        wave_lds_sync();
+        // ---- phase 2: each lane its query's samples, memory levels then LDS levels ----
+        const int4 *offs = &s_off[wave][jq * PAD];
+        const float4 *ws = &s_w[wave][jq * PAD];
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        auto blend = [&](const float4 &w, const float4 &v00, const float4 &v01, const float4 &v10,
+                         const float4 &v11) {
+            acc.x = __builtin_fmaf(w.x, v00.x, acc.x);
+            acc.y = __builtin_fmaf(w.x, v00.y, acc.y);
+            acc.z = __builtin_fmaf(w.x, v00.z, acc.z);
+            acc.w = __builtin_fmaf(w.x, v00.w, acc.w);
+            acc.x = __builtin_fmaf(w.y, v01.x, acc.x);
+            acc.y = __builtin_fmaf(w.y, v01.y, acc.y);
+            acc.z = __builtin_fmaf(w.y, v01.z, acc.z);
+            acc.w = __builtin_fmaf(w.y, v01.w, acc.w);
+            acc.x = __builtin_fmaf(w.z, v10.x, acc.x);
+            acc.y = __builtin_fmaf(w.z, v10.y, acc.y);
+            acc.z = __builtin_fmaf(w.z, v10.z, acc.z);
+            acc.w = __builtin_fmaf(w.z, v10.w, acc.w);
+            acc.x = __builtin_fmaf(w.w, v11.x, acc.x);
+            acc.y = __builtin_fmaf(w.w, v11.y, acc.y);
+            acc.z = __builtin_fmaf(w.w, v11.z, acc.z);
+            acc.w = __builtin_fmaf(w.w, v11.w, acc.w);
+        };
+#pragma unroll
+        for (int i = 0; i < LS * K; ++i) {
+            const int4 o = offs[i];
+            const float4 w = ws[i];
+            blend(w, ValueTraits<VT>::load4(rsrc, (uint32_t)o.x + lane_off),
+                  ValueTraits<VT>::load4(rsrc, (uint32_t)o.y + lane_off),
+                  ValueTraits<VT>::load4(rsrc, (uint32_t)o.z + lane_off),
+                  ValueTraits<VT>::load4(rsrc, (uint32_t)o.w + lane_off));
+        }
+#pragma unroll
+        for (int i = LS * K; i < LK; ++i) {
+            const int4 o = offs[i];
+            const float4 w = ws[i];
+            blend(w, StageChunk<VT>::widen(s_stage[o.x + c]), StageChunk<VT>::widen(s_stage[o.y + c]),
+                  StageChunk<VT>::widen(s_stage[o.z + c]), StageChunk<VT>::widen(s_stage[o.w + c]));
+        }
+        const int q = qb + jq;
+        if (q < q1) out[(((int64_t)b * g.Nq + q) * M + m) * LPH + c] = acc;
+        wave_lds_sync();  // the next pass rewrites this wave's records
+    }
+}
+
 // Generic path: one thread per output element (b, q, m, d).
 template <typename VT>
 __device__ __forceinline__ float load_scalar(const VT *p);
@@ -212,10 +427,68 @@ forward_generic_kernel(Geometry g, const VT *__restrict__ value, const float2 *_
     out[t] = acc;
 }
 
+template <typename VT, int M, int L, int K, int LS, bool FUSED>
+hipError_t launch_staged_ls(const Geometry &g, const void *value, const float *loc, const float *attn,
+                            float *out, const FusedInputs &fi, size_t dyn, hipStream_t st)
+{
+    const auto kernel = forward_staged_kernel<VT, M, L, K, LS, FUSED>;
+    static bool attr_set = false;  // once per instantiation (a repeat is harmless)
+    if (!attr_set) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void *>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)dyn) != hipSuccess)
+            (void)hipGetLastError();  // the launch below reports a real limit
+        attr_set = true;
+    }
+    StagePlan sp;
+    sp.nqr = std::max(1, (kStagedTargetWGs + g.B * M - 1) / (g.B * M));
+    sp.qpr = (g.Nq + sp.nqr - 1) / sp.nqr;
+    sp.nqr = (g.Nq + sp.qpr - 1) / sp.qpr;
+    const uint32_t grid = round_up8((uint32_t)(g.B * M * sp.nqr));
+    KernelScope ks_(FUSED ? "forward_fused_staged_kernel" : "forward_staged_kernel", st);
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kStagedThreads), dyn, st, g, static_cast<const VT *>(value),
+                       reinterpret_cast<const float2 *>(loc), attn, reinterpret_cast<float4 *>(out), sp, grid, fi);
+    return hipGetLastError();
+}
+
+// The first level whose rows (with those of every coarser level) fit in LDS
+// beside the records, or 0 when the staged kernel does not apply.
+template <typename VT, int M, int L, int K>
+int staged_first_level(const Geometry &g, size_t &dyn)
+{
+    constexpr int LPH = 256 / M / 4;
+    constexpr int QPW = kWave / LPH;
+    constexpr size_t kStatic = (size_t)kStagedWaves * QPW * (L * K + 1) * 32 + L * 16;
+    if (g.Nq < kStagedMinQueries) return 0;
+    for (int ls = 1; ls < L; ++ls) {
+        const int64_t rows = (int64_t)g.S - g.lv.start[ls];
+        const size_t bytes = (size_t)(rows + 1) * (LPH + kStageRowPad) * sizeof(typename StageChunk<VT>::type);
+        if (kStatic + bytes + 1024 <= kLdsPerWG) {
+            dyn = bytes;
+            return ls;
+        }
+    }
+    return 0;
+}
+
 template <typename VT, int M, int L, int K>
 hipError_t launch_c256(const Geometry &g, const void *value, const float *loc, const float *attn,
                        float *out, const FusedInputs *fi, hipStream_t st)
 {
+    if constexpr (M == 8 && L == 4 && K == 4) {
+        size_t dyn = 0;
+        const FusedInputs f = fi ? *fi : FusedInputs{};
+        switch (staged_first_level<VT, M, L, K>(g, dyn)) {
+#define MSDA_STAGED(LS_)                                                                                      \
+    case LS_:                                                                                                 \
+        return fi ? launch_staged_ls<VT, M, L, K, LS_, true>(g, value, loc, attn, out, f, dyn, st)            \
+                  : launch_staged_ls<VT, M, L, K, LS_, false>(g, value, loc, attn, out, f, dyn, st);
+            MSDA_STAGED(1)
+            MSDA_STAGED(2)
+            MSDA_STAGED(3)
+#undef MSDA_STAGED
+        default: break;
+        }
+    }
     const uint32_t tiles = (uint32_t)((g.queries() + kWaves - 1) / kWaves);
     const uint32_t grid = round_up8(tiles);
     if (fi) {
