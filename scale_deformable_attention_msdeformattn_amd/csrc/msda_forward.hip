@@ -19,6 +19,9 @@
 //           from LDS (a broadcast to the lanes of one head), gather the four
 //           corners with bounds-checked buffer loads (off-map corners read 0)
 //           and accumulate in fp32.
+// Staged path (8 heads, 4 levels, 4 points, at least 1024 queries): one
+// workgroup per (batch, head, query range) with the head's coarse-level rows
+// copied into LDS; see forward_staged_kernel below.
 // Generic path (any M, D): one thread per output element.
 #include <algorithm>
 
