@@ -435,13 +435,6 @@ hipError_t launch_staged_ls(const Geometry &g, const void *value, const float *l
                             float *out, const FusedInputs &fi, size_t dyn, hipStream_t st)
 {
     const auto kernel = forward_staged_kernel<VT, M, L, K, LS, FUSED>;
-    static bool attr_set = false;  // once per instantiation (a repeat is harmless)
-    if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void *>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)dyn) != hipSuccess)
-            (void)hipGetLastError();  // the launch below reports a real limit
-        attr_set = true;
-    }
     StagePlan sp;
     sp.nqr = std::max(1, (kStagedTargetWGs + g.B * M - 1) / (g.B * M));
     sp.qpr = (g.Nq + sp.nqr - 1) / sp.nqr;
