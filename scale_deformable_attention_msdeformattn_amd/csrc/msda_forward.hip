@@ -335,7 +335,7 @@ forward_staged_kernel(Geometry g, const VT *__restrict__ value, const float2 *__
             }
         }
         wave_lds_sync();
-        // ---- phase 2: each lane its query's samples, memory levels then LDS levels ----
+        // ---- phase 2: each lane its query's samples, memory and LDS levels interleaved ----
         const int4 *offs = &s_off[wave][jq * PAD];
         const float4 *ws = &s_w[wave][jq * PAD];
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -358,22 +358,36 @@ forward_staged_kernel(Geometry g, const VT *__restrict__ value, const float2 *__
             acc.z = __builtin_fmaf(w.w, v11.z, acc.z);
             acc.w = __builtin_fmaf(w.w, v11.w, acc.w);
         };
-#pragma unroll
-        for (int i = 0; i < LS * K; ++i) {
+        auto blend_staged = [&](int i) {
             const int4 o = offs[i];
-            const float4 w = ws[i];
-            blend(w, ValueTraits<VT>::load4(rsrc, (uint32_t)o.x + lane_off),
-                  ValueTraits<VT>::load4(rsrc, (uint32_t)o.y + lane_off),
-                  ValueTraits<VT>::load4(rsrc, (uint32_t)o.z + lane_off),
-                  ValueTraits<VT>::load4(rsrc, (uint32_t)o.w + lane_off));
-        }
-#pragma unroll
-        for (int i = LS * K; i < LK; ++i) {
-            const int4 o = offs[i];
-            const float4 w = ws[i];
-            blend(w, StageChunk<VT>::widen(s_stage[o.x + c]), StageChunk<VT>::widen(s_stage[o.y + c]),
+            blend(ws[i], StageChunk<VT>::widen(s_stage[o.x + c]), StageChunk<VT>::widen(s_stage[o.y + c]),
                   StageChunk<VT>::widen(s_stage[o.z + c]), StageChunk<VT>::widen(s_stage[o.w + c]));
+        };
+        // level by level: a memory level's gathers are issued, then a staged
+        // level is summed from LDS while they are in flight, then the memory
+        // level is summed (i, l and k are compile-time here)
+#pragma unroll
+        for (int l = 0; l < LS; ++l) {
+            float4 v[K][4];
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const int4 o = offs[l * K + k];
+                v[k][0] = ValueTraits<VT>::load4(rsrc, (uint32_t)o.x + lane_off);
+                v[k][1] = ValueTraits<VT>::load4(rsrc, (uint32_t)o.y + lane_off);
+                v[k][2] = ValueTraits<VT>::load4(rsrc, (uint32_t)o.z + lane_off);
+                v[k][3] = ValueTraits<VT>::load4(rsrc, (uint32_t)o.w + lane_off);
+            }
+            if (LS + l < L) {
+#pragma unroll
+                for (int k = 0; k < K; ++k) blend_staged((LS + l) * K + k);
+            }
+#pragma unroll
+            for (int k = 0; k < K; ++k) blend(ws[l * K + k], v[k][0], v[k][1], v[k][2], v[k][3]);
         }
+#pragma unroll
+        for (int l = 2 * LS; l < L; ++l)  // staged levels left over
+#pragma unroll
+            for (int k = 0; k < K; ++k) blend_staged(l * K + k);
         const int q = qb + jq;
         if (q < q1) out[(((int64_t)b * g.Nq + q) * M + m) * LPH + c] = acc;
         wave_lds_sync();  // the next pass rewrites this wave's records
