@@ -53,6 +53,8 @@ def parse():
     p.add_argument("--no-encoder-stack", action="store_true",
                    help="skip the 6-layer encoder stack measurement (projections + FFN around the core)")
     p.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP graph replay")
+    p.add_argument("--no-extra-configs", action="store_true",
+                   help="skip the decoder and large-batch bf16 forward timings")
     p.add_argument("--copy-mib", type=int, default=0,
                    help="only run a plain copy of this many MiB, 5 times (counter calibration)")
     p.add_argument("--ingest-counters", default=None, metavar="DIR",
@@ -321,6 +323,54 @@ def cpu_baseline(wl_name, min_seconds=10.0):
                       f"locations, softmax, forward, backward), single-threaded fp64 C, {dt:.2f} s"}
 
 
+def forward_configs(msda, workloads, dev, args, names=("decoder", "encoder_bf16_large")):
+    """The forward alone on the other forward workloads of the pages' shapes
+    (the decoder's 300 object queries; the large batch with bf16 value):
+    average kernel duration from the library's event pairs over 20 calls,
+    queries/s and effective HBM GB/s over the algorithmic bytes (the distinct
+    value rows touched, loc, A and the output)."""
+    import torch
+    out = {}
+    for name in names:
+        d = workloads.draw(name, 0)
+        w = d.workload
+        shapes = d.spatial_shapes
+        lsi, _ = msda.level_start_index_host(shapes)
+        vr = d.valid_ratios.to(dev)
+        if w.encoder:
+            ref = msda.msda_reference_points(shapes, valid_ratios=vr)
+        else:
+            ref = msda.msda_reference_points(shapes, valid_ratios=vr, query_ref=d.query_ref.to(dev))
+        loc = msda.msda_sampling_locations(shapes, ref, d.offsets_px.to(dev))
+        A = msda.msda_attention_softmax(shapes, d.logits.to(dev), w.points)
+        value = d.value.to(dev)
+        B, M, D, L, K, Nq = w.batch, w.heads, w.channels, w.levels, w.points, w.nq
+        elem = value.element_size()
+        vbytes, _ = unique_value_bytes(loc, shapes.to(dev), B, M, D * elem)
+        alg = vbytes + B * Nq * M * L * K * 3 * 4 + B * Nq * M * D * 4
+        for _ in range(5):
+            msda.msda_forward(value, shapes, lsi, loc, A)
+        torch.cuda.synchronize()
+        msda.msda_timing_reset()
+        msda.msda_timing_enable(True)
+        n = 20
+        for _ in range(n):
+            msda.msda_forward(value, shapes, lsi, loc, A)
+        torch.cuda.synchronize()
+        msda.msda_timing_enable(False)
+        t = msda.msda_timing_read()
+        msda.msda_timing_reset()
+        kernel, (ms, cnt) = max(t.items(), key=lambda kv: kv[1][0])
+        us = ms * 1e3 / cnt
+        gbps = alg / (us * 1e-6) / 1e9
+        out[name] = {"workload": w.description, "kernel": kernel, "avg_us": round(us, 3),
+                     "queries_per_s": B * Nq / (us * 1e-6), "algorithmic_bytes": alg,
+                     "effective_gbps": round(gbps, 1), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+        del value, loc, A, ref
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -578,6 +628,8 @@ def main():
     }
     if not args.no_encoder_stack:
         result["encoder_stack"] = encoder_stack(msda, shapes, lsi, vr, B, S, M, L, K, dev, args)
+    if not args.no_extra_configs:
+        result["other_forward_configs"] = forward_configs(msda, workloads, dev, args)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.workload)
     print(json.dumps(result), flush=True)
