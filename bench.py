@@ -615,7 +615,13 @@ def main():
                                 "L1/L2 (we measured 50-58 B/clk/CU for 16-byte lane gathers on that path, 31-36 TB/s "
                                 "on 256 CUs at 2.4 GHz), the coarse levels' from LDS when they are staged"}},
         "backward": {"queries_per_s": queries / (per_call["msda_backward"] * 1e-6),
-                     "note": "the whole msda_backward call, all its kernels"},
+                     "note": "the whole msda_backward call, all its kernels",
+                     "main_kernel_gather": None if "backward_c256_kernel" not in kstats else {
+                         "corner_reads": corner_reads, "bytes": corner_reads * D * elem,
+                         "tbps": round(corner_reads * D * elem / (kstats["backward_c256_kernel"]["avg_us"] * 1e-6)
+                                       / 1e12, 2),
+                         "note": "backward_c256 gathers the same in-map corner rows as the forward, all through "
+                                 "the L1/L2 path (31-36 TB/s measured ceiling on 256 CUs)"}},
         "fused_step": None if fused_ms is None else {
             "ms_per_step": fused_ms, "queries_per_s": queries / (fused_ms * 1e-3),
             "kernels_avg_us": {k: round(v[0] * 1e3 / v[1], 3) for k, v in timing_fused.items()},
