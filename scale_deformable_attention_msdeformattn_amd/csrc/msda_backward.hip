@@ -53,7 +53,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kBlock = kWaves * kWave;
 constexpr int kQueriesPerGroup = 32;     // queries per workgroup of bin_count and main
-constexpr int kMainAhead = 1;            // samples whose gathers run ahead in the main kernel
+constexpr int kMainAhead = 2;            // samples whose gathers run ahead in the main kernel
 constexpr int kChunk = 1024;             // records per LDS chunk in tile_accum
 constexpr int kTileTarget = 768;         // expected records per tile the planner aims at
 constexpr int kTilePix = 32;             // pixels per tile
