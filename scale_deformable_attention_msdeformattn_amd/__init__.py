@@ -6,7 +6,7 @@ that ABI. Entry points (same names as the C ABI):
 
     msda_reference_points, msda_sampling_locations, msda_attention_softmax,
     msda_forward, msda_backward, msda_forward_fused, msda_backward_fused,
-    msda_backward_prepare (the backward's binning ahead of it), msda_backward_plan
+    msda_backward_plan
 
 and the per-kernel timing aid msda_timing_enable / msda_timing_read /
 msda_timing_reset, plus ``MSDeformAttnFunction`` and ``MSDeformAttnFusedFunction``
@@ -14,7 +14,7 @@ msda_timing_reset, plus ``MSDeformAttnFunction`` and ``MSDeformAttnFusedFunction
 (location formation + softmax + core in three calls).
 """
 from ._binding import (MSDAError, declared_symbols, level_start_index_host, load, msda_attention_softmax,
-                       msda_backward, msda_backward_fused, msda_backward_plan, msda_backward_prepare, msda_forward,
+                       msda_backward, msda_backward_fused, msda_backward_plan, msda_forward,
                        msda_forward_fused, msda_reference_points, msda_sampling_locations, msda_timing_enable,
                        msda_timing_read, msda_timing_reset)
 from .autograd import MSDeformAttnFunction, MSDeformAttnFusedFunction, ms_deform_attn
@@ -22,6 +22,6 @@ from .autograd import MSDeformAttnFunction, MSDeformAttnFusedFunction, ms_deform
 __all__ = [
     "MSDAError", "MSDeformAttnFunction", "MSDeformAttnFusedFunction", "declared_symbols",
     "level_start_index_host", "load", "ms_deform_attn", "msda_attention_softmax", "msda_backward",
-    "msda_backward_fused", "msda_backward_plan", "msda_backward_prepare", "msda_forward", "msda_forward_fused", "msda_reference_points",
+    "msda_backward_fused", "msda_backward_plan", "msda_forward", "msda_forward_fused", "msda_reference_points",
     "msda_sampling_locations", "msda_timing_enable", "msda_timing_read", "msda_timing_reset",
 ]

@@ -208,24 +208,6 @@ int msda_backward_workspace_size(const msda_shape *shape, size_t *bytes)
     return ok();
 }
 
-int msda_backward_prepare(const msda_shape *shape, const float *sampling_locations, void *workspace,
-                          size_t workspace_bytes, void *stream)
-{
-    msda::Geometry g;
-    if (int st = make_geometry(shape, g)) return st;
-    if (g.B == 0 || g.Nq == 0) return ok();
-    const size_t need = msda::backward_workspace_bytes(g);
-    if (need == 0) return ok();  // no fast path for these sizes: nothing to prepare
-    if (!sampling_locations) return fail(MSDA_E_NULL, "sampling_locations is NULL");
-    if (!aligned(sampling_locations, 8)) return fail(MSDA_E_ALIGN, "sampling_locations needs 8-byte alignment");
-    if (!workspace || workspace_bytes < need)
-        return fail(MSDA_E_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
-                    need);
-    if (!aligned(workspace, 256)) return fail(MSDA_E_ALIGN, "workspace needs 256-byte alignment");
-    return launched(msda::launch_backward_prepare(g, sampling_locations, workspace, (hipStream_t)stream),
-                    "backward_prepare");
-}
-
 int msda_backward_plan(const msda_shape *shape, uint32_t *dense_levels, uint32_t *direct_levels,
                        uint32_t *split_levels)
 {
@@ -246,10 +228,9 @@ int msda_backward(const msda_shape *shape, const void *value, msda_dtype value_d
 {
     msda::Geometry g;
     if (int st = make_geometry(shape, g)) return st;
-    if (flags & ~(MSDA_BWD_ACCUMULATE | MSDA_BWD_PREPARED))
+    if (flags & ~MSDA_BWD_ACCUMULATE)
         return fail(MSDA_E_UNSUPPORTED, "unknown flags 0x%x", flags);
     const bool accumulate = (flags & MSDA_BWD_ACCUMULATE) != 0;
-    const bool prepared = (flags & MSDA_BWD_PREPARED) != 0;
     if (g.B == 0) return ok();
     if (g.Nq == 0) {  // no queries: grad_value is all zeros (or left as is when accumulating)
         if (accumulate) return ok();
@@ -273,7 +254,7 @@ int msda_backward(const msda_shape *shape, const void *value, msda_dtype value_d
     }
     return launched(msda::launch_backward(g, value, value_dtype, sampling_locations, attention_weights, grad_output,
                                           grad_value, grad_sampling_locations, grad_attention_weights, workspace,
-                                          accumulate, prepared, (hipStream_t)stream),
+                                          accumulate, (hipStream_t)stream),
                     "backward");
 }
 
@@ -313,10 +294,9 @@ int msda_backward_fused(const msda_shape *shape, const void *value, msda_dtype v
     if (int st = make_geometry(shape, g)) return st;
     if (reference_dims != 2 && reference_dims != 4)
         return fail(MSDA_E_UNSUPPORTED, "reference_dims %d (2 or 4)", reference_dims);
-    if (flags & ~(MSDA_BWD_ACCUMULATE | MSDA_BWD_PREPARED))
+    if (flags & ~MSDA_BWD_ACCUMULATE)
         return fail(MSDA_E_UNSUPPORTED, "unknown flags 0x%x", flags);
     const bool accumulate = (flags & MSDA_BWD_ACCUMULATE) != 0;
-    const bool prepared = (flags & MSDA_BWD_PREPARED) != 0;
     if (g.B == 0) return ok();
     if (g.Nq == 0) {  // no queries: grad_value is all zeros (or left as is when accumulating)
         if (accumulate) return ok();
@@ -346,7 +326,7 @@ int msda_backward_fused(const msda_shape *shape, const void *value, msda_dtype v
                               grad_reference_points};
     return launched(msda::launch_backward_fused(g, value, value_dtype, sampling_locations, attention_weights,
                                                 grad_output, grad_value, grad_sampling_offsets, grad_attention_logits,
-                                                fg, workspace, accumulate, prepared, (hipStream_t)stream),
+                                                fg, workspace, accumulate, (hipStream_t)stream),
                     "backward_fused");
 }
 

@@ -404,9 +404,8 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
             for (int j = 0; j < 4; ++j) pos[j] = atomicAdd(&s_cursor[keys[p][j]], 1u);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                // the bound only matters for a workspace that was not binned
-                // for these locations (a misused prepared flag): wrong sums
-                // then, never a stray write
+                // the bound keeps a record write inside the workspace whatever
+                // the counts hold
                 if (keys[p][j] < nkeys && pos[j] < rcap) records[pos[j]] = sidx;
         }
 #pragma unroll
@@ -1233,9 +1232,8 @@ hipError_t side_stream(SideStream **out)
     return hipSuccess;
 }
 
-// The binning of the sparse levels' samples into their tiles' record lists:
-// it depends on the locations only, so a caller may run it ahead
-// (msda_backward_prepare) and let the backward skip it.
+// The binning of the sparse levels' samples into their tiles' record lists
+// (it depends on the locations only).
 template <int M, int L, int K>
 hipError_t launch_binning(const Geometry &g, const TilePlan &tp, const float *loc, const Workspace &ws,
                           hipStream_t st)
@@ -1259,7 +1257,7 @@ hipError_t launch_binning(const Geometry &g, const TilePlan &tp, const float *lo
 template <typename VT, int M, int L, int K, bool FUSED>
 hipError_t launch_fast(const Geometry &g, const TilePlan &tp, const void *value, const float *loc,
                        const float *attn, const float *go, float *gv, float *gl, float *ga, const FusedGrads &fg,
-                       void *wsp, bool accumulate, bool prepared, hipStream_t st)
+                       void *wsp, bool accumulate, hipStream_t st)
 {
     Workspace ws;
     layout(g, tp, static_cast<char *>(wsp), &ws);
@@ -1288,7 +1286,7 @@ hipError_t launch_fast(const Geometry &g, const TilePlan &tp, const void *value,
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if ((e = hipEventRecord(side->join, side->s)) != hipSuccess) return e;
     }
-    if (!prepared) {
+    {
         const hipError_t e = launch_binning<M, L, K>(g, tp, loc, ws, st);
         if (e != hipSuccess) return e;
     }
@@ -1407,7 +1405,7 @@ fused_grads_kernel(Geometry g, const float *__restrict__ attn, float *__restrict
 template <typename VT>
 hipError_t launch_typed(const Geometry &g, const TilePlan *tpp, const void *value, const float *loc,
                         const float *attn, const float *go, float *gv, float *gl, float *ga, const FusedGrads *fg,
-                        void *ws, bool accumulate, bool prepared, hipStream_t st)
+                        void *ws, bool accumulate, hipStream_t st)
 {
     // fused gradients inside the main kernel where the L*K softmax fits the
     // wave's lanes; otherwise the plain gradients, converted afterwards
@@ -1417,9 +1415,9 @@ hipError_t launch_typed(const Geometry &g, const TilePlan *tpp, const void *valu
     bool done = false;
 #define MSDA_FAST(M_, L_, K_)                                                                                    \
     e = in_kernel ? launch_fast<VT, M_, L_, K_, true>(g, *tpp, value, loc, attn, go, gv, gl, ga, *fg, ws,        \
-                                                      accumulate, prepared, st)                                  \
+                                                      accumulate, st)                                            \
                   : launch_fast<VT, M_, L_, K_, false>(g, *tpp, value, loc, attn, go, gv, gl, ga, FusedGrads{},  \
-                                                       ws, accumulate, prepared, st);                            \
+                                                       ws, accumulate, st);                                      \
     done = true;
     switch (tpp ? fast_kind(g) : Fast::None) {
     case Fast::M8L4K4: MSDA_FAST(8, 4, 4) break;
@@ -1577,45 +1575,24 @@ bool backward_uses_workspace(const Geometry &g, const void *value, msda_dtype vt
 
 hipError_t launch_backward(const Geometry &g, const void *value, msda_dtype vt, const float *loc,
                            const float *attn, const float *go, float *gv, float *gl, float *ga, void *ws,
-                           bool accumulate, bool prepared, hipStream_t st)
+                           bool accumulate, hipStream_t st)
 {
     TilePlan tp;
     const TilePlan *tpp = backward_uses_workspace(g, value, vt, go, gv) && make_tile_plan(g, tp) ? &tp : nullptr;
     if (vt == MSDA_BF16)
-        return launch_typed<uint16_t>(g, tpp, value, loc, attn, go, gv, gl, ga, nullptr, ws, accumulate, prepared,
-                                      st);
-    return launch_typed<float>(g, tpp, value, loc, attn, go, gv, gl, ga, nullptr, ws, accumulate, prepared, st);
+        return launch_typed<uint16_t>(g, tpp, value, loc, attn, go, gv, gl, ga, nullptr, ws, accumulate, st);
+    return launch_typed<float>(g, tpp, value, loc, attn, go, gv, gl, ga, nullptr, ws, accumulate, st);
 }
 
 hipError_t launch_backward_fused(const Geometry &g, const void *value, msda_dtype vt, const float *loc,
                                  const float *attn, const float *go, float *gv, float *goff, float *glogits,
-                                 const FusedGrads &fg, void *ws, bool accumulate, bool prepared, hipStream_t st)
+                                 const FusedGrads &fg, void *ws, bool accumulate, hipStream_t st)
 {
     TilePlan tp;
     const TilePlan *tpp = backward_uses_workspace(g, value, vt, go, gv) && make_tile_plan(g, tp) ? &tp : nullptr;
     if (vt == MSDA_BF16)
-        return launch_typed<uint16_t>(g, tpp, value, loc, attn, go, gv, goff, glogits, &fg, ws, accumulate, prepared,
-                                      st);
-    return launch_typed<float>(g, tpp, value, loc, attn, go, gv, goff, glogits, &fg, ws, accumulate, prepared, st);
-}
-
-hipError_t launch_backward_prepare(const Geometry &g, const float *loc, void *wsp, hipStream_t st)
-{
-    TilePlan tp;
-    if (!make_tile_plan(g, tp)) return hipSuccess;  // no fast path: nothing to prepare
-    Workspace ws;
-    layout(g, tp, static_cast<char *>(wsp), &ws);
-    switch (fast_kind(g)) {
-    case Fast::M8L4K4: return launch_binning<8, 4, 4>(g, tp, loc, ws, st);
-    case Fast::M4L4K4: return launch_binning<4, 4, 4>(g, tp, loc, ws, st);
-    case Fast::M16L4K4: return launch_binning<16, 4, 4>(g, tp, loc, ws, st);
-    case Fast::M8L1K4: return launch_binning<8, 1, 4>(g, tp, loc, ws, st);
-    case Fast::M8L4K8: return launch_binning<8, 4, 8>(g, tp, loc, ws, st);
-    case Fast::M8L3K4: return launch_binning<8, 3, 4>(g, tp, loc, ws, st);
-    case Fast::M8L4K1: return launch_binning<8, 4, 1>(g, tp, loc, ws, st);
-    case Fast::None: break;
-    }
-    return hipSuccess;
+        return launch_typed<uint16_t>(g, tpp, value, loc, attn, go, gv, goff, glogits, &fg, ws, accumulate, st);
+    return launch_typed<float>(g, tpp, value, loc, attn, go, gv, goff, glogits, &fg, ws, accumulate, st);
 }
 
 }  // namespace msda
