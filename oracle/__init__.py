@@ -49,6 +49,8 @@ def swapped_library(path):
 
 
 def _bind(lib):
+    lib.msda_oracle_set_threads.restype = None
+    lib.msda_oracle_set_threads.argtypes = [ctypes.c_int]
     lib.msda_oracle_level_start_index.restype = ctypes.c_int64
     lib.msda_oracle_level_start_index.argtypes = [ctypes.c_int, _i64p, _i64p]
     lib.msda_oracle_reference_points_encoder.restype = None
@@ -81,6 +83,19 @@ def _bind(lib):
                                          ctypes.c_int, ctypes.c_int, _i64p, _i64p, _f64p, _f64p, _f64p, _f64p,
                                          _f64p, _f64p, _f64p]
     return lib
+
+
+@contextlib.contextmanager
+def threads(n):
+    """Run the forward and backward on n host threads inside the block
+    (results are bit-identical to one thread's: each output element is
+    computed by one thread in the serial order)."""
+    lib = _load()
+    lib.msda_oracle_set_threads(int(n))
+    try:
+        yield
+    finally:
+        lib.msda_oracle_set_threads(1)
 
 
 def _f64(x):

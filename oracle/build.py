@@ -13,7 +13,9 @@ LIB = os.path.join(HERE, "libmsda_oracle.so")
 
 def build(verbose: bool = False) -> str:
     # No fast-math and no FMA contraction: every operation rounds as written.
-    cmd = ["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-ffp-contract=off",
+    # OpenMP only splits whole queries / (image, head) pairs over threads
+    # (serial unless msda_oracle_set_threads asks for more).
+    cmd = ["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-ffp-contract=off", "-fopenmp",
            "-fno-fast-math", "-Wall", "-Wextra", "-o", LIB + ".tmp", SRC, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)

@@ -9,7 +9,12 @@
  * The operation has a plain definition (a sum of bilinear samples weighted by
  * attention weights), so the oracle is that definition written out in nested
  * loops in the order the pages state it, with no blocking, fusion or
- * reordering. Single-threaded on purpose.
+ * reordering. It runs on one thread unless msda_oracle_set_threads asks for
+ * more (the host-core baseline does): the forward then splits its queries
+ * over threads, and the backward its (image, head) pairs, whose grad_value
+ * slices are disjoint. Every output element is then still computed by one
+ * thread with the same operations in the same order, so the results are
+ * bit-identical for every thread count.
  *
  * Citations (page title, section):
  *   [P1] juhe.plus notes on a pure-PyTorch Deformable-DETR debug build,
@@ -38,6 +43,11 @@
 
 #include <math.h>
 #include <string.h>
+
+/* Threads of the forward and backward loops (OpenMP; 1 = serial). */
+static int g_threads = 1;
+
+void msda_oracle_set_threads(int n) { g_threads = n > 0 ? n : 1; }
 
 int64_t msda_oracle_level_start_index(int L, const int64_t *shapes, int64_t *lsi_out)
 {
@@ -292,6 +302,7 @@ void msda_oracle_forward(int B, int64_t S, int64_t Nq, int M, int D, int L, int 
                          const int64_t *query_ids, int64_t n_ids, double *out)
 {
     if (query_ids) {
+#pragma omp parallel for schedule(dynamic, 64) num_threads(g_threads)
         for (int64_t i = 0; i < n_ids; ++i) {
             const int b = (int)(query_ids[i] / Nq);
             const int64_t q = query_ids[i] % Nq;
@@ -300,10 +311,10 @@ void msda_oracle_forward(int B, int64_t S, int64_t Nq, int M, int D, int L, int 
         }
         return;
     }
-    for (int b = 0; b < B; ++b)
-        for (int64_t q = 0; q < Nq; ++q)
-            forward_one_query(b, q, S, Nq, M, D, L, K, shapes, lsi, value, loc, attn,
-                              out + (b * Nq + q) * (int64_t)M * D);
+#pragma omp parallel for schedule(dynamic, 64) num_threads(g_threads)
+    for (int64_t bq = 0; bq < (int64_t)B * Nq; ++bq)
+        forward_one_query((int)(bq / Nq), bq % Nq, S, Nq, M, D, L, K, shapes, lsi, value, loc, attn,
+                          out + bq * (int64_t)M * D);
 }
 
 /* Exact derivative of the forward. With x = lx*W - 0.5 and
@@ -313,6 +324,57 @@ void msda_oracle_forward(int B, int64_t S, int64_t Nq, int M, int D, int L, int 
  *   d out_d / d lx   = a * W * sum_c (d w_c / d fx) v_c[d]
  *   d out_d / d ly   = a * H * sum_c (d w_c / d fy) v_c[d]
  * with d w_c/d fx = (dx ? 1 : -1) * (dy ? fy : 1-fy) and likewise for fy. */
+/* One (image b, head m) of the backward: every query's samples of head m, in
+ * query order. The grad_value slice [b, :, m, :] receives contributions from
+ * this pair only, and in the same order as from a loop over b, q, m. */
+static void backward_one_head(int b, int m, int64_t S, int64_t Nq, int M, int D, int L, int K,
+                              const int64_t *shapes, const int64_t *lsi,
+                              const double *value, const double *loc, const double *attn,
+                              const double *grad_out, double *grad_value,
+                              double *grad_loc, double *grad_attn)
+{
+    for (int64_t q = 0; q < Nq; ++q) {
+        const double *g = grad_out + ((b * Nq + q) * M + m) * D;
+        for (int l = 0; l < L; ++l) {
+            const int64_t H = shapes[2 * l + 0];
+            const int64_t W = shapes[2 * l + 1];
+            for (int k = 0; k < K; ++k) {
+                const int64_t sidx = (((b * Nq + q) * M + m) * L + l) * K + k;
+                const double a = attn[sidx];
+                double ga = 0.0, glx = 0.0, gly = 0.0;
+                int64_t x0, y0;
+                double fx, fy;
+                if (sample_cell(loc[2 * sidx], loc[2 * sidx + 1], H, W, &x0, &y0, &fx, &fy)) {
+                    for (int dy = 0; dy < 2; ++dy) {
+                        for (int dx = 0; dx < 2; ++dx) {
+                            const int64_t xi = x0 + dx, yi = y0 + dy;
+                            if (!inside(xi, yi, H, W)) continue;
+                            const double wx = dx ? fx : 1.0 - fx;
+                            const double wy = dy ? fy : 1.0 - fy;
+                            const double dwx = dx ? 1.0 : -1.0; /* d wx / d fx */
+                            const double dwy = dy ? 1.0 : -1.0; /* d wy / d fy */
+                            const int64_t s = lsi[l] + yi * W + xi;
+                            const double *v = value + ((b * S + s) * M + m) * D;
+                            double *gv = grad_value + ((b * S + s) * M + m) * D;
+                            double gdotv = 0.0;
+                            for (int d = 0; d < D; ++d) {
+                                gdotv += g[d] * v[d];
+                                gv[d] += a * wx * wy * g[d];
+                            }
+                            ga += wx * wy * gdotv;
+                            glx += dwx * wy * gdotv;
+                            gly += wx * dwy * gdotv;
+                        }
+                    }
+                }
+                grad_attn[sidx] = ga;
+                grad_loc[2 * sidx + 0] = a * (double)W * glx;
+                grad_loc[2 * sidx + 1] = a * (double)H * gly;
+            }
+        }
+    }
+}
+
 void msda_oracle_backward(int B, int64_t S, int64_t Nq, int M, int D, int L, int K,
                           const int64_t *shapes, const int64_t *lsi,
                           const double *value, const double *loc, const double *attn,
@@ -320,49 +382,9 @@ void msda_oracle_backward(int B, int64_t S, int64_t Nq, int M, int D, int L, int
                           double *grad_loc, double *grad_attn)
 {
     memset(grad_value, 0, sizeof(double) * (size_t)B * (size_t)S * (size_t)M * (size_t)D);
-    for (int b = 0; b < B; ++b) {
-        for (int64_t q = 0; q < Nq; ++q) {
-            for (int m = 0; m < M; ++m) {
-                const double *g = grad_out + ((b * Nq + q) * M + m) * D;
-                for (int l = 0; l < L; ++l) {
-                    const int64_t H = shapes[2 * l + 0];
-                    const int64_t W = shapes[2 * l + 1];
-                    for (int k = 0; k < K; ++k) {
-                        const int64_t sidx = (((b * Nq + q) * M + m) * L + l) * K + k;
-                        const double a = attn[sidx];
-                        double ga = 0.0, glx = 0.0, gly = 0.0;
-                        int64_t x0, y0;
-                        double fx, fy;
-                        if (sample_cell(loc[2 * sidx], loc[2 * sidx + 1], H, W, &x0, &y0,
-                                        &fx, &fy)) {
-                            for (int dy = 0; dy < 2; ++dy) {
-                                for (int dx = 0; dx < 2; ++dx) {
-                                    const int64_t xi = x0 + dx, yi = y0 + dy;
-                                    if (!inside(xi, yi, H, W)) continue;
-                                    const double wx = dx ? fx : 1.0 - fx;
-                                    const double wy = dy ? fy : 1.0 - fy;
-                                    const double dwx = dx ? 1.0 : -1.0; /* d wx / d fx */
-                                    const double dwy = dy ? 1.0 : -1.0; /* d wy / d fy */
-                                    const int64_t s = lsi[l] + yi * W + xi;
-                                    const double *v = value + ((b * S + s) * M + m) * D;
-                                    double *gv = grad_value + ((b * S + s) * M + m) * D;
-                                    double gdotv = 0.0;
-                                    for (int d = 0; d < D; ++d) {
-                                        gdotv += g[d] * v[d];
-                                        gv[d] += a * wx * wy * g[d];
-                                    }
-                                    ga += wx * wy * gdotv;
-                                    glx += dwx * wy * gdotv;
-                                    gly += wx * dwy * gdotv;
-                                }
-                            }
-                        }
-                        grad_attn[sidx] = ga;
-                        grad_loc[2 * sidx + 0] = a * (double)W * glx;
-                        grad_loc[2 * sidx + 1] = a * (double)H * gly;
-                    }
-                }
-            }
-        }
-    }
+#pragma omp parallel for collapse(2) schedule(dynamic, 1) num_threads(g_threads)
+    for (int b = 0; b < B; ++b)
+        for (int m = 0; m < M; ++m)
+            backward_one_head(b, m, S, Nq, M, D, L, K, shapes, lsi, value, loc, attn, grad_out,
+                              grad_value, grad_loc, grad_attn);
 }

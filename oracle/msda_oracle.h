@@ -78,6 +78,11 @@ void msda_oracle_sampling_locations_backward(int B, int64_t Nq, int M, int L, in
                                              const int64_t *shapes, const double *grad_loc,
                                              double *grad_ref, double *grad_offset_px);
 
+/* Threads of msda_oracle_forward and msda_oracle_backward (default 1). The
+ * results are bit-identical for every count: each output element is computed
+ * by one thread in the serial order. */
+void msda_oracle_set_threads(int n);
+
 /* Forward ([P4] "Insight 2" equation, bracketed sum; [P2] "encoder" core:
  * bilinear sampling, zero padding, align_corners=False):
  * out[b,q,m*D+d] = sum_{l,k} A[b,q,m,l,k] * bilinear(value_l[b,:,:,m,d], loc).

@@ -55,8 +55,12 @@ MUTANTS = [
     ("align_corners_true", "lx * (double)W - 0.5", "lx * (double)(W - 1)", _forward_pins),
     ("transposed_row_index", "lsi[l] + yi * W + xi;\n                        const double *v",
      "lsi[l] + xi * H + yi;\n                        const double *v", _forward_pins),
-    ("h_w_swapped", "const int64_t H = shapes[2 * l + 0];\n            const int64_t W = shapes[2 * l + 1];\n            for (int k",
-     "const int64_t H = shapes[2 * l + 1];\n            const int64_t W = shapes[2 * l + 0];\n            for (int k", _forward_pins),
+    ("h_w_swapped", "const int64_t H = shapes[2 * l + 0];\n            const int64_t W = shapes[2 * l + 1];\n"
+     "            for (int k = 0; k < K; ++k) {\n                const int64_t sidx = (((b * Nq + q) * M + m) * L + l) * K + k;\n"
+     "                const double a = attn[sidx];\n                int64_t x0",
+     "const int64_t H = shapes[2 * l + 1];\n            const int64_t W = shapes[2 * l + 0];\n"
+     "            for (int k = 0; k < K; ++k) {\n                const int64_t sidx = (((b * Nq + q) * M + m) * L + l) * K + k;\n"
+     "                const double a = attn[sidx];\n                int64_t x0", _forward_pins),
     ("edge_corner_kept", "return xi >= 0 && xi < W", "return xi >= 0 && xi <= W", _forward_pins),
     ("dropped_attention_weight", "acc[d] += a * w * v[d]", "acc[d] += w * v[d]", _forward_pins),
     ("wrong_grad_sign", "const double dwx = dx ? 1.0 : -1.0;", "const double dwx = dx ? -1.0 : 1.0;", _backward_pins),
