@@ -9,19 +9,23 @@ every kernel from libmsda.so, inputs
 (seeded synthetic draws) resident in HBM before the timed region.
 
 Prints ONE JSON line. ``value`` is queries/s of that fwd+bwd step (a HIP graph
-of the step replayed K times). ``kernels`` gives every GPU kernel's average
+of the step replayed K times back to back: warm, the step's ~100 MB stay in
+the 256 MB Infinity Cache). ``kernels`` gives every GPU kernel's average
 duration, timed live with HIP event pairs that the library records around each
 launch on the launch's own stream (msda_timing_*), and its algorithmic bytes
-per launch; ``roofline`` is for the kernel with the largest share of the step.
-``cpu_baseline`` is the fp64 oracle on the host.
+per launch; ``roofline`` is for the kernel with the largest share of the step
+(warm event timing). ``cold`` times every entry point again with L2 and the
+Infinity Cache evicted before each call (a 1 GiB read in between), and
+``copy_ceiling`` is a plain device copy's rate, beside the 8 TB/s peak.
+``cpu_baseline`` is the fp64 oracle on the host's cores (and on one core).
 
     python bench.py [--steps K] [--warmup W] [--workload encoder_backward]
 
-Counter runs for the HBM traffic of the kernels (rocprofv3 --pmc, one counter
-per run) use ``--eager``; ``--copy-mib N`` runs only a plain elementwise copy
-of N MiB (the calibration kernel for FETCH_SIZE / WRITE_SIZE), and
-``--ingest-counters DIR [--copy-mib N]`` turns the four counter runs under DIR
-(fetch/, write/, copy_fetch/, copy_write/) into profiles/traffic.json.
+Counter runs (rocprofv3 --pmc, one pass of COUNTER_PASSES per run) use
+``--eager --profile-run``; ``--copy-mib N`` runs only a plain elementwise copy
+of N MiB (a check of the byte counting: it must read and write N MiB), and
+``--ingest-counters DIR`` turns the passes under DIR/<pass> into
+profiles/traffic.json and profiles/counters_encoder_step.md.
 """
 import argparse
 import csv
@@ -29,6 +33,7 @@ import glob
 import hashlib
 import json
 import os
+import platform
 import re
 import sys
 import time
@@ -39,7 +44,24 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD's published peak
 METRIC = "MSDeformAttn fwd/bwd queries/s and effective HBM GB/s (% of peak), encoder shape"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-COPY_MIB_DEFAULT = 256
+COUNTERS_MD = os.path.join(ROOT, "profiles", "counters_encoder_step.md")
+FLUSH_BYTES = 1 << 30   # read between cold calls: 4x the 256 MB Infinity Cache, 32x all L2
+
+# rocprofv3 --pmc passes read by --ingest-counters, one run each on
+# `bench.py --eager --profile-run` (rocprofv3 does not split counters over
+# runs: at most 8 SQ, 4 TCC, 4 TCP, 2 TA, 2 TD and 2 GRBM counters per pass).
+COUNTER_PASSES = {
+    # L2 -> fabric reads by request size (exact bytes) and writes (64 B or 32 B)
+    "tcc_read": ["TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum", "TCC_EA0_RDREQ_128B_sum"],
+    "tcc_write_hit": ["TCC_HIT_sum", "TCC_MISS_sum", "TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum"],
+    "sq_time": ["SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_INST_ANY", "SQ_WAIT_ANY",
+                "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_VMEM", "SQ_ACTIVE_INST_LDS"],
+    "sq_insts": ["SQ_INSTS_VALU", "SQ_INSTS_VMEM_RD", "SQ_INSTS_VMEM_WR", "SQ_INSTS_LDS", "SQ_INSTS_SALU",
+                 "SQ_LDS_BANK_CONFLICT", "SQ_INSTS_LDS_ATOMIC", "SQ_ACTIVE_INST_ANY"],
+    "units": ["TA_TA_BUSY_sum", "TA_ADDR_STALLED_BY_TC_CYCLES_sum", "TD_TC_STALL_sum", "TD_TD_BUSY_sum",
+              "TCP_TOTAL_CACHE_ACCESSES_sum", "TCP_TCC_READ_REQ_sum", "TCP_TCC_ATOMIC_WITHOUT_RET_REQ_sum",
+              "TCP_TCC_ATOMIC_WITH_RET_REQ_sum", "GRBM_GUI_ACTIVE", "GRBM_COUNT"],
+}
 
 
 def parse():
@@ -55,10 +77,15 @@ def parse():
     p.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP graph replay")
     p.add_argument("--no-extra-configs", action="store_true",
                    help="skip the decoder and large-batch bf16 forward timings")
+    p.add_argument("--profile-run", action="store_true",
+                   help="only the plain step, eager, for counter passes (no fused steps, timing loops or extras)")
+    p.add_argument("--cold-iters", type=int, default=20,
+                   help="calls per entry point in the cold-cache timing (0 skips it)")
     p.add_argument("--copy-mib", type=int, default=0,
-                   help="only run a plain copy of this many MiB, 5 times (counter calibration)")
+                   help="only run a plain copy of this many MiB, 5 times (a check of the counters' byte counts)")
     p.add_argument("--ingest-counters", default=None, metavar="DIR",
-                   help="write profiles/traffic.json from rocprofv3 --pmc runs under DIR and exit")
+                   help="write profiles/traffic.json and the counter summary from rocprofv3 --pmc passes under "
+                        "DIR/<pass> and exit")
     return p.parse_args()
 
 
@@ -167,16 +194,14 @@ def measured_traffic(kernel):
     return None if e is None else e.get("hbm_bytes_per_launch")
 
 
-def _counter_rows(d, counter):
-    """(kernel name, value in KiB) per dispatch from a rocprofv3 csv run."""
-    out = []
+def _counter_rows(d):
+    """{(kernel name, counter): [values per dispatch]} from rocprofv3 csv runs under d."""
+    out = {}
     for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
         with open(path, newline="") as f:
             for r in csv.DictReader(f):
-                if r.get("Counter_Name") == counter:
-                    out.append((r["Kernel_Name"], float(r["Counter_Value"])))
-    if not out:
-        raise SystemExit(f"no {counter} rows under {d}")
+                key = (_short_kernel_name(r["Kernel_Name"]), r["Counter_Name"])
+                out.setdefault(key, []).append(float(r["Counter_Value"]))
     return out
 
 
@@ -197,44 +222,103 @@ def _short_kernel_name(full):
     return name
 
 
-def ingest_counters(d, copy_mib, workload):
-    """profiles/traffic.json from four rocprofv3 --pmc runs (csv output):
-    d/fetch and d/write of `bench.py --eager`, d/copy_fetch and d/copy_write
-    of `bench.py --copy-mib N`. Each kernel's per-dispatch KiB is averaged and
-    scaled by the copy kernel's known bytes over its counter reading."""
-    copy_kib = copy_mib * 1024.0
-
-    def copy_avg(sub, counter):
-        vals = [v for n, v in _counter_rows(os.path.join(d, sub), counter) if "vectorized_elementwise_kernel" in n]
-        return sum(vals) / len(vals)
-
-    fetch_scale = copy_kib / copy_avg("copy_fetch", "FETCH_SIZE")
-    write_scale = copy_kib / copy_avg("copy_write", "WRITE_SIZE")
-    names = list(algorithmic_bytes(1, 1, 1, 1, [(1, 1)], 1, 0))
-    kernels = {}
-    for counter, sub in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
-        for full, v in _counter_rows(os.path.join(d, sub), counter):
-            short = _short_kernel_name(full)
-            if short not in names:
-                continue
-            e = kernels.setdefault(short, {"FETCH_SIZE": [], "WRITE_SIZE": []})
-            e[counter].append(v)
+def ingest_counters(d, workload):
+    """profiles/traffic.json and profiles/counters_encoder_step.md from the
+    COUNTER_PASSES runs under d/<pass> (csv output of rocprofv3 --pmc on
+    `bench.py --eager --profile-run`). Per kernel the counters are averaged
+    over its dispatches. L2 -> fabric bytes are exact: reads are counted by
+    request size (32, 64 and 128 B) and writes as 64 B or 32 B requests.
+    These bytes include what the 256 MB Infinity Cache (memory-side) serves,
+    so they bound the DRAM bytes from above."""
+    rows = {}
+    hashes = set()
+    for name in COUNTER_PASSES:
+        sub = os.path.join(d, name)
+        if not os.path.isdir(sub):
+            raise SystemExit(f"missing counter pass {sub}")
+        rows.update(_counter_rows(sub))
+        # the profiled run's own line names the kernel sources it ran on
+        for log in glob.glob(os.path.join(sub, "*.log")):
+            for ln in open(log):
+                if ln.startswith("{") and "profile_run" in ln:
+                    hashes.add(json.loads(ln)["source_hash"])
+    if len(hashes) != 1:
+        raise SystemExit(f"the passes under {d} do not name one kernel-source hash: {sorted(hashes)}")
+    source_hash = hashes.pop()
+    names = sorted({k for k, _ in rows})
+    w = __import__("scale_deformable_attention_msdeformattn_amd.workloads", fromlist=["WORKLOADS"]).WORKLOADS[workload]
+    shapes = [tuple(hw) for hw in w.spatial_shapes]
+    # every value row is touched at this workload (the bench line's unique-bytes count says 100%)
+    vbytes = w.batch * w.num_value * w.heads * w.channels * 4
+    alg = algorithmic_bytes(w.batch, w.heads, w.channels, w.nq, shapes, w.points, vbytes)
     table = {}
-    for k, e in kernels.items():
-        if not e["FETCH_SIZE"] or not e["WRITE_SIZE"]:
+    for k in names:
+        c = {cn: sum(v) / len(v) for (kn, cn), v in rows.items() if kn == k}
+        if "TCC_EA0_RDREQ_sum" not in c or "TCC_EA0_WRREQ_sum" not in c:
             continue
-        fk = sum(e["FETCH_SIZE"]) / len(e["FETCH_SIZE"])
-        wk = sum(e["WRITE_SIZE"]) / len(e["WRITE_SIZE"])
-        table[k] = {"fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
-                    "hbm_bytes_per_launch": int(round((fk * fetch_scale + wk * write_scale) * 1024)),
-                    "dispatches": len(e["FETCH_SIZE"])}
-    out = {"source_hash": kernel_source_hash(), "workload": workload,
-           "calibration": {"kernel": "torch elementwise copy (mul by 1) fp32", "copy_mib": copy_mib,
-                           "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4)},
+        n32, n64, n128 = (c.get(f"TCC_EA0_RDREQ_{b}B_sum", 0.0) for b in (32, 64, 128))
+        rd = 32 * n32 + 64 * n64 + 128 * n128
+        wr = 64 * c["TCC_EA0_WRREQ_64B_sum"] + 32 * (c["TCC_EA0_WRREQ_sum"] - c["TCC_EA0_WRREQ_64B_sum"])
+        hit, miss = c.get("TCC_HIT_sum", 0.0), c.get("TCC_MISS_sum", 0.0)
+        e = {"dispatches": len(rows[(k, "TCC_EA0_RDREQ_sum")]),
+             "read_bytes": int(round(rd)), "write_bytes": int(round(wr)),
+             "hbm_bytes_per_launch": int(round(rd + wr)),
+             "read_requests_other_sizes": int(round(c["TCC_EA0_RDREQ_sum"] - n32 - n64 - n128)),
+             "l2_hit_rate": round(hit / (hit + miss), 4) if hit + miss else None}
+        if k in alg and alg[k]:
+            e["algorithmic_bytes"] = alg[k]
+            e["hbm_over_algorithmic"] = round((rd + wr) / alg[k], 3)
+        for cn in ("SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_VMEM_RD", "SQ_INSTS_VMEM_WR", "SQ_INSTS_LDS",
+                   "SQ_INSTS_SALU", "SQ_LDS_BANK_CONFLICT", "SQ_INSTS_LDS_ATOMIC", "TCP_TCC_ATOMIC_WITHOUT_RET_REQ_sum",
+                   "TCP_TCC_ATOMIC_WITH_RET_REQ_sum", "GRBM_GUI_ACTIVE"):
+            if cn in c:
+                e[cn] = int(round(c[cn]))
+        if c.get("SQ_WAVE_CYCLES"):
+            e["wait_inst_share"] = round(c["SQ_WAIT_INST_ANY"] / c["SQ_WAVE_CYCLES"], 3)
+            e["wait_any_share"] = round(c["SQ_WAIT_ANY"] / c["SQ_WAVE_CYCLES"], 3)
+        if c.get("GRBM_GUI_ACTIVE"):
+            # GRBM_GUI_ACTIVE sums the 8 XCDs' busy cycles; SQ_INSTS_VALU counts
+            # wave instructions, each 4 cycles of a 16-lane SIMD (1024 SIMDs)
+            busy = c["GRBM_GUI_ACTIVE"] / 8
+            e["valu_share_of_busy"] = round(c.get("SQ_INSTS_VALU", 0.0) * 4 / 1024 / busy, 3)
+            e["ta_busy_share"] = round(c.get("TA_TA_BUSY_sum", 0.0) / (256 * busy), 3)
+        table[k] = e
+    out = {"source_hash": source_hash, "workload": workload,
+           "command": "rocprofv3 --pmc <pass counters> --output-format csv -d DIR/<pass> -o run -- "
+                      "python3 bench.py --eager --profile-run --steps 3 --warmup 1 > DIR/<pass>/bench.log",
+           "passes": COUNTER_PASSES,
+           "bytes": "L2 -> fabric (Infinity Cache included): reads by request size, writes 64 B or 32 B",
            "kernels": table}
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(out, f, indent=1)
+    _counter_summary(out)
     print(json.dumps(out))
+
+
+def _counter_summary(t):
+    lines = [f"# Counters per kernel — {t['workload']} step (plain path), one MI355X", "",
+             "Generated by `python bench.py --ingest-counters DIR` from the rocprofv3 passes below, each run as",
+             "", "```", "cd /tmp && export TMPDIR=/tmp",
+             "rocprofv3 --pmc <counters of the pass> --output-format csv -d <repo>/gpurun_out/pmc/<pass> -o run \\",
+             "    -- python3 <repo>/bench.py --eager --profile-run --steps 3 --warmup 1 \\",
+             "    > <repo>/gpurun_out/pmc/<pass>/bench.log", "```", ""]
+    for k, v in t["passes"].items():
+        lines.append(f"- `{k}`: {', '.join(v)}")
+    lines += ["", f"Kernel sources hash `{t['source_hash']}`. Bytes are L2 -> fabric traffic, exact by request "
+              "size; the Infinity Cache serves part of it, so DRAM bytes are at most these.", "",
+              "| kernel | disp. | read MB | write MB | / algorithmic | L2 hit | VALU share of busy | TA busy | "
+              "wait (inst) | LDS bank conflicts / LDS inst |",
+              "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    for k, e in sorted(t["kernels"].items(), key=lambda kv: -kv[1]["hbm_bytes_per_launch"]):
+        conf = "" if not e.get("SQ_INSTS_LDS") else f"{e.get('SQ_LDS_BANK_CONFLICT', 0) / e['SQ_INSTS_LDS']:.2f}"
+        hit = "" if e["l2_hit_rate"] is None else f"{100 * e['l2_hit_rate']:.1f}%"
+        ratio = f"{e['hbm_over_algorithmic']:.2f}x" if "hbm_over_algorithmic" in e else ""
+        lines.append(
+            f"| `{k}` | {e['dispatches']} | {e['read_bytes'] / 1e6:.1f} | {e['write_bytes'] / 1e6:.1f} | {ratio} | "
+            f"{hit} | {e.get('valu_share_of_busy', float('nan')):.2f} | {e.get('ta_busy_share', float('nan')):.2f} | "
+            f"{e.get('wait_inst_share', float('nan')):.2f} | {conf} |")
+    with open(COUNTERS_MD, "w") as f:
+        f.write("\n".join(lines) + "\n")
 
 
 def copy_calibration(mib):
@@ -292,10 +376,34 @@ def encoder_stack(msda, shapes, lsi, vr, B, S, M, L, K, dev, args, n_layers=6):
                     "GEMMs (fp32), layer norms and elementwise ops"}
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def host_threads():
+    """Host threads for the oracle baseline: the cores this process may run
+    on, at most 16 (one GPU's share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def cpu_baseline(wl_name, min_seconds=10.0):
-    """The fp64 oracle, as it stands (single-threaded C), on the same step:
-    reference points, locations, softmax, forward and backward of the whole
-    workload once."""
+    """The fp64 oracle, as it stands, on the same step (reference points,
+    locations, softmax, forward and backward of the whole workload): whole
+    passes until min_seconds of wall time, once on all the host threads
+    (the forward split over queries, the backward over (image, head) pairs,
+    results bit-identical to one thread) and once on one thread."""
     import oracle
     from scale_deformable_attention_msdeformattn_amd import workloads
     d = workloads.draw(wl_name, 0)
@@ -304,23 +412,86 @@ def cpu_baseline(wl_name, min_seconds=10.0):
     # host-side input upcasts are not timed
     vr, off, logits, G, value = (oracle._f64(x) for x in (d.valid_ratios, d.offsets_px, d.logits,
                                                           d.grad_output, d.value))
-    passes = 0
-    t0 = time.perf_counter()
-    while True:  # whole passes until at least min_seconds of CPU work
-        lsi, _ = oracle.level_start_index(shapes)
-        ref = oracle.reference_points_encoder(shapes, vr)
-        loc = oracle.sampling_locations(shapes, ref, off)
-        A = oracle.softmax(logits, w.levels * w.points).reshape(w.batch, w.nq, w.heads, w.levels, w.points)
-        oracle.forward(value, shapes, lsi, loc, A)
-        oracle.backward(value, shapes, lsi, loc, A, G)
-        passes += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds:
-            break
+
+    def run(threads):
+        passes = 0
+        with oracle.threads(threads):
+            t0 = time.perf_counter()
+            while True:
+                lsi, _ = oracle.level_start_index(shapes)
+                ref = oracle.reference_points_encoder(shapes, vr)
+                loc = oracle.sampling_locations(shapes, ref, off)
+                A = oracle.softmax(logits, w.levels * w.points).reshape(w.batch, w.nq, w.heads, w.levels,
+                                                                        w.points)
+                oracle.forward(value, shapes, lsi, loc, A)
+                oracle.backward(value, shapes, lsi, loc, A, G)
+                passes += 1
+                dt = time.perf_counter() - t0
+                if dt >= min_seconds:
+                    return passes, dt
+
     q = w.batch * w.nq
-    return {"value": passes * q / dt, "unit": "queries/s", "cores": 1, "kind": "oracle",
-            "sample": f"{passes} whole passes of the {w.name} workload ({q} queries each: reference points, "
-                      f"locations, softmax, forward, backward), single-threaded fp64 C, {dt:.2f} s"}
+    n = host_threads()
+    p_all, t_all = run(n)
+    p_one, t_one = run(1)
+    return {"value": p_all * q / t_all, "unit": "queries/s", "cores": n, "kind": "oracle",
+            "sample": f"{p_all} whole passes of the {w.name} workload ({q} queries each: reference points, "
+                      f"locations, softmax, forward, backward), fp64 C on {n} threads, {t_all:.2f} s",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "single_core": {"value": p_one * q / t_one, "unit": "queries/s", "cores": 1,
+                            "sample": f"{p_one} whole passes on one thread, {t_one:.2f} s"}}
+
+
+def copy_ceiling(dev, nbytes=FLUSH_BYTES, reps=10):
+    """A plain device copy of nbytes (torch's copy kernel) timed with events:
+    (read + write bytes) / time, the rate a streaming kernel reaches here."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    s = e0.elapsed_time(e1) * 1e-3 / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"gbps": round(2 * nbytes / s / 1e9, 1), "bytes_copied": nbytes, "kernel": "torch copy_ (fp32)",
+            "frac_of_8tbps": round(2 * nbytes / s / 1e9 / HBM_PEAK_GBPS, 4)}
+
+
+def cold_timing(msda, calls, dev, iters):
+    """Every entry point of the step timed with L2 and the 256 MB Infinity
+    Cache evicted before it: a 1 GiB read (a reduction over a buffer that no
+    call touches) runs between the calls, outside the timed pairs. Returns the
+    library's per-kernel event timing and per-call event timing, averaged."""
+    import torch
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    per_call = {name: 0.0 for name, _ in calls}
+    torch.cuda.synchronize()
+    msda.msda_timing_reset()
+    for _ in range(iters):
+        for name, f in calls:
+            torch.sum(flush, dim=0, out=sink)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            msda.msda_timing_enable(True)
+            e0.record(stream)
+            f()
+            e1.record(stream)
+            msda.msda_timing_enable(False)
+            e1.synchronize()
+            per_call[name] += e0.elapsed_time(e1) * 1e3 / iters
+    timing = msda.msda_timing_read()
+    msda.msda_timing_reset()
+    del flush
+    torch.cuda.empty_cache()
+    return {k: ms * 1e3 / n for k, (ms, n) in timing.items()}, per_call
 
 
 def forward_configs(msda, workloads, dev, args, names=("decoder", "encoder_bf16_large")):
@@ -378,7 +549,7 @@ def main():
               "single GPU (the op shards by batch or by head with no exchange between GPUs)", file=sys.stderr)
         sys.exit(2)
     if args.ingest_counters:
-        ingest_counters(args.ingest_counters, args.copy_mib or COPY_MIB_DEFAULT, args.workload)
+        ingest_counters(args.ingest_counters, args.workload)
         return
     if args.copy_mib:
         copy_calibration(args.copy_mib)
@@ -454,6 +625,13 @@ def main():
     for _ in range(max(1, args.warmup)):
         step()
     torch.cuda.synchronize()
+    if args.profile_run:  # counter passes: the plain step's kernels only, eager
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_run": w.name, "steps": args.steps, "source_hash": kernel_source_hash()}),
+              flush=True)
+        return
 
     vbytes, corner_reads = unique_value_bytes(state["loc"], shapes.to(dev), B, M, D * elem)
     alg = algorithmic_bytes(B, M, D, Nq, [tuple(int(v) for v in hw) for hw in shapes.tolist()], K, vbytes)
@@ -567,6 +745,21 @@ def main():
     timing_fused = msda.msda_timing_read()
     msda.msda_timing_reset()
 
+    # ---- timed region 4: every entry point again with the caches evicted
+    # before each call (cold), and a plain copy's rate ----
+    cold = None
+    if args.cold_iters > 0:
+        cold_kernels, cold_calls = cold_timing(msda, calls, dev, args.cold_iters)
+        cold = {"protocol": f"{args.cold_iters} calls per entry point; before each, a 1 GiB read (4x the 256 MB "
+                            "Infinity Cache) outside the timed pairs, so every input starts in HBM",
+                "entry_points_us": {k: round(v, 3) for k, v in cold_calls.items()},
+                "step_us_sum": round(sum(cold_calls.values()), 3),
+                "kernels": {k: {"avg_us": round(us, 3), **({} if k not in alg else {
+                    "gbps": round(alg[k] / (us * 1e-6) / 1e9, 1),
+                    "frac_of_hbm_peak": round(alg[k] / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)})}
+                            for k, us in cold_kernels.items()}}
+    copy = copy_ceiling(dev)
+
     kstats = {}
     for name, (ms, n) in timing.items():
         us = ms * 1e3 / n
@@ -601,12 +794,23 @@ def main():
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic(dominant), "avg_us": dom_us,
-                     "algorithmic_bytes": alg[dominant]},
+                     "algorithmic_bytes": alg[dominant],
+                     "timing": "warm: library event pairs around each launch over back-to-back eager steps",
+                     "cold_frac": None if cold is None or dominant not in cold["kernels"]
+                     else cold["kernels"][dominant].get("frac_of_hbm_peak"),
+                     "frac_of_copy_ceiling": round(dom_gbps / copy["gbps"], 4)},
         "kernels": kstats,
         "entry_points_us": {k: round(v, 3) for k, v in per_call.items()},
+        "cold": cold,
+        "copy_ceiling": copy,
         "eager_ms_per_step": eager_step_ms,
         "forward": {"kernel": fwd_name, "queries_per_s": queries / (fwd["avg_us"] * 1e-6) if fwd else None,
                     "effective_gbps": fwd.get("gbps"), "frac_of_hbm_peak": fwd.get("frac_of_hbm_peak"),
+                    "cold": None if cold is None or fwd_name not in cold["kernels"] else {
+                        "avg_us": cold["kernels"][fwd_name]["avg_us"],
+                        "queries_per_s": queries / (cold["kernels"][fwd_name]["avg_us"] * 1e-6),
+                        "effective_gbps": cold["kernels"][fwd_name].get("gbps"),
+                        "frac_of_hbm_peak": cold["kernels"][fwd_name].get("frac_of_hbm_peak")},
                     "traffic": measured_traffic(fwd_name) if fwd_name else None,
                     "gather": None if not fwd else {
                         "corner_reads": corner_reads, "bytes": corner_reads * D * elem,
@@ -615,6 +819,8 @@ def main():
                                 "L1/L2 (we measured 50-58 B/clk/CU for 16-byte lane gathers on that path, 31-36 TB/s "
                                 "on 256 CUs at 2.4 GHz), the coarse levels' from LDS when they are staged"}},
         "backward": {"queries_per_s": queries / (per_call["msda_backward"] * 1e-6),
+                     "cold_queries_per_s": None if cold is None else
+                     queries / (cold["entry_points_us"]["msda_backward"] * 1e-6),
                      "note": "the whole msda_backward call, all its kernels",
                      "main_kernel_gather": None if "backward_c256_kernel" not in kstats else {
                          "corner_reads": corner_reads, "bytes": corner_reads * D * elem,

@@ -57,7 +57,7 @@ extern "C" {
 #define MSDA_API
 #endif
 
-#define MSDA_ABI_VERSION 8
+#define MSDA_ABI_VERSION 9
 #define MSDA_MAX_LEVELS 16
 
 typedef enum {
@@ -202,6 +202,11 @@ MSDA_API int msda_backward(const msda_shape *shape, const void *value, msda_dtyp
  *  reference_points        [B,Nq,L,reference_dims] fp32, normalised
  *  sampling_offsets        [B,Nq,M,L,K,2] fp32 (x, y)
  *  attention_logits        [B,Nq,M,L*K]   fp32
+ *  key_padding_mask        [B,S] bytes, nonzero = padded position, or NULL:
+ *                          the value rows of padded positions read as zero
+ *                          (the module fills the projected value with zeros
+ *                          there before the core: paper notes, "Key code",
+ *                          MSDeformAttn.forward; walkthrough page, "encoder")
  *  output                  [B,Nq,M*D]     fp32, fully overwritten
  *  sampling_locations_out  [B,Nq,M,L,K,2] fp32, fully overwritten (for the
  *  attention_weights_out   [B,Nq,M,L,K]   fp32   backward; never NULL)
@@ -210,8 +215,8 @@ MSDA_API int msda_backward(const msda_shape *shape, const void *value, msda_dtyp
  * MSDA_E_UNSUPPORTED; otherwise the status codes of msda_forward. */
 MSDA_API int msda_forward_fused(const msda_shape *shape, const void *value, msda_dtype value_dtype,
                                 const float *reference_points, int reference_dims, const float *sampling_offsets,
-                                const float *attention_logits, float *output, float *sampling_locations_out,
-                                float *attention_weights_out, void *stream);
+                                const float *attention_logits, const uint8_t *key_padding_mask, float *output,
+                                float *sampling_locations_out, float *attention_weights_out, void *stream);
 
 /* Backward of msda_forward_fused, given the locations and weights it wrote:
  * grad_value as msda_backward, and, by the chain rule through the two fused
@@ -224,14 +229,17 @@ MSDA_API int msda_forward_fused(const msda_shape *shape, const void *value, msda
  *                                    (w, h)  (if not NULL)
  * reference_points and sampling_offsets are read for boxes only (NULL allowed
  * for points). Shapes [B,Nq,M,L,K,2], [B,Nq,M,L*K], [B,Nq,L,reference_dims],
- * fp32, fully overwritten. Workspace, flags, stream use and status codes as
- * msda_backward. */
+ * fp32, fully overwritten. key_padding_mask: the forward's [B,S] mask or
+ * NULL; padded value rows read as zero and get zero grad_value (with
+ * MSDA_BWD_ACCUMULATE they are left as they were). Workspace, flags, stream
+ * use and status codes as msda_backward. */
 MSDA_API int msda_backward_fused(const msda_shape *shape, const void *value, msda_dtype value_dtype,
                                  const float *sampling_locations, const float *attention_weights,
                                  const float *reference_points, const float *sampling_offsets, int reference_dims,
-                                 const float *grad_output, float *grad_value, float *grad_sampling_offsets,
-                                 float *grad_attention_logits, float *grad_reference_points, void *workspace,
-                                 size_t workspace_bytes, unsigned flags, void *stream);
+                                 const uint8_t *key_padding_mask, const float *grad_output, float *grad_value,
+                                 float *grad_sampling_offsets, float *grad_attention_logits,
+                                 float *grad_reference_points, void *workspace, size_t workspace_bytes,
+                                 unsigned flags, void *stream);
 
 /* Static English name of a status code. */
 MSDA_API const char *msda_status_string(int status);

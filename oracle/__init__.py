@@ -62,6 +62,9 @@ def _bind(lib):
                                                    ctypes.c_int, _i64p, _f64p, _f64p, _f64p]
     lib.msda_oracle_softmax.restype = None
     lib.msda_oracle_softmax.argtypes = [ctypes.c_int64, ctypes.c_int, _f64p, _f64p]
+    lib.msda_oracle_masked_fill.restype = None
+    lib.msda_oracle_masked_fill.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                            ctypes.POINTER(ctypes.c_ubyte), _f64p, _f64p]
     lib.msda_oracle_softmax_backward.restype = None
     lib.msda_oracle_softmax_backward.argtypes = [ctypes.c_int64, ctypes.c_int, _f64p, _f64p, _f64p]
     lib.msda_oracle_sampling_locations_backward.restype = None
@@ -176,6 +179,27 @@ def softmax(logits, n):
     out = np.empty_like(flat)
     _load().msda_oracle_softmax(flat.shape[0], n, _p(flat, _f64p), _p(out, _f64p))
     return out.reshape(shape)
+
+
+def masked_fill(x, key_padding_mask):
+    """x [B,S,...] with the rows of the padded positions (mask [B,S] nonzero)
+    set to zero: the module's masked_fill of the value before the core, and
+    the backward of that step for a gradient of the same shape."""
+    v = _f64(x)
+    try:
+        import torch
+        if isinstance(key_padding_mask, torch.Tensor):
+            key_padding_mask = key_padding_mask.detach().cpu().numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    mask = np.ascontiguousarray(np.asarray(key_padding_mask).astype(np.uint8))
+    B, S = v.shape[:2]
+    assert mask.shape == (B, S)
+    C = int(np.prod(v.shape[2:])) if v.ndim > 2 else 1
+    out = np.empty_like(v)
+    _load().msda_oracle_masked_fill(B, S, C, mask.ctypes.data_as(ctypes.POINTER(ctypes.c_ubyte)),
+                                    _p(v, _f64p), _p(out, _f64p))
+    return out
 
 
 def softmax_backward(attn, grad_attn, n):

@@ -104,6 +104,21 @@ void msda_oracle_reference_points_decoder(int B, int64_t Nq, int L, const double
                         u[(b * Nq + q) * 2 + c] * valid_ratios[(b * L + l) * 2 + c];
 }
 
+/* [P4] "Key code" (MSDeformAttn.forward) and [P2] "encoder": where the
+ * padding mask marks a position of the flattened value sequence, the
+ * projected value is filled with zeros before sampling. The same map sends a
+ * gradient with respect to the filled value back to the unfilled one (zero at
+ * the masked positions), so it serves the backward as well. mask is [B,S]
+ * (nonzero = padded); each of the S rows holds C = M*D numbers. */
+void msda_oracle_masked_fill(int B, int64_t S, int64_t C, const unsigned char *mask, const double *x,
+                             double *out)
+{
+    for (int b = 0; b < B; ++b)
+        for (int64_t s = 0; s < S; ++s)
+            for (int64_t c = 0; c < C; ++c)
+                out[(b * S + s) * C + c] = mask[b * S + s] ? 0.0 : x[(b * S + s) * C + c];
+}
+
 /* [P2] "encoder", [P4] "Key code": offsets are predicted in pixels of level l
  * and normalised by (W_l, H_l) before being added to the reference point. */
 void msda_oracle_sampling_locations(int B, int64_t Nq, int M, int L, int K,

@@ -83,6 +83,12 @@ void msda_oracle_sampling_locations_backward(int B, int64_t Nq, int M, int L, in
  * by one thread in the serial order. */
 void msda_oracle_set_threads(int n);
 
+/* Padding mask ([P4] "Key code", [P2] "encoder"): out = x with the rows of
+ * the masked positions set to zero; x and out are [B,S,C], mask [B,S]
+ * (nonzero = padded). Also the backward of that step. */
+void msda_oracle_masked_fill(int B, int64_t S, int64_t C, const unsigned char *mask, const double *x,
+                             double *out);
+
 /* Forward ([P4] "Insight 2" equation, bracketed sum; [P2] "encoder" core:
  * bilinear sampling, zero padding, align_corners=False):
  * out[b,q,m*D+d] = sum_{l,k} A[b,q,m,l,k] * bilinear(value_l[b,:,:,m,d], loc).

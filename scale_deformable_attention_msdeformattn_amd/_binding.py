@@ -99,10 +99,11 @@ def load():
     lib.msda_backward.argtypes = [_shp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                                   ctypes.c_uint, _vp]
     lib.msda_forward_fused.restype = ctypes.c_int
-    lib.msda_forward_fused.argtypes = [_shp, _vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp]
+    lib.msda_forward_fused.argtypes = [_shp, _vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp,
+                                       _vp]
     lib.msda_backward_fused.restype = ctypes.c_int
     lib.msda_backward_fused.argtypes = [_shp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp,
-                                        _vp, _vp, _vp, ctypes.c_size_t, ctypes.c_uint, _vp]
+                                        _vp, _vp, _vp, _vp, ctypes.c_size_t, ctypes.c_uint, _vp]
     lib.msda_timing_enable.restype = ctypes.c_int
     lib.msda_timing_enable.argtypes = [ctypes.c_int]
     lib.msda_timing_reset.restype = ctypes.c_int
@@ -314,12 +315,25 @@ def msda_backward(value: torch.Tensor, spatial_shapes, level_start_index, sampli
     return grad_value, gl, ga
 
 
+def _mask(key_padding_mask, B, S, device):
+    """The [B,S] padding mask as a contiguous uint8 device tensor (or None)."""
+    if key_padding_mask is None:
+        return None
+    if tuple(key_padding_mask.shape) != (B, S):
+        raise ValueError(f"key_padding_mask must be [{B}, {S}], got {tuple(key_padding_mask.shape)}")
+    if key_padding_mask.device != device:
+        raise ValueError("key_padding_mask must be on the value's device")
+    return key_padding_mask.to(torch.uint8).contiguous()
+
+
 def msda_forward_fused(value: torch.Tensor, spatial_shapes, level_start_index, reference_points: torch.Tensor,
-                       sampling_offsets: torch.Tensor, attention_logits: torch.Tensor):
+                       sampling_offsets: torch.Tensor, attention_logits: torch.Tensor,
+                       key_padding_mask: Optional[torch.Tensor] = None):
     """Fused forward: locations and the L*K softmax formed inside the core.
     reference_points [B,Nq,L,2] (offsets in pixels of level l) or boxes
     [B,Nq,L,4] (offsets relative to the box size), sampling_offsets
-    [B,Nq,M,L,K,2], attention_logits [B,Nq,M,L*K] ->
+    [B,Nq,M,L,K,2], attention_logits [B,Nq,M,L*K], key_padding_mask [B,S]
+    (True = padded: those value rows read as zero) or None ->
     (output [B,Nq,M*D], sampling_locations, attention_weights)."""
     if value.dtype not in (torch.float32, torch.bfloat16):
         raise ValueError(f"value must be float32 or bfloat16 (got {value.dtype})")
@@ -345,8 +359,9 @@ def msda_forward_fused(value: torch.Tensor, spatial_shapes, level_start_index, r
     out = torch.empty(B, Nq, M * D, dtype=torch.float32, device=value.device)
     loc = torch.empty_like(off)
     attn = torch.empty(B, Nq, M, L, K, dtype=torch.float32, device=value.device)
+    mask = _mask(key_padding_mask, B, S, value.device)
     _check(load().msda_forward_fused(sh.ptr, _p(value), vt, _p(ref), int(ref.shape[3]), _p(off), _p(logits),
-                                     _p(out), _p(loc), _p(attn), _stream(out)), "msda_forward_fused")
+                                     _p(mask), _p(out), _p(loc), _p(attn), _stream(out)), "msda_forward_fused")
     return out, loc, attn
 
 
@@ -354,12 +369,14 @@ def msda_backward_fused(value: torch.Tensor, spatial_shapes, level_start_index, 
                         attention_weights: torch.Tensor, grad_output: torch.Tensor,
                         grad_value: Optional[torch.Tensor] = None, reference_grad: bool = True,
                         box_references: Optional[torch.Tensor] = None,
-                        sampling_offsets: Optional[torch.Tensor] = None):
+                        sampling_offsets: Optional[torch.Tensor] = None,
+                        key_padding_mask: Optional[torch.Tensor] = None):
     """Backward of msda_forward_fused, from the locations and weights it
     returned -> (grad_value [B,S,M,D], grad_sampling_offsets [B,Nq,M,L,K,2],
     grad_attention_logits [B,Nq,M,L*K], grad_reference_points [B,Nq,L,2|4]
     or None). For 4-d box references pass the boxes and the offsets of the
-    forward. If grad_value is given it is accumulated into."""
+    forward, and the forward's key_padding_mask if it had one. If grad_value
+    is given it is accumulated into."""
     value, loc, attn, sh, vt = _core_shape(value, spatial_shapes, level_start_index, sampling_locations,
                                            attention_weights)
     B, S, M, D = value.shape
@@ -387,7 +404,9 @@ def msda_backward_fused(value: torch.Tensor, spatial_shapes, level_start_index, 
     glog = torch.empty(B, Nq, M, L * K, dtype=torch.float32, device=value.device)
     gref = torch.empty(B, Nq, L, dims, dtype=torch.float32, device=value.device) if reference_grad else None
     ws, nbytes = _workspace(sh, value.device)
-    _check(load().msda_backward_fused(sh.ptr, _p(value), vt, _p(loc), _p(attn), _p(box), _p(off), dims, _p(go),
+    mask = _mask(key_padding_mask, B, S, value.device)
+    _check(load().msda_backward_fused(sh.ptr, _p(value), vt, _p(loc), _p(attn), _p(box), _p(off), dims, _p(mask),
+                                      _p(go),
                                       _p(grad_value), _p(goff), _p(glog), _p(gref), _p(ws), nbytes, flags,
                                       _stream(go)), "msda_backward_fused")
     return grad_value, goff, glog, gref

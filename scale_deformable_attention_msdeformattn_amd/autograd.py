@@ -29,31 +29,34 @@ class MSDeformAttnFunction(torch.autograd.Function):
 
 
 class MSDeformAttnFusedFunction(torch.autograd.Function):
-    """value, reference points (2-d points or 4-d boxes), offsets and logits
-    -> output, with the location formation and the L*K softmax inside the
-    core; gradients for all four tensor inputs."""
+    """value, reference points (2-d points or 4-d boxes), offsets, logits and
+    an optional key padding mask [B,S] (True = padded: those value rows read
+    as zero) -> output, with the location formation and the L*K softmax
+    inside the core; gradients for all four float tensor inputs."""
 
     @staticmethod
     def forward(ctx, value, spatial_shapes, level_start_index, reference_points, sampling_offsets,
-                attention_logits):
+                attention_logits, key_padding_mask=None):
         out, loc, attn = B.msda_forward_fused(value, spatial_shapes, level_start_index, reference_points,
-                                              sampling_offsets, attention_logits)
+                                              sampling_offsets, attention_logits, key_padding_mask)
         box = reference_points.shape[-1] == 4
-        ctx.save_for_backward(value, loc, attn, reference_points if box else None, sampling_offsets if box else None)
+        ctx.save_for_backward(value, loc, attn, reference_points if box else None, sampling_offsets if box else None,
+                              key_padding_mask)
         ctx.shapes = spatial_shapes
         ctx.lsi = level_start_index
         return out
 
     @staticmethod
     def backward(ctx, grad_output):
-        value, loc, attn, box, off = ctx.saved_tensors
+        value, loc, attn, box, off, mask = ctx.saved_tensors
         gv, goff, glog, gref = B.msda_backward_fused(value, ctx.shapes, ctx.lsi, loc, attn,
                                                      grad_output.contiguous(),
                                                      reference_grad=ctx.needs_input_grad[3],
-                                                     box_references=box, sampling_offsets=off)
+                                                     box_references=box, sampling_offsets=off,
+                                                     key_padding_mask=mask)
         if value.dtype != torch.float32:
             gv = gv.to(value.dtype)
-        return gv, None, None, gref, goff, glog
+        return gv, None, None, gref, goff, glog, None
 
 
 def ms_deform_attn(value, spatial_shapes, reference_points, offsets_px, logits, points):

@@ -254,14 +254,14 @@ int msda_backward(const msda_shape *shape, const void *value, msda_dtype value_d
     }
     return launched(msda::launch_backward(g, value, value_dtype, sampling_locations, attention_weights, grad_output,
                                           grad_value, grad_sampling_locations, grad_attention_weights, workspace,
-                                          accumulate, (hipStream_t)stream),
+                                          accumulate, true, (hipStream_t)stream),
                     "backward");
 }
 
 int msda_forward_fused(const msda_shape *shape, const void *value, msda_dtype value_dtype,
                        const float *reference_points, int reference_dims, const float *sampling_offsets,
-                       const float *attention_logits, float *output, float *sampling_locations_out,
-                       float *attention_weights_out, void *stream)
+                       const float *attention_logits, const uint8_t *key_padding_mask, float *output,
+                       float *sampling_locations_out, float *attention_weights_out, void *stream)
 {
     msda::Geometry g;
     if (int st = make_geometry(shape, g)) return st;
@@ -278,7 +278,8 @@ int msda_forward_fused(const msda_shape *shape, const void *value, msda_dtype va
         return fail(MSDA_E_ALIGN, "value needs element alignment, (x, y) tensors 8 bytes, boxes 16, the others 4");
     msda::FusedInputs fi{reference_points, reference_dims, reinterpret_cast<const float2 *>(sampling_offsets),
                          attention_logits,
-                         reinterpret_cast<float2 *>(sampling_locations_out), attention_weights_out};
+                         reinterpret_cast<float2 *>(sampling_locations_out), attention_weights_out,
+                         key_padding_mask};
     return launched(msda::launch_forward_fused(g, value, value_dtype, fi, output, (hipStream_t)stream),
                     "forward_fused");
 }
@@ -286,7 +287,7 @@ int msda_forward_fused(const msda_shape *shape, const void *value, msda_dtype va
 int msda_backward_fused(const msda_shape *shape, const void *value, msda_dtype value_dtype,
                         const float *sampling_locations, const float *attention_weights,
                         const float *reference_points, const float *sampling_offsets, int reference_dims,
-                        const float *grad_output, float *grad_value, float *grad_sampling_offsets,
+                        const uint8_t *key_padding_mask, const float *grad_output, float *grad_value, float *grad_sampling_offsets,
                         float *grad_attention_logits, float *grad_reference_points, void *workspace,
                         size_t workspace_bytes, unsigned flags, void *stream)
 {
@@ -323,10 +324,10 @@ int msda_backward_fused(const msda_shape *shape, const void *value, msda_dtype v
         if (!aligned(workspace, 256)) return fail(MSDA_E_ALIGN, "workspace needs 256-byte alignment");
     }
     const msda::FusedGrads fg{reference_points, reinterpret_cast<const float2 *>(sampling_offsets), reference_dims,
-                              grad_reference_points};
+                              grad_reference_points, key_padding_mask};
     return launched(msda::launch_backward_fused(g, value, value_dtype, sampling_locations, attention_weights,
                                                 grad_output, grad_value, grad_sampling_offsets, grad_attention_logits,
-                                                fg, workspace, accumulate, (hipStream_t)stream),
+                                                fg, workspace, accumulate, true, (hipStream_t)stream),
                     "backward_fused");
 }
 

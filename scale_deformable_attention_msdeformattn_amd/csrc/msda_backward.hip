@@ -240,7 +240,8 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
                      const float *__restrict__ attn, const float4 *__restrict__ grad_out,
                      float2 *__restrict__ grad_loc, float *__restrict__ grad_attn,
                      const uint32_t *__restrict__ offsets, const uint32_t *__restrict__ totals,
-                     uint32_t *__restrict__ bases, uint32_t *__restrict__ records, uint32_t grid, FusedGrads fg)
+                     uint32_t *__restrict__ bases, uint32_t *__restrict__ records, uint32_t grid, FusedGrads fg,
+                     const uint8_t *__restrict__ mask)
 {
     constexpr int C = 256;
     constexpr int D = C / M;
@@ -352,13 +353,16 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
                 const bool x1ok = in & (cx + 1 >= 0) & (cx + 1 < lv.W);
                 const bool y0ok = (cy >= 0) & (cy < H);
                 const bool y1ok = (cy + 1 >= 0) & (cy + 1 < H);
-                const uint32_t o00 = (uint32_t)(lv.start + cy * lv.W + cx) * RB;
+                const int row = lv.start + cy * lv.W + cx;
+                bool k00 = y0ok & x0ok, k01 = y0ok & x1ok, k10 = y1ok & x0ok, k11 = y1ok & x1ok;
+                if (mask) unmask_corners(mask + (int64_t)b * g.S, row, lv.W, k00, k01, k10, k11);
+                const uint32_t o00 = (uint32_t)row * RB;
                 const uint32_t o10 = o00 + (uint32_t)lv.W * RB;
                 int4 o;
-                o.x = (int)((y0ok & x0ok) ? o00 : kOutOfRange);
-                o.y = (int)((y0ok & x1ok) ? o00 + RB : kOutOfRange);
-                o.z = (int)((y1ok & x0ok) ? o10 : kOutOfRange);
-                o.w = (int)((y1ok & x1ok) ? o10 + RB : kOutOfRange);
+                o.x = (int)(k00 ? o00 : kOutOfRange);
+                o.y = (int)(k01 ? o00 + RB : kOutOfRange);
+                o.z = (int)(k10 ? o10 : kOutOfRange);
+                o.w = (int)(k11 ? o10 + RB : kOutOfRange);
                 s_off[wave][pp] = o;
                 s_geo[wave][pp] = make_float4(fx, fy, a * lv.Wf, a * lv.Hf);
                 if (in && !((tp.dense_mask >> l) & 1)) {
@@ -509,7 +513,8 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
 // defined with the dense levels below; tile_accum runs it for its extra items
 template <int LG>
 __device__ void dense_reduce_one(const Geometry &g, const TilePlan &tp, const float4 *__restrict__ partials,
-                                 float4 *__restrict__ grad_value, int accumulate, int64_t t);
+                                 float4 *__restrict__ grad_value, int accumulate, const uint8_t *__restrict__ mask,
+                                 int64_t t);
 
 // One workgroup per tile (b, m, level, tile). Its records are counting-sorted
 // by cell in LDS; then each lane group (LG lanes, 4 channels each, D = 4*LG)
@@ -524,7 +529,7 @@ tile_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, const
                   const float4 *__restrict__ grad_out, float4 *__restrict__ grad_value,
                   const uint32_t *__restrict__ records, const uint32_t *__restrict__ bases,
                   const uint32_t *__restrict__ totals, int accumulate, const float4 *__restrict__ partials,
-                  int reduce_blocks)
+                  int reduce_blocks, const uint8_t *__restrict__ mask)
 {
     constexpr int NG = kBlock / LG;
     // (pixel, role, split) slots in use: npix*4 when cells >= NG, else at most 4*NG
@@ -546,7 +551,7 @@ tile_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, const
         // the items after the tiles add up the dense levels' query splits
         const int r = item - g.B * g.M * tp.ipb;
         if (r < reduce_blocks)
-            dense_reduce_one<LG>(g, tp, partials, grad_value, accumulate, (int64_t)r * kBlock + threadIdx.x);
+            dense_reduce_one<LG>(g, tp, partials, grad_value, accumulate, mask, (int64_t)r * kBlock + threadIdx.x);
         return;
     }
     const int bm = item / tp.ipb;
@@ -664,7 +669,9 @@ tile_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, const
                 v.w += t.w;
             }
             const int py = r0 + grp / pw, px = c0 + grp % pw;
-            float4 *dst = grad_value + (((int64_t)b * g.S + lstart + (int64_t)py * W + px) * g.M + m) * LG + lig;
+            const int64_t pix = (int64_t)b * g.S + lstart + (int64_t)py * W + px;
+            if (mask && mask[pix]) v = make_float4(0.f, 0.f, 0.f, 0.f);  // padded: no gradient
+            float4 *dst = grad_value + (pix * g.M + m) * LG + lig;
             if (nch > 1) {
                 // several workgroups share this tile: add the partial into the
                 // row (zeroed beforehand unless accumulating)
@@ -808,7 +815,9 @@ tile_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, const
             v.w += t.w;
         }
         const int py = r0 + pix / pw, px = c0 + pix % pw;
-        float4 *dst = grad_value + (((int64_t)b * g.S + lstart + (int64_t)py * W + px) * g.M + m) * LG + lig;
+        const int64_t row = (int64_t)b * g.S + lstart + (int64_t)py * W + px;
+        if (mask && mask[row]) v = make_float4(0.f, 0.f, 0.f, 0.f);  // padded: no gradient
+        float4 *dst = grad_value + (row * g.M + m) * LG + lig;
         if (accumulate) {
             const float4 o = *dst;
             v.x += o.x;
@@ -870,7 +879,7 @@ template <int LG>
 __global__ void __launch_bounds__(kDenseThreads)
 dense_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, const float *__restrict__ attn,
                    const float4 *__restrict__ grad_out, float4 *__restrict__ grad_value,
-                   float4 *__restrict__ partials, int accumulate)
+                   float4 *__restrict__ partials, int accumulate, const uint8_t *__restrict__ mask)
 {
     constexpr int NG = kDenseThreads / LG;                  // lane groups
     constexpr int PPG = kDensePix / NG;              // pixel slots per lane group
@@ -1051,7 +1060,9 @@ dense_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, cons
         if (splits > 1) {
             partials[((int64_t)item * kDensePix + pl) * LG + lig] = v;
         } else {
-            float4 *dst = grad_value + (((int64_t)b * g.S + lstart + p0 + pl) * g.M + m) * LG + lig;
+            const int64_t row = (int64_t)b * g.S + lstart + p0 + pl;
+            if (mask && mask[row]) v = make_float4(0.f, 0.f, 0.f, 0.f);  // padded: no gradient
+            float4 *dst = grad_value + (row * g.M + m) * LG + lig;
             if (accumulate) {
                 const float4 o = *dst;
                 v.x += o.x;
@@ -1068,7 +1079,8 @@ dense_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, cons
 // Thread t of (batch, pixel, head, float4 of channels) over the split levels.
 template <int LG>
 __device__ void dense_reduce_one(const Geometry &g, const TilePlan &tp, const float4 *__restrict__ partials,
-                                 float4 *__restrict__ grad_value, int accumulate, int64_t t)
+                                 float4 *__restrict__ grad_value, int accumulate, const uint8_t *__restrict__ mask,
+                                 int64_t t)
 {
     for (int l = 0; l < g.L; ++l) {
         if (!((tp.dense_mask >> l) & 1) || tp.dsplit[l] <= 1) continue;
@@ -1097,7 +1109,9 @@ __device__ void dense_reduce_one(const Geometry &g, const TilePlan &tp, const fl
             v.z += x.z;
             v.w += x.w;
         }
-        float4 *dst = grad_value + (((int64_t)b * g.S + g.lv.start[l] + p) * g.M + m) * LG + c;
+        const int64_t row = (int64_t)b * g.S + g.lv.start[l] + p;
+        if (mask && mask[row]) v = make_float4(0.f, 0.f, 0.f, 0.f);  // padded: no gradient
+        float4 *dst = grad_value + (row * g.M + m) * LG + c;
         if (accumulate) {
             const float4 o = *dst;
             v.x += o.x;
@@ -1127,7 +1141,7 @@ __global__ void __launch_bounds__(256)
 backward_generic_kernel(Geometry g, const VT *__restrict__ value, const float2 *__restrict__ loc,
                         const float *__restrict__ attn, const float *__restrict__ grad_out,
                         float *__restrict__ grad_value, float2 *__restrict__ grad_loc,
-                        float *__restrict__ grad_attn)
+                        float *__restrict__ grad_attn, const uint8_t *__restrict__ mask)
 {
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (t >= (int64_t)g.B * g.Nq * g.M) return;
@@ -1155,8 +1169,10 @@ backward_generic_kernel(Geometry g, const VT *__restrict__ value, const float2 *
                     for (int dx = 0; dx < 2; ++dx) {
                         const int xi = x0 + dx, yi = y0 + dy;
                         if (xi < 0 || xi >= W || yi < 0 || yi >= H) continue;
+                        const int64_t pix = g.lv.start[l] + (int64_t)yi * W + xi;
+                        if (mask && mask[(int64_t)b * g.S + pix]) continue;  // padded: reads zero, no gradient
                         const float wx = dx ? fx : 1.0f - fx, wy = dy ? fy : 1.0f - fy;
-                        const int64_t row = (g.lv.start[l] + (int64_t)yi * W + xi) * C;
+                        const int64_t row = pix * C;
                         float gv = 0.0f;
                         for (int d = 0; d < g.D; ++d) {
                             gv = __builtin_fmaf(G[d], vload<VT>(vb + row + d), gv);
@@ -1257,34 +1273,39 @@ hipError_t launch_binning(const Geometry &g, const TilePlan &tp, const float *lo
 template <typename VT, int M, int L, int K, bool FUSED>
 hipError_t launch_fast(const Geometry &g, const TilePlan &tp, const void *value, const float *loc,
                        const float *attn, const float *go, float *gv, float *gl, float *ga, const FusedGrads &fg,
-                       void *wsp, bool accumulate, hipStream_t st)
+                       void *wsp, bool accumulate, bool side_ok, const uint8_t *mask, hipStream_t st)
 {
     Workspace ws;
     layout(g, tp, static_cast<char *>(wsp), &ws);
     const int nkb = M * tp.tpb;
     const int nwg = g.B * tp.wpb;
-    const int nkeys = g.B * nkb;
     const size_t hist_bytes = (size_t)(nkb + kWave) * 4;  // + a slot per lane for its idle adds
     constexpr int LG = 256 / M / 4;
     // the dense levels on the side stream: they read only the inputs and
     // write their own grad_value rows and workspace section, so they run
     // beside the binning and the main kernel; tile_accum (which adds their
-    // query splits) waits for them
+    // query splits) waits for them. Without the side stream (side_ok false:
+    // the caller's stream only) they run first on `st`.
     SideStream *side = nullptr;
     if (tp.dipb > 0) {
-        hipError_t e = side_stream(&side);
-        if (e == hipSuccess) e = hipEventRecord(side->fork, st);
-        if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
-        if (e != hipSuccess) return e;
+        hipStream_t ds = st;
+        hipError_t e = hipSuccess;
+        if (side_ok) {
+            e = side_stream(&side);
+            if (e == hipSuccess) e = hipEventRecord(side->fork, st);
+            if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
+            if (e != hipSuccess) return e;
+            ds = side->s;
+        }
         const uint32_t ditems = (uint32_t)(g.B * g.M * tp.dipb);
         {
-            KernelScope ks_("dense_accum_kernel", side->s);
-            hipLaunchKernelGGL((dense_accum_kernel<LG>), dim3(round_up8(ditems)), dim3(kDenseThreads), 0, side->s, g,
+            KernelScope ks_("dense_accum_kernel", ds);
+            hipLaunchKernelGGL((dense_accum_kernel<LG>), dim3(round_up8(ditems)), dim3(kDenseThreads), 0, ds, g,
                                tp, reinterpret_cast<const float2 *>(loc), attn, reinterpret_cast<const float4 *>(go),
-                               reinterpret_cast<float4 *>(gv), ws.partials, accumulate ? 1 : 0);
+                               reinterpret_cast<float4 *>(gv), ws.partials, accumulate ? 1 : 0, mask);
         }
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        if ((e = hipEventRecord(side->join, side->s)) != hipSuccess) return e;
+        if (side && (e = hipEventRecord(side->join, side->s)) != hipSuccess) return e;
     }
     {
         const hipError_t e = launch_binning<M, L, K>(g, tp, loc, ws, st);
@@ -1297,7 +1318,7 @@ hipError_t launch_fast(const Geometry &g, const TilePlan &tp, const void *value,
                            dim3(MainWaves<M, L, K>::kValue * kWave), hist_bytes, st, g, tp,
                            static_cast<const VT *>(value), reinterpret_cast<const float2 *>(loc), attn,
                            reinterpret_cast<const float4 *>(go), reinterpret_cast<float2 *>(gl), ga, ws.counts,
-                           ws.totals, ws.bases, ws.records, grid, fg);
+                           ws.totals, ws.bases, ws.records, grid, fg, mask);
     }
     if (!accumulate) {
         int64_t n = 0;
@@ -1325,7 +1346,7 @@ hipError_t launch_fast(const Geometry &g, const TilePlan &tp, const void *value,
         hipLaunchKernelGGL((tile_accum_kernel<LG>), dim3(round_up8(items)), dim3(kBlock), 0, st, g, tp,
                            reinterpret_cast<const float2 *>(loc), attn, reinterpret_cast<const float4 *>(go),
                            reinterpret_cast<float4 *>(gv), ws.records, ws.bases, ws.totals, accumulate ? 1 : 0,
-                           ws.partials, reduce_blocks);
+                           ws.partials, reduce_blocks, mask);
     }
     return hipGetLastError();
 }
@@ -1405,7 +1426,7 @@ fused_grads_kernel(Geometry g, const float *__restrict__ attn, float *__restrict
 template <typename VT>
 hipError_t launch_typed(const Geometry &g, const TilePlan *tpp, const void *value, const float *loc,
                         const float *attn, const float *go, float *gv, float *gl, float *ga, const FusedGrads *fg,
-                        void *ws, bool accumulate, hipStream_t st)
+                        void *ws, bool accumulate, bool side_ok, const uint8_t *mask, hipStream_t st)
 {
     // fused gradients inside the main kernel where the L*K softmax fits the
     // wave's lanes; otherwise the plain gradients, converted afterwards
@@ -1415,9 +1436,9 @@ hipError_t launch_typed(const Geometry &g, const TilePlan *tpp, const void *valu
     bool done = false;
 #define MSDA_FAST(M_, L_, K_)                                                                                    \
     e = in_kernel ? launch_fast<VT, M_, L_, K_, true>(g, *tpp, value, loc, attn, go, gv, gl, ga, *fg, ws,        \
-                                                      accumulate, st)                                            \
+                                                      accumulate, side_ok, mask, st)                             \
                   : launch_fast<VT, M_, L_, K_, false>(g, *tpp, value, loc, attn, go, gv, gl, ga, FusedGrads{},  \
-                                                       ws, accumulate, st);                                      \
+                                                       ws, accumulate, side_ok, mask, st);                       \
     done = true;
     switch (tpp ? fast_kind(g) : Fast::None) {
     case Fast::M8L4K4: MSDA_FAST(8, 4, 4) break;
@@ -1440,7 +1461,7 @@ hipError_t launch_typed(const Geometry &g, const TilePlan *tpp, const void *valu
         KernelScope ks_("backward_generic_kernel", st);
         hipLaunchKernelGGL((backward_generic_kernel<VT>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, g,
                            static_cast<const VT *>(value), reinterpret_cast<const float2 *>(loc), attn, go, gv,
-                           reinterpret_cast<float2 *>(gl), ga);
+                           reinterpret_cast<float2 *>(gl), ga, mask);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -1575,24 +1596,28 @@ bool backward_uses_workspace(const Geometry &g, const void *value, msda_dtype vt
 
 hipError_t launch_backward(const Geometry &g, const void *value, msda_dtype vt, const float *loc,
                            const float *attn, const float *go, float *gv, float *gl, float *ga, void *ws,
-                           bool accumulate, hipStream_t st)
+                           bool accumulate, bool side_ok, hipStream_t st)
 {
     TilePlan tp;
     const TilePlan *tpp = backward_uses_workspace(g, value, vt, go, gv) && make_tile_plan(g, tp) ? &tp : nullptr;
     if (vt == MSDA_BF16)
-        return launch_typed<uint16_t>(g, tpp, value, loc, attn, go, gv, gl, ga, nullptr, ws, accumulate, st);
-    return launch_typed<float>(g, tpp, value, loc, attn, go, gv, gl, ga, nullptr, ws, accumulate, st);
+        return launch_typed<uint16_t>(g, tpp, value, loc, attn, go, gv, gl, ga, nullptr, ws, accumulate, side_ok,
+                                      nullptr, st);
+    return launch_typed<float>(g, tpp, value, loc, attn, go, gv, gl, ga, nullptr, ws, accumulate, side_ok, nullptr,
+                               st);
 }
 
 hipError_t launch_backward_fused(const Geometry &g, const void *value, msda_dtype vt, const float *loc,
                                  const float *attn, const float *go, float *gv, float *goff, float *glogits,
-                                 const FusedGrads &fg, void *ws, bool accumulate, hipStream_t st)
+                                 const FusedGrads &fg, void *ws, bool accumulate, bool side_ok, hipStream_t st)
 {
     TilePlan tp;
     const TilePlan *tpp = backward_uses_workspace(g, value, vt, go, gv) && make_tile_plan(g, tp) ? &tp : nullptr;
     if (vt == MSDA_BF16)
-        return launch_typed<uint16_t>(g, tpp, value, loc, attn, go, gv, goff, glogits, &fg, ws, accumulate, st);
-    return launch_typed<float>(g, tpp, value, loc, attn, go, gv, goff, glogits, &fg, ws, accumulate, st);
+        return launch_typed<uint16_t>(g, tpp, value, loc, attn, go, gv, goff, glogits, &fg, ws, accumulate, side_ok,
+                                      fg.mask, st);
+    return launch_typed<float>(g, tpp, value, loc, attn, go, gv, goff, glogits, &fg, ws, accumulate, side_ok,
+                               fg.mask, st);
 }
 
 }  // namespace msda

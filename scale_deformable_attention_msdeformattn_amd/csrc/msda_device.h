@@ -78,6 +78,20 @@ __device__ __forceinline__ bool sample_in_range(float u, float v, float Wf, floa
     return (x > -2.0f) & (x < Wf + 1.0f) & (y > -2.0f) & (y < Hf + 1.0f);
 }
 
+// The key padding mask for a sample's four corners: a corner whose value row
+// is padded (mask byte nonzero) is treated like an off-map corner (reads zero,
+// receives no gradient). `mask_b` is the mask row of the sample's batch,
+// `row` the flat value row of the top-left corner, `W` the level width; only
+// corners still marked valid are looked up.
+__device__ __forceinline__ void unmask_corners(const uint8_t *mask_b, int row, int W, bool &k00, bool &k01,
+                                               bool &k10, bool &k11)
+{
+    if (k00) k00 = mask_b[row] == 0;
+    if (k01) k01 = mask_b[row + 1] == 0;
+    if (k10) k10 = mask_b[row + W] == 0;
+    if (k11) k11 = mask_b[row + W + 1] == 0;
+}
+
 // Workgroup barrier that orders LDS accesses only. Unlike __syncthreads it
 // does not wait for the wave's outstanding global loads, so loads issued
 // before it (a prefetch) stay in flight across it. Use it only where the

@@ -45,7 +45,8 @@ struct LevelRec {  // one level, as read by lane-varying level index from LDS
 template <typename VT, int M, int L, int K, bool FUSED>
 __global__ void __launch_bounds__(kBlock)
 forward_c256_kernel(Geometry g, const VT *__restrict__ value, const float2 *__restrict__ loc,
-                    const float *__restrict__ attn, float4 *__restrict__ out, uint32_t grid, FusedInputs fi)
+                    const float *__restrict__ attn, float4 *__restrict__ out, uint32_t grid, FusedInputs fi,
+                    const uint8_t *__restrict__ mask)
 {
     constexpr int C = 256;
     constexpr int D = C / M;
@@ -75,6 +76,7 @@ forward_c256_kernel(Geometry g, const VT *__restrict__ value, const float2 *__re
     const int64_t nq_total = (int64_t)g.B * g.Nq;
     const int64_t gq = (int64_t)xcd_tile(blockIdx.x, grid) * kWaves + wave;
     const bool active = gq < nq_total;
+    const int b = active ? (int)(gq / g.Nq) : 0;
 
     // ---- phase 1: per-sample geometry, one sample per lane per pass ----
     if (active) {
@@ -113,13 +115,15 @@ forward_c256_kernel(Geometry g, const VT *__restrict__ value, const float2 *__re
                 const bool y0ok = in & (cy >= 0.0f) & (cy < lv.Hf);
                 const bool y1ok = in & (cy >= -1.0f) & (cy + 1.0f < lv.Hf);
                 const int row = lv.start + (int)cy * lv.W + (int)cx;
+                bool k00 = y0ok & x0ok, k01 = y0ok & x1ok, k10 = y1ok & x0ok, k11 = y1ok & x1ok;
+                if (mask) unmask_corners(mask + (int64_t)b * g.S, row, lv.W, k00, k01, k10, k11);
                 const uint32_t o00 = (uint32_t)row * RB;
                 const uint32_t o10 = o00 + (uint32_t)lv.W * RB;
                 int4 o;
-                o.x = (int)((y0ok & x0ok) ? o00 : kOutOfRange);
-                o.y = (int)((y0ok & x1ok) ? o00 + RB : kOutOfRange);
-                o.z = (int)((y1ok & x0ok) ? o10 : kOutOfRange);
-                o.w = (int)((y1ok & x1ok) ? o10 + RB : kOutOfRange);
+                o.x = (int)(k00 ? o00 : kOutOfRange);
+                o.y = (int)(k01 ? o00 + RB : kOutOfRange);
+                o.z = (int)(k10 ? o10 : kOutOfRange);
+                o.w = (int)(k11 ? o10 + RB : kOutOfRange);
                 const float wy0 = a * (1.0f - fy), wy1 = a * fy;
                 const int p = s + s / LK;
                 s_off[wave][p] = o;
@@ -131,7 +135,6 @@ forward_c256_kernel(Geometry g, const VT *__restrict__ value, const float2 *__re
     if (!active) return;
 
     // ---- phase 2: gather + blend + reduce, wave-uniform (l, k) loop ----
-    const int b = (int)(gq / g.Nq);
     const __amdgpu_buffer_rsrc_t rsrc =
         make_rsrc(value + (int64_t)b * g.S * C, (uint32_t)g.S * RB);
     const uint32_t lane_off = (uint32_t)lane * 4u * sizeof(VT);
@@ -210,7 +213,7 @@ template <typename VT, int M, int L, int K, int LS, bool FUSED>
 __global__ void __launch_bounds__(kStagedThreads)
 forward_staged_kernel(Geometry g, const VT *__restrict__ value, const float2 *__restrict__ loc,
                       const float *__restrict__ attn, float4 *__restrict__ out, StagePlan sp, uint32_t grid,
-                      FusedInputs fi)
+                      FusedInputs fi, const uint8_t *__restrict__ mask)
 {
     constexpr int C = 256;
     constexpr int D = C / M;
@@ -242,7 +245,8 @@ forward_staged_kernel(Geometry g, const VT *__restrict__ value, const float2 *__
         s_lv[l] = LevelRec{(float)g.lv.W[l], (float)g.lv.H[l], g.lv.W[l], g.lv.start[l]};
     }
     // head m's rows of the staged levels (pixels start[LS] .. S-1), then a zero
-    // row that off-map corners read
+    // row that off-map corners read; rows at padded positions are staged as
+    // zeros
     const int srow0 = g.lv.start[LS];
     const int nrows = g.S - srow0;
     {
@@ -255,7 +259,8 @@ forward_staged_kernel(Geometry g, const VT *__restrict__ value, const float2 *__
 #pragma unroll
             for (int k = 0; k < kStageBatch; ++k) {
                 const int i = i0 + k * kStagedThreads;
-                v[k] = i < n ? src[(int64_t)(i / LPH) * (C / 4) + i % LPH] : StageChunk<VT>::zero();
+                const bool keep = i < n && !(mask && mask[(int64_t)b * g.S + srow0 + i / LPH]);
+                v[k] = keep ? src[(int64_t)(i / LPH) * (C / 4) + i % LPH] : StageChunk<VT>::zero();
             }
 #pragma unroll
             for (int k = 0; k < kStageBatch; ++k) {
@@ -321,11 +326,13 @@ forward_staged_kernel(Geometry g, const VT *__restrict__ value, const float2 *__
                         o.z = (y1ok & x0ok) ? r10 : zero_row;
                         o.w = (y1ok & x1ok) ? r10 + RS : zero_row;
                     } else {
+                        bool k00 = y0ok & x0ok, k01 = y0ok & x1ok, k10 = y1ok & x0ok, k11 = y1ok & x1ok;
+                        if (mask) unmask_corners(mask + (int64_t)b * g.S, row, lv.W, k00, k01, k10, k11);
                         const uint32_t o00 = (uint32_t)row * RB, o10 = o00 + (uint32_t)lv.W * RB;
-                        o.x = (int)((y0ok & x0ok) ? o00 : kOutOfRange);
-                        o.y = (int)((y0ok & x1ok) ? o00 + RB : kOutOfRange);
-                        o.z = (int)((y1ok & x0ok) ? o10 : kOutOfRange);
-                        o.w = (int)((y1ok & x1ok) ? o10 + RB : kOutOfRange);
+                        o.x = (int)(k00 ? o00 : kOutOfRange);
+                        o.y = (int)(k01 ? o00 + RB : kOutOfRange);
+                        o.z = (int)(k10 ? o10 : kOutOfRange);
+                        o.w = (int)(k11 ? o10 + RB : kOutOfRange);
                     }
                     const float wy0 = a * (1.0f - fy), wy1 = a * fy;
                     w = make_float4(wy0 * (1.0f - fx), wy0 * fx, wy1 * (1.0f - fx), wy1 * fx);
@@ -406,7 +413,7 @@ template <> __device__ __forceinline__ float load_scalar<uint16_t>(const uint16_
 template <typename VT>
 __global__ void __launch_bounds__(256)
 forward_generic_kernel(Geometry g, const VT *__restrict__ value, const float2 *__restrict__ loc,
-                       const float *__restrict__ attn, float *__restrict__ out)
+                       const float *__restrict__ attn, float *__restrict__ out, const uint8_t *__restrict__ mask)
 {
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int C = g.M * g.D;
@@ -437,6 +444,7 @@ forward_generic_kernel(Geometry g, const VT *__restrict__ value, const float2 *_
                     if (xi < 0 || xi >= W || yi < 0 || yi >= H) continue;
                     const float w = (dx ? fx : 1.0f - fx) * (dy ? fy : 1.0f - fy);
                     const int64_t row = g.lv.start[l] + (int64_t)yi * W + xi;
+                    if (mask && mask[(int64_t)b * g.S + row]) continue;  // padded: reads zero
                     acc = __builtin_fmaf(a * w, load_scalar<VT>(vb + row * C), acc);
                 }
         }
@@ -446,7 +454,7 @@ forward_generic_kernel(Geometry g, const VT *__restrict__ value, const float2 *_
 
 template <typename VT, int M, int L, int K, int LS, bool FUSED>
 hipError_t launch_staged_ls(const Geometry &g, const void *value, const float *loc, const float *attn,
-                            float *out, const FusedInputs &fi, size_t dyn, hipStream_t st)
+                            float *out, const FusedInputs &fi, const uint8_t *mask, size_t dyn, hipStream_t st)
 {
     const auto kernel = forward_staged_kernel<VT, M, L, K, LS, FUSED>;
     StagePlan sp;
@@ -456,7 +464,7 @@ hipError_t launch_staged_ls(const Geometry &g, const void *value, const float *l
     const uint32_t grid = round_up8((uint32_t)(g.B * M * sp.nqr));
     KernelScope ks_(FUSED ? "forward_fused_staged_kernel" : "forward_staged_kernel", st);
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(kStagedThreads), dyn, st, g, static_cast<const VT *>(value),
-                       reinterpret_cast<const float2 *>(loc), attn, reinterpret_cast<float4 *>(out), sp, grid, fi);
+                       reinterpret_cast<const float2 *>(loc), attn, reinterpret_cast<float4 *>(out), sp, grid, fi, mask);
     return hipGetLastError();
 }
 
@@ -482,7 +490,7 @@ int staged_first_level(const Geometry &g, size_t &dyn)
 
 template <typename VT, int M, int L, int K>
 hipError_t launch_c256(const Geometry &g, const void *value, const float *loc, const float *attn,
-                       float *out, const FusedInputs *fi, hipStream_t st)
+                       float *out, const FusedInputs *fi, const uint8_t *mask, hipStream_t st)
 {
     if constexpr (M == 8 && L == 4 && K == 4) {
         size_t dyn = 0;
@@ -490,8 +498,8 @@ hipError_t launch_c256(const Geometry &g, const void *value, const float *loc, c
         switch (staged_first_level<VT, M, L, K>(g, dyn)) {
 #define MSDA_STAGED(LS_)                                                                                      \
     case LS_:                                                                                                 \
-        return fi ? launch_staged_ls<VT, M, L, K, LS_, true>(g, value, loc, attn, out, f, dyn, st)            \
-                  : launch_staged_ls<VT, M, L, K, LS_, false>(g, value, loc, attn, out, f, dyn, st);
+        return fi ? launch_staged_ls<VT, M, L, K, LS_, true>(g, value, loc, attn, out, f, mask, dyn, st)      \
+                  : launch_staged_ls<VT, M, L, K, LS_, false>(g, value, loc, attn, out, f, mask, dyn, st);
             MSDA_STAGED(1)
             MSDA_STAGED(2)
             MSDA_STAGED(3)
@@ -506,7 +514,7 @@ hipError_t launch_c256(const Geometry &g, const void *value, const float *loc, c
             KernelScope ks_("forward_fused_c256_kernel", st);
             hipLaunchKernelGGL((forward_c256_kernel<VT, M, L, K, true>), dim3(grid), dim3(kBlock), 0, st, g,
                                static_cast<const VT *>(value), nullptr, nullptr, reinterpret_cast<float4 *>(out),
-                               grid, *fi);
+                               grid, *fi, mask);
         } else {
             return hipErrorInvalidValue;  // callers check fused_forward_supported first
         }
@@ -514,14 +522,14 @@ hipError_t launch_c256(const Geometry &g, const void *value, const float *loc, c
         KernelScope ks_("forward_c256_kernel", st);
         hipLaunchKernelGGL((forward_c256_kernel<VT, M, L, K, false>), dim3(grid), dim3(kBlock), 0, st, g,
                            static_cast<const VT *>(value), reinterpret_cast<const float2 *>(loc), attn,
-                           reinterpret_cast<float4 *>(out), grid, FusedInputs{});
+                           reinterpret_cast<float4 *>(out), grid, FusedInputs{}, mask);
     }
     return hipGetLastError();
 }
 
 template <typename VT>
 hipError_t launch_typed(const Geometry &g, const void *value, const float *loc, const float *attn,
-                        float *out, const FusedInputs *fi, hipStream_t st)
+                        float *out, const FusedInputs *fi, const uint8_t *mask, hipStream_t st)
 {
     const bool c256 = g.M * g.D == 256 && (reinterpret_cast<uintptr_t>(value) % (4 * sizeof(VT))) == 0 &&
                       (reinterpret_cast<uintptr_t>(out) % 16) == 0;
@@ -529,17 +537,17 @@ hipError_t launch_typed(const Geometry &g, const void *value, const float *loc, 
     const bool ok = c256 && (!fi || fused_forward_supported(g));
     if (ok && g.L == 4 && g.K == 4) {
         switch (g.M) {
-        case 8: return launch_c256<VT, 8, 4, 4>(g, value, loc, attn, out, fi, st);
-        case 4: return launch_c256<VT, 4, 4, 4>(g, value, loc, attn, out, fi, st);
-        case 16: return launch_c256<VT, 16, 4, 4>(g, value, loc, attn, out, fi, st);
+        case 8: return launch_c256<VT, 8, 4, 4>(g, value, loc, attn, out, fi, mask, st);
+        case 4: return launch_c256<VT, 4, 4, 4>(g, value, loc, attn, out, fi, mask, st);
+        case 16: return launch_c256<VT, 16, 4, 4>(g, value, loc, attn, out, fi, mask, st);
         default: break;
         }
     }
     if (ok && g.M == 8) {
-        if (g.L == 1 && g.K == 4) return launch_c256<VT, 8, 1, 4>(g, value, loc, attn, out, fi, st);
-        if (g.L == 4 && g.K == 8) return launch_c256<VT, 8, 4, 8>(g, value, loc, attn, out, fi, st);
-        if (g.L == 3 && g.K == 4) return launch_c256<VT, 8, 3, 4>(g, value, loc, attn, out, fi, st);
-        if (g.L == 4 && g.K == 1) return launch_c256<VT, 8, 4, 1>(g, value, loc, attn, out, fi, st);
+        if (g.L == 1 && g.K == 4) return launch_c256<VT, 8, 1, 4>(g, value, loc, attn, out, fi, mask, st);
+        if (g.L == 4 && g.K == 8) return launch_c256<VT, 8, 4, 8>(g, value, loc, attn, out, fi, mask, st);
+        if (g.L == 3 && g.K == 4) return launch_c256<VT, 8, 3, 4>(g, value, loc, attn, out, fi, mask, st);
+        if (g.L == 4 && g.K == 1) return launch_c256<VT, 8, 4, 1>(g, value, loc, attn, out, fi, mask, st);
     }
     if (fi) {
         // no fused kernel for this shape: the three steps, through the caller's
@@ -552,14 +560,14 @@ hipError_t launch_typed(const Geometry &g, const void *value, const float *loc, 
         if (e == hipSuccess) e = launch_softmax(g, fi->logits, fi->attn_out, st);
         if (e != hipSuccess) return e;
         return launch_typed<VT>(g, value, reinterpret_cast<const float *>(fi->loc_out), fi->attn_out, out,
-                                nullptr, st);
+                                nullptr, mask, st);
     }
     const int64_t n = g.queries() * g.M * g.D;
     {
         KernelScope ks_("forward_generic_kernel", st);
         hipLaunchKernelGGL((forward_generic_kernel<VT>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
                            g, static_cast<const VT *>(value), reinterpret_cast<const float2 *>(loc), attn,
-                           out);
+                           out, mask);
     }
     return hipGetLastError();
 }
@@ -569,15 +577,15 @@ hipError_t launch_typed(const Geometry &g, const void *value, const float *loc, 
 hipError_t launch_forward(const Geometry &g, const void *value, msda_dtype vt, const float *loc,
                           const float *attn, float *out, hipStream_t st)
 {
-    if (vt == MSDA_BF16) return launch_typed<uint16_t>(g, value, loc, attn, out, nullptr, st);
-    return launch_typed<float>(g, value, loc, attn, out, nullptr, st);
+    if (vt == MSDA_BF16) return launch_typed<uint16_t>(g, value, loc, attn, out, nullptr, nullptr, st);
+    return launch_typed<float>(g, value, loc, attn, out, nullptr, nullptr, st);
 }
 
 hipError_t launch_forward_fused(const Geometry &g, const void *value, msda_dtype vt, const FusedInputs &fi,
                                 float *out, hipStream_t st)
 {
-    if (vt == MSDA_BF16) return launch_typed<uint16_t>(g, value, nullptr, nullptr, out, &fi, st);
-    return launch_typed<float>(g, value, nullptr, nullptr, out, &fi, st);
+    if (vt == MSDA_BF16) return launch_typed<uint16_t>(g, value, nullptr, nullptr, out, &fi, fi.mask, st);
+    return launch_typed<float>(g, value, nullptr, nullptr, out, &fi, fi.mask, st);
 }
 
 }  // namespace msda

@@ -103,6 +103,7 @@ struct FusedInputs {
     const float *logits;
     float2 *loc_out;
     float *attn_out;
+    const uint8_t *mask;  // key padding mask [B,S] (nonzero = padded, reads zero), or null
 };
 
 // One sample's location from its reference and offset.
@@ -124,6 +125,7 @@ struct FusedGrads {
     const float2 *off;
     int ref_dims;
     float *grad_ref;
+    const uint8_t *mask;  // key padding mask [B,S] of the fused forward, or null
 };
 
 // The fused kernels form the L*K softmax across adjacent lanes of a wave.
@@ -146,17 +148,19 @@ hipError_t launch_forward_fused(const Geometry &g, const void *value, msda_dtype
 hipError_t launch_zero_fill(float *p, int64_t n, hipStream_t st);
 // grad_value is fully overwritten unless `accumulate`. `workspace` must hold
 // backward_workspace_bytes(g) bytes when backward_uses_workspace(...) holds.
+// `side_ok`: the dense levels may run on the library's side stream (else
+// everything runs on `st`, and no stream or event is created).
 hipError_t launch_backward(const Geometry &g, const void *value, msda_dtype vt, const float *loc,
                            const float *attn, const float *grad_out, float *grad_value,
                            float *grad_loc, float *grad_attn, void *workspace, bool accumulate,
-                           hipStream_t st);
+                           bool side_ok, hipStream_t st);
 // The same, carried back to the fused forward's inputs: grad_offsets,
 // grad_logits and (if fg.grad_ref is not null) grad_ref instead of grad_loc
 // and grad_attn.
 hipError_t launch_backward_fused(const Geometry &g, const void *value, msda_dtype vt, const float *loc,
                                  const float *attn, const float *grad_out, float *grad_value,
                                  float *grad_offsets, float *grad_logits, const FusedGrads &fg, void *workspace,
-                                 bool accumulate, hipStream_t st);
+                                 bool accumulate, bool side_ok, hipStream_t st);
 hipError_t launch_sampling_locations_box(const Geometry &g, const float *ref, const float *off, float *loc,
                                          hipStream_t st);
 

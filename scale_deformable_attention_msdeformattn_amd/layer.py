@@ -56,14 +56,13 @@ class MSDeformAttnLayer(nn.Module):
         B, Nq, _ = query.shape
         S = input_flatten.shape[1]
         M, L, K = self.n_heads, self.n_levels, self.n_points
-        value = self.value_proj(input_flatten)
-        if padding_mask is not None:
-            value = value.masked_fill(padding_mask[..., None], 0.0)
-        value = value.view(B, S, M, self.d_model // M)
+        # the padded positions of the value are filled with zeros inside the
+        # core (the mask goes to the fused op instead of a masked_fill pass)
+        value = self.value_proj(input_flatten).view(B, S, M, self.d_model // M)
         offsets = self.sampling_offsets(query).view(B, Nq, M, L, K, 2)
         logits = self.attention_weights(query).view(B, Nq, M, L * K)
         out = MSDeformAttnFusedFunction.apply(value, spatial_shapes, level_start_index, reference_points,
-                                              offsets, logits)
+                                              offsets, logits, padding_mask)
         return self.output_proj(out)
 
 

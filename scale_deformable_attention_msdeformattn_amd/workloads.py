@@ -151,3 +151,28 @@ def draw_level_valid_ratios(batch: int, levels: int, seed: int = 0) -> torch.Ten
     g = torch.Generator(device="cpu")
     g.manual_seed(seed)
     return torch.empty(batch, levels, 2, dtype=torch.float32).uniform_(0.5, 1.0, generator=g)
+
+
+def padding_mask(spatial_shapes, valid_ratios: torch.Tensor, seed: Optional[int] = None,
+                 extra: float = 0.0) -> torch.Tensor:
+    """A key padding mask [B,S] (True = padded) shaped like an image batch's:
+    on level l of image b the columns from ceil(vr[b,l,0] * W_l) and the rows
+    from ceil(vr[b,l,1] * H_l) on are padding (the valid region is the
+    top-left part, as for images padded to a common size). With `extra` > 0
+    a further random fraction of positions is masked too (seeded), so that
+    padded rows also sit inside the maps in tests."""
+    shapes = [(int(h), int(w)) for h, w in torch.as_tensor(spatial_shapes).tolist()]
+    B = valid_ratios.shape[0]
+    parts = []
+    for l, (H, W) in enumerate(shapes):
+        vw = torch.ceil(valid_ratios[:, l, 0].double() * W).long().clamp(1, W)
+        vh = torch.ceil(valid_ratios[:, l, 1].double() * H).long().clamp(1, H)
+        xs = torch.arange(W).view(1, 1, W)
+        ys = torch.arange(H).view(1, H, 1)
+        parts.append(((xs >= vw.view(B, 1, 1)) | (ys >= vh.view(B, 1, 1))).reshape(B, H * W))
+    mask = torch.cat(parts, dim=1)
+    if extra > 0:
+        g = torch.Generator(device="cpu")
+        g.manual_seed(0 if seed is None else seed)
+        mask |= torch.rand(mask.shape, generator=g) < extra
+    return mask

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.msda_abi_version() == 8
+    assert lib.msda_abi_version() == 9
     assert lib.msda_status_string(0) == b"ok"
     for code in range(-8, 0):
         assert lib.msda_status_string(code) not in (b"", b"unknown status")
@@ -96,22 +96,26 @@ def test_null_arguments(lib):
 @cpu_only
 def test_fused_entry_points_validate_on_the_host(lib):
     ptrs = [FAKE] * 6   # ref, offsets, logits, output, loc_out, attn_out
+
+    def fwd(dtype, ref, dims, p, mask=None):
+        # (..., ref, dims, offsets, logits, key_padding_mask, output, loc_out, attn_out, stream)
+        return lib.msda_forward_fused(_shape().ptr, FAKE, dtype, ref, dims, p[0], p[1], mask, p[2], p[3], p[4], None)
     for i in range(6):
         p = list(ptrs)
         p[i] = None
-        assert lib.msda_forward_fused(_shape().ptr, FAKE, B.MSDA_F32, p[0], 2, *p[1:], None) == B.MSDA_E_NULL, i
-    assert lib.msda_forward_fused(_shape().ptr, FAKE, 7, FAKE, 2, *ptrs[1:], None) == B.MSDA_E_UNSUPPORTED
-    assert lib.msda_forward_fused(_shape().ptr, FAKE, B.MSDA_F32, FAKE, 3, *ptrs[1:], None) == B.MSDA_E_UNSUPPORTED
+        assert fwd(B.MSDA_F32, p[0], 2, p[1:]) == B.MSDA_E_NULL, i
+    assert fwd(7, FAKE, 2, ptrs[1:]) == B.MSDA_E_UNSUPPORTED
+    assert fwd(B.MSDA_F32, FAKE, 3, ptrs[1:]) == B.MSDA_E_UNSUPPORTED
     odd = ctypes.c_void_p(0x10004)   # 4-byte aligned, not 8: (x, y) tensors need 8
-    assert lib.msda_forward_fused(_shape().ptr, FAKE, B.MSDA_F32, odd, 2, FAKE, FAKE, FAKE, FAKE, FAKE,
-                                  None) == B.MSDA_E_ALIGN
+    assert fwd(B.MSDA_F32, odd, 2, ptrs[1:]) == B.MSDA_E_ALIGN
     box8 = ctypes.c_void_p(0x10008)  # 8-byte aligned, not 16: boxes need 16
-    assert lib.msda_forward_fused(_shape().ptr, FAKE, B.MSDA_F32, box8, 4, FAKE, FAKE, FAKE, FAKE, FAKE,
-                                  None) == B.MSDA_E_ALIGN
+    assert fwd(B.MSDA_F32, box8, 4, ptrs[1:]) == B.MSDA_E_ALIGN
+    # a mask (bytes: any alignment) does not change the validation
+    assert fwd(B.MSDA_F32, FAKE, 3, ptrs[1:], mask=ctypes.c_void_p(0x10001)) == B.MSDA_E_UNSUPPORTED
 
-    def bwd(g, ref=None, off=None, dims=2, flags=0):
-        return lib.msda_backward_fused(_shape().ptr, FAKE, B.MSDA_F32, FAKE, FAKE, ref, off, dims, FAKE, *g, None, 0,
-                                       flags, None)
+    def bwd(g, ref=None, off=None, dims=2, flags=0, mask=None):
+        return lib.msda_backward_fused(_shape().ptr, FAKE, B.MSDA_F32, FAKE, FAKE, ref, off, dims, mask, FAKE, *g,
+                                       None, 0, flags, None)
     for i in range(3):   # grad_value, grad_offsets, grad_logits required; grad_ref optional
         g = [FAKE, FAKE, FAKE, FAKE]
         g[i] = None
@@ -119,6 +123,7 @@ def test_fused_entry_points_validate_on_the_host(lib):
     assert bwd([FAKE] * 3 + [None], dims=4) == B.MSDA_E_NULL        # boxes need references and offsets
     assert bwd([FAKE] * 3 + [None], dims=5) == B.MSDA_E_UNSUPPORTED
     assert bwd([FAKE] * 3 + [None], flags=0x4) == B.MSDA_E_UNSUPPORTED
+    assert bwd([FAKE] * 3 + [None], mask=ctypes.c_void_p(0x10001)) == B.MSDA_E_WORKSPACE
     assert bwd([FAKE] * 3 + [None]) == B.MSDA_E_WORKSPACE
 
 

@@ -44,19 +44,26 @@ def box_case(ci, seed=11):
     return torch.cat([ref32, wh], dim=-1), off, logits
 
 
-def check_fused(ci, vtol, name, box=False):
+def check_fused(ci, vtol, name, box=False, mask=None):
+    """mask: a [B,S] key padding mask for the fused pair; the oracle chain then
+    fills the value with zeros at the padded rows before its core and zeroes
+    its grad_value there (the module's masked_fill and its backward)."""
     w = ci.draws.workload
     ref32, off, logits = box_case(ci) if box else fused_case(ci)
-    out, loc, A = msda.msda_forward_fused(dev(ci.value), ci.shapes, ci.lsi, dev(ref32), dev(off), dev(logits))
+    dmask = None if mask is None else dev(mask)
+    value_o = ci.value if mask is None else oracle.masked_fill(ci.value, mask)
+    out, loc, A = msda.msda_forward_fused(dev(ci.value), ci.shapes, ci.lsi, dev(ref32), dev(off), dev(logits),
+                                          key_padding_mask=dmask)
     torch.cuda.synchronize()
     loc, A = loc.cpu(), A.cpu()
     want_loc = (oracle.sampling_locations_box(ref32, off) if box
                 else oracle.sampling_locations(ci.shapes, ref32, off))
     tolerance_check(loc, want_loc, PRO_TOL, f"fused loc {name}")
     tolerance_check(A, oracle.softmax(logits, w.levels * w.points).reshape(A.shape), PRO_TOL, f"fused A {name}")
-    tolerance_check(out.cpu(), oracle.forward(ci.value, ci.shapes, ci.lsi, loc, A), vtol, f"fused out {name}")
+    tolerance_check(out.cpu(), oracle.forward(value_o, ci.shapes, ci.lsi, loc, A), vtol, f"fused out {name}")
     # the core is the same code as msda_forward: identical output at the same locations and weights
-    plain = msda.msda_forward(dev(ci.value), ci.shapes, ci.lsi, dev(loc), dev(A))
+    plain_value = ci.value if mask is None else ci.value.masked_fill(mask[..., None, None], 0)
+    plain = msda.msda_forward(dev(plain_value), ci.shapes, ci.lsi, dev(loc), dev(A))
     torch.cuda.synchronize()
     assert torch.equal(plain.cpu(), out.cpu()), f"fused and plain forward differ {name}"
     if ci.grad_output is None:
@@ -64,9 +71,12 @@ def check_fused(ci, vtol, name, box=False):
     G = ci.grad_output
     gv, goff, glog, gref = msda.msda_backward_fused(dev(ci.value), ci.shapes, ci.lsi, dev(loc), dev(A), dev(G),
                                                     box_references=dev(ref32) if box else None,
-                                                    sampling_offsets=dev(off) if box else None)
+                                                    sampling_offsets=dev(off) if box else None,
+                                                    key_padding_mask=dmask)
     torch.cuda.synchronize()
-    rgv, rgl, rga = oracle.backward(ci.value, ci.shapes, ci.lsi, loc, A, G)
+    rgv, rgl, rga = oracle.backward(value_o, ci.shapes, ci.lsi, loc, A, G)
+    if mask is not None:
+        rgv = oracle.masked_fill(rgv, mask)
     if box:
         rgref, rgoff = oracle.sampling_locations_box_backward(ref32, off, rgl)
     else:
@@ -157,3 +167,55 @@ def test_fused_empty_queries(gpu_lib):
                                                     torch.zeros(out.shape, device="cuda"))
     torch.cuda.synchronize()
     assert float(gv.abs().max()) == 0.0
+
+
+MASK_CASES = {
+    "encoder_backward": None,                      # staged kernels, binned backward with dense levels
+    "tiny": None,                                  # generic kernels (M*D = 8)
+    "fast": GEOMS[0],                              # per-query kernel, 37 queries
+    "lk12": GEOMS[5],                              # L*K = 12: plain kernels, then the conversion kernel
+    "split": dict(batch=1, heads=8, channels=32, points=4, spatial_shapes=((46, 46),),
+                  num_query=50000),                # direct-mode tiles merged by float atomics
+}
+
+
+@pytest.mark.parametrize("case", list(MASK_CASES), ids=list(MASK_CASES))
+def test_fused_key_padding_mask(gpu_lib, case):
+    """The fused pair with a key padding mask shaped like an image batch's
+    (the bottom and right parts of every level padded, from valid ratios
+    drawn in [0.6, 0.9]) plus 5% of positions at random."""
+    geom = MASK_CASES[case]
+    if geom is None:
+        ci = build(case)
+    else:
+        wl = workloads.custom(name="mask", offset_sigma_px=2.5, random_valid_ratios=True, backward=True, **geom)
+        ci = build(wl, seed=8)
+    B = ci.value.shape[0]
+    g = torch.Generator().manual_seed(4)
+    vr = 0.6 + 0.3 * torch.rand(B, len(ci.shapes), 2, generator=g)
+    mask = workloads.padding_mask(ci.shapes, vr, seed=9, extra=0.05)
+    assert mask.any() and not mask.all()
+    print(f"[fused mask] {case}: {int(mask.sum())} of {mask.numel()} positions padded", flush=True)
+    check_fused(ci, FWD_TOL, f"mask {case}", mask=mask)
+
+
+def test_fused_key_padding_mask_accumulate_and_bf16(gpu_lib):
+    """With MSDA_BWD_ACCUMULATE the padded rows keep what grad_value held;
+    bf16 value with a mask."""
+    wl = workloads.custom(name="maskacc", batch=2, heads=8, channels=32, points=4,
+                          spatial_shapes=((17, 21), (9, 11), (5, 6), (3, 3)), num_query=None,
+                          value_dtype=torch.bfloat16, offset_sigma_px=2.5, random_valid_ratios=True, backward=True)
+    ci = build(wl, seed=12)
+    mask = workloads.padding_mask(ci.shapes, ci.draws.valid_ratios * 0.8, seed=3, extra=0.05)
+    check_fused(ci, BF16_TOL, "mask bf16", mask=mask)
+    ref32, off, logits = fused_case(ci)
+    _, loc, A = msda.msda_forward_fused(dev(ci.value), ci.shapes, ci.lsi, dev(ref32), dev(off), dev(logits),
+                                        key_padding_mask=dev(mask))
+    base = torch.randn(tuple(ci.value.shape), generator=torch.Generator().manual_seed(2))
+    gv, _, _, _ = msda.msda_backward_fused(dev(ci.value), ci.shapes, ci.lsi, loc, A, dev(ci.grad_output),
+                                           grad_value=dev(base), key_padding_mask=dev(mask))
+    torch.cuda.synchronize()
+    rgv, _, _ = oracle.backward(oracle.masked_fill(ci.value, mask), ci.shapes, ci.lsi, loc.cpu(), A.cpu(),
+                                ci.grad_output)
+    tolerance_check(gv.cpu(), base.double().numpy() + oracle.masked_fill(rgv, mask), BWD_TOL, "mask accumulate")
+    assert torch.equal(gv.cpu()[mask], base[mask])

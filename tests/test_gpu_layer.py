@@ -34,9 +34,10 @@ def _np(t):
     return t.detach().cpu().double().numpy()
 
 
-def _oracle_chain(layer, x, q, ref, lsi, core_in=None):
+def _oracle_chain(layer, x, q, ref, lsi, core_in=None, mask=None):
     """fp64 projections + oracle core. core_in = (value, offsets, logits) fp32
-    tensors to feed the core instead of the fp64 projections."""
+    tensors to feed the core instead of the fp64 projections; mask = a [B,S]
+    key padding mask (the value is filled with zeros there)."""
     M, L, K = layer.n_heads, layer.n_levels, layer.n_points
     B, S, d = x.shape
     Nq = q.shape[1]
@@ -49,6 +50,8 @@ def _oracle_chain(layer, x, q, ref, lsi, core_in=None):
         logits = (_np(q) @ W["a"][0].T + W["a"][1]).reshape(B, Nq, M, L * K)
     else:
         value, off, logits = (_np(t) for t in core_in)
+    if mask is not None:
+        value = oracle.masked_fill(value, mask)
     loc = oracle.sampling_locations(SHAPES, _np(ref), off)
     A = oracle.softmax(logits, L * K).reshape(B, Nq, M, L, K)
     core = oracle.forward(value, SHAPES, lsi, loc, A)
@@ -65,15 +68,31 @@ def test_layer_forward_matches_oracle_chain(gpu_lib):
     tolerance_check(got, want["out"], 1e-4, "layer output")
 
 
-def test_layer_backward_matches_oracle_chain(gpu_lib):
+def _mask(B):
+    from scale_deformable_attention_msdeformattn_amd import workloads
+    vr = torch.tensor([[0.7, 0.8], [0.9, 0.6]]).view(B, 1, 2).expand(B, len(SHAPES), 2)
+    return workloads.padding_mask(SHAPES, vr, seed=2, extra=0.1)
+
+
+def test_layer_forward_with_padding_mask(gpu_lib):
+    layer, x, q, ref, lsi = _case(seed=2)
+    mask = _mask(x.shape[0])
+    got = layer.cuda()(q.cuda(), ref.cuda(), x.cuda(), SHAPES, lsi, mask.cuda()).detach().cpu()
+    want = _oracle_chain(layer.cpu(), x, q, ref, lsi, mask=mask)
+    tolerance_check(got, want["out"], 1e-4, "layer output with padding mask")
+
+
+@pytest.mark.parametrize("masked", [False, True], ids=["no_mask", "padding_mask"])
+def test_layer_backward_matches_oracle_chain(gpu_lib, masked):
     """Gradients of <R, layer(...)> w.r.t. the input, the query and the
     reference points, against the oracle's chain evaluated at the GPU's own
     projection outputs (so that the core sees identical inputs)."""
     layer, x, q, ref, lsi = _case(seed=1)
+    mask = _mask(x.shape[0]) if masked else None
     M, L, K = layer.n_heads, layer.n_levels, layer.n_points
     layer = layer.cuda()
     xg, qg, rg = (t.cuda().requires_grad_(True) for t in (x, q, ref))
-    out = layer(qg, rg, xg, SHAPES, lsi)
+    out = layer(qg, rg, xg, SHAPES, lsi, None if mask is None else mask.cuda())
     R = torch.randn(out.shape, device="cuda")
     out.backward(R)
     with torch.no_grad():
@@ -82,9 +101,11 @@ def test_layer_backward_matches_oracle_chain(gpu_lib):
         value = layer.value_proj(xg).view(B, S, M, d // M)
         off = layer.sampling_offsets(qg).view(B, Nq, M, L, K, 2)
         logits = layer.attention_weights(qg).view(B, Nq, M, L * K)
-    c = _oracle_chain(layer.cpu(), x, q, ref, lsi, core_in=(value, off, logits))
+    c = _oracle_chain(layer.cpu(), x, q, ref, lsi, core_in=(value, off, logits), mask=mask)
     g_core = _np(R) @ c["W"]["out"][0]
     gv, gl, ga = oracle.backward(c["value"], SHAPES, lsi, c["loc"], c["A"], g_core)
+    if mask is not None:
+        gv = oracle.masked_fill(gv, mask)
     g_ref, g_off = oracle.sampling_locations_backward(SHAPES, gl)
     g_logits = oracle.softmax_backward(c["A"], ga, L * K)
     g_x = gv.reshape(B, S, d) @ c["W"]["v"][0]

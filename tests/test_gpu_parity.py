@@ -70,21 +70,17 @@ def test_forward_workloads(gpu_lib, name):
     check_forward(build(name), name=name)
 
 
-def test_forward_bf16_large_sampled_queries(gpu_lib):
-    """B=8, S=Nq=22223 bf16 value, in the same launch configuration the bench
-    times; the oracle computes a sample of queries one by one."""
-    print("[forward parity] encoder_bf16_large (sampled)", flush=True)
+def test_forward_bf16_large_every_element(gpu_lib):
+    """B=8, S=Nq=22223 bf16 value (177,784 queries, 22.8M samples), in the
+    launch configuration the bench times (the kernel with the coarse levels
+    staged in LDS): every output element against the oracle."""
+    print("[forward parity] encoder_bf16_large (every element)", flush=True)
     ci = build("encoder_bf16_large")
-    B, Nq = ci.loc.shape[:2]
-    out = run_forward(ci).reshape(B * Nq, -1)
-    rng = np.random.default_rng(0)
-    ids = np.unique(np.concatenate([rng.integers(0, B * Nq, 3000), [0, 1, Nq - 1, Nq, B * Nq - 1],
-                                    np.arange(B * Nq - 64, B * Nq)]))
-    ref = oracle.forward(ci.value, ci.shapes, ci.lsi, ci.loc, ci.attn, query_ids=ids)
-    tolerance_check(out[ids], ref, BF16_TOL, "forward bf16 sampled")
-    # context only: the bf16 path is much closer than its bound
-    err = np.abs(out[ids].numpy() - ref).max()
-    assert err < 1e-4, err
+    out = run_forward(ci)
+    ref = oracle.forward(ci.value, ci.shapes, ci.lsi, ci.loc, ci.attn)
+    tolerance_check(out, ref, BF16_TOL, "forward bf16 large")
+    # context only: with fp32 accumulation the bf16 path is far inside its bound
+    assert float(np.abs(out.numpy() - ref).max()) < 1e-4
 
 
 @pytest.mark.parametrize("name", ["tiny", "encoder_backward"])

@@ -11,6 +11,7 @@ from oracle import build as obuild
 from tests import test_oracle_backward as tb
 from tests import test_oracle_forward as tf
 from tests import test_oracle_fused_grads as tg
+from tests import test_oracle_mask as tmk
 from tests import test_oracle_prologue as tp
 
 
@@ -46,6 +47,13 @@ def _fused_grad_pins():
     tg.test_box_locations_reduce_to_pixel_offsets()
     tg.test_box_locations_worked_value()
     tg.test_box_locations_backward_central_differences()
+
+
+def _mask_pins():
+    tmk.test_mask_fill_identity_zero_idempotent_and_self_adjoint()
+    tmk.test_masking_rows_no_corner_touches_changes_nothing()
+    tmk.test_masked_pixel_centre_reads_zero()
+    tmk.test_masked_chain_gradient_by_central_differences()
 
 
 MUTANTS = [
@@ -85,6 +93,9 @@ MUTANTS = [
      _fused_grad_pins),
     ("box_grad_wh_term", "gr[2] += grad_loc[idx + 0] * offset[idx + 0] * 0.5 / (double)K;",
      "gr[2] += grad_loc[idx + 0] * offset[idx + 0] / (double)K;", _fused_grad_pins),
+    ("mask_inverted", "mask[b * S + s] ? 0.0 : x[(b * S + s) * C + c]", "mask[b * S + s] ? x[(b * S + s) * C + c] : 0.0",
+     _mask_pins),
+    ("mask_wrong_row", "mask[b * S + s] ? 0.0", "mask[s] ? 0.0", _mask_pins),
 ]
 
 
