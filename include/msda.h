@@ -57,7 +57,7 @@ extern "C" {
 #define MSDA_API
 #endif
 
-#define MSDA_ABI_VERSION 9
+#define MSDA_ABI_VERSION 10
 #define MSDA_MAX_LEVELS 16
 
 typedef enum {
@@ -189,6 +189,28 @@ MSDA_API int msda_backward(const msda_shape *shape, const void *value, msda_dtyp
                   const float *grad_output, float *grad_value,
                   float *grad_sampling_locations, float *grad_attention_weights,
                   void *workspace, size_t workspace_bytes, unsigned flags, void *stream);
+
+/* Bytes of device scratch that msda_backward_noalloc holds (per GPU). */
+#define MSDA_NOALLOC_SCRATCH_BYTES (96u * 1024u * 1024u)
+
+/* msda_backward for callers that cannot allocate device memory during the
+ * call (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same arguments, results and status codes as
+ * msda_backward, without the workspace. Its scratch is a device array inside
+ * the library, MSDA_NOALLOC_SCRATCH_BYTES (96 MiB) per GPU, which each GPU
+ * the library runs on holds until the process ends; its address is resolved
+ * on the first call per device. Sizes whose workspace
+ * (msda_backward_workspace_size) exceeds it return MSDA_E_WORKSPACE before
+ * any device work. The call allocates nothing, creates no stream or event
+ * (the dense levels run on `stream` too, and the timing aid records nothing
+ * for it) and leaves no state in the scratch that a later call relies on.
+ * All calls on one GPU share that GPU's scratch: calls that may overlap in
+ * time on one GPU (other streams, other host threads) race and must not be
+ * made. */
+MSDA_API int msda_backward_noalloc(const msda_shape *shape, const void *value, msda_dtype value_dtype,
+                                   const float *sampling_locations, const float *attention_weights,
+                                   const float *grad_output, float *grad_value, float *grad_sampling_locations,
+                                   float *grad_attention_weights, unsigned flags, void *stream);
 
 /* Fused forward (the adjacent steps formed inside the core): for every sample
  *   loc = reference_points[b,q,l] + sampling_offsets[b,q,m,l,k] / (W_l, H_l)

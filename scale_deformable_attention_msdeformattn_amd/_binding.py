@@ -98,6 +98,8 @@ def load():
     lib.msda_backward.restype = ctypes.c_int
     lib.msda_backward.argtypes = [_shp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                                   ctypes.c_uint, _vp]
+    lib.msda_backward_noalloc.restype = ctypes.c_int
+    lib.msda_backward_noalloc.argtypes = [_shp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_uint, _vp]
     lib.msda_forward_fused.restype = ctypes.c_int
     lib.msda_forward_fused.argtypes = [_shp, _vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp,
                                        _vp]
@@ -312,6 +314,32 @@ def msda_backward(value: torch.Tensor, spatial_shapes, level_start_index, sampli
     ws, nbytes = _workspace(sh, value.device)
     _check(load().msda_backward(sh.ptr, _p(value), vt, _p(loc), _p(attn), _p(go), _p(grad_value), _p(gl),
                                 _p(ga), _p(ws), nbytes, flags, _stream(go)), "msda_backward")
+    return grad_value, gl, ga
+
+
+def msda_backward_noalloc(value: torch.Tensor, spatial_shapes, level_start_index, sampling_locations: torch.Tensor,
+                          attention_weights: torch.Tensor, grad_output: torch.Tensor,
+                          grad_value: Optional[torch.Tensor] = None):
+    """msda_backward through the entry point that allocates nothing (its
+    scratch is the library's own device array); outputs as msda_backward."""
+    value, loc, attn, sh, vt = _core_shape(value, spatial_shapes, level_start_index, sampling_locations,
+                                           attention_weights)
+    B, S, M, D = value.shape
+    go = _dev(grad_output, "grad_output")
+    if tuple(go.shape) != (B, loc.shape[1], M * D):
+        raise ValueError(f"grad_output must be {(B, loc.shape[1], M * D)}, got {tuple(go.shape)}")
+    flags = 0
+    if grad_value is None:
+        grad_value = torch.empty(B, S, M, D, dtype=torch.float32, device=value.device)
+    else:
+        if grad_value.dtype != torch.float32 or tuple(grad_value.shape) != (B, S, M, D) or \
+                not grad_value.is_contiguous():
+            raise ValueError("grad_value to accumulate into must be a contiguous fp32 [B,S,M,D] tensor")
+        flags = MSDA_BWD_ACCUMULATE
+    gl = torch.empty_like(loc)
+    ga = torch.empty_like(attn)
+    _check(load().msda_backward_noalloc(sh.ptr, _p(value), vt, _p(loc), _p(attn), _p(go), _p(grad_value), _p(gl),
+                                        _p(ga), flags, _stream(go)), "msda_backward_noalloc")
     return grad_value, gl, ga
 
 

@@ -258,6 +258,45 @@ int msda_backward(const msda_shape *shape, const void *value, msda_dtype value_d
                     "backward");
 }
 
+int msda_backward_noalloc(const msda_shape *shape, const void *value, msda_dtype value_dtype,
+                          const float *sampling_locations, const float *attention_weights, const float *grad_output,
+                          float *grad_value, float *grad_sampling_locations, float *grad_attention_weights,
+                          unsigned flags, void *stream)
+{
+    msda::Geometry g;
+    if (int st = make_geometry(shape, g)) return st;
+    if (flags & ~MSDA_BWD_ACCUMULATE) return fail(MSDA_E_UNSUPPORTED, "unknown flags 0x%x", flags);
+    const bool accumulate = (flags & MSDA_BWD_ACCUMULATE) != 0;
+    if (g.B == 0) return ok();
+    msda::TimingOff no_events;
+    if (g.Nq == 0) {  // no queries: grad_value is all zeros (or left as is when accumulating)
+        if (accumulate) return ok();
+        if (!grad_value) return fail(MSDA_E_NULL, "grad_value is NULL");
+        if (!aligned(grad_value, 4)) return fail(MSDA_E_ALIGN, "grad_value needs 4-byte alignment");
+        return launched(msda::launch_zero_fill(grad_value, (int64_t)g.B * g.S * g.M * g.D, (hipStream_t)stream),
+                        "zero_fill");
+    }
+    if (int st = check_core(g, value, value_dtype, sampling_locations, attention_weights)) return st;
+    if (!grad_output || !grad_value || !grad_sampling_locations || !grad_attention_weights)
+        return fail(MSDA_E_NULL, "NULL gradient tensor");
+    if (!aligned(grad_output, 4) || !aligned(grad_value, 4) || !aligned(grad_sampling_locations, 8) ||
+        !aligned(grad_attention_weights, 4))
+        return fail(MSDA_E_ALIGN, "gradient tensors need 4-byte (locations 8-byte) alignment");
+    void *scratch = nullptr;
+    if (msda::backward_uses_workspace(g, value, value_dtype, grad_output, grad_value)) {
+        const size_t need = msda::backward_workspace_bytes(g);
+        if (need > msda::kNoAllocScratchBytes)
+            return fail(MSDA_E_WORKSPACE, "these sizes need %zu bytes of scratch; msda_backward_noalloc holds %zu",
+                        need, msda::kNoAllocScratchBytes);
+        const hipError_t e = msda::noalloc_scratch(&scratch);
+        if (e != hipSuccess) return fail(MSDA_E_HIP, "scratch address: %s", hipGetErrorString(e));
+    }
+    return launched(msda::launch_backward(g, value, value_dtype, sampling_locations, attention_weights, grad_output,
+                                          grad_value, grad_sampling_locations, grad_attention_weights, scratch,
+                                          accumulate, false, (hipStream_t)stream),
+                    "backward_noalloc");
+}
+
 int msda_forward_fused(const msda_shape *shape, const void *value, msda_dtype value_dtype,
                        const float *reference_points, int reference_dims, const float *sampling_offsets,
                        const float *attention_logits, const uint8_t *key_padding_mask, float *output,

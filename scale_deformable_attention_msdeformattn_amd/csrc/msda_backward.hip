@@ -43,6 +43,7 @@
 // their records over several workgroups whose partials meet in atomics.
 // Shapes outside the fast path use one thread per (b, q, m) with float atomics.
 #include <algorithm>
+#include <mutex>
 
 #include "msda_device.h"
 #include "msda_internal.h"
@@ -1618,6 +1619,35 @@ hipError_t launch_backward_fused(const Geometry &g, const void *value, msda_dtyp
                                       fg.mask, st);
     return launch_typed<float>(g, tpp, value, loc, attn, go, gv, goff, glogits, &fg, ws, accumulate, side_ok,
                                fg.mask, st);
+}
+
+// ---------------------------------------------------- allocation-free scratch
+
+// The workspace of msda_backward_noalloc: a file-scope device array (each GPU
+// the library runs on holds its own copy, at its own address, until the
+// process ends). Host code never passes `scratch` itself to a kernel (on the
+// host it is only a stand-in for the symbol): the device address comes from
+// hipGetSymbolAddress, once per device, and is used everywhere instead.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void **out)
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return hipSuccess;
 }
 
 }  // namespace msda

@@ -135,6 +135,23 @@ inline bool fused_forward_supported(const Geometry &g)
     return lk <= 64 && (64 % lk) == 0;
 }
 
+// Largest workspace msda_backward_noalloc serves from its device array.
+constexpr size_t kNoAllocScratchBytes = (size_t)MSDA_NOALLOC_SCRATCH_BYTES;
+
+// The calling device's address of that array (resolved with
+// hipGetSymbolAddress on the first call per device, then cached).
+hipError_t noalloc_scratch(void **out);
+
+// While an object of this type lives, the calling thread's launches record no
+// timing events (the allocation-free entry point creates no events).
+class TimingOff {
+  public:
+    TimingOff();
+    ~TimingOff();
+    TimingOff(const TimingOff &) = delete;
+    TimingOff &operator=(const TimingOff &) = delete;
+};
+
 // Launchers (each returns a hipError_t from the launch).
 hipError_t launch_reference_points(const Geometry &g, const float *valid_ratios,
                                    const float *query_ref, float *ref_out, hipStream_t st);

@@ -25,6 +25,7 @@ bool g_enabled = false;
 std::vector<Pending> g_pending;
 std::vector<hipEvent_t> g_pool;  // recycled events
 std::vector<Entry> g_entries;
+thread_local int g_suppressed = 0;  // TimingOff scopes open on this thread
 
 hipEvent_t take_event()
 {
@@ -68,8 +69,12 @@ hipError_t drain(bool discard)
 
 }  // namespace
 
+TimingOff::TimingOff() { ++g_suppressed; }
+TimingOff::~TimingOff() { --g_suppressed; }
+
 KernelScope::KernelScope(const char *name, hipStream_t st) : name_(name), st_(st), start_(nullptr)
 {
+    if (g_suppressed) return;
     std::lock_guard<std::mutex> lock(g_mu);
     if (!g_enabled) return;
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;

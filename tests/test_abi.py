@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.msda_abi_version() == 9
+    assert lib.msda_abi_version() == 10
     assert lib.msda_status_string(0) == b"ok"
     for code in range(-8, 0):
         assert lib.msda_status_string(code) not in (b"", b"unknown status")
@@ -255,3 +255,28 @@ def test_backward_plan_per_level(lib):
     # empty calls have no plan either, and NULL outputs are allowed
     assert B.msda_backward_plan(_shape(B_=0)) == {"dense": [], "direct": [], "split": []}
     assert lib.msda_backward_plan(_shape().ptr, None, None, None) == B.MSDA_OK
+
+
+@cpu_only
+def test_backward_noalloc_validates_on_the_host(lib):
+    """msda_backward_noalloc refuses bad arguments, and sizes whose workspace
+    exceeds its fixed scratch, before any device work."""
+    f = lib.msda_backward_noalloc
+
+    def call(sh, flags=0, grads=(FAKE, FAKE, FAKE, FAKE), value=FAKE):
+        return f(sh.ptr, value, B.MSDA_F32, FAKE, FAKE, *grads, flags, None)
+
+    sh = _shape()
+    assert call(sh, flags=0x2) == B.MSDA_E_UNSUPPORTED
+    assert call(sh, grads=(FAKE, None, FAKE, FAKE)) == B.MSDA_E_NULL
+    assert call(sh, grads=(FAKE, FAKE, MISALIGNED, FAKE)) == B.MSDA_E_ALIGN
+    assert call(sh, value=None) == B.MSDA_E_NULL
+    assert call(_shape(B_=0)) == B.MSDA_OK
+    # the large-batch pyramid at B=8 needs far more workspace than the scratch
+    big = _shape(B_=8, shapes=((100, 167), (50, 84), (25, 42), (13, 21)))
+    need = B.msda_backward_workspace_size(big)
+    assert need > 96 * 2**20
+    assert call(big) == B.MSDA_E_WORKSPACE
+    assert b"scratch" in lib.msda_last_error()
+    # the encoder step's backward fits
+    assert B.msda_backward_workspace_size(_shape()) <= 96 * 2**20
