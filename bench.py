@@ -155,8 +155,12 @@ def algorithmic_bytes(B, M, D, Nq, shapes, K, vbytes):
         "zero_fill_kernel": S * gv_row,
         "clear_totals_kernel": 0,
         "bin_count_kernel": sparse_samples * 2 * f32,
+        # the same binning grouped per (batch, head, query range)
+        "bin_count_head_kernel": sparse_samples * 2 * f32,
         # value rows, loc, A, grad_output in; grad_loc, grad_A out
         "backward_c256_kernel": vbytes + samples * 3 * f32 + rows + samples * 3 * f32,
+        # the same outputs per (batch, head, query range), coarse levels staged in LDS
+        "backward_head_kernel": vbytes + samples * 3 * f32 + rows + samples * 3 * f32,
         # sparse levels: grad_output, their loc and A in, their grad_value rows
         # out; the sums of split dense levels ride along as extra items
         "tile_accum_kernel": rows + sparse_samples * 3 * f32 + (S - dense_pix + split_pix) * gv_row,
@@ -209,8 +213,9 @@ def _short_kernel_name(full):
     """'void ns::(anonymous namespace)::name<T, 8>(args)' -> 'name'. The fused
     instantiations of the c256 and staged kernels (last template argument
     true) get the names the library's own timing uses for them,
-    forward_fused_c256_kernel, backward_fused_c256_kernel and
-    forward_fused_staged_kernel, so their counters are kept apart."""
+    forward_fused_c256_kernel, backward_fused_c256_kernel,
+    forward_fused_staged_kernel and backward_fused_head_kernel, so their
+    counters are kept apart."""
     head = full.replace("(anonymous namespace)", "")
     tmpl = head.split("(")[0]
     name = tmpl.split("<")[0]
@@ -219,6 +224,8 @@ def _short_kernel_name(full):
         name = name.replace("_c256", "_fused_c256")
     if name == "forward_staged_kernel" and tmpl.rstrip().endswith("true>"):
         name = "forward_fused_staged_kernel"
+    if name == "backward_head_kernel" and tmpl.rstrip().endswith("true>"):
+        name = "backward_fused_head_kernel"
     return name
 
 
@@ -776,6 +783,8 @@ def main():
     # the forward kernel this shape takes (coarse levels staged in LDS, or one wave per query)
     fwd_name = next((k for k in ("forward_staged_kernel", "forward_c256_kernel") if k in kstats), None)
     fwd = kstats.get(fwd_name, {}) if fwd_name else {}
+    # the backward's main kernel on this shape (per head with staged levels, or per query)
+    bwd_main = next((k for k in ("backward_head_kernel", "backward_c256_kernel") if k in kstats), None)
     result = {
         "metric": METRIC,
         "value": queries / (step_ms * 1e-3),
@@ -822,12 +831,13 @@ def main():
                      "cold_queries_per_s": None if cold is None else
                      queries / (cold["entry_points_us"]["msda_backward"] * 1e-6),
                      "note": "the whole msda_backward call, all its kernels",
-                     "main_kernel_gather": None if "backward_c256_kernel" not in kstats else {
-                         "corner_reads": corner_reads, "bytes": corner_reads * D * elem,
-                         "tbps": round(corner_reads * D * elem / (kstats["backward_c256_kernel"]["avg_us"] * 1e-6)
+                     "main_kernel_gather": None if bwd_main is None else {
+                         "kernel": bwd_main, "corner_reads": corner_reads, "bytes": corner_reads * D * elem,
+                         "tbps": round(corner_reads * D * elem / (kstats[bwd_main]["avg_us"] * 1e-6)
                                        / 1e12, 2),
-                         "note": "backward_c256 gathers the same in-map corner rows as the forward, all through "
-                                 "the L1/L2 path (31-36 TB/s measured ceiling on 256 CUs)"}},
+                         "note": "the main backward kernel gathers the same in-map corner rows as the forward "
+                                 "(the per-head kernel serves the coarse levels' from LDS, the per-query kernel all "
+                                 "through the L1/L2 path, 31-36 TB/s measured ceiling on 256 CUs)"}},
         "fused_step": None if fused_ms is None else {
             "ms_per_step": fused_ms, "queries_per_s": queries / (fused_ms * 1e-3),
             "kernels_avg_us": {k: round(v[0] * 1e3 / v[1], 3) for k, v in timing_fused.items()},

@@ -509,6 +509,417 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
     }
 }
 
+// ------------------------------------------- 2b. per-head path (8x4x4 shapes)
+
+// The main kernel above serves a query with all its heads, so every corner of
+// every level comes through the cache-side gather path. On the shapes the
+// forward stages (8 heads, 4 levels, 4 points, many queries) the backward
+// takes this path instead: one workgroup per (batch, head, range of queries),
+// the head's coarse-level rows staged in LDS as in the forward, QPW queries
+// of the head side by side in a wave. Its binning is grouped the same way, so
+// each workgroup's record cursors cover the tiles of its own head only.
+constexpr int kHeadWaves = 16;
+constexpr int kHeadThreads = kHeadWaves * kWave;
+constexpr int kHeadTargetWGs = 512;       // as the forward: two rounds of one workgroup per CU
+constexpr int kHeadMinQueries = 1024;     // fewer queries per (batch, head) do not repay the staging
+constexpr size_t kHeadLds = 160 * 1024;   // gfx950
+
+// Workgroup (b, m, r) counts, for head m, the samples of queries
+// [r * hqpr, (r + 1) * hqpr) on the sparse levels per tile of that head (an
+// LDS histogram), then reserves its range in each touched tile's record list
+// with one global atomic add per tile.
+template <int M, int L, int K>
+__global__ void __launch_bounds__(kBinThreads)
+bin_count_head_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, uint32_t *__restrict__ offsets,
+                      uint32_t *__restrict__ totals)
+{
+    extern __shared__ uint32_t s_hist[];  // [tpb]
+    __shared__ LevelRec s_lv[L];
+    __shared__ TileLevel s_tl[L];
+    __shared__ int s_sparse[L];
+    const int nkeys = tp.tpb;
+    for (int i = threadIdx.x; i < nkeys; i += kBinThreads) s_hist[i] = 0;
+    if (threadIdx.x < L) {
+        const int l = threadIdx.x;
+        s_lv[l] = LevelRec{(float)g.lv.W[l], (float)g.lv.H[l], g.lv.W[l], g.lv.start[l]};
+        s_tl[l] = tile_level(tp, l);
+    }
+    int nsl = 0;
+#pragma unroll
+    for (int l = 0; l < L; ++l)
+        if (!((tp.dense_mask >> l) & 1)) {
+            if (threadIdx.x == 0) s_sparse[nsl] = l;
+            ++nsl;
+        }
+    __syncthreads();
+    const int w = blockIdx.x;
+    const int bm = w / tp.hqr, r = w - (w / tp.hqr) * tp.hqr;
+    const int b = bm / M, m = bm - (bm / M) * M;
+    const int q0 = r * tp.hqpr, q1 = min(q0 + tp.hqpr, g.Nq);
+    const int nblk = (q1 - q0) * nsl;
+    for (int i = threadIdx.x; i < nblk; i += kBinThreads) {
+        const int qi = i / nsl;
+        const int l = s_sparse[i - qi * nsl];
+        const LevelRec lv = s_lv[l];
+        const int H = (int)lv.Hf;
+        const float2 *u = loc + ((((int64_t)b * g.Nq + q0 + qi) * M + m) * L + l) * K;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            int cx, cy;
+            float fx, fy;
+            if (!sample_cell(u[k], lv.Wf, lv.Hf, cx, cy, fx, fy)) continue;
+            const SampleTiles st = sample_tiles(s_tl[l], lv.W, H, cx, cy);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (st.t[j] >= 0) atomicAdd(&s_hist[st.t[j]], 1u);
+        }
+    }
+    __syncthreads();
+    uint32_t *row = offsets + (int64_t)w * nkeys;
+    uint32_t *tot = totals + (int64_t)bm * nkeys;
+    constexpr int kKeysInFlight = 8;
+    for (int i0 = threadIdx.x; i0 < nkeys; i0 += kBinThreads * kKeysInFlight) {
+        uint32_t rv[kKeysInFlight];
+#pragma unroll
+        for (int j = 0; j < kKeysInFlight; ++j) {
+            const int i = i0 + j * kBinThreads;
+            const uint32_t c = i < nkeys ? s_hist[i] : 0u;
+            rv[j] = c ? atomicAdd(&tot[i], c) : 0u;
+        }
+#pragma unroll
+        for (int j = 0; j < kKeysInFlight; ++j) {
+            const int i = i0 + j * kBinThreads;
+            if (i < nkeys && s_hist[i]) row[i] = rv[j];
+        }
+    }
+}
+
+// The per-head main kernel: grad_attn and grad_loc of head m for a range of
+// queries, and the record lists of the sparse levels' tiles. The records of
+// head (b, m) fill [(b*M + m) * 4 * Nq * L * K, ...) tile after tile (a sample
+// lands in at most four tiles); the workgroup scans its head's tile totals
+// into its cursors, and the head's first workgroup publishes the list bases.
+//
+// FUSED: the gradients of the fused forward's inputs (as the main kernel's
+// fused form): grad_loc becomes the offsets' gradient and grad_attn the
+// logits' (the L*K softmax of the head's samples sits in adjacent lanes of
+// phase 3). The reference-point gradient sums over heads, which live in other
+// workgroups, so each workgroup writes its head's sums over the K points to
+// ref_part[b, q, m, l] and ref_grad_sum_kernel adds the heads in order.
+template <typename VT, int M, int L, int K, int LS, bool FUSED>
+__global__ void __launch_bounds__(kHeadThreads)
+backward_head_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, const float2 *__restrict__ loc,
+                     const float *__restrict__ attn, const float4 *__restrict__ grad_out,
+                     float2 *__restrict__ grad_loc, float *__restrict__ grad_attn,
+                     const uint32_t *__restrict__ offsets, const uint32_t *__restrict__ totals,
+                     uint32_t *__restrict__ bases, uint32_t *__restrict__ records, uint32_t stage_bytes,
+                     uint32_t grid, const uint8_t *__restrict__ mask, FusedGrads fg, float4 *__restrict__ ref_part)
+{
+    constexpr int C = 256;
+    constexpr int D = C / M;
+    constexpr int LPH = D / 4;         // lanes (4 channels each) per query
+    constexpr int QPW = kWave / LPH;   // queries side by side in a wave
+    constexpr int LK = L * K;
+    constexpr int PAD = LK + 1;
+    constexpr int NPASS = (QPW * LK + kWave - 1) / kWave;  // samples per lane in phase 1
+    constexpr uint32_t RB = C * sizeof(VT);
+    static_assert(0 < LS && LS < L, "some levels from memory, some from LDS");
+    using Chunk = typename StageChunk<VT>::type;
+
+    extern __shared__ __align__(16) unsigned char s_raw[];
+    Chunk *s_stage = reinterpret_cast<Chunk *>(s_raw);                      // [(rows + 1) * LPH]
+    uint32_t *s_cursor = reinterpret_cast<uint32_t *>(s_raw + stage_bytes);  // [tpb + kWave]
+    __shared__ LevelRec s_lv[L];
+    __shared__ TileLevel s_tl[L];
+    __shared__ int4 s_off[kHeadWaves][QPW * PAD];
+    // (fx, fy, A*W_l, A*H_l) per sample, overwritten in place by (grad_attn,
+    // grad_x, grad_y, -) once the wave has read it
+    __shared__ float4 s_geo[kHeadWaves][QPW * PAD];
+    __shared__ uint32_t s_wsum[kHeadWaves];
+
+    const int lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint32_t wg = xcd_tile(blockIdx.x, grid);
+    if (wg >= (uint32_t)(g.B * M * tp.hqr)) return;  // whole workgroup: before any barrier
+    const int bm = (int)(wg / tp.hqr), r = (int)(wg - (wg / tp.hqr) * tp.hqr);
+    const int b = bm / M, m = bm - (bm / M) * M;
+    const int q0 = r * tp.hqpr, q1 = min(q0 + tp.hqpr, g.Nq);
+    const int nkeys = tp.tpb;
+    if (threadIdx.x < L) {
+        const int l = threadIdx.x;
+        s_lv[l] = LevelRec{(float)g.lv.W[l], (float)g.lv.H[l], g.lv.W[l], g.lv.start[l]};
+        s_tl[l] = tile_level(tp, l);
+    }
+    // head m's rows of the staged levels, then a zero row that off-map
+    // corners read; rows at padded positions are staged as zeros
+    const int srow0 = g.lv.start[LS];
+    const int nrows = g.S - srow0;
+    {
+        constexpr int kStageBatch = 8;
+        const Chunk *src = reinterpret_cast<const Chunk *>(value + ((int64_t)b * g.S + srow0) * C + m * D);
+        const int n = nrows * LPH;
+        for (int i0 = threadIdx.x; i0 < n; i0 += kHeadThreads * kStageBatch) {
+            Chunk v[kStageBatch];
+#pragma unroll
+            for (int k = 0; k < kStageBatch; ++k) {
+                const int i = i0 + k * kHeadThreads;
+                const bool keep = i < n && !(mask && mask[(int64_t)b * g.S + srow0 + i / LPH]);
+                v[k] = keep ? src[(int64_t)(i / LPH) * (C / 4) + i % LPH] : StageChunk<VT>::zero();
+            }
+#pragma unroll
+            for (int k = 0; k < kStageBatch; ++k) {
+                const int i = i0 + k * kHeadThreads;
+                if (i < n) s_stage[i] = v[k];
+            }
+        }
+        if (threadIdx.x < LPH) s_stage[nrows * LPH + threadIdx.x] = StageChunk<VT>::zero();
+    }
+    // the record cursors of head (b, m)'s tiles: region base + exclusive
+    // prefix of the tile totals + this workgroup's reserved offset
+    const uint32_t *tot = totals + (int64_t)bm * nkeys;
+    for (int i = threadIdx.x; i < nkeys; i += kHeadThreads) s_cursor[i] = tot[i];
+    if (threadIdx.x < kWave) s_cursor[nkeys + threadIdx.x] = 0;  // lanes' idle slots
+    __syncthreads();
+    {
+        const int per = (nkeys + kHeadThreads - 1) / kHeadThreads;
+        const int i0 = min((int)threadIdx.x * per, nkeys), i1 = min(i0 + per, nkeys);
+        uint32_t sum = 0;
+        for (int i = i0; i < i1; ++i) sum += s_cursor[i];
+        uint32_t incl = sum;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const uint32_t t = __shfl_up(incl, o, kWave);
+            if (lane >= o) incl += t;
+        }
+        if (lane == kWave - 1) s_wsum[wave] = incl;
+        __syncthreads();
+        uint32_t run = (uint32_t)bm * 4u * (uint32_t)(g.Nq * LK) + incl - sum;
+        for (int v = 0; v < wave; ++v) run += s_wsum[v];
+        for (int i = i0; i < i1; ++i) {
+            const uint32_t c = s_cursor[i];
+            s_cursor[i] = run;
+            run += c;
+        }
+        __syncthreads();
+        const uint32_t *off = offsets + (int64_t)wg * nkeys;
+        for (int i = threadIdx.x; i < nkeys; i += kHeadThreads) {
+            const uint32_t base = s_cursor[i];
+            if (r == 0) bases[(int64_t)bm * nkeys + i] = base;
+            s_cursor[i] = base + off[i];
+        }
+    }
+    __syncthreads();
+
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(value + (int64_t)b * g.S * C, (uint32_t)g.S * RB);
+    const int jq = lane / LPH, c = lane - (lane / LPH) * LPH;
+    const uint32_t lane_off = (uint32_t)(m * D + c * 4) * sizeof(VT);
+    const int zero_row = nrows * LPH;
+    const uint32_t rcap = (uint32_t)g.B * 4u * (uint32_t)(g.Nq * M * LK);  // record slots
+    for (int qb = q0 + wave * QPW; qb < q1; qb += kHeadWaves * QPW) {
+        // the lane index, opaque to the compiler within each pass (what phase 1
+        // derives from it is recomputed per pass, not held across the loop)
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        // ---- phase 1: the QPW*L*K samples of this pass, one per lane per step ----
+        int keys[NPASS][4];
+#pragma unroll
+        for (int p = 0; p < NPASS; ++p) {
+            const int t = p * kWave + ln;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) keys[p][j] = nkeys + ln;
+            if ((QPW * LK) % kWave == 0 || t < QPW * LK) {
+                const int j = t / LK, i = t - (t / LK) * LK;
+                const int l = i / K;
+                const bool staged = l >= LS;
+                const int q = qb + j;
+                int4 o = staged ? make_int4(zero_row, zero_row, zero_row, zero_row)
+                                : make_int4((int)kOutOfRange, (int)kOutOfRange, (int)kOutOfRange, (int)kOutOfRange);
+                float4 geo = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (q < q1) {
+                    const int64_t si = (((int64_t)b * g.Nq + q) * M + m) * LK + i;
+                    const LevelRec lv = s_lv[l];
+                    int cx, cy;
+                    float fx, fy;
+                    const bool in = sample_cell(loc[si], lv.Wf, lv.Hf, cx, cy, fx, fy);
+                    const float a = attn[si];
+                    const int H = (int)lv.Hf;
+                    const bool x0ok = in & (cx >= 0) & (cx < lv.W);
+                    const bool x1ok = in & (cx + 1 >= 0) & (cx + 1 < lv.W);
+                    const bool y0ok = (cy >= 0) & (cy < H);
+                    const bool y1ok = (cy + 1 >= 0) & (cy + 1 < H);
+                    const int row = lv.start + cy * lv.W + cx;
+                    bool k00 = y0ok & x0ok, k01 = y0ok & x1ok, k10 = y1ok & x0ok, k11 = y1ok & x1ok;
+                    if (staged) {
+                        const int r00 = (row - srow0) * LPH, r10 = r00 + lv.W * LPH;
+                        o.x = k00 ? r00 : zero_row;
+                        o.y = k01 ? r00 + LPH : zero_row;
+                        o.z = k10 ? r10 : zero_row;
+                        o.w = k11 ? r10 + LPH : zero_row;
+                    } else {
+                        if (mask) unmask_corners(mask + (int64_t)b * g.S, row, lv.W, k00, k01, k10, k11);
+                        const uint32_t o00 = (uint32_t)row * RB, o10 = o00 + (uint32_t)lv.W * RB;
+                        o.x = (int)(k00 ? o00 : kOutOfRange);
+                        o.y = (int)(k01 ? o00 + RB : kOutOfRange);
+                        o.z = (int)(k10 ? o10 : kOutOfRange);
+                        o.w = (int)(k11 ? o10 + RB : kOutOfRange);
+                    }
+                    geo = make_float4(fx, fy, a * lv.Wf, a * lv.Hf);
+                    if (in && !((tp.dense_mask >> l) & 1)) {
+                        const SampleTiles st = sample_tiles(s_tl[l], lv.W, H, cx, cy);
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj)
+                            if (st.t[jj] >= 0) keys[p][jj] = st.t[jj];
+                    }
+                }
+                s_off[wave][j * PAD + i] = o;
+                s_geo[wave][j * PAD + i] = geo;
+            }
+        }
+        wave_lds_sync();
+        // ---- phase 2: each lane its query's samples; gathers, dots with G, sums over the query's lanes ----
+        const int qg = qb + jq;
+        const float4 G = qg < q1 ? grad_out[((int64_t)b * g.Nq + qg) * (C / 4) + m * LPH + c]
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+        const int4 *offs = &s_off[wave][jq * PAD];
+        const float4 *geo = &s_geo[wave][jq * PAD];
+        float4 *res = &s_geo[wave][jq * PAD];
+        auto grad_sample = [&](int i, const float4 &v00, const float4 &v01, const float4 &v10, const float4 &v11) {
+            const float4 f = geo[i];
+            const float d00 = dot4(G, v00), d01 = dot4(G, v01);
+            const float d10 = dot4(G, v10), d11 = dot4(G, v11);
+            const float fx = f.x, fy = f.y;
+            const float hx = 1.0f - fx, hy = 1.0f - fy;
+            float ga = hy * (hx * d00 + fx * d01) + fy * (hx * d10 + fx * d11);
+            float gx = hy * (d01 - d00) + fy * (d11 - d10);
+            float gy = hx * (d10 - d00) + fx * (d11 - d01);
+            ga = group_sum<LPH>(ga);
+            gx = group_sum<LPH>(gx);
+            gy = group_sum<LPH>(gy);
+            res[i] = make_float4(ga, f.z * gx, f.w * gy, 0.0f);  // the query's lanes all write the same
+        };
+        auto staged_sample = [&](int i) {
+            const int4 o = offs[i];
+            grad_sample(i, StageChunk<VT>::widen(s_stage[o.x + c]), StageChunk<VT>::widen(s_stage[o.y + c]),
+                        StageChunk<VT>::widen(s_stage[o.z + c]), StageChunk<VT>::widen(s_stage[o.w + c]));
+        };
+        // level by level: a memory level's gathers are issued, the records of
+        // the pass are written after the first of them (a wait on a load also
+        // waits on every store issued before it), a staged level is done from
+        // LDS while they are in flight, then the memory level
+#pragma unroll
+        for (int l = 0; l < LS; ++l) {
+            float4 v[K][4];
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const int4 o = offs[l * K + k];
+                v[k][0] = ValueTraits<VT>::load4(rsrc, (uint32_t)o.x + lane_off);
+                v[k][1] = ValueTraits<VT>::load4(rsrc, (uint32_t)o.y + lane_off);
+                v[k][2] = ValueTraits<VT>::load4(rsrc, (uint32_t)o.z + lane_off);
+                v[k][3] = ValueTraits<VT>::load4(rsrc, (uint32_t)o.w + lane_off);
+            }
+            if (l == 0) {
+#pragma unroll
+                for (int p = 0; p < NPASS; ++p) {
+                    const int t = p * kWave + ln;
+                    const int j = t / LK, i = t - (t / LK) * LK;
+                    const uint32_t sidx = (uint32_t)((((int64_t)b * g.Nq + qb + j) * M + m) * LK + i);
+                    uint32_t pos[4];
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) pos[jj] = atomicAdd(&s_cursor[keys[p][jj]], 1u);
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj)
+                        if (keys[p][jj] < nkeys && pos[jj] < rcap) records[pos[jj]] = sidx;
+                }
+            }
+            if (LS + l < L) {
+#pragma unroll
+                for (int k = 0; k < K; ++k) staged_sample((LS + l) * K + k);
+            }
+#pragma unroll
+            for (int k = 0; k < K; ++k) grad_sample(l * K + k, v[k][0], v[k][1], v[k][2], v[k][3]);
+        }
+#pragma unroll
+        for (int l = 2 * LS; l < L; ++l)  // staged levels left over
+#pragma unroll
+            for (int k = 0; k < K; ++k) staged_sample(l * K + k);
+        wave_lds_sync();
+        // ---- phase 3: the pass's results, one sample per lane per step ----
+#pragma unroll
+        for (int p = 0; p < NPASS; ++p) {
+            const int t = p * kWave + ln;
+            if ((QPW * LK) % kWave == 0 || t < QPW * LK) {
+                const int j = t / LK, i = t - (t / LK) * LK;
+                const int q = qb + j;
+                const float4 rr = s_geo[wave][j * PAD + i];
+                const int64_t si = (((int64_t)b * g.Nq + q) * M + m) * LK + i;
+                if constexpr (FUSED) {
+                    // the lanes of one query (LK adjacent lanes) share q < q1
+                    const bool valid = q < q1;
+                    const int l = i / K, k = i - (i / K) * K;
+                    const float a = valid ? attn[si] : 0.0f;
+                    const float tsum = group_sum<LK>(a * rr.x);
+                    float4 bx = make_float4(0.f, 0.f, 0.f, 0.f);
+                    float2 o = make_float2(0.f, 0.f);
+                    if (fg.ref_dims == 4 && valid) {
+                        bx = reinterpret_cast<const float4 *>(fg.ref)[((int64_t)b * g.Nq + q) * L + l];
+                        o = fg.off[si];
+                    }
+                    if (valid) {
+                        grad_attn[si] = a * (rr.x - tsum);
+                        const LevelRec lv = s_lv[l];
+                        grad_loc[si] = fg.ref_dims == 4
+                                           ? make_float2(rr.y * (bx.z * 0.5f / (float)K), rr.z * (bx.w * 0.5f / (float)K))
+                                           : make_float2(rr.y / lv.Wf, rr.z / lv.Hf);
+                    }
+                    if (fg.grad_ref) {
+                        // (x, y) from grad_loc; for boxes (w, h) from grad_loc * offset / (2K); summed
+                        // over the K points of the level (adjacent lanes)
+                        float4 pr = make_float4(rr.y, rr.z, 0.f, 0.f);
+                        if (fg.ref_dims == 4) {
+                            pr.z = rr.y * o.x * 0.5f / (float)K;
+                            pr.w = rr.z * o.y * 0.5f / (float)K;
+                        }
+                        pr.x = group_sum<K>(pr.x);
+                        pr.y = group_sum<K>(pr.y);
+                        pr.z = group_sum<K>(pr.z);
+                        pr.w = group_sum<K>(pr.w);
+                        if (valid && k == 0) ref_part[(((int64_t)b * g.Nq + q) * M + m) * L + l] = pr;
+                    }
+                } else if (q < q1) {
+                    grad_attn[si] = rr.x;
+                    grad_loc[si] = make_float2(rr.y, rr.z);
+                }
+            }
+        }
+        wave_lds_sync();  // the next pass rewrites this wave's records
+    }
+}
+
+// grad_ref[b, q, l] = the sum over heads m of ref_part[b, q, m, l] (heads in
+// order), one thread per (b, q, l).
+template <int M, int L>
+__global__ void __launch_bounds__(256)
+ref_grad_sum_kernel(Geometry g, const float4 *__restrict__ ref_part, FusedGrads fg)
+{
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= g.queries() * L) return;
+    const int64_t bq = t / L;
+    const int l = (int)(t - bq * L);
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const float4 v = ref_part[(bq * M + m) * L + l];
+        s.x += v.x;
+        s.y += v.y;
+        s.z += v.z;
+        s.w += v.w;
+    }
+    if (fg.ref_dims == 4)
+        reinterpret_cast<float4 *>(fg.grad_ref)[t] = s;
+    else
+        reinterpret_cast<float2 *>(fg.grad_ref)[t] = make_float2(s.x, s.y);
+}
+
 // --------------------------------------------------------------- 3. tile_accum
 
 // defined with the dense levels below; tile_accum runs it for its extra items
@@ -523,8 +934,10 @@ __device__ void dense_reduce_one(const Geometry &g, const TilePlan &tp, const fl
 // split s), loads each record's G row once and accumulates A*w_c*G into four
 // corner accumulators, kBatch records at a time so that many loads are in
 // flight. The corner sums go to single-writer LDS slots (pixel, corner role,
-// split); finally every pixel adds its slots and is written once.
-template <int LG>
+// split); finally every pixel adds its slots and is written once. The
+// compiled (M, L, K) make the sample-index division and the level lookups
+// compile-time.
+template <int M, int L, int K>
 __global__ void __launch_bounds__(kBlock)
 tile_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, const float *__restrict__ attn,
                   const float4 *__restrict__ grad_out, float4 *__restrict__ grad_value,
@@ -532,6 +945,8 @@ tile_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, const
                   const uint32_t *__restrict__ totals, int accumulate, const float4 *__restrict__ partials,
                   int reduce_blocks, const uint8_t *__restrict__ mask)
 {
+    constexpr int LG = 256 / M / 4;  // lanes (4 channels each) per head row
+    constexpr int NS = M * L * K;    // samples per query
     constexpr int NG = kBlock / LG;
     // (pixel, role, split) slots in use: npix*4 when cells >= NG, else at most 4*NG
     constexpr int kPartSlots0 = 4 * (kTilePix > NG ? kTilePix : NG);
@@ -556,15 +971,15 @@ tile_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, const
         return;
     }
     const int bm = item / tp.ipb;
-    const int b = bm / g.M, m = bm - (bm / g.M) * g.M;
+    const int b = bm / M, m = bm - (bm / M) * M;
     const int r_in = item - bm * tp.ipb;
     int l = 0;
 #pragma unroll
-    for (int i = 1; i < MSDA_MAX_LEVELS; ++i)
-        if (i < g.L && r_in >= tp.ibase[i]) l = i;
+    for (int i = 1; i < L; ++i)
+        if (r_in >= tp.ibase[i]) l = i;
     int th = 1, tw = 1, ntw = 1, tb = 0, nch = 1, ib = 0, W = 1, H = 1, lstart = 0;
 #pragma unroll
-    for (int i = 0; i < MSDA_MAX_LEVELS; ++i)
+    for (int i = 0; i < L; ++i)
         if (i == l) {
             th = tp.th[i];
             tw = tp.tw[i];
@@ -589,7 +1004,6 @@ tile_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, const
     const int npix = ph * pw;
     const int S = ncells >= NG ? 1 : NG / ncells;   // lane groups per cell
     const int ntask = ncells * S;
-    const int NS = g.M * g.L * g.K;
     const uint32_t nsamples = (uint32_t)g.samples();
     const int grp = threadIdx.x / LG;
     const int lig = threadIdx.x % LG;
@@ -876,12 +1290,13 @@ constexpr int kDenseMaxParts = 8;          // pixel parts of a dense level at mo
 constexpr double kDenseItemSamples = 3072; // samples per dense work item (sets the query splits)
 constexpr int kDenseMaxSplit = 64;
 
-template <int LG>
+template <int M, int L, int K>
 __global__ void __launch_bounds__(kDenseThreads)
 dense_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, const float *__restrict__ attn,
                    const float4 *__restrict__ grad_out, float4 *__restrict__ grad_value,
                    float4 *__restrict__ partials, int accumulate, const uint8_t *__restrict__ mask)
 {
+    constexpr int LG = 256 / M / 4;                         // lanes (4 channels each) per head row
     constexpr int NG = kDenseThreads / LG;                  // lane groups
     constexpr int PPG = kDensePix / NG;              // pixel slots per lane group
     constexpr int kPer = kDenseSub / kDenseThreads;         // samples per thread per sub-chunk
@@ -895,15 +1310,15 @@ dense_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, cons
     const int item = (int)xcd_tile(blockIdx.x, gridDim.x);
     if (item >= g.B * g.M * tp.dipb) return;
     const int bm = item / tp.dipb;
-    const int b = bm / g.M, m = bm - (bm / g.M) * g.M;
+    const int b = bm / M, m = bm - (bm / M) * M;
     const int r_in = item - bm * tp.dipb;
     int l = 0;
     int parts = 1, splits = 1, dib = 0, W = 1, H = 1, lstart = 0;
 #pragma unroll
-    for (int i = 0; i < MSDA_MAX_LEVELS; ++i)
-        if (i < g.L && ((tp.dense_mask >> i) & 1) && r_in >= tp.dibase[i]) l = i;
+    for (int i = 0; i < L; ++i)
+        if (((tp.dense_mask >> i) & 1) && r_in >= tp.dibase[i]) l = i;
 #pragma unroll
-    for (int i = 0; i < MSDA_MAX_LEVELS; ++i)
+    for (int i = 0; i < L; ++i)
         if (i == l) {
             parts = tp.dparts[i];
             splits = tp.dsplit[i];
@@ -920,9 +1335,8 @@ dense_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, cons
     const int qa0 = (int)((int64_t)g.Nq * split / splits);
     const int qa1 = (int)((int64_t)g.Nq * (split + 1) / splits);
     const float Wf = (float)W, Hf = (float)H;
-    const int K = g.K;
-    const int QS = min(kDenseQ, kDenseSub / K);  // queries per sub-chunk
-    const int64_t LKs = (int64_t)g.L * K;
+    constexpr int QS = kDenseQ < kDenseSub / K ? kDenseQ : kDenseSub / K;  // queries per sub-chunk
+    constexpr int64_t LKs = (int64_t)L * K;
     const int grp = threadIdx.x / LG;
     const int lig = threadIdx.x % LG;
 
@@ -1195,6 +1609,7 @@ backward_generic_kernel(Geometry g, const VT *__restrict__ value, const float2 *
 struct Workspace {
     uint32_t *counts, *totals, *bases, *records;
     float4 *partials;  // per dense work item: kDensePix pixels x D channels
+    float4 *ref_part;  // fused per-head path: [B, Nq, M, L] sums of the reference-point gradient
 };
 
 inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
@@ -1202,7 +1617,8 @@ inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 size_t layout(const Geometry &g, const TilePlan &tp, char *base, Workspace *ws)
 {
     const size_t nkeys = (size_t)g.B * g.M * tp.tpb;
-    const size_t ncount = (size_t)g.B * tp.wpb * g.M * tp.tpb;
+    // per-workgroup counts of the query-range binning or of the per-head one
+    const size_t ncount = std::max((size_t)g.B * tp.wpb, (size_t)g.B * tp.hqr) * g.M * tp.tpb;
     const size_t nrec = 4 * (size_t)g.samples();
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -1216,6 +1632,7 @@ size_t layout(const Geometry &g, const TilePlan &tp, char *base, Workspace *ws)
     w.bases = take(nkeys * 4);
     w.records = take(nrec * 4);
     w.partials = reinterpret_cast<float4 *>(take((size_t)g.B * g.M * tp.dipb * kDensePix * g.D * 4));
+    w.ref_part = reinterpret_cast<float4 *>(take((size_t)g.queries() * g.M * g.L * 16));
     if (ws) *ws = w;
     return off;
 }
@@ -1271,6 +1688,65 @@ hipError_t launch_binning(const Geometry &g, const TilePlan &tp, const float *lo
     return hipGetLastError();
 }
 
+// The first level whose rows (with every coarser level's) fit in LDS beside
+// the per-head kernel's records and tile cursors, or 0 when the per-head path
+// does not apply (other shapes, fewer queries, or nothing fits).
+template <typename VT, int M, int L, int K>
+int head_stage_level(const Geometry &g, const TilePlan &tp, uint32_t &stage_bytes)
+{
+    if constexpr (!(M == 8 && L == 4 && K == 4)) {
+        return 0;
+    } else {
+        constexpr int LPH = 256 / M / 4, QPW = kWave / LPH;
+        constexpr size_t kStatic = (size_t)kHeadWaves * QPW * (L * K + 1) * 32 + 2 * 16 * L + 4 * kHeadWaves;
+        if (g.Nq < kHeadMinQueries) return 0;
+        const size_t cursors = (size_t)(tp.tpb + kWave) * 4;
+        for (int ls = 1; ls < L; ++ls) {
+            const int64_t rows = (int64_t)g.S - g.lv.start[ls];
+            const size_t bytes = ((size_t)(rows + 1) * LPH * sizeof(typename StageChunk<VT>::type) + 15) & ~(size_t)15;
+            if (kStatic + bytes + cursors + 1024 <= kHeadLds) {
+                stage_bytes = (uint32_t)bytes;
+                return ls;
+            }
+        }
+        return 0;
+    }
+}
+
+template <typename VT, int M, int L, int K, int LS, bool FUSED>
+hipError_t launch_head(const Geometry &g, const TilePlan &tp, const void *value, const float *loc,
+                       const float *attn, const float *go, float *gl, float *ga, const Workspace &ws,
+                       uint32_t stage_bytes, const uint8_t *mask, const FusedGrads &fg, hipStream_t st)
+{
+    const int nkeys = g.B * M * tp.tpb;
+    const int nwg = g.B * M * tp.hqr;
+    {
+        KernelScope ks_("clear_totals_kernel", st);
+        hipLaunchKernelGGL(clear_totals_kernel, dim3((nkeys + kBlock - 1) / kBlock), dim3(kBlock), 0, st, nkeys,
+                           ws.totals);
+    }
+    {
+        KernelScope ks_("bin_count_head_kernel", st);
+        hipLaunchKernelGGL((bin_count_head_kernel<M, L, K>), dim3(nwg), dim3(kBinThreads), (size_t)tp.tpb * 4, st, g,
+                           tp, reinterpret_cast<const float2 *>(loc), ws.counts, ws.totals);
+    }
+    const uint32_t grid = round_up8((uint32_t)nwg);
+    const size_t dyn = (size_t)stage_bytes + (size_t)(tp.tpb + kWave) * 4;
+    {
+        KernelScope ks_(FUSED ? "backward_fused_head_kernel" : "backward_head_kernel", st);
+        hipLaunchKernelGGL((backward_head_kernel<VT, M, L, K, LS, FUSED>), dim3(grid), dim3(kHeadThreads), dyn, st, g,
+                           tp, static_cast<const VT *>(value), reinterpret_cast<const float2 *>(loc), attn,
+                           reinterpret_cast<const float4 *>(go), reinterpret_cast<float2 *>(gl), ga, ws.counts,
+                           ws.totals, ws.bases, ws.records, stage_bytes, grid, mask, fg, ws.ref_part);
+    }
+    if (FUSED && fg.grad_ref) {
+        KernelScope ks_("ref_grad_sum_kernel", st);
+        hipLaunchKernelGGL((ref_grad_sum_kernel<M, L>), dim3((unsigned)((g.queries() * L + 255) / 256)), dim3(256),
+                           0, st, g, ws.ref_part, fg);
+    }
+    return hipGetLastError();
+}
+
 template <typename VT, int M, int L, int K, bool FUSED>
 hipError_t launch_fast(const Geometry &g, const TilePlan &tp, const void *value, const float *loc,
                        const float *attn, const float *go, float *gv, float *gl, float *ga, const FusedGrads &fg,
@@ -1301,19 +1777,34 @@ hipError_t launch_fast(const Geometry &g, const TilePlan &tp, const void *value,
         const uint32_t ditems = (uint32_t)(g.B * g.M * tp.dipb);
         {
             KernelScope ks_("dense_accum_kernel", ds);
-            hipLaunchKernelGGL((dense_accum_kernel<LG>), dim3(round_up8(ditems)), dim3(kDenseThreads), 0, ds, g,
+            hipLaunchKernelGGL((dense_accum_kernel<M, L, K>), dim3(round_up8(ditems)), dim3(kDenseThreads), 0, ds, g,
                                tp, reinterpret_cast<const float2 *>(loc), attn, reinterpret_cast<const float4 *>(go),
                                reinterpret_cast<float4 *>(gv), ws.partials, accumulate ? 1 : 0, mask);
         }
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (side && (e = hipEventRecord(side->join, side->s)) != hipSuccess) return e;
     }
-    {
+    uint32_t stage_bytes = 0;
+    const int hls = head_stage_level<VT, M, L, K>(g, tp, stage_bytes);
+    if (hls > 0) {
+        // the per-head path: binning and main kernel per (batch, head, query range)
+        hipError_t e = hipErrorInvalidValue;
+        if constexpr (M == 8 && L == 4 && K == 4) {
+#define MSDA_HEAD(LS_)                                                                                            \
+    if (hls == LS_)                                                                                               \
+        e = launch_head<VT, M, L, K, LS_, FUSED>(g, tp, value, loc, attn, go, gl, ga, ws, stage_bytes, mask, fg, st);
+            MSDA_HEAD(1)
+            MSDA_HEAD(2)
+            MSDA_HEAD(3)
+#undef MSDA_HEAD
+        }
+        if (e != hipSuccess) return e;
+    } else {
         const hipError_t e = launch_binning<M, L, K>(g, tp, loc, ws, st);
         if (e != hipSuccess) return e;
     }
     const uint32_t grid = round_up8((uint32_t)nwg);
-    {
+    if (hls == 0) {
         KernelScope ks_(FUSED ? "backward_fused_c256_kernel" : "backward_c256_kernel", st);
         hipLaunchKernelGGL((backward_c256_kernel<VT, M, L, K, FUSED>), dim3(grid),
                            dim3(MainWaves<M, L, K>::kValue * kWave), hist_bytes, st, g, tp,
@@ -1344,7 +1835,7 @@ hipError_t launch_fast(const Geometry &g, const TilePlan &tp, const void *value,
     const uint32_t items = (uint32_t)(g.B * g.M * tp.ipb) + (uint32_t)reduce_blocks;
     if (items > 0) {
         KernelScope ks_("tile_accum_kernel", st);
-        hipLaunchKernelGGL((tile_accum_kernel<LG>), dim3(round_up8(items)), dim3(kBlock), 0, st, g, tp,
+        hipLaunchKernelGGL((tile_accum_kernel<M, L, K>), dim3(round_up8(items)), dim3(kBlock), 0, st, g, tp,
                            reinterpret_cast<const float2 *>(loc), attn, reinterpret_cast<const float4 *>(go),
                            reinterpret_cast<float4 *>(gv), ws.records, ws.bases, ws.totals, accumulate ? 1 : 0,
                            ws.partials, reduce_blocks, mask);
@@ -1557,6 +2048,9 @@ bool make_tile_plan(const Geometry &g, TilePlan &tp)
     tp.dipb = dibase;
     tp.qpw = kQueriesPerGroup;
     tp.wpb = (g.Nq + tp.qpw - 1) / tp.qpw;
+    tp.hqr = std::max(1, (kHeadTargetWGs + g.B * g.M - 1) / (g.B * g.M));
+    tp.hqpr = std::max(1, (g.Nq + tp.hqr - 1) / tp.hqr);
+    tp.hqr = std::max(1, (g.Nq + tp.hqpr - 1) / tp.hqpr);
     // the per-workgroup histogram / cursors live in LDS; record indices are 32-bit
     if (((size_t)g.M * tp.tpb + kWave) * 4 > 64 * 1024) return false;  // the main kernel's LDS cursors
     if ((uint64_t)g.samples() * 4 >= (1ull << 32)) return false;

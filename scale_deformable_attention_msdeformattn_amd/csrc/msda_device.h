@@ -50,6 +50,24 @@ template <> struct ValueTraits<uint16_t> {  // bf16 bit patterns
     __device__ static float4 load4(__amdgpu_buffer_rsrc_t r, uint32_t off) { return load_bf16x4(r, off); }
 };
 
+// Four channels of one value row as staged in LDS (fp32: 16 bytes; bf16: 8
+// bytes, widened to fp32 when read).
+template <typename VT> struct StageChunk;
+template <> struct StageChunk<float> {
+    using type = float4;
+    __device__ static float4 zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+    __device__ static float4 widen(const float4 &v) { return v; }
+};
+template <> struct StageChunk<uint16_t> {
+    using type = uint2;
+    __device__ static uint2 zero() { return make_uint2(0u, 0u); }
+    __device__ static float4 widen(const uint2 &v)
+    {
+        return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                           __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
+    }
+};
+
 // One axis of a bilinear sample in the align_corners=False convention:
 // the continuous pixel coordinate is x = u*n - 0.5; returns the cell start
 // c = floor(x) (as float) and the fraction f = x - c in [0, 1].

@@ -193,22 +193,6 @@ struct StagePlan {
     int32_t qpr;  // queries per range
 };
 
-template <typename VT> struct StageChunk;  // four channels of one staged row
-template <> struct StageChunk<float> {
-    using type = float4;
-    __device__ static float4 zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
-    __device__ static float4 widen(const float4 &v) { return v; }
-};
-template <> struct StageChunk<uint16_t> {
-    using type = uint2;
-    __device__ static uint2 zero() { return make_uint2(0u, 0u); }
-    __device__ static float4 widen(const uint2 &v)
-    {
-        return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
-                           __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
-    }
-};
-
 template <typename VT, int M, int L, int K, int LS, bool FUSED>
 __global__ void __launch_bounds__(kStagedThreads)
 forward_staged_kernel(Geometry g, const VT *__restrict__ value, const float2 *__restrict__ loc,

@@ -44,6 +44,9 @@ struct TilePlan {
     int32_t tpb;  // tiles per (batch, head)
     int32_t qpw;  // queries per workgroup
     int32_t wpb;  // workgroups per batch
+    // per-head path (one workgroup per batch, head and range of queries)
+    int32_t hqr;   // query ranges per (batch, head)
+    int32_t hqpr;  // queries per range
     // Dense levels (bit l of dense_mask) have no tiles and no records: their
     // grad_value is accumulated from the samples directly, per (pixel part,
     // query split) work item.

@@ -49,7 +49,9 @@ def test_timing_counts_each_kernel_launch_and_skips_capture(gpu_lib):
     # (this shape takes the forward with the coarse levels staged in LDS)
     assert t["forward_staged_kernel"][1] == 4
     assert "forward_c256_kernel" not in t
-    for name in ("bin_count_kernel", "backward_c256_kernel", "tile_accum_kernel"):
+    # (and the backward the per-head path with its own binning and main kernel)
+    assert "bin_count_kernel" not in t and "backward_c256_kernel" not in t
+    for name in ("bin_count_head_kernel", "backward_head_kernel", "tile_accum_kernel"):
         ms, n = t[name]
         assert n == 3 and ms > 0.0, (name, t[name])
     assert msda.msda_timing_read() == {}
