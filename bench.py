@@ -161,9 +161,12 @@ def algorithmic_bytes(B, M, D, Nq, shapes, K, vbytes):
         "backward_c256_kernel": vbytes + samples * 3 * f32 + rows + samples * 3 * f32,
         # the same outputs per (batch, head, query range), coarse levels staged in LDS
         "backward_head_kernel": vbytes + samples * 3 * f32 + rows + samples * 3 * f32,
-        # sparse levels: grad_output, their loc and A in, their grad_value rows
-        # out; the sums of split dense levels ride along as extra items
-        "tile_accum_kernel": rows + sparse_samples * 3 * f32 + (S - dense_pix + split_pix) * gv_row,
+        # sparse levels: grad_output in, their grad_value rows out (each
+        # sample's cell and weights come from its records, in the workspace)
+        "tile_accum_kernel": rows + (S - dense_pix) * gv_row,
+        # the dense levels split over queries: their grad_value rows out (the
+        # split sums come from the workspace)
+        "dense_reduce_kernel": split_pix * gv_row,
         # dense levels: grad_output, their loc and A in; grad_value rows out
         # for levels with one query split (the others park sums in workspace)
         "dense_accum_kernel": rows + dense_samples * 3 * f32 + (dense_pix - split_pix) * gv_row,

@@ -9,6 +9,7 @@ If the library is missing or fails to load, every call raises.
 import ctypes
 import os
 import re
+import weakref
 from typing import Optional, Sequence, Tuple, Union
 
 import torch
@@ -152,6 +153,49 @@ def _host_i64(x):
     return torch.as_tensor(x, dtype=torch.int64)
 
 
+# Host copies of small integer tensors that live on the device (spatial
+# shapes, level start indices), so that a call does not wait on the device to
+# read them again: keyed by the tensor object, dropped when it is freed, and
+# read again when its version counter has moved (any in-place write).
+_DEV_INTS = {}
+
+
+def _ints(x) -> tuple:
+    """The values of a small integer array, flattened, as Python ints."""
+    if isinstance(x, torch.Tensor) and x.device.type != "cpu":
+        key = id(x)
+        e = _DEV_INTS.get(key)
+        if e is not None and e[0]() is x and e[1] == x._version:
+            return e[2]
+        vals = tuple(x.detach().to("cpu", torch.int64).reshape(-1).tolist())
+        _DEV_INTS[key] = (weakref.ref(x, lambda _r, k=key: _DEV_INTS.pop(k, None)), x._version, vals)
+        return vals
+    if isinstance(x, tuple) and all(type(v) is int for v in x):
+        return x
+    return tuple(_host_i64(x).reshape(-1).tolist())
+
+
+# Shape objects per distinct set of sizes: building one (ctypes arrays, the
+# level start index) costs more than the launches of a small call.
+_SHAPES = {}
+_SHAPES_MAX = 256
+
+
+def _shape(spatial_shapes, batch, heads, channels, points, num_query, level_start_index=None, num_value=None):
+    sv = _ints(spatial_shapes)
+    lv = None if level_start_index is None else _ints(level_start_index)
+    key = (sv, lv, int(batch), int(heads), int(channels), int(points), int(num_query), num_value)
+    sh = _SHAPES.get(key)
+    if sh is None:
+        sh = Shape(sv, batch, heads, channels, points, num_query, lv)
+        if num_value is not None:
+            sh.c.num_value = int(num_value)  # the library checks it against sum H_l*W_l
+        if len(_SHAPES) >= _SHAPES_MAX:
+            _SHAPES.clear()
+        _SHAPES[key] = sh
+    return sh
+
+
 def level_start_index_host(spatial_shapes) -> Tuple[list, int]:
     """(level_start_index as a list, S) computed by the library's host helper."""
     shapes = _host_i64(spatial_shapes).reshape(-1, 2)
@@ -191,8 +235,8 @@ def msda_reference_points(spatial_shapes, valid_ratios: Optional[torch.Tensor] =
     """Reference points [B, Nq, L, 2]. Encoder mode when query_ref is None
     (every pixel of every level is a query, Nq = S); decoder mode with
     query_ref = u [B, Nq, 2]. valid_ratios [B, L, 2] or None (all ones)."""
-    shapes = _host_i64(spatial_shapes).reshape(-1, 2)
-    L = int(shapes.shape[0])
+    sv = _ints(spatial_shapes)
+    L = len(sv) // 2
     ref_dev = valid_ratios if valid_ratios is not None else query_ref
     if valid_ratios is not None:
         valid_ratios = _dev(valid_ratios, "valid_ratios")
@@ -206,12 +250,12 @@ def msda_reference_points(spatial_shapes, valid_ratios: Optional[torch.Tensor] =
             raise ValueError("query_ref must be [B, Nq, 2]")
     else:
         B = valid_ratios.shape[0] if valid_ratios is not None else int(batch)
-        Nq = int((shapes[:, 0] * shapes[:, 1]).sum())
+        Nq = sum(sv[2 * i] * sv[2 * i + 1] for i in range(L))
     if valid_ratios is not None and valid_ratios.shape[0] != B:
         raise ValueError("valid_ratios and query_ref disagree on the batch size")
     device = ref_dev.device if ref_dev is not None else torch.device(device or "cuda")
     out = torch.empty(B, Nq, L, 2, dtype=torch.float32, device=device)
-    sh = Shape(shapes, B, 1, 1, 1, Nq)
+    sh = _shape(sv, B, 1, 1, 1, Nq)
     _check(load().msda_reference_points(sh.ptr, _p(valid_ratios), _p(query_ref), _p(out), _stream(out)),
            "msda_reference_points")
     return out
@@ -228,7 +272,7 @@ def msda_sampling_locations(spatial_shapes, reference_points: torch.Tensor,
     if tuple(ref.shape) != (B, Nq, L, 2):
         raise ValueError(f"reference_points must be [{B}, {Nq}, {L}, 2], got {tuple(ref.shape)}")
     out = torch.empty_like(off)
-    sh = Shape(spatial_shapes, B, M, 1, K, Nq)
+    sh = _shape(spatial_shapes, B, M, 1, K, Nq)
     if sh.levels != L:
         raise ValueError("spatial_shapes and offsets_px disagree on the level count")
     _check(load().msda_sampling_locations(sh.ptr, _p(ref), _p(off), _p(out), _stream(out)),
@@ -239,13 +283,13 @@ def msda_sampling_locations(spatial_shapes, reference_points: torch.Tensor,
 def msda_attention_softmax(spatial_shapes, logits: torch.Tensor, points: int) -> torch.Tensor:
     """Softmax of logits [B,Nq,M,L*K] over L*K -> weights [B,Nq,M,L,K]."""
     x = _dev(logits, "logits")
-    shapes = _host_i64(spatial_shapes).reshape(-1, 2)
-    L = int(shapes.shape[0])
+    sv = _ints(spatial_shapes)
+    L = len(sv) // 2
     B, Nq, M, LK = x.shape
     if LK != L * points:
         raise ValueError(f"logits last dim {LK} != L*K = {L * points}")
     out = torch.empty(B, Nq, M, L, points, dtype=torch.float32, device=x.device)
-    sh = Shape(shapes, B, M, 1, points, Nq)
+    sh = _shape(sv, B, M, 1, points, Nq)
     _check(load().msda_attention_softmax(sh.ptr, _p(x), _p(out), _stream(out)), "msda_attention_softmax")
     return out
 
@@ -264,10 +308,9 @@ def _core_shape(value, spatial_shapes, level_start_index, loc, attn):
     _, Nq, _, L, K, _ = loc.shape
     if tuple(attn.shape) != (B, Nq, M, L, K):
         raise ValueError(f"attention_weights must be {(B, Nq, M, L, K)}, got {tuple(attn.shape)}")
-    sh = Shape(spatial_shapes, B, M, D, K, Nq, level_start_index)
+    sh = _shape(spatial_shapes, B, M, D, K, Nq, level_start_index, S)
     if sh.levels != L:
         raise ValueError("spatial_shapes and sampling_locations disagree on the level count")
-    sh.c.num_value = S  # the library checks it against sum H_l*W_l
     vt = MSDA_BF16 if value.dtype == torch.bfloat16 else MSDA_F32
     return value, loc, attn, sh, vt
 
@@ -286,7 +329,9 @@ def msda_forward(value: torch.Tensor, spatial_shapes, level_start_index, samplin
 
 def _workspace(sh, device):
     """(workspace tensor, bytes) for a backward of these sizes."""
-    nbytes = msda_backward_workspace_size(sh)
+    nbytes = getattr(sh, "workspace_bytes", None)
+    if nbytes is None:
+        nbytes = sh.workspace_bytes = msda_backward_workspace_size(sh)
     return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device), nbytes
 
 
@@ -379,10 +424,9 @@ def msda_forward_fused(value: torch.Tensor, spatial_shapes, level_start_index, r
         raise ValueError(f"reference_points must be [{B}, {Nq}, {L}, 2 or 4], got {tuple(ref.shape)}")
     if tuple(logits.shape) != (B, Nq, M, L * K):
         raise ValueError(f"attention_logits must be {(B, Nq, M, L * K)}, got {tuple(logits.shape)}")
-    sh = Shape(spatial_shapes, B, M, D, K, Nq, level_start_index)
+    sh = _shape(spatial_shapes, B, M, D, K, Nq, level_start_index, S)
     if sh.levels != L:
         raise ValueError("spatial_shapes and sampling_offsets disagree on the level count")
-    sh.c.num_value = S
     vt = MSDA_BF16 if value.dtype == torch.bfloat16 else MSDA_F32
     out = torch.empty(B, Nq, M * D, dtype=torch.float32, device=value.device)
     loc = torch.empty_like(off)

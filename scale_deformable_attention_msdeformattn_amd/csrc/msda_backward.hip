@@ -76,9 +76,12 @@ __device__ __forceinline__ float dot4(const float4 &a, const float4 &b)
 }
 
 // The pixel tiles (of one head and level) that a sample's in-map corners fall
-// in: up to four distinct ids, -1 for none. (cx, cy) is the sample's cell.
+// in: up to four distinct ids, -1 for none, and the sample's cell numbered
+// within each of those tiles. (cx, cy) is the sample's cell: its top-left
+// corner pixel (-1 when that corner is off the map).
 struct SampleTiles {
     int t[4];
+    int cell[4];
 };
 
 // One level's tiling, staged in LDS: a lane-varying level index into the
@@ -86,11 +89,32 @@ struct SampleTiles {
 struct TileLevel {
     float iw, ih;     // 1/tw, 1/th
     int32_t ntw, base;
+    int32_t tw, th;
 };
 
 __device__ __forceinline__ TileLevel tile_level(const TilePlan &tp, int l)
 {
-    return TileLevel{tp.tinv_w[l], tp.tinv_h[l], tp.ntw[l], tp.tbase[l]};
+    return TileLevel{tp.tinv_w[l], tp.tinv_h[l], tp.ntw[l], tp.tbase[l], tp.tw[l], tp.th[l]};
+}
+
+// A tile record: everything tile_accum needs of one (sample, tile) pair, 16 B.
+//   x: (b*Nq + q) << kCellBits | the sample's cell within the tile
+//   y, z, w: fx, A*(1-fy), A*fy as float bits (the corner weights are
+//            (1-fx, fx) times these)
+// A tile's cells are its pixels plus one halo row above and one halo column
+// to the left, numbered row by row: cell (ry, rx) has its top-left corner at
+// tile pixel (ry-1, rx-1).
+constexpr int kCellBits = 7;
+static_assert(kTileCells <= (1 << kCellBits), "cell numbers fit the record");
+// The main kernels carry a record's cell in a key's bits from kKeyBits up
+// (keys, the LDS cursor indices, stay below 2^kKeyBits: checked by the plan).
+constexpr int kKeyBits = 24;
+constexpr int kKeyMask = (1 << kKeyBits) - 1;
+
+__device__ __forceinline__ uint4 tile_record(uint32_t bq, int cell, float fx, float fy, float a)
+{
+    return make_uint4((bq << kCellBits) | (uint32_t)cell, __float_as_uint(fx), __float_as_uint(a * (1.0f - fy)),
+                      __float_as_uint(a * fy));
 }
 
 __device__ __forceinline__ SampleTiles sample_tiles(const TileLevel &tl, int W, int H, int cx, int cy)
@@ -113,6 +137,15 @@ __device__ __forceinline__ SampleTiles sample_tiles(const TileLevel &tl, int W, 
     r.t[1] = (r0 >= 0 && c1 >= 0) ? base + r0 * ntw + c1 : -1;
     r.t[2] = (r1 >= 0 && c0 >= 0) ? base + r1 * ntw + c0 : -1;
     r.t[3] = (r1 >= 0 && c1 >= 0) ? base + r1 * ntw + c1 : -1;
+    // the cell within tile (ty, tx): row cy - ty*th + 1, column cx - tx*tw + 1,
+    // in rows of (pixel columns of the tile) + 1 cells
+    const int ry0 = cy - r0 * tl.th + 1, ry1 = cy - r1 * tl.th + 1;
+    const int rx0 = cx - c0 * tl.tw + 1, rx1 = cx - c1 * tl.tw + 1;
+    const int cw0 = min(tl.tw, W - c0 * tl.tw) + 1, cw1 = min(tl.tw, W - c1 * tl.tw) + 1;
+    r.cell[0] = ry0 * cw0 + rx0;
+    r.cell[1] = ry0 * cw1 + rx1;
+    r.cell[2] = ry1 * cw0 + rx0;
+    r.cell[3] = ry1 * cw1 + rx1;
     return r;
 }
 
@@ -241,7 +274,7 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
                      const float *__restrict__ attn, const float4 *__restrict__ grad_out,
                      float2 *__restrict__ grad_loc, float *__restrict__ grad_attn,
                      const uint32_t *__restrict__ offsets, const uint32_t *__restrict__ totals,
-                     uint32_t *__restrict__ bases, uint32_t *__restrict__ records, uint32_t grid, FusedGrads fg,
+                     uint32_t *__restrict__ bases, uint4 *__restrict__ records, uint32_t grid, FusedGrads fg,
                      const uint8_t *__restrict__ mask)
 {
     constexpr int C = 256;
@@ -271,7 +304,7 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
     const int q0 = wg_active ? (int)(w - b * tp.wpb) * tp.qpw : 0;
     const int q1 = wg_active ? min(q0 + tp.qpw, g.Nq) : 0;
     const int nkeys = M * tp.tpb;
-    const uint32_t rcap = (uint32_t)g.B * 4u * (uint32_t)(g.Nq * NS);  // record slots
+    const uint32_t rcap = (uint32_t)g.B * (uint32_t)(g.Nq * M * tp.rslots);  // record slots
     if (threadIdx.x < L) {
         const int l = threadIdx.x;
         s_lv[l] = LevelRec{(float)g.lv.W[l], (float)g.lv.H[l], g.lv.W[l], g.lv.start[l]};
@@ -299,7 +332,7 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
         }
         if (lane == kWave - 1) s_wsum[wave] = incl;
         __syncthreads();
-        uint32_t run = (uint32_t)b * 4u * (uint32_t)(g.Nq * NS) + incl - sum;
+        uint32_t run = (uint32_t)b * (uint32_t)(g.Nq * M * tp.rslots) + incl - sum;
         for (int v = 0; v < wave; ++v) run += s_wsum[v];
         for (int i = i0; i < i1; ++i) {
             const uint32_t c = s_cursor[i];
@@ -335,9 +368,11 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
         // record keys (head * tiles + tile) of the sparse-level samples, or
         // the lane's idle slot
         int keys[NP][4];
+        float rfx[NP], rfy[NP], ra[NP];
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
             const int s = p * kWave + ln;
+            rfx[p] = rfy[p] = ra[p] = 0.0f;
 #pragma unroll
             for (int j = 0; j < 4; ++j) keys[p][j] = nkeys + ln;
             if (NS % kWave == 0 || s < NS) {
@@ -370,7 +405,10 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
                     const SampleTiles st = sample_tiles(s_tl[l], lv.W, H, cx, cy);
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
-                        if (st.t[j] >= 0) keys[p][j] = sm * tp.tpb + st.t[j];
+                        if (st.t[j] >= 0) keys[p][j] = (sm * tp.tpb + st.t[j]) | (st.cell[j] << kKeyBits);
+                    rfx[p] = fx;
+                    rfy[p] = fy;
+                    ra[p] = a;
                 }
             }
         }
@@ -403,15 +441,15 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
         // cursor, all adds in flight at once
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
-            const uint32_t sidx = (uint32_t)(gq * NS + p * kWave + ln);
             uint32_t pos[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) pos[j] = atomicAdd(&s_cursor[keys[p][j]], 1u);
+            for (int j = 0; j < 4; ++j) pos[j] = atomicAdd(&s_cursor[keys[p][j] & kKeyMask], 1u);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 // the bound keeps a record write inside the workspace whatever
                 // the counts hold
-                if (keys[p][j] < nkeys && pos[j] < rcap) records[pos[j]] = sidx;
+                if ((keys[p][j] & kKeyMask) < nkeys && pos[j] < rcap)
+                    records[pos[j]] = tile_record((uint32_t)gq, keys[p][j] >> kKeyBits, rfx[p], rfy[p], ra[p]);
         }
 #pragma unroll
         for (int l = 0; l < L; ++l) {
@@ -526,12 +564,12 @@ constexpr size_t kHeadLds = 160 * 1024;   // gfx950
 
 // Workgroup (b, m, r) counts, for head m, the samples of queries
 // [r * hqpr, (r + 1) * hqpr) on the sparse levels per tile of that head (an
-// LDS histogram), then reserves its range in each touched tile's record list
-// with one global atomic add per tile.
+// LDS histogram) and stores the counts as row (b*M + m)*hqr + r of `counts`
+// (every tile, zeros included: nothing needs clearing beforehand). The main
+// kernel's workgroups sum these rows into their record cursors.
 template <int M, int L, int K>
 __global__ void __launch_bounds__(kBinThreads)
-bin_count_head_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, uint32_t *__restrict__ offsets,
-                      uint32_t *__restrict__ totals)
+bin_count_head_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, uint32_t *__restrict__ counts)
 {
     extern __shared__ uint32_t s_hist[];  // [tpb]
     __shared__ LevelRec s_lv[L];
@@ -575,30 +613,17 @@ bin_count_head_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, u
         }
     }
     __syncthreads();
-    uint32_t *row = offsets + (int64_t)w * nkeys;
-    uint32_t *tot = totals + (int64_t)bm * nkeys;
-    constexpr int kKeysInFlight = 8;
-    for (int i0 = threadIdx.x; i0 < nkeys; i0 += kBinThreads * kKeysInFlight) {
-        uint32_t rv[kKeysInFlight];
-#pragma unroll
-        for (int j = 0; j < kKeysInFlight; ++j) {
-            const int i = i0 + j * kBinThreads;
-            const uint32_t c = i < nkeys ? s_hist[i] : 0u;
-            rv[j] = c ? atomicAdd(&tot[i], c) : 0u;
-        }
-#pragma unroll
-        for (int j = 0; j < kKeysInFlight; ++j) {
-            const int i = i0 + j * kBinThreads;
-            if (i < nkeys && s_hist[i]) row[i] = rv[j];
-        }
-    }
+    uint32_t *row = counts + (int64_t)w * nkeys;
+    for (int i = threadIdx.x; i < nkeys; i += kBinThreads) row[i] = s_hist[i];
 }
 
 // The per-head main kernel: grad_attn and grad_loc of head m for a range of
 // queries, and the record lists of the sparse levels' tiles. The records of
 // head (b, m) fill [(b*M + m) * 4 * Nq * L * K, ...) tile after tile (a sample
-// lands in at most four tiles); the workgroup scans its head's tile totals
-// into its cursors, and the head's first workgroup publishes the list bases.
+// lands in at most four tiles); the workgroup sums its head's count rows into
+// tile totals, scans them into its cursors (plus the counts of the head's
+// workgroups before it), and the head's first workgroup publishes the totals
+// and list bases.
 //
 // FUSED: the gradients of the fused forward's inputs (as the main kernel's
 // fused form): grad_loc becomes the offsets' gradient and grad_attn the
@@ -611,8 +636,8 @@ __global__ void __launch_bounds__(kHeadThreads)
 backward_head_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, const float2 *__restrict__ loc,
                      const float *__restrict__ attn, const float4 *__restrict__ grad_out,
                      float2 *__restrict__ grad_loc, float *__restrict__ grad_attn,
-                     const uint32_t *__restrict__ offsets, const uint32_t *__restrict__ totals,
-                     uint32_t *__restrict__ bases, uint32_t *__restrict__ records, uint32_t stage_bytes,
+                     const uint32_t *__restrict__ counts, uint32_t *__restrict__ totals,
+                     uint32_t *__restrict__ bases, uint4 *__restrict__ records, uint32_t stage_bytes,
                      uint32_t grid, const uint8_t *__restrict__ mask, FusedGrads fg, float4 *__restrict__ ref_part)
 {
     constexpr int C = 256;
@@ -629,6 +654,7 @@ backward_head_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
     extern __shared__ __align__(16) unsigned char s_raw[];
     Chunk *s_stage = reinterpret_cast<Chunk *>(s_raw);                      // [(rows + 1) * LPH]
     uint32_t *s_cursor = reinterpret_cast<uint32_t *>(s_raw + stage_bytes);  // [tpb + kWave]
+    uint32_t *s_pre = s_cursor + tp.tpb + kWave;  // [tpb]: counts of the head's workgroups before this one
     __shared__ LevelRec s_lv[L];
     __shared__ TileLevel s_tl[L];
     __shared__ int4 s_off[kHeadWaves][QPW * PAD];
@@ -675,9 +701,32 @@ backward_head_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
         if (threadIdx.x < LPH) s_stage[nrows * LPH + threadIdx.x] = StageChunk<VT>::zero();
     }
     // the record cursors of head (b, m)'s tiles: region base + exclusive
-    // prefix of the tile totals + this workgroup's reserved offset
-    const uint32_t *tot = totals + (int64_t)bm * nkeys;
-    for (int i = threadIdx.x; i < nkeys; i += kHeadThreads) s_cursor[i] = tot[i];
+    // prefix of the tile totals + the counts of the head's workgroups before
+    // this one. A tile's total sums the head's hqr count rows; the head's
+    // first workgroup publishes the totals and bases for tile_accum.
+    const uint32_t *cnt = counts + (int64_t)bm * tp.hqr * nkeys;
+    for (int i = threadIdx.x; i < nkeys; i += kHeadThreads) {
+        uint32_t t = 0, pre = 0;
+        int rr = 0;
+        for (; rr + 8 <= tp.hqr; rr += 8) {
+            uint32_t c[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) c[k] = cnt[(int64_t)(rr + k) * nkeys + i];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                pre += rr + k < r ? c[k] : 0u;
+                t += c[k];
+            }
+        }
+        for (; rr < tp.hqr; ++rr) {
+            const uint32_t c = cnt[(int64_t)rr * nkeys + i];
+            pre += rr < r ? c : 0u;
+            t += c;
+        }
+        s_cursor[i] = t;
+        s_pre[i] = pre;
+        if (r == 0) totals[(int64_t)bm * nkeys + i] = t;
+    }
     if (threadIdx.x < kWave) s_cursor[nkeys + threadIdx.x] = 0;  // lanes' idle slots
     __syncthreads();
     {
@@ -693,7 +742,7 @@ backward_head_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
         }
         if (lane == kWave - 1) s_wsum[wave] = incl;
         __syncthreads();
-        uint32_t run = (uint32_t)bm * 4u * (uint32_t)(g.Nq * LK) + incl - sum;
+        uint32_t run = (uint32_t)bm * (uint32_t)(g.Nq * tp.rslots) + incl - sum;
         for (int v = 0; v < wave; ++v) run += s_wsum[v];
         for (int i = i0; i < i1; ++i) {
             const uint32_t c = s_cursor[i];
@@ -701,11 +750,10 @@ backward_head_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
             run += c;
         }
         __syncthreads();
-        const uint32_t *off = offsets + (int64_t)wg * nkeys;
         for (int i = threadIdx.x; i < nkeys; i += kHeadThreads) {
             const uint32_t base = s_cursor[i];
             if (r == 0) bases[(int64_t)bm * nkeys + i] = base;
-            s_cursor[i] = base + off[i];
+            s_cursor[i] = base + s_pre[i];
         }
     }
     __syncthreads();
@@ -714,17 +762,21 @@ backward_head_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
     const int jq = lane / LPH, c = lane - (lane / LPH) * LPH;
     const uint32_t lane_off = (uint32_t)(m * D + c * 4) * sizeof(VT);
     const int zero_row = nrows * LPH;
-    const uint32_t rcap = (uint32_t)g.B * 4u * (uint32_t)(g.Nq * M * LK);  // record slots
+    const uint32_t rcap = (uint32_t)g.B * (uint32_t)(g.Nq * M * tp.rslots);  // record slots
     for (int qb = q0 + wave * QPW; qb < q1; qb += kHeadWaves * QPW) {
         // the lane index, opaque to the compiler within each pass (what phase 1
         // derives from it is recomputed per pass, not held across the loop)
         int ln = lane;
         asm volatile("" : "+v"(ln));
         // ---- phase 1: the QPW*L*K samples of this pass, one per lane per step ----
+        // record keys (tile, with the sample's cell in that tile in the bits
+        // from kKeyBits up) and record weights
         int keys[NPASS][4];
+        float rfx[NPASS], rfy[NPASS], ra[NPASS];
 #pragma unroll
         for (int p = 0; p < NPASS; ++p) {
             const int t = p * kWave + ln;
+            rfx[p] = rfy[p] = ra[p] = 0.0f;
 #pragma unroll
             for (int j = 0; j < 4; ++j) keys[p][j] = nkeys + ln;
             if ((QPW * LK) % kWave == 0 || t < QPW * LK) {
@@ -768,12 +820,26 @@ backward_head_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
                         const SampleTiles st = sample_tiles(s_tl[l], lv.W, H, cx, cy);
 #pragma unroll
                         for (int jj = 0; jj < 4; ++jj)
-                            if (st.t[jj] >= 0) keys[p][jj] = st.t[jj];
+                            if (st.t[jj] >= 0) keys[p][jj] = st.t[jj] | (st.cell[jj] << kKeyBits);
+                        rfx[p] = fx;
+                        rfy[p] = fy;
+                        ra[p] = a;
                     }
                 }
                 s_off[wave][j * PAD + i] = o;
                 s_geo[wave][j * PAD + i] = geo;
             }
+            // the pass's records: a position per key from the LDS cursor (all
+            // adds in flight at once; a lane without a record adds on a spare
+            // slot of its own)
+            const uint32_t bq = (uint32_t)(b * g.Nq + qb + t / LK);
+            uint32_t pos[4];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) pos[jj] = atomicAdd(&s_cursor[keys[p][jj] & kKeyMask], 1u);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                if ((keys[p][jj] & kKeyMask) < nkeys && pos[jj] < rcap)
+                    records[pos[jj]] = tile_record(bq, keys[p][jj] >> kKeyBits, rfx[p], rfy[p], ra[p]);
         }
         wave_lds_sync();
         // ---- phase 2: each lane its query's samples; gathers, dots with G, sums over the query's lanes ----
@@ -802,10 +868,8 @@ backward_head_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
             grad_sample(i, StageChunk<VT>::widen(s_stage[o.x + c]), StageChunk<VT>::widen(s_stage[o.y + c]),
                         StageChunk<VT>::widen(s_stage[o.z + c]), StageChunk<VT>::widen(s_stage[o.w + c]));
         };
-        // level by level: a memory level's gathers are issued, the records of
-        // the pass are written after the first of them (a wait on a load also
-        // waits on every store issued before it), a staged level is done from
-        // LDS while they are in flight, then the memory level
+        // level by level: a memory level's gathers are issued, a staged level
+        // is done from LDS while they are in flight, then the memory level
 #pragma unroll
         for (int l = 0; l < LS; ++l) {
             float4 v[K][4];
@@ -816,20 +880,6 @@ backward_head_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
                 v[k][1] = ValueTraits<VT>::load4(rsrc, (uint32_t)o.y + lane_off);
                 v[k][2] = ValueTraits<VT>::load4(rsrc, (uint32_t)o.z + lane_off);
                 v[k][3] = ValueTraits<VT>::load4(rsrc, (uint32_t)o.w + lane_off);
-            }
-            if (l == 0) {
-#pragma unroll
-                for (int p = 0; p < NPASS; ++p) {
-                    const int t = p * kWave + ln;
-                    const int j = t / LK, i = t - (t / LK) * LK;
-                    const uint32_t sidx = (uint32_t)((((int64_t)b * g.Nq + qb + j) * M + m) * LK + i);
-                    uint32_t pos[4];
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) pos[jj] = atomicAdd(&s_cursor[keys[p][jj]], 1u);
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj)
-                        if (keys[p][jj] < nkeys && pos[jj] < rcap) records[pos[jj]] = sidx;
-                }
             }
             if (LS + l < L) {
 #pragma unroll
@@ -923,11 +973,6 @@ ref_grad_sum_kernel(Geometry g, const float4 *__restrict__ ref_part, FusedGrads 
 // --------------------------------------------------------------- 3. tile_accum
 
 // defined with the dense levels below; tile_accum runs it for its extra items
-template <int LG>
-__device__ void dense_reduce_one(const Geometry &g, const TilePlan &tp, const float4 *__restrict__ partials,
-                                 float4 *__restrict__ grad_value, int accumulate, const uint8_t *__restrict__ mask,
-                                 int64_t t);
-
 // One workgroup per tile (b, m, level, tile). Its records are counting-sorted
 // by cell in LDS; then each lane group (LG lanes, 4 channels each, D = 4*LG)
 // takes (cell, split) tasks: it walks the cell's records (every S-th one for
@@ -939,11 +984,9 @@ __device__ void dense_reduce_one(const Geometry &g, const TilePlan &tp, const fl
 // compile-time.
 template <int M, int L, int K>
 __global__ void __launch_bounds__(kBlock)
-tile_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, const float *__restrict__ attn,
-                  const float4 *__restrict__ grad_out, float4 *__restrict__ grad_value,
-                  const uint32_t *__restrict__ records, const uint32_t *__restrict__ bases,
-                  const uint32_t *__restrict__ totals, int accumulate, const float4 *__restrict__ partials,
-                  int reduce_blocks, const uint8_t *__restrict__ mask)
+tile_accum_kernel(Geometry g, TilePlan tp, const float4 *__restrict__ grad_out, float4 *__restrict__ grad_value,
+                  const uint4 *__restrict__ records, const uint32_t *__restrict__ bases,
+                  const uint32_t *__restrict__ totals, int accumulate, const uint8_t *__restrict__ mask)
 {
     constexpr int LG = 256 / M / 4;  // lanes (4 channels each) per head row
     constexpr int NS = M * L * K;    // samples per query
@@ -963,13 +1006,7 @@ tile_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, const
     // head, neighbouring tiles) read G rows of neighbouring queries, so each
     // XCD (private L2) gets a contiguous item range
     const int item = (int)xcd_tile(blockIdx.x, gridDim.x);
-    if (item >= g.B * g.M * tp.ipb) {
-        // the items after the tiles add up the dense levels' query splits
-        const int r = item - g.B * g.M * tp.ipb;
-        if (r < reduce_blocks)
-            dense_reduce_one<LG>(g, tp, partials, grad_value, accumulate, mask, (int64_t)r * kBlock + threadIdx.x);
-        return;
-    }
+    if (item >= g.B * g.M * tp.ipb) return;
     const int bm = item / tp.ipb;
     const int b = bm / M, m = bm - (bm / M) * M;
     const int r_in = item - bm * tp.ipb;
@@ -995,7 +1032,6 @@ tile_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, const
     const int chunk = r_in - ib - t_in * nch;
     const int key = bm * tp.tpb + tb + t_in;
     const int ty = t_in / ntw, tx = t_in - ty * ntw;
-    const float Wf = (float)W, Hf = (float)H;
     const int r0 = ty * th, r1 = min(r0 + th, H);
     const int c0 = tx * tw, c1 = min(c0 + tw, W);
     const int pw = c1 - c0, ph = r1 - r0;   // pixels of this tile
@@ -1004,7 +1040,7 @@ tile_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, const
     const int npix = ph * pw;
     const int S = ncells >= NG ? 1 : NG / ncells;   // lane groups per cell
     const int ntask = ncells * S;
-    const uint32_t nsamples = (uint32_t)g.samples();
+    const uint32_t nqueries = (uint32_t)g.queries();
     const int grp = threadIdx.x / LG;
     const int lig = threadIdx.x % LG;
     // grad_output rows through a buffer resource: 32-bit offsets, and an
@@ -1016,7 +1052,7 @@ tile_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, const
     uint32_t rtot = totals[key];
     {
         // keep the range inside the record array whatever the workspace holds
-        const uint32_t rcap = (uint32_t)(4 * g.samples());
+        const uint32_t rcap = (uint32_t)g.B * (uint32_t)(g.Nq * M * tp.rslots);
         rtot = rbeg < rcap ? min(rtot, rcap - rbeg) : 0u;
     }
 
@@ -1034,35 +1070,34 @@ tile_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, const
 #pragma unroll
         for (int p = 0; p < kDirectPix; ++p) acc[p] = make_float4(0.f, 0.f, 0.f, 0.f);
         for (uint32_t i0 = grp; i0 < rtot; i0 += NG * kBatch) {
-            uint32_t sidx[kBatch];
+            uint4 rec[kBatch];
 #pragma unroll
             for (int j = 0; j < kBatch; ++j) {
                 const uint32_t i = i0 + j * NG;
-                sidx[j] = i < rtot ? records[rbeg + i] : nsamples;
+                rec[j] = i < rtot ? records[rbeg + i] : make_uint4(nqueries << kCellBits, 0u, 0u, 0u);
             }
-            float2 u[kBatch];
-            float a[kBatch];
             float4 gv[kBatch];
 #pragma unroll
             for (int j = 0; j < kBatch; ++j) {
-                const bool ok = sidx[j] < nsamples;  // see the chunked path below
-                u[j] = ok ? loc[sidx[j]] : make_float2(-1e30f, -1e30f);
-                a[j] = ok ? attn[sidx[j]] : 0.0f;
-                const uint32_t bq = ok ? sidx[j] / (uint32_t)NS : 0u;
+                const uint32_t bq = rec[j].x >> kCellBits;
+                const bool ok = bq < nqueries;  // see the chunked path below
                 gv[j] = ok ? grad_out[((int64_t)bq * g.M + m) * LG + lig] : make_float4(0.f, 0.f, 0.f, 0.f);
             }
 #pragma unroll
             for (int j = 0; j < kBatch; ++j) {
-                int cx, cy;
-                float fx, fy;
-                const bool in = sample_cell(u[j], Wf, Hf, cx, cy, fx, fy);
+                // the record's cell (ry, rx) has its top-left corner at tile pixel (ry - 1, rx - 1)
+                const int cell = (int)(rec[j].x & ((1u << kCellBits) - 1));
+                const int ry = cell / cw, rx = cell - (cell / cw) * cw;
+                const bool in = (rec[j].x >> kCellBits) < nqueries;
+                const float fx = __uint_as_float(rec[j].y);
+                const float ay0 = __uint_as_float(rec[j].z), ay1 = __uint_as_float(rec[j].w);
 #pragma unroll
                 for (int p = 0; p < kDirectPix; ++p) {
-                    // pixel (py, px) of the tile is corner (px - (cx - c0), py - (cy - r0)) of the cell
-                    const int py = r0 + p / pw, px = c0 + p % pw;
-                    const int dx = px - cx, dy = py - cy;
+                    // pixel (py, px) of the tile is corner (dx, dy) of the cell
+                    const int py = p / pw, px = p % pw;
+                    const int dx = px - (rx - 1), dy = py - (ry - 1);
                     const bool hit = in && p < npix && (dx == 0 || dx == 1) && (dy == 0 || dy == 1);
-                    const float w = hit ? a[j] * (dx ? fx : 1.0f - fx) * (dy ? fy : 1.0f - fy) : 0.0f;
+                    const float w = hit ? (dy ? ay1 : ay0) * (dx ? fx : 1.0f - fx) : 0.0f;
                     acc[p].x = __builtin_fmaf(w, gv[j].x, acc[p].x);
                     acc[p].y = __builtin_fmaf(w, gv[j].y, acc[p].y);
                     acc[p].z = __builtin_fmaf(w, gv[j].z, acc[p].z);
@@ -1127,19 +1162,16 @@ tile_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, const
 #pragma unroll
         for (int k = 0; k < RPT; ++k) {
             const int i = threadIdx.x + k * kBlock;
-            const uint32_t sidx = i < n ? records[rbeg + c0r + i] : nsamples;
-            // the main kernel wrote each record for this tile with the same
-            // cell computation; the checks only keep a corrupt record from
-            // addressing outside loc/attn or the cell table
-            int cx, cy;
-            float fx, fy;
-            sample_cell(sidx < nsamples ? loc[sidx] : make_float2(0.f, 0.f), Wf, Hf, cx, cy, fx, fy);
-            const float a = sidx < nsamples ? attn[sidx] : 0.0f;
-            const float ay0 = a * (1.0f - fy), ay1 = a * fy;
+            const uint4 rec = i < n ? records[rbeg + c0r + i] : make_uint4(nqueries << kCellBits, 0u, 0u, 0u);
+            // the checks only keep a corrupt record from addressing outside
+            // grad_output or the cell table
+            const uint32_t bq = rec.x >> kCellBits;
+            const int cell = (int)(rec.x & ((1u << kCellBits) - 1));
+            const float fx = __uint_as_float(rec.y);
+            const float ay0 = __uint_as_float(rec.z), ay1 = __uint_as_float(rec.w);
             rw[k] = make_float4(ay0 * (1.0f - fx), ay0 * fx, ay1 * (1.0f - fx), ay1 * fx);
-            rq[k] = (sidx / (uint32_t)NS) * grow_bytes;
-            const int ry = cy - r0 + 1, rx = cx - c0 + 1;
-            rc[k] = (sidx < nsamples && ry >= 0 && ry <= ph && rx >= 0 && rx < cw) ? ry * cw + rx : -1;
+            rq[k] = bq * grow_bytes;
+            rc[k] = (bq < nqueries && cell < ncells) ? cell : -1;
         }
 #pragma unroll
         for (int k = 0; k < RPT; ++k)
@@ -1280,13 +1312,13 @@ zero_split_levels_kernel(Geometry g, TilePlan tp, float4 *__restrict__ grad_valu
 // stay in flight across the LDS-only barriers. A level whose queries are split
 // over several items parks each item's sums in the workspace; extra items of
 // tile_accum add them up in split order and write every pixel once.
-constexpr int kDensePix = 256;             // pixels per part at most
+constexpr int kDensePix = 384;             // pixels per part at most
 constexpr int kDenseSub = 1024;             // samples per sub-chunk at most
 constexpr int kDenseQ = 256;               // queries per sub-chunk at most
 constexpr int kDenseBatch = 4;             // pairs in flight per lane group
 constexpr int kDenseThreads = 512;         // threads per dense workgroup
 constexpr double kDenseMinPerPix = 24.0;   // samples per pixel (per batch and head) that make a level dense
-constexpr int kDenseMaxParts = 8;          // pixel parts of a dense level at most
+constexpr int kDenseMaxPix = 2048;         // pixels of a dense level at most
 constexpr double kDenseItemSamples = 3072; // samples per dense work item (sets the query splits)
 constexpr int kDenseMaxSplit = 64;
 
@@ -1473,7 +1505,7 @@ dense_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, cons
         if (pl >= npix) break;
         float4 v = acc[j];
         if (splits > 1) {
-            partials[((int64_t)item * kDensePix + pl) * LG + lig] = v;
+            partials[((int64_t)bm * tp.ppb + tp.pbase[l] + (int64_t)split * npix_l + p0 + pl) * LG + lig] = v;
         } else {
             const int64_t row = (int64_t)b * g.S + lstart + p0 + pl;
             if (mask && mask[row]) v = make_float4(0.f, 0.f, 0.f, 0.f);  // padded: no gradient
@@ -1509,16 +1541,11 @@ __device__ void dense_reduce_one(const Geometry &g, const TilePlan &tp, const fl
         const int m = (int)((t / LG) % g.M);
         const int p = (int)((t / ((int64_t)LG * g.M)) % npix_l);
         const int b = (int)(t / ((int64_t)LG * g.M * npix_l));
-        const int parts = tp.dparts[l], splits = tp.dsplit[l];
-        // the part holding pixel p: parts start at floor(npix_l * k / parts)
-        int part = (int)((int64_t)p * parts / npix_l);
-        while (part + 1 < parts && (int)((int64_t)npix_l * (part + 1) / parts) <= p) ++part;
-        while (part > 0 && (int)((int64_t)npix_l * part / parts) > p) --part;
-        const int pl = p - (int)((int64_t)npix_l * part / parts);
-        const int64_t item0 = (int64_t)(b * g.M + m) * tp.dipb + tp.dibase[l] + (int64_t)part * splits;
+        const int splits = tp.dsplit[l];
+        const int64_t p0 = (int64_t)(b * g.M + m) * tp.ppb + tp.pbase[l] + p;
         float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
         for (int s = 0; s < splits; ++s) {
-            const float4 x = partials[((item0 + s) * kDensePix + pl) * LG + c];
+            const float4 x = partials[(p0 + (int64_t)s * npix_l) * LG + c];
             v.x += x.x;
             v.y += x.y;
             v.z += x.z;
@@ -1537,6 +1564,16 @@ __device__ void dense_reduce_one(const Geometry &g, const TilePlan &tp, const fl
         *dst = v;
         return;
     }
+}
+
+// The dense levels' query splits added up, one thread per (batch, pixel,
+// head, float4 of channels) over the split levels.
+template <int LG>
+__global__ void __launch_bounds__(kBlock)
+dense_reduce_kernel(Geometry g, TilePlan tp, const float4 *__restrict__ partials, float4 *__restrict__ grad_value,
+                    int accumulate, const uint8_t *__restrict__ mask)
+{
+    dense_reduce_one<LG>(g, tp, partials, grad_value, accumulate, mask, (int64_t)blockIdx.x * kBlock + threadIdx.x);
 }
 
 // ------------------------------------------------------------ generic fallback
@@ -1607,8 +1644,9 @@ backward_generic_kernel(Geometry g, const VT *__restrict__ value, const float2 *
 // ------------------------------------------------------------------- host side
 
 struct Workspace {
-    uint32_t *counts, *totals, *bases, *records;
-    float4 *partials;  // per dense work item: kDensePix pixels x D channels
+    uint32_t *counts, *totals, *bases;
+    uint4 *records;
+    float4 *partials;  // the dense levels' query-split sums (TilePlan::pbase)
     float4 *ref_part;  // fused per-head path: [B, Nq, M, L] sums of the reference-point gradient
 };
 
@@ -1619,7 +1657,7 @@ size_t layout(const Geometry &g, const TilePlan &tp, char *base, Workspace *ws)
     const size_t nkeys = (size_t)g.B * g.M * tp.tpb;
     // per-workgroup counts of the query-range binning or of the per-head one
     const size_t ncount = std::max((size_t)g.B * tp.wpb, (size_t)g.B * tp.hqr) * g.M * tp.tpb;
-    const size_t nrec = 4 * (size_t)g.samples();
+    const size_t nrec = (size_t)g.queries() * g.M * tp.rslots;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         char *p = base ? base + off : nullptr;
@@ -1630,8 +1668,8 @@ size_t layout(const Geometry &g, const TilePlan &tp, char *base, Workspace *ws)
     w.counts = take(ncount * 4);
     w.totals = take(nkeys * 4);
     w.bases = take(nkeys * 4);
-    w.records = take(nrec * 4);
-    w.partials = reinterpret_cast<float4 *>(take((size_t)g.B * g.M * tp.dipb * kDensePix * g.D * 4));
+    w.records = reinterpret_cast<uint4 *>(take(nrec * sizeof(uint4)));
+    w.partials = reinterpret_cast<float4 *>(take((size_t)g.B * g.M * tp.ppb * g.D * 4));
     w.ref_part = reinterpret_cast<float4 *>(take((size_t)g.queries() * g.M * g.L * 16));
     if (ws) *ws = w;
     return off;
@@ -1700,7 +1738,7 @@ int head_stage_level(const Geometry &g, const TilePlan &tp, uint32_t &stage_byte
         constexpr int LPH = 256 / M / 4, QPW = kWave / LPH;
         constexpr size_t kStatic = (size_t)kHeadWaves * QPW * (L * K + 1) * 32 + 2 * 16 * L + 4 * kHeadWaves;
         if (g.Nq < kHeadMinQueries) return 0;
-        const size_t cursors = (size_t)(tp.tpb + kWave) * 4;
+        const size_t cursors = (size_t)(2 * tp.tpb + kWave) * 4;  // cursors and prefix counts
         for (int ls = 1; ls < L; ++ls) {
             const int64_t rows = (int64_t)g.S - g.lv.start[ls];
             const size_t bytes = ((size_t)(rows + 1) * LPH * sizeof(typename StageChunk<VT>::type) + 15) & ~(size_t)15;
@@ -1713,25 +1751,29 @@ int head_stage_level(const Geometry &g, const TilePlan &tp, uint32_t &stage_byte
     }
 }
 
+// The per-head path's binning: one row of tile counts per (batch, head, query range).
+template <int M, int L, int K>
+hipError_t launch_head_binning(const Geometry &g, const TilePlan &tp, const float *loc, const Workspace &ws,
+                               hipStream_t st)
+{
+    const int nwg = g.B * M * tp.hqr;
+    {
+        KernelScope ks_("bin_count_head_kernel", st);
+        hipLaunchKernelGGL((bin_count_head_kernel<M, L, K>), dim3(nwg), dim3(kBinThreads), (size_t)tp.tpb * 4, st, g,
+                           tp, reinterpret_cast<const float2 *>(loc), ws.counts);
+    }
+    return hipGetLastError();
+}
+
+// The per-head main kernel (after launch_head_binning on the same stream).
 template <typename VT, int M, int L, int K, int LS, bool FUSED>
 hipError_t launch_head(const Geometry &g, const TilePlan &tp, const void *value, const float *loc,
                        const float *attn, const float *go, float *gl, float *ga, const Workspace &ws,
                        uint32_t stage_bytes, const uint8_t *mask, const FusedGrads &fg, hipStream_t st)
 {
-    const int nkeys = g.B * M * tp.tpb;
     const int nwg = g.B * M * tp.hqr;
-    {
-        KernelScope ks_("clear_totals_kernel", st);
-        hipLaunchKernelGGL(clear_totals_kernel, dim3((nkeys + kBlock - 1) / kBlock), dim3(kBlock), 0, st, nkeys,
-                           ws.totals);
-    }
-    {
-        KernelScope ks_("bin_count_head_kernel", st);
-        hipLaunchKernelGGL((bin_count_head_kernel<M, L, K>), dim3(nwg), dim3(kBinThreads), (size_t)tp.tpb * 4, st, g,
-                           tp, reinterpret_cast<const float2 *>(loc), ws.counts, ws.totals);
-    }
     const uint32_t grid = round_up8((uint32_t)nwg);
-    const size_t dyn = (size_t)stage_bytes + (size_t)(tp.tpb + kWave) * 4;
+    const size_t dyn = (size_t)stage_bytes + (size_t)(2 * tp.tpb + kWave) * 4;
     {
         KernelScope ks_(FUSED ? "backward_fused_head_kernel" : "backward_head_kernel", st);
         hipLaunchKernelGGL((backward_head_kernel<VT, M, L, K, LS, FUSED>), dim3(grid), dim3(kHeadThreads), dyn, st, g,
@@ -1758,22 +1800,13 @@ hipError_t launch_fast(const Geometry &g, const TilePlan &tp, const void *value,
     const int nwg = g.B * tp.wpb;
     const size_t hist_bytes = (size_t)(nkb + kWave) * 4;  // + a slot per lane for its idle adds
     constexpr int LG = 256 / M / 4;
-    // the dense levels on the side stream: they read only the inputs and
-    // write their own grad_value rows and workspace section, so they run
-    // beside the binning and the main kernel; tile_accum (which adds their
-    // query splits) waits for them. Without the side stream (side_ok false:
-    // the caller's stream only) they run first on `st`.
+    // The dense levels (and the sum of their query splits) read only the
+    // inputs and write their own grad_value rows and workspace section, so
+    // they run on the side stream beside everything else on `st`, which
+    // waits for them only at the end. Without the side stream (side_ok
+    // false: the caller's stream only) they run last on `st`.
     SideStream *side = nullptr;
-    if (tp.dipb > 0) {
-        hipStream_t ds = st;
-        hipError_t e = hipSuccess;
-        if (side_ok) {
-            e = side_stream(&side);
-            if (e == hipSuccess) e = hipEventRecord(side->fork, st);
-            if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
-            if (e != hipSuccess) return e;
-            ds = side->s;
-        }
+    auto launch_dense = [&](hipStream_t ds) -> hipError_t {
         const uint32_t ditems = (uint32_t)(g.B * g.M * tp.dipb);
         {
             KernelScope ks_("dense_accum_kernel", ds);
@@ -1781,14 +1814,32 @@ hipError_t launch_fast(const Geometry &g, const TilePlan &tp, const void *value,
                                tp, reinterpret_cast<const float2 *>(loc), attn, reinterpret_cast<const float4 *>(go),
                                reinterpret_cast<float4 *>(gv), ws.partials, accumulate ? 1 : 0, mask);
         }
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        if (side && (e = hipEventRecord(side->join, side->s)) != hipSuccess) return e;
+        int64_t nred = 0;
+        for (int l = 0; l < g.L; ++l)
+            if (((tp.dense_mask >> l) & 1) && tp.dsplit[l] > 1)
+                nred += (int64_t)g.B * g.lv.H[l] * g.lv.W[l] * g.M * LG;
+        if (nred > 0) {
+            KernelScope ks_("dense_reduce_kernel", ds);
+            hipLaunchKernelGGL((dense_reduce_kernel<LG>), dim3((unsigned)((nred + kBlock - 1) / kBlock)), dim3(kBlock),
+                               0, ds, g, tp, ws.partials, reinterpret_cast<float4 *>(gv), accumulate ? 1 : 0, mask);
+        }
+        return hipGetLastError();
+    };
+    if (tp.dipb > 0 && side_ok) {
+        hipError_t e = side_stream(&side);
+        if (e == hipSuccess) e = hipEventRecord(side->fork, st);
+        if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
+        if (e == hipSuccess) e = launch_dense(side->s);
+        if (e == hipSuccess) e = hipEventRecord(side->join, side->s);
+        if (e != hipSuccess) return e;
     }
     uint32_t stage_bytes = 0;
     const int hls = head_stage_level<VT, M, L, K>(g, tp, stage_bytes);
     if (hls > 0) {
         // the per-head path: binning and main kernel per (batch, head, query range)
-        hipError_t e = hipErrorInvalidValue;
+        hipError_t e = launch_head_binning<M, L, K>(g, tp, loc, ws, st);
+        if (e != hipSuccess) return e;
+        e = hipErrorInvalidValue;
         if constexpr (M == 8 && L == 4 && K == 4) {
 #define MSDA_HEAD(LS_)                                                                                            \
     if (hls == LS_)                                                                                               \
@@ -1822,25 +1873,19 @@ hipError_t launch_fast(const Geometry &g, const TilePlan &tp, const void *value,
                                st, g, tp, reinterpret_cast<float4 *>(gv));
         }
     }
-    if (side) {
-        const hipError_t e = hipStreamWaitEvent(st, side->join, 0);
-        if (e != hipSuccess) return e;
-    }
-    // the sparse tiles, then (as extra items of the same launch) the sums of
-    // the dense levels' query splits
-    int64_t nred = 0;
-    for (int l = 0; l < g.L; ++l)
-        if (((tp.dense_mask >> l) & 1) && tp.dsplit[l] > 1) nred += (int64_t)g.B * g.lv.H[l] * g.lv.W[l] * g.M * LG;
-    const int reduce_blocks = (int)((nred + kBlock - 1) / kBlock);
-    const uint32_t items = (uint32_t)(g.B * g.M * tp.ipb) + (uint32_t)reduce_blocks;
+    // the sparse levels' tiles
+    const uint32_t items = (uint32_t)(g.B * g.M * tp.ipb);
     if (items > 0) {
         KernelScope ks_("tile_accum_kernel", st);
         hipLaunchKernelGGL((tile_accum_kernel<M, L, K>), dim3(round_up8(items)), dim3(kBlock), 0, st, g, tp,
-                           reinterpret_cast<const float2 *>(loc), attn, reinterpret_cast<const float4 *>(go),
-                           reinterpret_cast<float4 *>(gv), ws.records, ws.bases, ws.totals, accumulate ? 1 : 0,
-                           ws.partials, reduce_blocks, mask);
+                           reinterpret_cast<const float4 *>(go), reinterpret_cast<float4 *>(gv), ws.records, ws.bases,
+                           ws.totals, accumulate ? 1 : 0, mask);
     }
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (side) return hipStreamWaitEvent(st, side->join, 0);
+    if (tp.dipb > 0) return launch_dense(st);
+    return hipSuccess;
 }
 
 // Which (VT-independent) fast-path instantiation serves g, if any.
@@ -1978,7 +2023,7 @@ bool make_tile_plan(const Geometry &g, TilePlan &tp)
     const double target = kTileTarget;
     // every (cell, split) task needs a slot: cells <= kTaskSlots * lane groups
     const int max_cells = std::min(kTileCells, kTaskSlots * (kBlock / (g.D / 4)));
-    int base = 0, ibase = 0, dibase = 0;
+    int base = 0, ibase = 0, dibase = 0, ppb = 0;
     tp.dense_mask = 0;
     for (int l = 0; l < g.L; ++l) {
         const int H = g.lv.H[l], W = g.lv.W[l];
@@ -1987,13 +2032,18 @@ bool make_tile_plan(const Geometry &g, TilePlan &tp)
         const double per_cell = (double)g.Nq * g.K / ((double)H * W);
         tp.dparts[l] = tp.dsplit[l] = 1;
         tp.dibase[l] = dibase;
-        if (per_cell >= kDenseMinPerPix && H * W <= kDenseMaxParts * kDensePix) {
+        tp.pbase[l] = ppb;
+        if (per_cell >= kDenseMinPerPix && H * W <= kDenseMaxPix) {
             // dense level: no tiles; (pixel part, query split) items
             tp.dense_mask |= 1 << l;
             tp.dparts[l] = (H * W + kDensePix - 1) / kDensePix;
             const double s = std::ceil((double)g.Nq * g.K / kDenseItemSamples);
             tp.dsplit[l] = (int)std::min<double>(kDenseMaxSplit, std::max(1.0, s));
             dibase += tp.dparts[l] * tp.dsplit[l];
+            if (tp.dsplit[l] > 1) {
+                tp.pbase[l] = ppb;
+                ppb += tp.dsplit[l] * H * W;
+            }
             tp.th[l] = tp.tw[l] = tp.ntw[l] = tp.nchunk[l] = 1;
             tp.tinv_h[l] = tp.tinv_w[l] = 1.0f;
             tp.tbase[l] = base;
@@ -2041,8 +2091,9 @@ bool make_tile_plan(const Geometry &g, TilePlan &tp)
     for (int l = g.L; l < MSDA_MAX_LEVELS; ++l) {
         tp.th[l] = tp.tw[l] = tp.ntw[l] = tp.nchunk[l] = 1, tp.tbase[l] = base, tp.ibase[l] = ibase;
         tp.tinv_h[l] = tp.tinv_w[l] = 1.0f;
-        tp.dparts[l] = tp.dsplit[l] = 1, tp.dibase[l] = dibase;
+        tp.dparts[l] = tp.dsplit[l] = 1, tp.dibase[l] = dibase, tp.pbase[l] = ppb;
     }
+    tp.ppb = ppb;
     tp.tpb = base;
     tp.ipb = ibase;
     tp.dipb = dibase;
@@ -2051,9 +2102,16 @@ bool make_tile_plan(const Geometry &g, TilePlan &tp)
     tp.hqr = std::max(1, (kHeadTargetWGs + g.B * g.M - 1) / (g.B * g.M));
     tp.hqpr = std::max(1, (g.Nq + tp.hqr - 1) / tp.hqr);
     tp.hqr = std::max(1, (g.Nq + tp.hqpr - 1) / tp.hqpr);
-    // the per-workgroup histogram / cursors live in LDS; record indices are 32-bit
+    int nsparse = 0;
+    for (int l = 0; l < g.L; ++l) nsparse += !((tp.dense_mask >> l) & 1);
+    tp.rslots = 4 * g.K * nsparse;
+    // the per-workgroup histogram / cursors live in LDS (and their indices
+    // below 2^kKeyBits); record positions are 32-bit and a record holds its
+    // query index in 32 - kCellBits bits
     if (((size_t)g.M * tp.tpb + kWave) * 4 > 64 * 1024) return false;  // the main kernel's LDS cursors
-    if ((uint64_t)g.samples() * 4 >= (1ull << 32)) return false;
+    static_assert((64 * 1024 / 4) <= (1 << kKeyBits), "cursor indices fit below the key bits");
+    if ((uint64_t)g.queries() * g.M * tp.rslots >= (1ull << 32)) return false;
+    if ((uint64_t)g.queries() >= (1ull << (32 - kCellBits))) return false;
     // grad_output is read through 32-bit buffer offsets below the out-of-range marker
     if ((uint64_t)g.queries() * g.M * g.D * 4 >= (uint64_t)kOutOfRange) return false;
     return true;

@@ -47,6 +47,9 @@ struct TilePlan {
     // per-head path (one workgroup per batch, head and range of queries)
     int32_t hqr;   // query ranges per (batch, head)
     int32_t hqpr;  // queries per range
+    // record slots per (batch, query, head): a sample of a sparse level has a
+    // record in each tile its in-map corners touch, at most four
+    int32_t rslots;
     // Dense levels (bit l of dense_mask) have no tiles and no records: their
     // grad_value is accumulated from the samples directly, per (pixel part,
     // query split) work item.
@@ -55,6 +58,10 @@ struct TilePlan {
     int32_t dsplit[MSDA_MAX_LEVELS];  // query splits of a dense level
     int32_t dibase[MSDA_MAX_LEVELS];  // first dense item of the level within (batch, head)
     int32_t dipb;                     // dense items per (batch, head)
+    // the query splits' sums of the dense levels with several splits: per
+    // (batch, head) ppb rows of D channels, level l's [dsplit][H*W] from pbase
+    int32_t pbase[MSDA_MAX_LEVELS];
+    int32_t ppb;
     // 1/tw and 1/th as floats: floor((c + 0.5) * (1/t)) is c / t exactly for
     // 0 <= c < 2^20 and t <= 128 (checked exhaustively), without a division
     float tinv_w[MSDA_MAX_LEVELS];
