@@ -25,7 +25,9 @@ Counter runs (rocprofv3 --pmc, one pass of COUNTER_PASSES per run) use
 ``--eager --profile-run``; ``--copy-mib N`` runs only a plain elementwise copy
 of N MiB (a check of the byte counting: it must read and write N MiB), and
 ``--ingest-counters DIR`` turns the passes under DIR/<pass> into
-profiles/traffic.json and profiles/counters_encoder_step.md.
+profiles/traffic.json and profiles/counters_encoder_step.md, and
+``--trace-summary DIR`` turns a ``rocprofv3 --kernel-trace --stats`` run of
+this script (csv output under DIR) into profiles/kernel_trace_encoder_step.md.
 """
 import argparse
 import csv
@@ -45,6 +47,7 @@ HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD's published peak
 METRIC = "MSDeformAttn fwd/bwd queries/s and effective HBM GB/s (% of peak), encoder shape"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 COUNTERS_MD = os.path.join(ROOT, "profiles", "counters_encoder_step.md")
+TRACE_MD = os.path.join(ROOT, "profiles", "kernel_trace_encoder_step.md")
 FLUSH_BYTES = 1 << 30   # read between cold calls: 4x the 256 MB Infinity Cache, 32x all L2
 
 # rocprofv3 --pmc passes read by --ingest-counters, one run each on
@@ -83,6 +86,9 @@ def parse():
                    help="calls per entry point in the cold-cache timing (0 skips it)")
     p.add_argument("--copy-mib", type=int, default=0,
                    help="only run a plain copy of this many MiB, 5 times (a check of the counters' byte counts)")
+    p.add_argument("--trace-summary", default=None, metavar="DIR",
+                   help="write profiles/kernel_trace_encoder_step.md from a rocprofv3 --kernel-trace --stats run "
+                        "of this script with the same --steps and --warmup (csv output under DIR)")
     p.add_argument("--ingest-counters", default=None, metavar="DIR",
                    help="write profiles/traffic.json and the counter summary from rocprofv3 --pmc passes under "
                         "DIR/<pass> and exit")
@@ -331,6 +337,102 @@ def _counter_summary(t):
         f.write("\n".join(lines) + "\n")
 
 
+LIB_KERNELS = ("reference_points_kernel", "sampling_locations_kernel", "softmax_vec_kernel", "forward_",
+               "bin_count", "backward_", "clear_totals_kernel", "tile_accum_kernel", "dense_accum_kernel",
+               "dense_reduce_kernel", "zero_", "ref_grad_sum_kernel", "fused_grads_kernel")
+
+
+def trace_summary(d, steps, warmup):
+    """profiles/kernel_trace_encoder_step.md from the kernel trace of
+    `bench.py --steps K --warmup W` under rocprofv3 --kernel-trace --stats.
+    The run's plain steps (reference points, then sampling locations, ...)
+    come in this order: max(1, W) warm-up steps and one captured step
+    (eager), 3 + W + K graph replays, then K eager steps timed per entry
+    point and K eager steps timed per kernel by the library's event pairs
+    (the figures of the bench line). Per kernel: rocprofv3's average over
+    every launch of the run, and the medians over the graph replays and over
+    the library-timed eager steps; then the timeline of the median graph
+    replay."""
+    import statistics as st
+    stats = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    trace = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if not stats or not trace:
+        raise SystemExit(f"no kernel_stats/kernel_trace csv under {d}")
+    all_avg = {}
+    for r in csv.DictReader(open(stats[0])):
+        n = _short_kernel_name(r["Name"])
+        if n.startswith(LIB_KERNELS):
+            c, t = all_avg.get(n, (0, 0.0))
+            all_avg[n] = (c + int(r["Calls"]), t + float(r["TotalDurationNs"]))
+    rows = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), _short_kernel_name(r["Kernel_Name"]))
+                  for r in csv.DictReader(open(trace[0])))
+    starts = [i for i, r in enumerate(rows)
+              if r[2] == "reference_points_kernel" and i + 1 < len(rows) and rows[i + 1][2] == "sampling_locations_kernel"]
+    plain = []
+    for si in starts:
+        j = si + 1
+        while j < len(rows) and rows[j][2] != "reference_points_kernel":
+            j += 1
+        plain.append(rows[si:j])
+    w0 = max(1, warmup) + 1
+    nrep = 3 + warmup + steps
+    want = w0 + nrep + 2 * steps
+    if len(plain) < want:
+        raise SystemExit(f"{len(plain)} plain steps in the trace, expected at least {want} for "
+                         f"--steps {steps} --warmup {warmup}")
+    # the replays after the three that are checked against eager (those are
+    # followed by torch's comparison kernels); library kernels only
+    graph = [[r for r in seg if r[2].startswith(LIB_KERNELS)] for seg in plain[w0 + 3:w0 + nrep]]
+    timed = [[r for r in seg if r[2].startswith(LIB_KERNELS)] for seg in plain[w0 + nrep + steps:w0 + nrep + 2 * steps]]
+
+    def per_kernel(group):
+        k = {}
+        for seg in group:
+            for s0, e0, n in seg:
+                k.setdefault(n, []).append((e0 - s0) / 1e3)
+        return {n: st.median(v) for n, v in k.items()}
+
+    kg, kt = per_kernel(graph), per_kernel(timed)
+    spans = sorted(((max(r[1] for r in seg) - seg[0][0]) / 1e3, i) for i, seg in enumerate(graph))
+    med = graph[spans[len(spans) // 2][1]]
+    flags = "" if (steps, warmup) == (50, 10) else f" --steps {steps} --warmup {warmup}"  # the defaults, or not
+    cmd = (f"cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <repo>/gpurun_out/"
+           f"trace -o run -- python3 <repo>/bench.py{flags} > <repo>/gpurun_out/trace/bench.log")
+    lines = ["# Kernel trace — encoder_backward step (B=2, M=8, D=32, L=4 76x106..8x13, S=Nq=10687, K=4, fp32)", "",
+             "Generated by `python bench.py --trace-summary DIR --steps {0} --warmup {1}` from the csv output of".format(
+                 steps, warmup), "", "```", cmd, "```", "",
+             f"Kernel sources hash `{kernel_source_hash()}`. The library's kernels only (torch's own kernels omitted). "
+             "`all launches` is rocprofv3's average over every launch of the run (plain, fused and box steps, "
+             "graph replays and eager loops, the cold loop); the medians are per launch over the "
+             f"{len(graph)} graph replays of the plain step (warm-up and timed) and over the {len(timed)} eager plain steps whose "
+             "kernels the library times with HIP event pairs (the `kernels` figures of the bench line).", "",
+             "| kernel | launches | avg µs, all launches | median µs, graph replays | median µs, event-timed eager steps |",
+             "|---|---:|---:|---:|---:|"]
+    for n, (c, t) in sorted(all_avg.items(), key=lambda kv: -kv[1][1]):
+        g_ = f"{kg[n]:.1f}" if n in kg else ""
+        t_ = f"{kt[n]:.1f}" if n in kt else ""
+        lines.append(f"| `{n}` | {c} | {t / c / 1e3:.1f} | {g_} | {t_} |")
+    blog = os.path.join(d, "bench.log")
+    if os.path.exists(blog):
+        bl = [ln for ln in open(blog) if ln.startswith('{"metric"')]
+        if bl:
+            b = json.loads(bl[-1])
+            lines += ["", f"The bench line this profiled run printed: {b['ms_per_step'] * 1e3:.1f} µs per graph-replayed "
+                      f"step; per kernel (library event pairs, eager): " +
+                      ", ".join(f"{k} {v['avg_us']:.1f}" for k, v in b["kernels"].items()) + " µs; roofline kernel "
+                      f"`{b['roofline']['kernel']}` at {b['roofline']['avg_us']:.1f} µs."]
+    lines += ["", f"Graph-replay step spans (first kernel start to last kernel end): median "
+              f"{spans[len(spans) // 2][0]:.1f} µs, min {spans[0][0]:.1f} µs, max {spans[-1][0]:.1f} µs. "
+              "The timeline of the median replay (µs from its first kernel's start; kernels on two HW queues "
+              "overlap):", "", "| start | end | µs | kernel |", "|---:|---:|---:|---|"]
+    t0 = med[0][0]
+    for s0, e0, n in med:
+        lines.append(f"| {(s0 - t0) / 1e3:.1f} | {(e0 - t0) / 1e3:.1f} | {(e0 - s0) / 1e3:.1f} | `{n}` |")
+    with open(TRACE_MD, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def copy_calibration(mib):
     import torch
     n = mib * 1024 * 1024 // 4
@@ -477,26 +579,33 @@ def copy_ceiling(dev, nbytes=FLUSH_BYTES, reps=10):
 def cold_timing(msda, calls, dev, iters):
     """Every entry point of the step timed with L2 and the 256 MB Infinity
     Cache evicted before it: a 1 GiB read (a reduction over a buffer that no
-    call touches) runs between the calls, outside the timed pairs. Returns the
-    library's per-kernel event timing and per-call event timing, averaged."""
+    call touches) runs between the calls, outside the timed pairs. Two rounds:
+    per call with HIP events around it (the library's timing off, so the
+    backward runs as in the step), then per kernel with the library's event
+    pairs. Returns both, averaged."""
     import torch
     flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
     sink = torch.empty((), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     per_call = {name: 0.0 for name, _ in calls}
     torch.cuda.synchronize()
-    msda.msda_timing_reset()
     for _ in range(iters):
         for name, f in calls:
             torch.sum(flush, dim=0, out=sink)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            msda.msda_timing_enable(True)
             e0.record(stream)
             f()
             e1.record(stream)
-            msda.msda_timing_enable(False)
             e1.synchronize()
             per_call[name] += e0.elapsed_time(e1) * 1e3 / iters
+    msda.msda_timing_reset()
+    for _ in range(iters):
+        for name, f in calls:
+            torch.sum(flush, dim=0, out=sink)
+            msda.msda_timing_enable(True)
+            f()
+            msda.msda_timing_enable(False)
+            torch.cuda.synchronize()
     timing = msda.msda_timing_read()
     msda.msda_timing_reset()
     del flush
@@ -506,10 +615,12 @@ def cold_timing(msda, calls, dev, iters):
 
 def forward_configs(msda, workloads, dev, args, names=("decoder", "encoder_bf16_large")):
     """The forward alone on the other forward workloads of the pages' shapes
-    (the decoder's 300 object queries; the large batch with bf16 value):
-    average kernel duration from the library's event pairs over 20 calls,
-    queries/s and effective HBM GB/s over the algorithmic bytes (the distinct
-    value rows touched, loc, A and the output)."""
+    (the decoder's 300 object queries; the large batch with bf16 value): the
+    time per call of a HIP graph of 20 back-to-back calls (the library's
+    event pairs name the kernel, and their own figure, which overstates a
+    kernel of a few microseconds, is kept as event_us), queries/s and
+    effective HBM GB/s over the algorithmic bytes (the distinct value rows
+    touched, loc, A and the output)."""
     import torch
     out = {}
     for name in names:
@@ -542,9 +653,31 @@ def forward_configs(msda, workloads, dev, args, names=("decoder", "encoder_bf16_
         t = msda.msda_timing_read()
         msda.msda_timing_reset()
         kernel, (ms, cnt) = max(t.items(), key=lambda kv: kv[1][0])
-        us = ms * 1e3 / cnt
+        event_us = ms * 1e3 / cnt
+        s2 = torch.cuda.Stream(dev)
+        s2.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(s2):
+            msda.msda_forward(value, shapes, lsi, loc, A)
+        torch.cuda.current_stream(dev).wait_stream(s2)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(n):
+                msda.msda_forward(value, shapes, lsi, loc, A)
+        graph.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 5
+        g0.record()
+        for _ in range(reps):
+            graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        us = g0.elapsed_time(g1) * 1e3 / (reps * n)
+        del graph
         gbps = alg / (us * 1e-6) / 1e9
         out[name] = {"workload": w.description, "kernel": kernel, "avg_us": round(us, 3),
+                     "event_us": round(event_us, 3), "timing": f"graph of {n} calls, replayed {reps} times",
                      "queries_per_s": B * Nq / (us * 1e-6), "algorithmic_bytes": alg,
                      "effective_gbps": round(gbps, 1), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
         del value, loc, A, ref
@@ -563,6 +696,9 @@ def main():
         return
     if args.copy_mib:
         copy_calibration(args.copy_mib)
+        return
+    if args.trace_summary:
+        trace_summary(args.trace_summary, args.steps, args.warmup)
         return
 
     import numpy as np
@@ -761,7 +897,9 @@ def main():
     if args.cold_iters > 0:
         cold_kernels, cold_calls = cold_timing(msda, calls, dev, args.cold_iters)
         cold = {"protocol": f"{args.cold_iters} calls per entry point; before each, a 1 GiB read (4x the 256 MB "
-                            "Infinity Cache) outside the timed pairs, so every input starts in HBM",
+                            "Infinity Cache) outside the timed pairs, so every input starts in HBM; one round "
+                            "timed per call (as in the step), one per kernel (library event pairs, the backward's "
+                            "kernels in turn on one stream)",
                 "entry_points_us": {k: round(v, 3) for k, v in cold_calls.items()},
                 "step_us_sum": round(sum(cold_calls.values()), 3),
                 "kernels": {k: {"avg_us": round(us, 3), **({} if k not in alg else {

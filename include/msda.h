@@ -276,8 +276,11 @@ MSDA_API int msda_abi_version(void);
  * the op). While enabled (on != 0), every kernel this library launches on a
  * stream that is not being captured into a graph is bracketed by two HIP
  * events recorded on that stream; the elapsed time between them is added to
- * the kernel's entry. Enabling adds a little launch overhead; it is off by
- * default. Host only, thread safe. Returns MSDA_OK. */
+ * the kernel's entry. While it is on, the backward runs all of its kernels on
+ * the caller's stream (the dense levels too, which otherwise run on a second
+ * stream beside the others), so that each pair times its kernel alone.
+ * Enabling adds a little launch overhead; it is off by default. Host only,
+ * thread safe. Returns MSDA_OK. */
 MSDA_API int msda_timing_enable(int on);
 
 /* Drops all timing entries and unread event pairs (waits for the latter). */

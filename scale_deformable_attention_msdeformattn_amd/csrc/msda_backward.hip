@@ -1804,7 +1804,8 @@ hipError_t launch_fast(const Geometry &g, const TilePlan &tp, const void *value,
     // inputs and write their own grad_value rows and workspace section, so
     // they run on the side stream beside everything else on `st`, which
     // waits for them only at the end. Without the side stream (side_ok
-    // false: the caller's stream only) they run last on `st`.
+    // false: the caller's stream only; or while the launches are timed, so
+    // that each event pair times its kernel alone) they run last on `st`.
     SideStream *side = nullptr;
     auto launch_dense = [&](hipStream_t ds) -> hipError_t {
         const uint32_t ditems = (uint32_t)(g.B * g.M * tp.dipb);
@@ -1825,7 +1826,7 @@ hipError_t launch_fast(const Geometry &g, const TilePlan &tp, const void *value,
         }
         return hipGetLastError();
     };
-    if (tp.dipb > 0 && side_ok) {
+    if (tp.dipb > 0 && side_ok && !timing_on(st)) {
         hipError_t e = side_stream(&side);
         if (e == hipSuccess) e = hipEventRecord(side->fork, st);
         if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);

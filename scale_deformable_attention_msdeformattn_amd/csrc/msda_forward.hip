@@ -262,6 +262,22 @@ forward_staged_kernel(Geometry g, const VT *__restrict__ value, const float2 *__
     const int zero_row = nrows * RS;
     for (int qb = q0 + wave * QPW; qb < q1; qb += kStagedWaves * QPW) {
         // ---- phase 1: the QPW*L*K samples of this pass, one per lane ----
+        // (the plain form's loc and A loads of every step are issued first,
+        // so that their latencies overlap)
+        constexpr int NP1 = (QPW * LK + kWave - 1) / kWave;
+        float2 pu[NP1];
+        float pa[NP1];
+        if constexpr (!FUSED) {
+#pragma unroll
+            for (int p = 0; p < NP1; ++p) {
+                const int t = p * kWave + lane;
+                const int j = t / LK, i = t - (t / LK) * LK;
+                const bool ok = ((QPW * LK) % kWave == 0 || t < QPW * LK) && qb + j < q1;
+                const int64_t si = ok ? (((int64_t)b * g.Nq + qb + j) * M + m) * LK + i : 0;
+                pu[p] = loc[si];
+                pa[p] = attn[si];
+            }
+        }
 #pragma unroll
         for (int t0 = 0; t0 < QPW * LK; t0 += kWave) {
             const int t = t0 + lane;
@@ -288,8 +304,8 @@ forward_staged_kernel(Geometry g, const VT *__restrict__ value, const float2 *__
                         fi.loc_out[si] = u;
                         fi.attn_out[si] = a;
                     } else {
-                        u = loc[si];
-                        a = attn[si];
+                        u = pu[t0 / kWave];
+                        a = pa[t0 / kWave];
                     }
                     const bool in = sample_in_range(u.x, u.y, lv.Wf, lv.Hf);
                     u.x = in ? u.x : 0.0f;

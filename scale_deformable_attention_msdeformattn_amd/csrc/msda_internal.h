@@ -152,6 +152,10 @@ constexpr size_t kNoAllocScratchBytes = (size_t)MSDA_NOALLOC_SCRATCH_BYTES;
 // hipGetSymbolAddress on the first call per device, then cached).
 hipError_t noalloc_scratch(void **out);
 
+// Whether launches on `st` from this thread are being timed now (timing
+// enabled, not suppressed, `st` not capturing).
+bool timing_on(hipStream_t st);
+
 // While an object of this type lives, the calling thread's launches record no
 // timing events (the allocation-free entry point creates no events).
 class TimingOff {

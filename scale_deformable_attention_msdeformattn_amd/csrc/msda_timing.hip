@@ -69,6 +69,17 @@ hipError_t drain(bool discard)
 
 }  // namespace
 
+bool timing_on(hipStream_t st)
+{
+    if (g_suppressed) return false;
+    {
+        std::lock_guard<std::mutex> lock(g_mu);
+        if (!g_enabled) return false;
+    }
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    return hipStreamIsCapturing(st, &cs) == hipSuccess && cs == hipStreamCaptureStatusNone;
+}
+
 TimingOff::TimingOff() { ++g_suppressed; }
 TimingOff::~TimingOff() { --g_suppressed; }
 
