@@ -126,11 +126,17 @@ def unique_value_bytes(loc, shapes, B, M, row_bytes):
 
 
 def dense_levels(shapes, Nq, K):
-    """The levels the backward treats as dense (no tile records): at least 24
-    samples per pixel per batch and head, and at most 8 x 256 pixels. This
-    mirrors the library's tile planner so that each backward kernel is
-    charged for the levels it handles."""
-    return [l for l, (H, W) in enumerate(shapes) if Nq * K >= 24 * H * W and H * W <= 8 * 256]
+    """The levels the backward treats as dense (no tile records): the last
+    run of adjacent levels with at least 24 samples per pixel per batch and
+    head and at most 2048 pixels. This mirrors the library's tile planner so
+    that each backward kernel is charged for the levels it handles."""
+    out = []
+    for l, (H, W) in enumerate(shapes):
+        if Nq * K >= 24 * H * W and H * W <= 2048:
+            out.append(l)
+        elif out:
+            out = []
+    return out
 
 
 def algorithmic_bytes(B, M, D, Nq, shapes, K, vbytes):
@@ -146,8 +152,8 @@ def algorithmic_bytes(B, M, D, Nq, shapes, K, vbytes):
     rows = B * Nq * M * D * f32             # output / grad_output
     dense = dense_levels(shapes, Nq, K)
     dense_pix = sum(shapes[l][0] * shapes[l][1] for l in dense)
-    # a dense level is split over queries when it has over 3072 samples
-    split_pix = sum(shapes[l][0] * shapes[l][1] for l in dense if Nq * K > 3072)
+    # the dense levels are split over queries when they have over 3072 samples
+    split_pix = dense_pix if Nq * K * len(dense) > 3072 else 0
     sparse_samples = per_level * (L - len(dense))
     dense_samples = per_level * len(dense)
     gv_row = B * M * D * f32                 # grad_value bytes per pixel

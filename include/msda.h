@@ -191,13 +191,13 @@ MSDA_API int msda_backward(const msda_shape *shape, const void *value, msda_dtyp
                   void *workspace, size_t workspace_bytes, unsigned flags, void *stream);
 
 /* Bytes of device scratch that msda_backward_noalloc holds (per GPU). */
-#define MSDA_NOALLOC_SCRATCH_BYTES (128u * 1024u * 1024u)
+#define MSDA_NOALLOC_SCRATCH_BYTES (160u * 1024u * 1024u)
 
 /* msda_backward for callers that cannot allocate device memory during the
  * call (code under HIP graph capture, tight serving loops, harnesses that
  * forbid allocation): the same arguments, results and status codes as
  * msda_backward, without the workspace. Its scratch is a device array inside
- * the library, MSDA_NOALLOC_SCRATCH_BYTES (128 MiB) per GPU, which each GPU
+ * the library, MSDA_NOALLOC_SCRATCH_BYTES (160 MiB) per GPU, which each GPU
  * the library runs on holds until the process ends; its address is resolved
  * on the first call per device. Sizes whose workspace
  * (msda_backward_workspace_size) exceeds it return MSDA_E_WORKSPACE before

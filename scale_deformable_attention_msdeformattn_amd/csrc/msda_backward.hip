@@ -133,19 +133,21 @@ __device__ __forceinline__ SampleTiles sample_tiles(const TileLevel &tl, int W, 
     const int r0 = ty0, r1 = ty1 != ty0 ? ty1 : -1;
     const int c0 = tx0, c1 = tx1 != tx0 ? tx1 : -1;
     SampleTiles r;
-    r.t[0] = (r0 >= 0 && c0 >= 0) ? base + r0 * ntw + c0 : -1;
-    r.t[1] = (r0 >= 0 && c1 >= 0) ? base + r0 * ntw + c1 : -1;
-    r.t[2] = (r1 >= 0 && c0 >= 0) ? base + r1 * ntw + c0 : -1;
-    r.t[3] = (r1 >= 0 && c1 >= 0) ? base + r1 * ntw + c1 : -1;
+    // (every product below is of values under 2^20 in magnitude, or unused:
+    // 24-bit multiplies, full rate where a 32-bit one is quarter rate)
+    r.t[0] = (r0 >= 0 && c0 >= 0) ? base + __mul24(r0, ntw) + c0 : -1;
+    r.t[1] = (r0 >= 0 && c1 >= 0) ? base + __mul24(r0, ntw) + c1 : -1;
+    r.t[2] = (r1 >= 0 && c0 >= 0) ? base + __mul24(r1, ntw) + c0 : -1;
+    r.t[3] = (r1 >= 0 && c1 >= 0) ? base + __mul24(r1, ntw) + c1 : -1;
     // the cell within tile (ty, tx): row cy - ty*th + 1, column cx - tx*tw + 1,
     // in rows of (pixel columns of the tile) + 1 cells
-    const int ry0 = cy - r0 * tl.th + 1, ry1 = cy - r1 * tl.th + 1;
-    const int rx0 = cx - c0 * tl.tw + 1, rx1 = cx - c1 * tl.tw + 1;
-    const int cw0 = min(tl.tw, W - c0 * tl.tw) + 1, cw1 = min(tl.tw, W - c1 * tl.tw) + 1;
-    r.cell[0] = ry0 * cw0 + rx0;
-    r.cell[1] = ry0 * cw1 + rx1;
-    r.cell[2] = ry1 * cw0 + rx0;
-    r.cell[3] = ry1 * cw1 + rx1;
+    const int ry0 = cy - __mul24(r0, tl.th) + 1, ry1 = cy - __mul24(r1, tl.th) + 1;
+    const int rx0 = cx - __mul24(c0, tl.tw) + 1, rx1 = cx - __mul24(c1, tl.tw) + 1;
+    const int cw0 = min(tl.tw, W - __mul24(c0, tl.tw)) + 1, cw1 = min(tl.tw, W - __mul24(c1, tl.tw)) + 1;
+    r.cell[0] = __mul24(ry0, cw0) + rx0;
+    r.cell[1] = __mul24(ry0, cw1) + rx1;
+    r.cell[2] = __mul24(ry1, cw0) + rx0;
+    r.cell[3] = __mul24(ry1, cw1) + rx1;
     return r;
 }
 
@@ -389,7 +391,7 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
                 const bool x1ok = in & (cx + 1 >= 0) & (cx + 1 < lv.W);
                 const bool y0ok = (cy >= 0) & (cy < H);
                 const bool y1ok = (cy + 1 >= 0) & (cy + 1 < H);
-                const int row = lv.start + cy * lv.W + cx;
+                const int row = lv.start + __mul24(cy, lv.W) + cx;  // |cy|, W < 2^20
                 bool k00 = y0ok & x0ok, k01 = y0ok & x1ok, k10 = y1ok & x0ok, k11 = y1ok & x1ok;
                 if (mask) unmask_corners(mask + (int64_t)b * g.S, row, lv.W, k00, k01, k10, k11);
                 const uint32_t o00 = (uint32_t)row * RB;
@@ -769,18 +771,23 @@ backward_head_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
         int ln = lane;
         asm volatile("" : "+v"(ln));
         // ---- phase 1: the QPW*L*K samples of this pass, one per lane per step ----
-        // record keys (tile, with the sample's cell in that tile in the bits
-        // from kKeyBits up) and record weights
+        // Step p takes samples [p*SPS, (p+1)*SPS) of every query of the pass,
+        // so that with the levels split evenly over the steps a step's levels
+        // are all staged or all from memory, all dense or all sparse, and the
+        // branches below are uniform. Record keys (tile, with the sample's
+        // cell in that tile in the bits from kKeyBits up) and record weights.
+        constexpr int SPS = LK / NPASS;  // samples of a query per step
+        static_assert(NPASS * kWave == QPW * LK && LK % NPASS == 0, "whole queries per step");
         int keys[NPASS][4];
         float rfx[NPASS], rfy[NPASS], ra[NPASS];
 #pragma unroll
         for (int p = 0; p < NPASS; ++p) {
-            const int t = p * kWave + ln;
             rfx[p] = rfy[p] = ra[p] = 0.0f;
 #pragma unroll
             for (int j = 0; j < 4; ++j) keys[p][j] = nkeys + ln;
-            if ((QPW * LK) % kWave == 0 || t < QPW * LK) {
-                const int j = t / LK, i = t - (t / LK) * LK;
+            const int j = ln / SPS;
+            {
+                const int i = p * SPS + ln % SPS;
                 const int l = i / K;
                 const bool staged = l >= LS;
                 const int q = qb + j;
@@ -799,7 +806,7 @@ backward_head_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
                     const bool x1ok = in & (cx + 1 >= 0) & (cx + 1 < lv.W);
                     const bool y0ok = (cy >= 0) & (cy < H);
                     const bool y1ok = (cy + 1 >= 0) & (cy + 1 < H);
-                    const int row = lv.start + cy * lv.W + cx;
+                    const int row = lv.start + __mul24(cy, lv.W) + cx;  // |cy|, W < 2^20
                     bool k00 = y0ok & x0ok, k01 = y0ok & x1ok, k10 = y1ok & x0ok, k11 = y1ok & x1ok;
                     if (staged) {
                         const int r00 = (row - srow0) * LPH, r10 = r00 + lv.W * LPH;
@@ -829,17 +836,22 @@ backward_head_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
                 s_off[wave][j * PAD + i] = o;
                 s_geo[wave][j * PAD + i] = geo;
             }
-            // the pass's records: a position per key from the LDS cursor (all
+            // the step's records: a position per key from the LDS cursor (all
             // adds in flight at once; a lane without a record adds on a spare
-            // slot of its own)
-            const uint32_t bq = (uint32_t)(b * g.Nq + qb + t / LK);
-            uint32_t pos[4];
+            // slot of its own), unless no lane of the wave has one
+            bool has = false;
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) pos[jj] = atomicAdd(&s_cursor[keys[p][jj] & kKeyMask], 1u);
+            for (int jj = 0; jj < 4; ++jj) has |= (keys[p][jj] & kKeyMask) < nkeys;
+            if (__any(has)) {
+                const uint32_t bq = (uint32_t)(b * g.Nq + qb + j);
+                uint32_t pos[4];
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-                if ((keys[p][jj] & kKeyMask) < nkeys && pos[jj] < rcap)
-                    records[pos[jj]] = tile_record(bq, keys[p][jj] >> kKeyBits, rfx[p], rfy[p], ra[p]);
+                for (int jj = 0; jj < 4; ++jj) pos[jj] = atomicAdd(&s_cursor[keys[p][jj] & kKeyMask], 1u);
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    if ((keys[p][jj] & kKeyMask) < nkeys && pos[jj] < rcap)
+                        records[pos[jj]] = tile_record(bq, keys[p][jj] >> kKeyBits, rfx[p], rfy[p], ra[p]);
+            }
         }
         wave_lds_sync();
         // ---- phase 2: each lane its query's samples; gathers, dots with G, sums over the query's lanes ----
@@ -1299,22 +1311,24 @@ zero_split_levels_kernel(Geometry g, TilePlan tp, float4 *__restrict__ grad_valu
 
 // Dense levels: many samples per pixel, few pixels. Binning them into tiles
 // would write each sample's record up to four times; instead one workgroup
-// per (b, m, level, pixel part, query split) reads its queries' samples of
-// the level directly (contiguous per query) together with their grad_output
+// per (b, m, pixel part, query split) reads its queries' samples of every
+// dense level directly (adjacent in memory per query when the dense levels
+// are adjacent, as the coarsest ones are) together with their grad_output
 // rows, and, sub-chunk after sub-chunk:
 //  - ranks each (sample, corner) pair whose pixel lies in its part within
-//    the pixel's LDS count (integer LDS atomics),
+//    the pixel's LDS count (integer LDS atomics); the pixels of all dense
+//    levels are numbered one after the other (TilePlan::dbase),
 //  - scans the counts and writes every pair's weight A*w_c and query slot,
 //    sorted by pixel,
 //  - lets each lane group sum weight * G over the pairs of the pixels it
 //    owns, in registers.
 // The next sub-chunk's loads are issued before the current one is sorted and
-// stay in flight across the LDS-only barriers. A level whose queries are split
-// over several items parks each item's sums in the workspace; extra items of
-// tile_accum add them up in split order and write every pixel once.
-constexpr int kDensePix = 384;             // pixels per part at most
-constexpr int kDenseSub = 1024;             // samples per sub-chunk at most
-constexpr int kDenseQ = 256;               // queries per sub-chunk at most
+// stay in flight across the LDS-only barriers. With several query splits each
+// item parks its sums in the workspace and dense_reduce_kernel adds them up in
+// split order, writing every pixel once.
+constexpr int kDensePix = 640;             // pixels per part at most
+constexpr int kDenseSub = 1024;            // samples per sub-chunk at most
+constexpr int kDenseQ = 128;               // queries per sub-chunk at most
 constexpr int kDenseBatch = 4;             // pairs in flight per lane group
 constexpr int kDenseThreads = 512;         // threads per dense workgroup
 constexpr double kDenseMinPerPix = 24.0;   // samples per pixel (per batch and head) that make a level dense
@@ -1330,61 +1344,67 @@ dense_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, cons
 {
     constexpr int LG = 256 / M / 4;                         // lanes (4 channels each) per head row
     constexpr int NG = kDenseThreads / LG;                  // lane groups
-    constexpr int PPG = kDensePix / NG;              // pixel slots per lane group
+    constexpr int PPG = (kDensePix + NG - 1) / NG;          // pixel slots per lane group
     constexpr int kPer = kDenseSub / kDenseThreads;         // samples per thread per sub-chunk
     constexpr int kGRows = (kDenseQ * LG + kDenseThreads - 1) / kDenseThreads;  // float4 of G staged per thread
-    static_assert(kDensePix % NG == 0 && kDenseSub % kDenseThreads == 0, "dense tiling");
+    static_assert(kDenseSub % kDenseThreads == 0 && kDensePix % kWave == 0, "dense tiling");
     __shared__ float4 s_g[kDenseQ * LG];       // G rows of the sub-chunk's queries
     __shared__ uint2 s_pair[4 * kDenseSub];    // (bits(A * w_c), query slot), sorted by pixel
     __shared__ uint32_t s_cnt[kDensePix];
     __shared__ uint32_t s_start[kDensePix + 1];
+    __shared__ LevelRec s_lv[L];               // the dense levels, in order
+    __shared__ int s_dbase[L];                 // their first pixel in the dense numbering
 
     const int item = (int)xcd_tile(blockIdx.x, gridDim.x);
     if (item >= g.B * g.M * tp.dipb) return;
     const int bm = item / tp.dipb;
     const int b = bm / M, m = bm - (bm / M) * M;
     const int r_in = item - bm * tp.dipb;
-    int l = 0;
-    int parts = 1, splits = 1, dib = 0, W = 1, H = 1, lstart = 0;
-#pragma unroll
-    for (int i = 0; i < L; ++i)
-        if (((tp.dense_mask >> i) & 1) && r_in >= tp.dibase[i]) l = i;
-#pragma unroll
-    for (int i = 0; i < L; ++i)
-        if (i == l) {
-            parts = tp.dparts[i];
-            splits = tp.dsplit[i];
-            dib = tp.dibase[i];
-            W = g.lv.W[i];
-            H = g.lv.H[i];
-            lstart = g.lv.start[i];
-        }
-    const int r = r_in - dib;
-    const int part = r / splits, split = r - (r / splits) * splits;
-    const int npix_l = H * W;
-    const int p0 = (int)((int64_t)npix_l * part / parts);
-    const int npix = (int)((int64_t)npix_l * (part + 1) / parts) - p0;
-    const int qa0 = (int)((int64_t)g.Nq * split / splits);
-    const int qa1 = (int)((int64_t)g.Nq * (split + 1) / splits);
-    const float Wf = (float)W, Hf = (float)H;
-    constexpr int QS = kDenseQ < kDenseSub / K ? kDenseQ : kDenseSub / K;  // queries per sub-chunk
+    const int part = r_in / tp.dsplits, split = r_in - (r_in / tp.dsplits) * tp.dsplits;
+    const int ndl = tp.ndl;
+    if (threadIdx.x == 0) {
+        int j = 0;
+        for (int l = 0; l < L; ++l)
+            if ((tp.dense_mask >> l) & 1) {
+                s_lv[j] = LevelRec{(float)g.lv.W[l], (float)g.lv.H[l], g.lv.W[l], g.lv.start[l]};
+                s_dbase[j] = tp.dbase[l];
+                ++j;
+            }
+    }
+    // this part's pixels of the dense numbering, this split's queries
+    const int p0 = (int)((int64_t)tp.ndpix * part / tp.dparts);
+    const int npix = (int)((int64_t)tp.ndpix * (part + 1) / tp.dparts) - p0;
+    const int qa0 = (int)((int64_t)g.Nq * split / tp.dsplits);
+    const int qa1 = (int)((int64_t)g.Nq * (split + 1) / tp.dsplits);
+    const int spq = ndl * K;                   // dense samples per query
+    const int QS = min(kDenseQ, kDenseSub / spq);  // queries per sub-chunk
     constexpr int64_t LKs = (int64_t)L * K;
     const int grp = threadIdx.x / LG;
     const int lig = threadIdx.x % LG;
 
     for (int i = threadIdx.x; i < kDensePix; i += kDenseThreads) s_cnt[i] = 0;
+    __syncthreads();  // s_lv, s_dbase
 
-    // loads of one sub-chunk (starting at query qa), held in registers
+    // loads of one sub-chunk (starting at query qa), held in registers; the
+    // dense levels' samples of a query are taken in level order, then point
+    // order, with the dense levels' first index `lfirst` (dense levels are
+    // adjacent: checked by the plan)
+    int lfirst = 0;
+    for (int l = 0; l < L; ++l)
+        if ((tp.dense_mask >> l) & 1) {
+            lfirst = l;
+            break;
+        }
     float2 u[kPer];
     float a[kPer];
     float4 gst[kGRows];
     auto fetch_samples = [&](int qa) {
-        const int ns = min(QS, qa1 - qa) * K;
+        const int ns = min(QS, qa1 - qa) * spq;
 #pragma unroll
         for (int t = 0; t < kPer; ++t) {
             const int i = threadIdx.x + t * kDenseThreads;
-            const int qi = i / K, k = i - (i / K) * K;
-            const int64_t sidx = (((int64_t)b * g.Nq + qa + qi) * g.M + m) * LKs + (int64_t)l * K + k;
+            const int qi = i / spq, r = i - (i / spq) * spq;
+            const int64_t sidx = (((int64_t)b * g.Nq + qa + qi) * g.M + m) * LKs + (int64_t)lfirst * K + r;
             u[t] = i < ns ? loc[sidx] : make_float2(-1e30f, -1e30f);
             a[t] = i < ns ? attn[sidx] : 0.0f;
         }
@@ -1412,7 +1432,8 @@ dense_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, cons
         lds_barrier();  // s_cnt cleared; the previous sub-chunk is done with s_g and s_pair
 #pragma unroll
         for (int t = 0; t < kGRows; ++t)
-            if ((kDenseQ * LG) % kDenseThreads == 0 || threadIdx.x + t * kDenseThreads < kDenseQ * LG) s_g[threadIdx.x + t * kDenseThreads] = gst[t];
+            if ((kDenseQ * LG) % kDenseThreads == 0 || threadIdx.x + t * kDenseThreads < kDenseQ * LG)
+                s_g[threadIdx.x + t * kDenseThreads] = gst[t];
         // the next sub-chunk's G rows: in flight through this one's ranking
         if (qa + QS < qa1) fetch_g(qa + QS);
         // rank this part's pairs within their pixel's count
@@ -1421,13 +1442,18 @@ dense_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, cons
         float wpair[kPer][4];
 #pragma unroll
         for (int t = 0; t < kPer; ++t) {
+            const int i = threadIdx.x + t * kDenseThreads;
+            const int dl = (i - (i / spq) * spq) / K;
+            const LevelRec lv = s_lv[dl < ndl ? dl : 0];
+            const int H = (int)lv.Hf, W = lv.W;
+            const int pbase = s_dbase[dl < ndl ? dl : 0] - p0;
             int cx, cy;
             float fx, fy;
-            const bool in = sample_cell(u[t], Wf, Hf, cx, cy, fx, fy);
+            const bool in = sample_cell(u[t], lv.Wf, lv.Hf, cx, cy, fx, fy);
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const int px = cx + (c & 1), py = cy + (c >> 1);
-                const int p = py * W + px - p0;
+                const int p = pbase + py * W + px;
                 wpair[t][c] = a[t] * ((c & 1) ? fx : 1.0f - fx) * ((c & 2) ? fy : 1.0f - fy);
                 pix[t][c] = -1;
                 if (in && px >= 0 && px < W && py >= 0 && py < H && p >= 0 && p < npix) {
@@ -1465,7 +1491,7 @@ dense_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, cons
         lds_barrier();
 #pragma unroll
         for (int t = 0; t < kPer; ++t) {
-            const uint32_t qi = (uint32_t)((threadIdx.x + t * kDenseThreads) / K);
+            const uint32_t qi = (uint32_t)((threadIdx.x + t * kDenseThreads) / spq);
 #pragma unroll
             for (int c = 0; c < 4; ++c)
                 if (pix[t][c] >= 0)
@@ -1498,16 +1524,19 @@ dense_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, cons
         }
     }
     // one query split: write the part's pixels; several: park the sums in the
-    // item's workspace slot, which tile_accum's extra items add up
+    // workspace for dense_reduce_kernel
 #pragma unroll
     for (int j = 0; j < PPG; ++j) {
         const int pl = grp + j * NG;
         if (pl >= npix) break;
         float4 v = acc[j];
-        if (splits > 1) {
-            partials[((int64_t)bm * tp.ppb + tp.pbase[l] + (int64_t)split * npix_l + p0 + pl) * LG + lig] = v;
+        const int p = p0 + pl;  // in the dense numbering
+        if (tp.dsplits > 1) {
+            partials[((int64_t)bm * tp.ppb + (int64_t)split * tp.ndpix + p) * LG + lig] = v;
         } else {
-            const int64_t row = (int64_t)b * g.S + lstart + p0 + pl;
+            int dl = 0;
+            while (dl + 1 < ndl && p >= s_dbase[dl + 1]) ++dl;
+            const int64_t row = (int64_t)b * g.S + s_lv[dl].start + (p - s_dbase[dl]);
             if (mask && mask[row]) v = make_float4(0.f, 0.f, 0.f, 0.f);  // padded: no gradient
             float4 *dst = grad_value + (row * g.M + m) * LG + lig;
             if (accumulate) {
@@ -1522,48 +1551,42 @@ dense_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, cons
     }
 }
 
-// Sum the query splits of the dense levels, in split order, into grad_value.
-// Thread t of (batch, pixel, head, float4 of channels) over the split levels.
+// Sum the dense levels' query splits, in split order, into grad_value.
+// Thread t of (batch, dense pixel, head, float4 of channels).
 template <int LG>
 __device__ void dense_reduce_one(const Geometry &g, const TilePlan &tp, const float4 *__restrict__ partials,
                                  float4 *__restrict__ grad_value, int accumulate, const uint8_t *__restrict__ mask,
                                  int64_t t)
 {
-    for (int l = 0; l < g.L; ++l) {
-        if (!((tp.dense_mask >> l) & 1) || tp.dsplit[l] <= 1) continue;
-        const int npix_l = g.lv.H[l] * g.lv.W[l];
-        const int64_t n = (int64_t)g.B * npix_l * g.M * LG;
-        if (t >= n) {
-            t -= n;
-            continue;
-        }
-        const int c = (int)(t % LG);
-        const int m = (int)((t / LG) % g.M);
-        const int p = (int)((t / ((int64_t)LG * g.M)) % npix_l);
-        const int b = (int)(t / ((int64_t)LG * g.M * npix_l));
-        const int splits = tp.dsplit[l];
-        const int64_t p0 = (int64_t)(b * g.M + m) * tp.ppb + tp.pbase[l] + p;
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int s = 0; s < splits; ++s) {
-            const float4 x = partials[(p0 + (int64_t)s * npix_l) * LG + c];
-            v.x += x.x;
-            v.y += x.y;
-            v.z += x.z;
-            v.w += x.w;
-        }
-        const int64_t row = (int64_t)b * g.S + g.lv.start[l] + p;
-        if (mask && mask[row]) v = make_float4(0.f, 0.f, 0.f, 0.f);  // padded: no gradient
-        float4 *dst = grad_value + (row * g.M + m) * LG + c;
-        if (accumulate) {
-            const float4 o = *dst;
-            v.x += o.x;
-            v.y += o.y;
-            v.z += o.z;
-            v.w += o.w;
-        }
-        *dst = v;
-        return;
+    if (tp.dsplits <= 1 || t >= (int64_t)g.B * tp.ndpix * g.M * LG) return;
+    const int c = (int)(t % LG);
+    const int m = (int)((t / LG) % g.M);
+    const int p = (int)((t / ((int64_t)LG * g.M)) % tp.ndpix);
+    const int b = (int)(t / ((int64_t)LG * g.M * tp.ndpix));
+    const int64_t p0 = (int64_t)(b * g.M + m) * tp.ppb + p;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s = 0; s < tp.dsplits; ++s) {
+        const float4 x = partials[(p0 + (int64_t)s * tp.ndpix) * LG + c];
+        v.x += x.x;
+        v.y += x.y;
+        v.z += x.z;
+        v.w += x.w;
     }
+    // the dense level holding pixel p
+    int l = -1;
+    for (int i = 0; i < g.L; ++i)
+        if (((tp.dense_mask >> i) & 1) && p >= tp.dbase[i]) l = i;
+    const int64_t row = (int64_t)b * g.S + g.lv.start[l] + (p - tp.dbase[l]);
+    if (mask && mask[row]) v = make_float4(0.f, 0.f, 0.f, 0.f);  // padded: no gradient
+    float4 *dst = grad_value + (row * g.M + m) * LG + c;
+    if (accumulate) {
+        const float4 o = *dst;
+        v.x += o.x;
+        v.y += o.y;
+        v.z += o.z;
+        v.w += o.w;
+    }
+    *dst = v;
 }
 
 // The dense levels' query splits added up, one thread per (batch, pixel,
@@ -1815,10 +1838,7 @@ hipError_t launch_fast(const Geometry &g, const TilePlan &tp, const void *value,
                                tp, reinterpret_cast<const float2 *>(loc), attn, reinterpret_cast<const float4 *>(go),
                                reinterpret_cast<float4 *>(gv), ws.partials, accumulate ? 1 : 0, mask);
         }
-        int64_t nred = 0;
-        for (int l = 0; l < g.L; ++l)
-            if (((tp.dense_mask >> l) & 1) && tp.dsplit[l] > 1)
-                nred += (int64_t)g.B * g.lv.H[l] * g.lv.W[l] * g.M * LG;
+        const int64_t nred = tp.dsplits > 1 ? (int64_t)g.B * tp.ndpix * g.M * LG : 0;
         if (nred > 0) {
             KernelScope ks_("dense_reduce_kernel", ds);
             hipLaunchKernelGGL((dense_reduce_kernel<LG>), dim3((unsigned)((nred + kBlock - 1) / kBlock)), dim3(kBlock),
@@ -2024,27 +2044,43 @@ bool make_tile_plan(const Geometry &g, TilePlan &tp)
     const double target = kTileTarget;
     // every (cell, split) task needs a slot: cells <= kTaskSlots * lane groups
     const int max_cells = std::min(kTileCells, kTaskSlots * (kBlock / (g.D / 4)));
-    int base = 0, ibase = 0, dibase = 0, ppb = 0;
+    int base = 0, ibase = 0;
+    // dense levels (at least kDenseMinPerPix samples per pixel, at most
+    // kDenseMaxPix pixels): the last run of adjacent such levels, so that a
+    // query's dense samples are adjacent in memory
     tp.dense_mask = 0;
     for (int l = 0; l < g.L; ++l) {
         const int H = g.lv.H[l], W = g.lv.W[l];
         // tile indices come from float reciprocals, exact below 2^20
         if (H >= (1 << 20) || W >= (1 << 20)) return false;
         const double per_cell = (double)g.Nq * g.K / ((double)H * W);
-        tp.dparts[l] = tp.dsplit[l] = 1;
-        tp.dibase[l] = dibase;
-        tp.pbase[l] = ppb;
-        if (per_cell >= kDenseMinPerPix && H * W <= kDenseMaxPix) {
-            // dense level: no tiles; (pixel part, query split) items
+        if (per_cell >= kDenseMinPerPix && H * W <= kDenseMaxPix)
             tp.dense_mask |= 1 << l;
-            tp.dparts[l] = (H * W + kDensePix - 1) / kDensePix;
-            const double s = std::ceil((double)g.Nq * g.K / kDenseItemSamples);
-            tp.dsplit[l] = (int)std::min<double>(kDenseMaxSplit, std::max(1.0, s));
-            dibase += tp.dparts[l] * tp.dsplit[l];
-            if (tp.dsplit[l] > 1) {
-                tp.pbase[l] = ppb;
-                ppb += tp.dsplit[l] * H * W;
-            }
+        else if (tp.dense_mask)
+            tp.dense_mask = 0;  // a sparse level after dense ones: only a later run counts
+    }
+    tp.ndl = tp.ndpix = 0;
+    for (int l = 0; l < MSDA_MAX_LEVELS; ++l) {
+        tp.dbase[l] = tp.ndpix;
+        if (l < g.L && ((tp.dense_mask >> l) & 1)) {
+            ++tp.ndl;
+            tp.ndpix += g.lv.H[l] * g.lv.W[l];
+        }
+    }
+    // (pixel part, query split) work items over all dense levels
+    tp.dparts = tp.dsplits = 1;
+    if (tp.ndl > 0) {
+        tp.dparts = (tp.ndpix + kDensePix - 1) / kDensePix;
+        const double s = std::ceil((double)g.Nq * g.K * tp.ndl / kDenseItemSamples);
+        tp.dsplits = (int)std::min<double>(kDenseMaxSplit, std::max(1.0, s));
+    }
+    tp.dipb = tp.ndl > 0 ? tp.dparts * tp.dsplits : 0;
+    tp.ppb = tp.ndl > 0 && tp.dsplits > 1 ? tp.dsplits * tp.ndpix : 0;
+    for (int l = 0; l < g.L; ++l) {
+        const int H = g.lv.H[l], W = g.lv.W[l];
+        const double per_cell = (double)g.Nq * g.K / ((double)H * W);
+        if ((tp.dense_mask >> l) & 1) {
+            // dense level: no tiles
             tp.th[l] = tp.tw[l] = tp.ntw[l] = tp.nchunk[l] = 1;
             tp.tinv_h[l] = tp.tinv_w[l] = 1.0f;
             tp.tbase[l] = base;
@@ -2092,12 +2128,9 @@ bool make_tile_plan(const Geometry &g, TilePlan &tp)
     for (int l = g.L; l < MSDA_MAX_LEVELS; ++l) {
         tp.th[l] = tp.tw[l] = tp.ntw[l] = tp.nchunk[l] = 1, tp.tbase[l] = base, tp.ibase[l] = ibase;
         tp.tinv_h[l] = tp.tinv_w[l] = 1.0f;
-        tp.dparts[l] = tp.dsplit[l] = 1, tp.dibase[l] = dibase, tp.pbase[l] = ppb;
     }
-    tp.ppb = ppb;
     tp.tpb = base;
     tp.ipb = ibase;
-    tp.dipb = dibase;
     tp.qpw = kQueriesPerGroup;
     tp.wpb = (g.Nq + tp.qpw - 1) / tp.qpw;
     tp.hqr = std::max(1, (kHeadTargetWGs + g.B * g.M - 1) / (g.B * g.M));

@@ -114,7 +114,7 @@ forward_c256_kernel(Geometry g, const VT *__restrict__ value, const float2 *__re
                 const bool x1ok = (cx >= -1.0f) & (cx + 1.0f < lv.Wf);
                 const bool y0ok = in & (cy >= 0.0f) & (cy < lv.Hf);
                 const bool y1ok = in & (cy >= -1.0f) & (cy + 1.0f < lv.Hf);
-                const int row = lv.start + (int)cy * lv.W + (int)cx;
+                const int row = lv.start + __mul24((int)cy, lv.W) + (int)cx;  // |cy|, W < 2^22: one batch of 256 channels is under 2^31 bytes
                 bool k00 = y0ok & x0ok, k01 = y0ok & x1ok, k10 = y1ok & x0ok, k11 = y1ok & x1ok;
                 if (mask) unmask_corners(mask + (int64_t)b * g.S, row, lv.W, k00, k01, k10, k11);
                 const uint32_t o00 = (uint32_t)row * RB;
@@ -262,17 +262,33 @@ forward_staged_kernel(Geometry g, const VT *__restrict__ value, const float2 *__
     const int zero_row = nrows * RS;
     for (int qb = q0 + wave * QPW; qb < q1; qb += kStagedWaves * QPW) {
         // ---- phase 1: the QPW*L*K samples of this pass, one per lane ----
-        // (the plain form's loc and A loads of every step are issued first,
-        // so that their latencies overlap)
+        // Step p of the plain form takes samples [p*SPS, (p+1)*SPS) of every
+        // query of the pass, so that with the levels split evenly over the
+        // steps a step's levels are all staged or all from memory (uniform
+        // branches); the fused form keeps a query's L*K samples in adjacent
+        // lanes for its softmax. The plain form's loc and A loads of every
+        // step are issued first, so that their latencies overlap.
         constexpr int NP1 = (QPW * LK + kWave - 1) / kWave;
+        constexpr bool kStepLevels = !FUSED && NP1 * kWave == QPW * LK && LK % NP1 == 0;
+        constexpr int SPS = kStepLevels ? LK / NP1 : LK;
+        auto sample_of = [&](int p, int &j, int &i) {
+            if constexpr (kStepLevels) {
+                j = lane / SPS;
+                i = p * SPS + lane % SPS;
+            } else {
+                const int t = p * kWave + lane;
+                j = t / LK;
+                i = t - (t / LK) * LK;
+            }
+        };
         float2 pu[NP1];
         float pa[NP1];
         if constexpr (!FUSED) {
 #pragma unroll
             for (int p = 0; p < NP1; ++p) {
-                const int t = p * kWave + lane;
-                const int j = t / LK, i = t - (t / LK) * LK;
-                const bool ok = ((QPW * LK) % kWave == 0 || t < QPW * LK) && qb + j < q1;
+                int j, i;
+                sample_of(p, j, i);
+                const bool ok = ((QPW * LK) % kWave == 0 || p * kWave + lane < QPW * LK) && qb + j < q1;
                 const int64_t si = ok ? (((int64_t)b * g.Nq + qb + j) * M + m) * LK + i : 0;
                 pu[p] = loc[si];
                 pa[p] = attn[si];
@@ -282,7 +298,8 @@ forward_staged_kernel(Geometry g, const VT *__restrict__ value, const float2 *__
         for (int t0 = 0; t0 < QPW * LK; t0 += kWave) {
             const int t = t0 + lane;
             if ((QPW * LK) % kWave == 0 || t < QPW * LK) {
-                const int j = t / LK, i = t - (t / LK) * LK;
+                int j, i;
+                sample_of(t0 / kWave, j, i);
                 const int l = i / K;
                 const bool staged = l >= LS;
                 const int q = qb + j;
@@ -317,7 +334,7 @@ forward_staged_kernel(Geometry g, const VT *__restrict__ value, const float2 *__
                     const bool x1ok = (cx >= -1.0f) & (cx + 1.0f < lv.Wf);
                     const bool y0ok = in & (cy >= 0.0f) & (cy < lv.Hf);
                     const bool y1ok = in & (cy >= -1.0f) & (cy + 1.0f < lv.Hf);
-                    const int row = lv.start + (int)cy * lv.W + (int)cx;
+                    const int row = lv.start + __mul24((int)cy, lv.W) + (int)cx;  // |cy|, W < 2^22: one batch of 256 channels is under 2^31 bytes
                     if (staged) {
                         // chunk index of the corner's row in LDS
                         const int r00 = (row - srow0) * RS, r10 = r00 + lv.W * RS;

@@ -50,17 +50,19 @@ struct TilePlan {
     // record slots per (batch, query, head): a sample of a sparse level has a
     // record in each tile its in-map corners touch, at most four
     int32_t rslots;
-    // Dense levels (bit l of dense_mask) have no tiles and no records: their
-    // grad_value is accumulated from the samples directly, per (pixel part,
-    // query split) work item.
+    // Dense levels (bit l of dense_mask; adjacent levels) have no tiles and no
+    // records: their grad_value is accumulated from the samples directly, per
+    // (pixel part, query split) work item. Their pixels are numbered one level
+    // after the other: level l's from dbase[l], ndpix in all.
     int32_t dense_mask;
-    int32_t dparts[MSDA_MAX_LEVELS];  // pixel parts of a dense level
-    int32_t dsplit[MSDA_MAX_LEVELS];  // query splits of a dense level
-    int32_t dibase[MSDA_MAX_LEVELS];  // first dense item of the level within (batch, head)
-    int32_t dipb;                     // dense items per (batch, head)
-    // the query splits' sums of the dense levels with several splits: per
-    // (batch, head) ppb rows of D channels, level l's [dsplit][H*W] from pbase
-    int32_t pbase[MSDA_MAX_LEVELS];
+    int32_t ndl;     // dense levels
+    int32_t ndpix;   // their pixels (per batch and head)
+    int32_t dbase[MSDA_MAX_LEVELS];
+    int32_t dparts;  // pixel parts of the dense numbering
+    int32_t dsplits; // query splits
+    int32_t dipb;    // dense items per (batch, head): dparts * dsplits (0 without dense levels)
+    // the query splits' sums (dsplits > 1): per (batch, head) ppb = dsplits *
+    // ndpix rows of D channels, split s's from s * ndpix
     int32_t ppb;
     // 1/tw and 1/th as floats: floor((c + 0.5) * (1/t)) is c / t exactly for
     // 0 <= c < 2^20 and t <= 128 (checked exhaustively), without a division

@@ -275,8 +275,8 @@ def test_backward_noalloc_validates_on_the_host(lib):
     # the large-batch pyramid at B=8 needs far more workspace than the scratch
     big = _shape(B_=8, shapes=((100, 167), (50, 84), (25, 42), (13, 21)))
     need = B.msda_backward_workspace_size(big)
-    assert need > 128 * 2**20
+    assert need > 160 * 2**20
     assert call(big) == B.MSDA_E_WORKSPACE
     assert b"scratch" in lib.msda_last_error()
     # the encoder step's backward fits
-    assert B.msda_backward_workspace_size(_shape()) <= 128 * 2**20
+    assert B.msda_backward_workspace_size(_shape()) <= 160 * 2**20

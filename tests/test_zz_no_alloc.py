@@ -58,7 +58,7 @@ def _compare(got, want, name):
 
 
 def test_noalloc_matches_backward_twice_second_smaller(gpu_lib):
-    big = build("encoder_backward")  # the encoder step's backward: 118 MiB of scratch
+    big = build("encoder_backward")  # the encoder step's backward: 135 MiB of scratch
     small = build(workloads.custom(name="small", batch=1, heads=8, channels=32, points=4,
                                    spatial_shapes=((23, 31), (12, 16), (6, 8), (3, 4)), num_query=None,
                                    offset_sigma_px=2.0, random_valid_ratios=True), seed=7)
