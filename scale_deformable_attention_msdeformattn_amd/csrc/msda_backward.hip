@@ -559,6 +559,7 @@ backward_c256_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
 // of the head side by side in a wave. Its binning is grouped the same way, so
 // each workgroup's record cursors cover the tiles of its own head only.
 constexpr int kHeadWaves = 16;
+constexpr int kHeadTeam = 4;              // lanes per value row in the per-head kernel's gathers
 constexpr int kHeadThreads = kHeadWaves * kWave;
 constexpr int kHeadTargetWGs = 512;       // as the forward: two rounds of one workgroup per CU
 constexpr int kHeadMinQueries = 1024;     // fewer queries per (batch, head) do not repay the staging
@@ -761,8 +762,7 @@ backward_head_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
     __syncthreads();
 
     const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(value + (int64_t)b * g.S * C, (uint32_t)g.S * RB);
-    const int jq = lane / LPH, c = lane - (lane / LPH) * LPH;
-    const uint32_t lane_off = (uint32_t)(m * D + c * 4) * sizeof(VT);
+    const int jq = lane / LPH;
     const int zero_row = nrows * LPH;
     const uint32_t rcap = (uint32_t)g.B * (uint32_t)(g.Nq * M * tp.rslots);  // record slots
     for (int qb = q0 + wave * QPW; qb < q1; qb += kHeadWaves * QPW) {
@@ -854,56 +854,84 @@ backward_head_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
             }
         }
         wave_lds_sync();
-        // ---- phase 2: each lane its query's samples; gathers, dots with G, sums over the query's lanes ----
+        // ---- phase 2: a query's samples split over teams of its lanes ----
+        // The query's LPH lanes form NT teams of TEAM lanes; a team takes K/NT
+        // of each level's samples, and each of its lanes CPL = NT chunks (4
+        // channels each) of the row: gathers, dots with G over the lane's
+        // channels, sums over the team's lanes (fewer cross-lane sums and
+        // per-sample arithmetic per lane than one sample per whole query).
+        constexpr int TEAM = kHeadTeam;
+        constexpr int NT = LPH / TEAM;   // teams per query
+        constexpr int CPL = LPH / TEAM;  // row chunks per lane
+        constexpr int KT = K / NT;       // samples of a level per team
+        static_assert(LPH % TEAM == 0 && K % NT == 0, "teams divide the row and the points");
+        const int lq = lane - (lane / LPH) * LPH;
+        const int team = lq / TEAM, tl = lq - (lq / TEAM) * TEAM;
         const int qg = qb + jq;
-        const float4 G = qg < q1 ? grad_out[((int64_t)b * g.Nq + qg) * (C / 4) + m * LPH + c]
-                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+        float4 G[CPL];
+#pragma unroll
+        for (int k = 0; k < CPL; ++k)
+            G[k] = qg < q1 ? grad_out[((int64_t)b * g.Nq + qg) * (C / 4) + m * LPH + tl * CPL + k]
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
+        const uint32_t team_off = (uint32_t)(m * D + tl * CPL * 4) * sizeof(VT);
         const int4 *offs = &s_off[wave][jq * PAD];
         const float4 *geo = &s_geo[wave][jq * PAD];
         float4 *res = &s_geo[wave][jq * PAD];
-        auto grad_sample = [&](int i, const float4 &v00, const float4 &v01, const float4 &v10, const float4 &v11) {
+        auto grad_sample = [&](int i, const float4 (&vv)[4][CPL]) {
             const float4 f = geo[i];
-            const float d00 = dot4(G, v00), d01 = dot4(G, v01);
-            const float d10 = dot4(G, v10), d11 = dot4(G, v11);
+            float d[4];
+#pragma unroll
+            for (int cn = 0; cn < 4; ++cn) {
+                d[cn] = dot4(G[0], vv[cn][0]);
+#pragma unroll
+                for (int k = 1; k < CPL; ++k) d[cn] += dot4(G[k], vv[cn][k]);
+            }
             const float fx = f.x, fy = f.y;
             const float hx = 1.0f - fx, hy = 1.0f - fy;
-            float ga = hy * (hx * d00 + fx * d01) + fy * (hx * d10 + fx * d11);
-            float gx = hy * (d01 - d00) + fy * (d11 - d10);
-            float gy = hx * (d10 - d00) + fx * (d11 - d01);
-            ga = group_sum<LPH>(ga);
-            gx = group_sum<LPH>(gx);
-            gy = group_sum<LPH>(gy);
-            res[i] = make_float4(ga, f.z * gx, f.w * gy, 0.0f);  // the query's lanes all write the same
+            float ga = hy * (hx * d[0] + fx * d[1]) + fy * (hx * d[2] + fx * d[3]);
+            float gx = hy * (d[1] - d[0]) + fy * (d[3] - d[2]);
+            float gy = hx * (d[2] - d[0]) + fx * (d[3] - d[1]);
+            ga = group_sum<TEAM>(ga);
+            gx = group_sum<TEAM>(gx);
+            gy = group_sum<TEAM>(gy);
+            res[i] = make_float4(ga, f.z * gx, f.w * gy, 0.0f);  // the team's lanes all write the same
         };
         auto staged_sample = [&](int i) {
             const int4 o = offs[i];
-            grad_sample(i, StageChunk<VT>::widen(s_stage[o.x + c]), StageChunk<VT>::widen(s_stage[o.y + c]),
-                        StageChunk<VT>::widen(s_stage[o.z + c]), StageChunk<VT>::widen(s_stage[o.w + c]));
+            const int oc[4] = {o.x, o.y, o.z, o.w};
+            float4 vv[4][CPL];
+#pragma unroll
+            for (int cn = 0; cn < 4; ++cn)
+#pragma unroll
+                for (int k = 0; k < CPL; ++k) vv[cn][k] = StageChunk<VT>::widen(s_stage[oc[cn] + tl * CPL + k]);
+            grad_sample(i, vv);
         };
         // level by level: a memory level's gathers are issued, a staged level
         // is done from LDS while they are in flight, then the memory level
 #pragma unroll
         for (int l = 0; l < LS; ++l) {
-            float4 v[K][4];
+            float4 v[KT][4][CPL];
 #pragma unroll
-            for (int k = 0; k < K; ++k) {
-                const int4 o = offs[l * K + k];
-                v[k][0] = ValueTraits<VT>::load4(rsrc, (uint32_t)o.x + lane_off);
-                v[k][1] = ValueTraits<VT>::load4(rsrc, (uint32_t)o.y + lane_off);
-                v[k][2] = ValueTraits<VT>::load4(rsrc, (uint32_t)o.z + lane_off);
-                v[k][3] = ValueTraits<VT>::load4(rsrc, (uint32_t)o.w + lane_off);
+            for (int kk = 0; kk < KT; ++kk) {
+                const int4 o = offs[l * K + team * KT + kk];
+                const uint32_t oc[4] = {(uint32_t)o.x, (uint32_t)o.y, (uint32_t)o.z, (uint32_t)o.w};
+#pragma unroll
+                for (int cn = 0; cn < 4; ++cn)
+#pragma unroll
+                    for (int k = 0; k < CPL; ++k)
+                        v[kk][cn][k] = ValueTraits<VT>::load4(rsrc, oc[cn] + team_off + (uint32_t)(k * 4 * sizeof(VT)));
             }
             if (LS + l < L) {
 #pragma unroll
-                for (int k = 0; k < K; ++k) staged_sample((LS + l) * K + k);
+                for (int kk = 0; kk < KT; ++kk) staged_sample((LS + l) * K + team * KT + kk);
             }
 #pragma unroll
-            for (int k = 0; k < K; ++k) grad_sample(l * K + k, v[k][0], v[k][1], v[k][2], v[k][3]);
+            for (int kk = 0; kk < KT; ++kk) grad_sample(l * K + team * KT + kk, v[kk]);
         }
 #pragma unroll
         for (int l = 2 * LS; l < L; ++l)  // staged levels left over
 #pragma unroll
-            for (int k = 0; k < K; ++k) staged_sample(l * K + k);
+            for (int kk = 0; kk < KT; ++kk) staged_sample(l * K + team * KT + kk);
         wave_lds_sync();
         // ---- phase 3: the pass's results, one sample per lane per step ----
 #pragma unroll
@@ -1001,7 +1029,6 @@ tile_accum_kernel(Geometry g, TilePlan tp, const float4 *__restrict__ grad_out, 
                   const uint32_t *__restrict__ totals, int accumulate, const uint8_t *__restrict__ mask)
 {
     constexpr int LG = 256 / M / 4;  // lanes (4 channels each) per head row
-    constexpr int NS = M * L * K;    // samples per query
     constexpr int NG = kBlock / LG;
     // (pixel, role, split) slots in use: npix*4 when cells >= NG, else at most 4*NG
     constexpr int kPartSlots0 = 4 * (kTilePix > NG ? kTilePix : NG);
