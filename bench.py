@@ -399,6 +399,15 @@ def trace_summary(d, steps, warmup):
         return {n: st.median(v) for n, v in k.items()}
 
     kg, kt = per_kernel(graph), per_kernel(timed)
+    # the kernel sources the profiled run used (its bench line names them)
+    src_hash = kernel_source_hash()
+    blog = os.path.join(d, "bench.log")
+    bline = None
+    if os.path.exists(blog):
+        bl = [ln for ln in open(blog) if ln.startswith('{"metric"')]
+        if bl:
+            bline = json.loads(bl[-1])
+            src_hash = bline.get("source_hash", src_hash)
     spans = sorted(((max(r[1] for r in seg) - seg[0][0]) / 1e3, i) for i, seg in enumerate(graph))
     med = graph[spans[len(spans) // 2][1]]
     flags = "" if (steps, warmup) == (50, 10) else f" --steps {steps} --warmup {warmup}"  # the defaults, or not
@@ -407,7 +416,7 @@ def trace_summary(d, steps, warmup):
     lines = ["# Kernel trace — encoder_backward step (B=2, M=8, D=32, L=4 76x106..8x13, S=Nq=10687, K=4, fp32)", "",
              "Generated by `python bench.py --trace-summary DIR --steps {0} --warmup {1}` from the csv output of".format(
                  steps, warmup), "", "```", cmd, "```", "",
-             f"Kernel sources hash `{kernel_source_hash()}`. The library's kernels only (torch's own kernels omitted). "
+             f"Kernel sources hash `{src_hash}`. The library's kernels only (torch's own kernels omitted). "
              "`all launches` is rocprofv3's average over every launch of the run (plain, fused and box steps, "
              "graph replays and eager loops, the cold loop); the medians are per launch over the "
              f"{len(graph)} graph replays of the plain step (warm-up and timed) and over the {len(timed)} eager plain steps whose "
@@ -418,11 +427,9 @@ def trace_summary(d, steps, warmup):
         g_ = f"{kg[n]:.1f}" if n in kg else ""
         t_ = f"{kt[n]:.1f}" if n in kt else ""
         lines.append(f"| `{n}` | {c} | {t / c / 1e3:.1f} | {g_} | {t_} |")
-    blog = os.path.join(d, "bench.log")
-    if os.path.exists(blog):
-        bl = [ln for ln in open(blog) if ln.startswith('{"metric"')]
-        if bl:
-            b = json.loads(bl[-1])
+    if bline is not None:
+        if True:
+            b = bline
             lines += ["", f"The bench line this profiled run printed: {b['ms_per_step'] * 1e3:.1f} µs per graph-replayed "
                       f"step; per kernel (library event pairs, eager): " +
                       ", ".join(f"{k} {v['avg_us']:.1f}" for k, v in b["kernels"].items()) + " µs; roofline kernel "
@@ -947,6 +954,7 @@ def main():
         "data": "synthetic (seeded draws with Deformable DETR's encoder shapes and distributions; no dataset)",
         "config": {"workload": w.description, "step": "reference points + locations + softmax + forward + "
                    "backward", "graph_replay": graph is not None},
+        "source_hash": kernel_source_hash(),
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic(dominant), "avg_us": dom_us,
