@@ -8,7 +8,10 @@ path, against the fp64 oracle at the backward tolerance 1e-4 * (1 + |ref|):
   - the same with the records split over two workgroups whose partial sums
     meet in float atomics (about 94 samples per pixel), with the split
     levels zeroed first, and with the accumulate flag (no zeroing);
-  - dense levels split over queries, with the accumulate flag.
+  - dense levels split over queries, with the accumulate flag;
+  - only the last run of adjacent dense levels summed from the samples;
+  - three dense levels numbered across two pixel parts, beside the per-head
+    main kernel.
 """
 import numpy as np
 import pytest
@@ -95,3 +98,32 @@ def test_dense_levels_split_over_queries(gpu_lib):
     plan = _plan(ci)
     assert plan["dense"] == [1, 2], plan
     _check(ci, "dense")
+
+
+def test_dense_levels_last_run_only(gpu_lib):
+    print("[backward paths] dense: last run of levels", flush=True)
+    # levels 0 and 2 both have hundreds of samples per pixel, but only the
+    # last run of adjacent dense levels is summed from the samples (the dense
+    # samples of a query must be adjacent in memory): level 0 is tiled
+    ci = _decoder("dense_last", ((4, 4), (40, 40), (6, 6)), 3000, 1.5, seed=9, batch=2)
+    plan = _plan(ci)
+    assert plan["dense"] == [2], plan
+    _check(ci, "dense last run")
+
+
+def test_dense_levels_over_several_parts(gpu_lib):
+    print("[backward paths] dense: three levels over two pixel parts", flush=True)
+    # levels 1-3 are dense (896 pixels numbered across them: two pixel parts of
+    # at most 640), level 0 is tiled; 8 heads, 4 levels, 4 points and 12000
+    # queries take the per-head main kernel with levels 2-3 staged in LDS
+    ci = _decoder("dense_parts", ((64, 64), (24, 24), (16, 16), (8, 8)), 12000, 2.0, seed=10, batch=2)
+    plan = _plan(ci)
+    assert plan["dense"] == [1, 2, 3], plan
+    msda.msda_timing_reset()
+    msda.msda_timing_enable(True)
+    _run(ci)
+    msda.msda_timing_enable(False)
+    ran = set(msda.msda_timing_read())
+    msda.msda_timing_reset()
+    assert {"backward_head_kernel", "dense_accum_kernel", "dense_reduce_kernel", "tile_accum_kernel"} <= ran, ran
+    _check(ci, "dense parts")
