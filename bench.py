@@ -698,6 +698,89 @@ def forward_configs(msda, workloads, dev, args, names=("decoder", "encoder_bf16_
     return out
 
 
+def generic_path(msda, workloads, dev, shapes):
+    """The paths for shapes without compiled kernels, timed on the encoder
+    maps with 8 heads of 16 channels (C = 128): the generic 4-channel
+    forward (a graph of 20 calls) and the generic backward (grad_value by
+    float atomics; HIP events around 10 calls). Effective GB/s over the same kind
+    of algorithmic bytes as the fast path's."""
+    import torch
+    wl = workloads.custom(name="generic_c128", batch=2, heads=8, channels=16, points=4,
+                          spatial_shapes=[tuple(int(v) for v in hw) for hw in shapes.tolist()], num_query=None,
+                          offset_sigma_px=2.0, random_valid_ratios=True, backward=True)
+    d = workloads.draw(wl, 0)
+    w = d.workload
+    B, M, D, L, K, Nq = w.batch, w.heads, w.channels, w.levels, w.points, w.nq
+    lsi, _ = msda.level_start_index_host(d.spatial_shapes)
+    vr = d.valid_ratios.to(dev)
+    ref = msda.msda_reference_points(d.spatial_shapes, valid_ratios=vr)
+    loc = msda.msda_sampling_locations(d.spatial_shapes, ref, d.offsets_px.to(dev))
+    A = msda.msda_attention_softmax(d.spatial_shapes, d.logits.to(dev), K)
+    value = d.value.to(dev)
+    G = d.grad_output.to(dev)
+    vbytes, _ = unique_value_bytes(loc, d.spatial_shapes.to(dev), B, M, D * 4)
+    samples = B * Nq * M * L * K
+    fwd_alg = vbytes + samples * 3 * 4 + B * Nq * M * D * 4
+    bwd_alg = 2 * vbytes + samples * 6 * 4 + B * Nq * M * D * 4
+    f = lambda: msda.msda_forward(value, d.spatial_shapes, lsi, loc, A)
+    for _ in range(3):
+        f()
+    torch.cuda.synchronize()
+    msda.msda_timing_reset()
+    msda.msda_timing_enable(True)
+    f()
+    torch.cuda.synchronize()
+    msda.msda_timing_enable(False)
+    fwd_kernel = max(msda.msda_timing_read().items(), key=lambda kv: kv[1][0])[0]
+    msda.msda_timing_reset()
+    s2 = torch.cuda.Stream(dev)
+    s2.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(s2):
+        f()
+    torch.cuda.current_stream(dev).wait_stream(s2)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    n = 20
+    with torch.cuda.graph(graph):
+        for _ in range(n):
+            f()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    fwd_us = e0.elapsed_time(e1) * 1e3 / (5 * n)
+    del graph
+    bwd = lambda: msda.msda_backward(value, d.spatial_shapes, lsi, loc, A, G)
+    for _ in range(2):
+        bwd()
+    torch.cuda.synchronize()
+    msda.msda_timing_reset()
+    msda.msda_timing_enable(True)
+    bwd()
+    torch.cuda.synchronize()
+    msda.msda_timing_enable(False)
+    bwd_kernel = max(msda.msda_timing_read().items(), key=lambda kv: kv[1][0])[0]
+    msda.msda_timing_reset()
+    e0.record()
+    for _ in range(10):
+        bwd()
+    e1.record()
+    torch.cuda.synchronize()
+    bwd_us = e0.elapsed_time(e1) * 1e3 / 10
+    out = {"workload": f"encoder maps, B={B} M={M} D={D} (C={M * D}) L={L} K={K} S=Nq={Nq} fp32",
+           "forward": {"kernel": fwd_kernel, "avg_us": round(fwd_us, 2),
+                       "effective_gbps": round(fwd_alg / (fwd_us * 1e-6) / 1e9, 1)},
+           "backward": {"kernel": bwd_kernel + " (grad_value by float atomics)", "call_us": round(bwd_us, 2),
+                        "effective_gbps": round(bwd_alg / (bwd_us * 1e-6) / 1e9, 1)}}
+    del value, loc, A, ref, G
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -1007,6 +1090,7 @@ def main():
         result["encoder_stack"] = encoder_stack(msda, shapes, lsi, vr, B, S, M, L, K, dev, args)
     if not args.no_extra_configs:
         result["other_forward_configs"] = forward_configs(msda, workloads, dev, args)
+        result["generic_path"] = generic_path(msda, workloads, dev, shapes)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.workload)
     print(json.dumps(result), flush=True)

@@ -1691,6 +1691,94 @@ backward_generic_kernel(Geometry g, const VT *__restrict__ value, const float2 *
     }
 }
 
+// One thread per (b, q, m, 4 channels) where D/4 is a power of two up to 64:
+// the D/4 threads of a head are adjacent lanes of one wave. Each corner is one
+// 4-channel buffer load (off-map or padded corners read zero and add nothing),
+// the grad_value row takes four float atomics per corner (zeroed first unless
+// accumulating), and the head's partial sums for the sample's weight and
+// location gradients are added across its lanes with lane exchanges.
+template <typename VT>
+__global__ void __launch_bounds__(256)
+backward_generic4_kernel(Geometry g, const VT *__restrict__ value, const float2 *__restrict__ loc,
+                         const float *__restrict__ attn, const float4 *__restrict__ grad_out,
+                         float *__restrict__ grad_value, float2 *__restrict__ grad_loc,
+                         float *__restrict__ grad_attn, const uint8_t *__restrict__ mask)
+{
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int D4 = g.D / 4, C = g.M * g.D;
+    // the thread count is a whole number of heads, so a head's lanes are all
+    // present or all gone
+    if (t >= g.queries() * g.M * D4) return;
+    const int64_t bqm = t / D4;
+    const int c4 = (int)(t - bqm * D4);
+    const int64_t bq = bqm / g.M;
+    const int m = (int)(bqm - bq * g.M);
+    const int b = (int)(bq / g.Nq);
+    const uint32_t RB = (uint32_t)C * sizeof(VT);
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(value + (int64_t)b * g.S * C, (uint32_t)g.S * RB);
+    const uint32_t lane_off = (uint32_t)(m * g.D + c4 * 4) * sizeof(VT);
+    const uint8_t *mask_b = mask ? mask + (int64_t)b * g.S : nullptr;
+    float *gvb = grad_value + (int64_t)b * g.S * C + m * g.D + c4 * 4;
+    const float4 G = grad_out[t];  // [B, Nq, M*D]: element 4t is (b, q, m, 4*c4)
+    for (int l = 0; l < g.L; ++l) {
+        const int W = g.lv.W[l], H = g.lv.H[l];
+        const float Wf = (float)W, Hf = (float)H;
+        for (int k = 0; k < g.K; ++k) {
+            const int64_t s = (bqm * g.L + l) * g.K + k;
+            float2 u = loc[s];
+            const float a = attn[s];
+            const bool in = sample_in_range(u.x, u.y, Wf, Hf);
+            u.x = in ? u.x : 0.0f;
+            u.y = in ? u.y : 0.0f;
+            float cx, fx, cy, fy;
+            cell_1d(u.x, Wf, cx, fx);
+            cell_1d(u.y, Hf, cy, fy);
+            const bool x0ok = (cx >= 0.0f) & (cx < Wf);
+            const bool x1ok = (cx >= -1.0f) & (cx + 1.0f < Wf);
+            const bool y0ok = in & (cy >= 0.0f) & (cy < Hf);
+            const bool y1ok = in & (cy >= -1.0f) & (cy + 1.0f < Hf);
+            bool k00 = y0ok & x0ok, k01 = y0ok & x1ok, k10 = y1ok & x0ok, k11 = y1ok & x1ok;
+            const int row = g.lv.start[l] + (int)cy * W + (int)cx;
+            if (mask_b) unmask_corners(mask_b, row, W, k00, k01, k10, k11);
+            const uint32_t o00 = (uint32_t)row * RB + lane_off, o10 = o00 + (uint32_t)W * RB;
+            const float4 v00 = ValueTraits<VT>::load4(rsrc, k00 ? o00 : kOutOfRange);
+            const float4 v01 = ValueTraits<VT>::load4(rsrc, k01 ? o00 + RB : kOutOfRange);
+            const float4 v10 = ValueTraits<VT>::load4(rsrc, k10 ? o10 : kOutOfRange);
+            const float4 v11 = ValueTraits<VT>::load4(rsrc, k11 ? o10 + RB : kOutOfRange);
+            const float d00 = G.x * v00.x + G.y * v00.y + G.z * v00.z + G.w * v00.w;
+            const float d01 = G.x * v01.x + G.y * v01.y + G.z * v01.z + G.w * v01.w;
+            const float d10 = G.x * v10.x + G.y * v10.y + G.z * v10.z + G.w * v10.w;
+            const float d11 = G.x * v11.x + G.y * v11.y + G.z * v11.z + G.w * v11.w;
+            const float wy0 = 1.0f - fy, wx0 = 1.0f - fx;
+            float ga = wy0 * (wx0 * d00 + fx * d01) + fy * (wx0 * d10 + fx * d11);
+            float gx = wy0 * (d01 - d00) + fy * (d11 - d10);
+            float gy = wx0 * (d10 - d00) + fx * (d11 - d01);
+            const float ay0 = a * wy0, ay1 = a * fy;
+            const float w[4] = {ay0 * wx0, ay0 * fx, ay1 * wx0, ay1 * fx};
+            const bool kk[4] = {k00, k01, k10, k11};
+            const int64_t rows[4] = {row, row + 1, row + W, row + W + 1};
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (kk[j]) {
+                    float *d = gvb + rows[j] * C;
+                    atomicAdd(d + 0, w[j] * G.x);
+                    atomicAdd(d + 1, w[j] * G.y);
+                    atomicAdd(d + 2, w[j] * G.z);
+                    atomicAdd(d + 3, w[j] * G.w);
+                }
+            for (int o = 1; o < D4; o <<= 1) {
+                ga += __shfl_xor(ga, o);
+                gx += __shfl_xor(gx, o);
+                gy += __shfl_xor(gy, o);
+            }
+            if (c4 == 0) {
+                grad_attn[s] = ga;
+                grad_loc[s] = make_float2(a * Wf * gx, a * Hf * gy);
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------------------- host side
 
 struct Workspace {
@@ -2042,11 +2130,21 @@ hipError_t launch_typed(const Geometry &g, const TilePlan *tpp, const void *valu
             e = launch_zero_fill(gv, (int64_t)g.B * g.S * g.M * g.D, st);
             if (e != hipSuccess) return e;
         }
-        const int64_t n = g.queries() * g.M;
-        KernelScope ks_("backward_generic_kernel", st);
-        hipLaunchKernelGGL((backward_generic_kernel<VT>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, g,
-                           static_cast<const VT *>(value), reinterpret_cast<const float2 *>(loc), attn, go, gv,
-                           reinterpret_cast<float2 *>(gl), ga, mask);
+        const int d4 = g.D / 4;
+        if (g.D % 4 == 0 && d4 <= kWave && (d4 & (d4 - 1)) == 0 &&
+            reinterpret_cast<uintptr_t>(value) % (4 * sizeof(VT)) == 0 && reinterpret_cast<uintptr_t>(go) % 16 == 0) {
+            const int64_t n = g.queries() * g.M * d4;
+            KernelScope ks_("backward_generic4_kernel", st);
+            hipLaunchKernelGGL((backward_generic4_kernel<VT>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                               g, static_cast<const VT *>(value), reinterpret_cast<const float2 *>(loc), attn,
+                               reinterpret_cast<const float4 *>(go), gv, reinterpret_cast<float2 *>(gl), ga, mask);
+        } else {
+            const int64_t n = g.queries() * g.M;
+            KernelScope ks_("backward_generic_kernel", st);
+            hipLaunchKernelGGL((backward_generic_kernel<VT>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                               g, static_cast<const VT *>(value), reinterpret_cast<const float2 *>(loc), attn, go,
+                               gv, reinterpret_cast<float2 *>(gl), ga, mask);
+        }
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -469,6 +469,65 @@ forward_generic_kernel(Geometry g, const VT *__restrict__ value, const float2 *_
     out[t] = acc;
 }
 
+// Generic path for any shape with D a multiple of 4 (and 4-channel aligned
+// value): one thread per (b, q, m, 4 channels), adjacent threads on adjacent
+// channels of one head; the sample geometry is formed once per thread (D/4
+// threads of a head share it) and each corner is one 4-channel buffer load,
+// off-map or padded corners taking the out-of-range offset (they read zero).
+template <typename VT>
+__global__ void __launch_bounds__(256)
+forward_generic4_kernel(Geometry g, const VT *__restrict__ value, const float2 *__restrict__ loc,
+                        const float *__restrict__ attn, float4 *__restrict__ out, const uint8_t *__restrict__ mask)
+{
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int D4 = g.D / 4, C = g.M * g.D;
+    if (t >= g.queries() * g.M * D4) return;
+    const int64_t bqm = t / D4;
+    const int c4 = (int)(t - bqm * D4);
+    const int64_t bq = bqm / g.M;
+    const int m = (int)(bqm - bq * g.M);
+    const int b = (int)(bq / g.Nq);
+    const uint32_t RB = (uint32_t)C * sizeof(VT);
+    const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(value + (int64_t)b * g.S * C, (uint32_t)g.S * RB);
+    const uint32_t lane_off = (uint32_t)(m * g.D + c4 * 4) * sizeof(VT);
+    const uint8_t *mask_b = mask ? mask + (int64_t)b * g.S : nullptr;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int l = 0; l < g.L; ++l) {
+        const int W = g.lv.W[l], H = g.lv.H[l];
+        const float Wf = (float)W, Hf = (float)H;
+        for (int k = 0; k < g.K; ++k) {
+            const int64_t s = (bqm * g.L + l) * g.K + k;
+            float2 u = loc[s];
+            const float a = attn[s];
+            const bool in = sample_in_range(u.x, u.y, Wf, Hf);
+            u.x = in ? u.x : 0.0f;
+            u.y = in ? u.y : 0.0f;
+            float cx, fx, cy, fy;
+            cell_1d(u.x, Wf, cx, fx);
+            cell_1d(u.y, Hf, cy, fy);
+            const bool x0ok = (cx >= 0.0f) & (cx < Wf);
+            const bool x1ok = (cx >= -1.0f) & (cx + 1.0f < Wf);
+            const bool y0ok = in & (cy >= 0.0f) & (cy < Hf);
+            const bool y1ok = in & (cy >= -1.0f) & (cy + 1.0f < Hf);
+            bool k00 = y0ok & x0ok, k01 = y0ok & x1ok, k10 = y1ok & x0ok, k11 = y1ok & x1ok;
+            const int row = g.lv.start[l] + (int)cy * W + (int)cx;
+            if (mask_b) unmask_corners(mask_b, row, W, k00, k01, k10, k11);
+            const uint32_t o00 = (uint32_t)row * RB + lane_off, o10 = o00 + (uint32_t)W * RB;
+            const float4 v00 = ValueTraits<VT>::load4(rsrc, k00 ? o00 : kOutOfRange);
+            const float4 v01 = ValueTraits<VT>::load4(rsrc, k01 ? o00 + RB : kOutOfRange);
+            const float4 v10 = ValueTraits<VT>::load4(rsrc, k10 ? o10 : kOutOfRange);
+            const float4 v11 = ValueTraits<VT>::load4(rsrc, k11 ? o10 + RB : kOutOfRange);
+            const float wy0 = a * (1.0f - fy), wy1 = a * fy;
+            const float w00 = wy0 * (1.0f - fx), w01 = wy0 * fx, w10 = wy1 * (1.0f - fx), w11 = wy1 * fx;
+            acc.x = __builtin_fmaf(w00, v00.x, __builtin_fmaf(w01, v01.x, __builtin_fmaf(w10, v10.x, __builtin_fmaf(w11, v11.x, acc.x))));
+            acc.y = __builtin_fmaf(w00, v00.y, __builtin_fmaf(w01, v01.y, __builtin_fmaf(w10, v10.y, __builtin_fmaf(w11, v11.y, acc.y))));
+            acc.z = __builtin_fmaf(w00, v00.z, __builtin_fmaf(w01, v01.z, __builtin_fmaf(w10, v10.z, __builtin_fmaf(w11, v11.z, acc.z))));
+            acc.w = __builtin_fmaf(w00, v00.w, __builtin_fmaf(w01, v01.w, __builtin_fmaf(w10, v10.w, __builtin_fmaf(w11, v11.w, acc.w))));
+        }
+    }
+    out[t] = acc;
+}
+
 template <typename VT, int M, int L, int K, int LS, bool FUSED>
 hipError_t launch_staged_ls(const Geometry &g, const void *value, const float *loc, const float *attn,
                             float *out, const FusedInputs &fi, const uint8_t *mask, size_t dyn, hipStream_t st)
@@ -578,6 +637,15 @@ hipError_t launch_typed(const Geometry &g, const void *value, const float *loc, 
         if (e != hipSuccess) return e;
         return launch_typed<VT>(g, value, reinterpret_cast<const float *>(fi->loc_out), fi->attn_out, out,
                                 nullptr, mask, st);
+    }
+    if (g.D % 4 == 0 && reinterpret_cast<uintptr_t>(value) % (4 * sizeof(VT)) == 0 &&
+        reinterpret_cast<uintptr_t>(out) % 16 == 0) {
+        const int64_t n4 = g.queries() * g.M * (g.D / 4);
+        KernelScope ks_("forward_generic4_kernel", st);
+        hipLaunchKernelGGL((forward_generic4_kernel<VT>), dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, g,
+                           static_cast<const VT *>(value), reinterpret_cast<const float2 *>(loc), attn,
+                           reinterpret_cast<float4 *>(out), mask);
+        return hipGetLastError();
     }
     const int64_t n = g.queries() * g.M * g.D;
     {

@@ -129,9 +129,13 @@ def test_fused_box_shapes(gpu_lib, geom):
     check_fused(build(wl, seed=6), FWD_TOL, str(geom), box=True)
 
 
-def test_fused_bf16_value(gpu_lib):
-    wl = workloads.custom(name="bf16", batch=2, heads=8, channels=32, points=4,
-                          spatial_shapes=((9, 13), (5, 7), (3, 4), (1, 2)), num_query=None,
+@pytest.mark.parametrize("heads,channels,points,shapes", [
+    (8, 32, 4, ((9, 13), (5, 7), (3, 4), (1, 2))),   # fast kernels
+    (4, 16, 3, ((9, 13), (5, 7))),                   # generic, 4-channel loads
+], ids=["fast", "generic4"])
+def test_fused_bf16_value(gpu_lib, heads, channels, points, shapes):
+    wl = workloads.custom(name="bf16", batch=2, heads=heads, channels=channels, points=points,
+                          spatial_shapes=shapes, num_query=None,
                           value_dtype=torch.bfloat16, offset_sigma_px=2.0, random_valid_ratios=True, backward=True)
     check_fused(build(wl, seed=2), BF16_TOL, "bf16")
 
@@ -171,7 +175,9 @@ def test_fused_empty_queries(gpu_lib):
 
 MASK_CASES = {
     "encoder_backward": None,                      # staged kernels, binned backward with dense levels
-    "tiny": None,                                  # generic kernels (M*D = 8)
+    "tiny": None,                                  # generic kernels (M*D = 8; 4-channel loads)
+    "generic4": dict(batch=2, heads=4, channels=16, points=3, spatial_shapes=((9, 13), (5, 7)),
+                     num_query=23),                # generic 4-channel forward (no fast kernel for L=2, K=3)
     "fast": GEOMS[0],                              # per-query kernel, 37 queries
     "lk12": GEOMS[5],                              # L*K = 12: plain kernels, then the conversion kernel
     "split": dict(batch=1, heads=8, channels=32, points=4, spatial_shapes=((46, 46),),

@@ -130,6 +130,52 @@ def test_shapes_forward_backward(gpu_lib, geom, vdtype):
     check_backward(ci, name=str(geom))
 
 
+def _kernels_run(fn):
+    msda.msda_timing_reset()
+    msda.msda_timing_enable(True)
+    res = fn()
+    torch.cuda.synchronize()
+    msda.msda_timing_enable(False)
+    ran = set(msda.msda_timing_read())
+    msda.msda_timing_reset()
+    return res, ran
+
+
+@pytest.mark.parametrize("geom,aligned,fwd,bwd", [
+    (GEOMS[10], True, "forward_generic4_kernel", "backward_generic4_kernel"),      # D = 8
+    (GEOMS[10], False, "forward_generic_kernel", "backward_generic_kernel"),       # value 4 bytes off
+    (dict(GEOMS[10], channels=12), True, "forward_generic4_kernel", "backward_generic_kernel"),  # D/4 = 3
+    (GEOMS[7], True, "forward_generic_kernel", "backward_generic_kernel"),         # D = 5
+], ids=["d8", "d8_misaligned", "d12", "d5"])
+def test_generic_kernel_choice(gpu_lib, geom, aligned, fwd, bwd):
+    """Shapes without compiled kernels: four channels per thread when D is a
+    multiple of 4 and the operands are 16-byte aligned (in the backward also
+    D/4 a power of two, a head's lanes adding their sums by lane exchange),
+    else one channel (forward) or one head (backward) per thread; each matches
+    the oracle."""
+    print(f"[shape parity] generic kernel choice {geom} aligned={aligned}", flush=True)
+    wl = workloads.custom(name="geom", offset_sigma_px=2.5, random_valid_ratios=True, backward=True, **geom)
+    ci = build(wl, seed=5)
+    value = dev(ci.value)
+    if not aligned:
+        # the same values 4 bytes past a 16-byte boundary
+        buf = torch.zeros(ci.value.numel() + 1, dtype=ci.value.dtype, device="cuda")
+        value = buf[1:].view(ci.value.shape)
+        value.copy_(dev(ci.value))
+        assert value.data_ptr() % 16 == 4
+    loc, attn, go = dev(ci.loc), dev(ci.attn), dev(ci.grad_output)
+    out, ran = _kernels_run(lambda: msda.msda_forward(value, ci.shapes, ci.lsi, loc, attn))
+    assert ran == {fwd}, ran
+    tolerance_check(out.cpu(), oracle.forward(ci.value, ci.shapes, ci.lsi, ci.loc, ci.attn), FWD_TOL,
+                    "forward generic")
+    (gv, gl, ga), ran = _kernels_run(lambda: msda.msda_backward(value, ci.shapes, ci.lsi, loc, attn, go))
+    assert bwd in ran, ran
+    rgv, rgl, rga = oracle.backward(ci.value, ci.shapes, ci.lsi, ci.loc, ci.attn, ci.grad_output)
+    tolerance_check(gv.cpu(), rgv, BWD_TOL, "grad_value generic")
+    tolerance_check(gl.cpu(), rgl, BWD_TOL, "grad_loc generic")
+    tolerance_check(ga.cpu(), rga, BWD_TOL, "grad_attn generic")
+
+
 # ------------------------------------------------------------------ edge cases
 
 def _edge_case():
