@@ -1580,25 +1580,44 @@ dense_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, cons
 
 // Sum the dense levels' query splits, in split order, into grad_value.
 // Thread t of (batch, dense pixel, head, float4 of channels).
+// Lanes that share one output's query splits: R adjacent groups of LG lanes,
+// each adding every R-th split; their sums are then added across the groups
+// by lane exchange, in a fixed order.
+constexpr int kReduceWays = 4;
+
 template <int LG>
 __device__ void dense_reduce_one(const Geometry &g, const TilePlan &tp, const float4 *__restrict__ partials,
                                  float4 *__restrict__ grad_value, int accumulate, const uint8_t *__restrict__ mask,
                                  int64_t t)
 {
-    if (tp.dsplits <= 1 || t >= (int64_t)g.B * tp.ndpix * g.M * LG) return;
+    constexpr int R = kReduceWays;
+    static_assert((LG & (LG - 1)) == 0 && LG * R <= kWave, "an output's lanes within one wave");
+    // the thread count is a whole number of outputs, so an output's lanes are
+    // all present or all gone
+    if (tp.dsplits <= 1 || t >= (int64_t)g.B * tp.ndpix * g.M * LG * R) return;
     const int c = (int)(t % LG);
-    const int m = (int)((t / LG) % g.M);
-    const int p = (int)((t / ((int64_t)LG * g.M)) % tp.ndpix);
-    const int b = (int)(t / ((int64_t)LG * g.M * tp.ndpix));
+    const int r = (int)((t / LG) % R);
+    const int64_t o = t / (LG * R);  // (b, p, m)
+    const int m = (int)(o % g.M);
+    const int p = (int)((o / g.M) % tp.ndpix);
+    const int b = (int)(o / ((int64_t)g.M * tp.ndpix));
     const int64_t p0 = (int64_t)(b * g.M + m) * tp.ppb + p;
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s = 0; s < tp.dsplits; ++s) {
+#pragma unroll 4
+    for (int s = r; s < tp.dsplits; s += R) {
         const float4 x = partials[(p0 + (int64_t)s * tp.ndpix) * LG + c];
         v.x += x.x;
         v.y += x.y;
         v.z += x.z;
         v.w += x.w;
     }
+    for (int d = LG; d < LG * R; d <<= 1) {
+        v.x += __shfl_xor(v.x, d);
+        v.y += __shfl_xor(v.y, d);
+        v.z += __shfl_xor(v.z, d);
+        v.w += __shfl_xor(v.w, d);
+    }
+    if (r != 0) return;
     // the dense level holding pixel p
     int l = -1;
     for (int i = 0; i < g.L; ++i)
@@ -1616,8 +1635,8 @@ __device__ void dense_reduce_one(const Geometry &g, const TilePlan &tp, const fl
     *dst = v;
 }
 
-// The dense levels' query splits added up, one thread per (batch, pixel,
-// head, float4 of channels) over the split levels.
+// The dense levels' query splits added up: kReduceWays threads per (batch,
+// dense pixel, head, float4 of channels).
 template <int LG>
 __global__ void __launch_bounds__(kBlock)
 dense_reduce_kernel(Geometry g, TilePlan tp, const float4 *__restrict__ partials, float4 *__restrict__ grad_value,
@@ -1953,7 +1972,7 @@ hipError_t launch_fast(const Geometry &g, const TilePlan &tp, const void *value,
                                tp, reinterpret_cast<const float2 *>(loc), attn, reinterpret_cast<const float4 *>(go),
                                reinterpret_cast<float4 *>(gv), ws.partials, accumulate ? 1 : 0, mask);
         }
-        const int64_t nred = tp.dsplits > 1 ? (int64_t)g.B * tp.ndpix * g.M * LG : 0;
+        const int64_t nred = tp.dsplits > 1 ? (int64_t)g.B * tp.ndpix * g.M * LG * kReduceWays : 0;
         if (nred > 0) {
             KernelScope ks_("dense_reduce_kernel", ds);
             hipLaunchKernelGGL((dense_reduce_kernel<LG>), dim3((unsigned)((nred + kBlock - 1) / kBlock)), dim3(kBlock),
