@@ -780,9 +780,10 @@ backward_head_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
         static_assert(NPASS * kWave == QPW * LK && LK % NPASS == 0, "whole queries per step");
         int keys[NPASS][4];
         float rfx[NPASS], rfy[NPASS], ra[NPASS];
+        float pa[NPASS];  // the samples' A, for phase 3 of the fused form
 #pragma unroll
         for (int p = 0; p < NPASS; ++p) {
-            rfx[p] = rfy[p] = ra[p] = 0.0f;
+            rfx[p] = rfy[p] = ra[p] = pa[p] = 0.0f;
 #pragma unroll
             for (int j = 0; j < 4; ++j) keys[p][j] = nkeys + ln;
             const int j = ln / SPS;
@@ -801,6 +802,7 @@ backward_head_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
                     float fx, fy;
                     const bool in = sample_cell(loc[si], lv.Wf, lv.Hf, cx, cy, fx, fy);
                     const float a = attn[si];
+                    pa[p] = a;
                     const int H = (int)lv.Hf;
                     const bool x0ok = in & (cx >= 0) & (cx < lv.W);
                     const bool x1ok = in & (cx + 1 >= 0) & (cx + 1 < lv.W);
@@ -933,21 +935,30 @@ backward_head_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
 #pragma unroll
             for (int kk = 0; kk < KT; ++kk) staged_sample(l * K + team * KT + kk);
         wave_lds_sync();
-        // ---- phase 3: the pass's results, one sample per lane per step ----
+        // ---- phase 3: the pass's results ----
+        // Each lane takes back its phase-1 samples (step p: sample p*SPS +
+        // ln % SPS of query ln / SPS), so the fused form has their A in
+        // registers; a query's sum over its L*K samples is the lane's own
+        // sum over the steps, then over the query's SPS lanes, and a level's
+        // K points sit in K adjacent lanes of a step.
+        static_assert((SPS & (SPS - 1)) == 0 && SPS % K == 0, "a query's lanes and a level's points in aligned groups");
+        {
+            const int j = ln / SPS;
+            const int q = qb + j;
+            const bool valid = q < q1;  // the same for the SPS lanes of a query
+            float4 rr[NPASS];
 #pragma unroll
-        for (int p = 0; p < NPASS; ++p) {
-            const int t = p * kWave + ln;
-            if ((QPW * LK) % kWave == 0 || t < QPW * LK) {
-                const int j = t / LK, i = t - (t / LK) * LK;
-                const int q = qb + j;
-                const float4 rr = s_geo[wave][j * PAD + i];
-                const int64_t si = (((int64_t)b * g.Nq + q) * M + m) * LK + i;
-                if constexpr (FUSED) {
-                    // the lanes of one query (LK adjacent lanes) share q < q1
-                    const bool valid = q < q1;
+            for (int p = 0; p < NPASS; ++p) rr[p] = s_geo[wave][j * PAD + p * SPS + ln % SPS];
+            if constexpr (FUSED) {
+                float ts = 0.0f;
+#pragma unroll
+                for (int p = 0; p < NPASS; ++p) ts += pa[p] * rr[p].x;
+                const float tsum = group_sum<SPS>(ts);
+#pragma unroll
+                for (int p = 0; p < NPASS; ++p) {
+                    const int i = p * SPS + ln % SPS;
                     const int l = i / K, k = i - (i / K) * K;
-                    const float a = valid ? attn[si] : 0.0f;
-                    const float tsum = group_sum<LK>(a * rr.x);
+                    const int64_t si = (((int64_t)b * g.Nq + q) * M + m) * LK + i;
                     float4 bx = make_float4(0.f, 0.f, 0.f, 0.f);
                     float2 o = make_float2(0.f, 0.f);
                     if (fg.ref_dims == 4 && valid) {
@@ -955,19 +966,19 @@ backward_head_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
                         o = fg.off[si];
                     }
                     if (valid) {
-                        grad_attn[si] = a * (rr.x - tsum);
+                        grad_attn[si] = pa[p] * (rr[p].x - tsum);
                         const LevelRec lv = s_lv[l];
-                        grad_loc[si] = fg.ref_dims == 4
-                                           ? make_float2(rr.y * (bx.z * 0.5f / (float)K), rr.z * (bx.w * 0.5f / (float)K))
-                                           : make_float2(rr.y / lv.Wf, rr.z / lv.Hf);
+                        grad_loc[si] = fg.ref_dims == 4 ? make_float2(rr[p].y * (bx.z * 0.5f / (float)K),
+                                                                      rr[p].z * (bx.w * 0.5f / (float)K))
+                                                        : make_float2(rr[p].y / lv.Wf, rr[p].z / lv.Hf);
                     }
                     if (fg.grad_ref) {
                         // (x, y) from grad_loc; for boxes (w, h) from grad_loc * offset / (2K); summed
                         // over the K points of the level (adjacent lanes)
-                        float4 pr = make_float4(rr.y, rr.z, 0.f, 0.f);
+                        float4 pr = make_float4(rr[p].y, rr[p].z, 0.f, 0.f);
                         if (fg.ref_dims == 4) {
-                            pr.z = rr.y * o.x * 0.5f / (float)K;
-                            pr.w = rr.z * o.y * 0.5f / (float)K;
+                            pr.z = rr[p].y * o.x * 0.5f / (float)K;
+                            pr.w = rr[p].z * o.y * 0.5f / (float)K;
                         }
                         pr.x = group_sum<K>(pr.x);
                         pr.y = group_sum<K>(pr.y);
@@ -975,9 +986,14 @@ backward_head_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
                         pr.w = group_sum<K>(pr.w);
                         if (valid && k == 0) ref_part[(((int64_t)b * g.Nq + q) * M + m) * L + l] = pr;
                     }
-                } else if (q < q1) {
-                    grad_attn[si] = rr.x;
-                    grad_loc[si] = make_float2(rr.y, rr.z);
+                }
+            } else if (valid) {
+#pragma unroll
+                for (int p = 0; p < NPASS; ++p) {
+                    const int i = p * SPS + ln % SPS;
+                    const int64_t si = (((int64_t)b * g.Nq + q) * M + m) * LK + i;
+                    grad_attn[si] = rr[p].x;
+                    grad_loc[si] = make_float2(rr[p].y, rr[p].z);
                 }
             }
         }

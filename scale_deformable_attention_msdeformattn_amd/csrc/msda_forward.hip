@@ -262,15 +262,18 @@ forward_staged_kernel(Geometry g, const VT *__restrict__ value, const float2 *__
     const int zero_row = nrows * RS;
     for (int qb = q0 + wave * QPW; qb < q1; qb += kStagedWaves * QPW) {
         // ---- phase 1: the QPW*L*K samples of this pass, one per lane ----
-        // Step p of the plain form takes samples [p*SPS, (p+1)*SPS) of every
-        // query of the pass, so that with the levels split evenly over the
-        // steps a step's levels are all staged or all from memory (uniform
-        // branches); the fused form keeps a query's L*K samples in adjacent
-        // lanes for its softmax. The plain form's loc and A loads of every
-        // step are issued first, so that their latencies overlap.
+        // Step p takes samples [p*SPS, (p+1)*SPS) of every query of the pass
+        // (SPS adjacent lanes per query), so that with the levels split
+        // evenly over the steps a step's levels are all staged or all from
+        // memory (uniform branches). The inputs of every step are loaded
+        // first, so that their latencies overlap; the fused form then takes
+        // each query's L*K softmax over its lane group, across the steps.
+        // Where the samples do not split so, the fused form keeps a query's
+        // L*K samples in adjacent lanes of one step.
         constexpr int NP1 = (QPW * LK + kWave - 1) / kWave;
-        constexpr bool kStepLevels = !FUSED && NP1 * kWave == QPW * LK && LK % NP1 == 0;
-        constexpr int SPS = kStepLevels ? LK / NP1 : LK;
+        constexpr int kSps = NP1 * kWave == QPW * LK && LK % NP1 == 0 ? LK / NP1 : 0;
+        constexpr bool kStepLevels = kSps > 0 && (!FUSED || (kSps & (kSps - 1)) == 0);
+        constexpr int SPS = kStepLevels ? kSps : LK;
         auto sample_of = [&](int p, int &j, int &i) {
             if constexpr (kStepLevels) {
                 j = lane / SPS;
@@ -293,6 +296,44 @@ forward_staged_kernel(Geometry g, const VT *__restrict__ value, const float2 *__
                 pu[p] = loc[si];
                 pa[p] = attn[si];
             }
+        } else if constexpr (kStepLevels) {
+            // a lane's NP1 samples and its group's SPS lanes hold one query's
+            // L*K logits: the maximum and the sum over the lane's own, then
+            // over the group
+            float x[NP1];
+            bool ok[NP1];
+            int64_t si[NP1];
+#pragma unroll
+            for (int p = 0; p < NP1; ++p) {
+                int j, i;
+                sample_of(p, j, i);
+                ok[p] = qb + j < q1;
+                si[p] = ok[p] ? (((int64_t)b * g.Nq + qb + j) * M + m) * LK + i : 0;
+                const int l = i / K;
+                const LevelRec lv = s_lv[l];
+                x[p] = fi.logits[si[p]];
+                pu[p] = fused_location(fi.ref, fi.ref_dims, ok[p] ? ((int64_t)b * g.Nq + qb + j) * L + l : 0,
+                                       fi.off[si[p]], lv.Wf, lv.Hf, (float)K);
+            }
+            float mx = x[0];
+#pragma unroll
+            for (int p = 1; p < NP1; ++p) mx = fmaxf(mx, x[p]);
+            mx = group_max<SPS>(mx);
+            float e[NP1], es = 0.0f;
+#pragma unroll
+            for (int p = 0; p < NP1; ++p) {
+                e[p] = expf(x[p] - mx);
+                es += e[p];
+            }
+            es = group_sum<SPS>(es);
+#pragma unroll
+            for (int p = 0; p < NP1; ++p) {
+                pa[p] = e[p] / es;
+                if (ok[p]) {
+                    fi.loc_out[si[p]] = pu[p];
+                    fi.attn_out[si[p]] = pa[p];
+                }
+            }
         }
 #pragma unroll
         for (int t0 = 0; t0 < QPW * LK; t0 += kWave) {
@@ -311,7 +352,7 @@ forward_staged_kernel(Geometry g, const VT *__restrict__ value, const float2 *__
                     const LevelRec lv = s_lv[l];
                     float2 u;
                     float a;
-                    if constexpr (FUSED) {
+                    if constexpr (FUSED && !kStepLevels) {
                         u = fused_location(fi.ref, fi.ref_dims, ((int64_t)b * g.Nq + q) * L + l, fi.off[si], lv.Wf,
                                            lv.Hf, (float)K);
                         const float x = fi.logits[si];
