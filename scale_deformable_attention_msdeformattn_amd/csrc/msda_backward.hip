@@ -55,12 +55,12 @@ constexpr int kWaves = 4;
 constexpr int kBlock = kWaves * kWave;
 constexpr int kQueriesPerGroup = 32;     // queries per workgroup of bin_count and main
 constexpr int kMainAhead = 2;            // samples whose gathers run ahead in the main kernel
-constexpr int kChunk = 1024;             // records per LDS chunk in tile_accum
+constexpr int kChunk = 512;              // records per LDS chunk in tile_accum
 constexpr int kTileTarget = 768;         // expected records per tile the planner aims at
 constexpr int kTilePix = 32;             // pixels per tile
 constexpr int kTileCells = 2 * kWave;    // cells per tile (the tile plus one row and column of halo)
 constexpr int kTaskSlots = 2;            // (cell, split) tasks per lane group in tile_accum
-constexpr int kBatch = 6;                // records in flight per task
+constexpr int kBatch = 4;                // records in flight per task
 constexpr int kDirectPix = 4;            // tiles this small skip the per-cell sort
 constexpr int kDirectRecords = 768;      // records per workgroup in direct mode
 constexpr int kMaxSplit = 64;            // workgroups sharing one direct-mode tile
@@ -166,6 +166,7 @@ __device__ __forceinline__ bool sample_cell(float2 u, float Wf, float Hf, int &c
 // ---------------------------------------------------------------- 1. bin_count
 
 constexpr int kBinThreads = 512;
+constexpr int kBinBatch = 2;  // (query, level) blocks per bin_count_head thread in flight at once
 
 // Clear the per-tile record totals before bin_count adds into them.
 __global__ void __launch_bounds__(kBlock) clear_totals_kernel(int nkeys, uint32_t *__restrict__ totals)
@@ -598,21 +599,37 @@ bin_count_head_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, u
     const int b = bm / M, m = bm - (bm / M) * M;
     const int q0 = r * tp.hqpr, q1 = min(q0 + tp.hqpr, g.Nq);
     const int nblk = (q1 - q0) * nsl;
-    for (int i = threadIdx.x; i < nblk; i += kBinThreads) {
-        const int qi = i / nsl;
-        const int l = s_sparse[i - qi * nsl];
-        const LevelRec lv = s_lv[l];
-        const int H = (int)lv.Hf;
-        const float2 *u = loc + ((((int64_t)b * g.Nq + q0 + qi) * M + m) * L + l) * K;
+    // kBinBatch (query, level) blocks per thread at a time, their loads issued
+    // together
+    for (int i0 = threadIdx.x; i0 < nblk; i0 += kBinThreads * kBinBatch) {
+        float2 u[kBinBatch][K];
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-            int cx, cy;
-            float fx, fy;
-            if (!sample_cell(u[k], lv.Wf, lv.Hf, cx, cy, fx, fy)) continue;
-            const SampleTiles st = sample_tiles(s_tl[l], lv.W, H, cx, cy);
+        for (int h = 0; h < kBinBatch; ++h) {
+            const int i = min(i0 + h * kBinThreads, nblk - 1);
+            const int qi = i / nsl;
+            const int l = s_sparse[i - qi * nsl];
+            const float2 *src = loc + ((((int64_t)b * g.Nq + q0 + qi) * M + m) * L + l) * K;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (st.t[j] >= 0) atomicAdd(&s_hist[st.t[j]], 1u);
+            for (int k = 0; k < K; ++k) u[h][k] = src[k];
+        }
+#pragma unroll
+        for (int h = 0; h < kBinBatch; ++h) {
+            const int i = i0 + h * kBinThreads;
+            if (i >= nblk) break;
+            const int qi = i / nsl;
+            const int l = s_sparse[i - qi * nsl];
+            const LevelRec lv = s_lv[l];
+            const int H = (int)lv.Hf;
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                int cx, cy;
+                float fx, fy;
+                if (!sample_cell(u[h][k], lv.Wf, lv.Hf, cx, cy, fx, fy)) continue;
+                const SampleTiles st = sample_tiles(s_tl[l], lv.W, H, cx, cy);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (st.t[j] >= 0) atomicAdd(&s_hist[st.t[j]], 1u);
+            }
         }
     }
     __syncthreads();
