@@ -2077,7 +2077,7 @@ hipError_t launch_fast(const Geometry &g, const TilePlan &tp, const void *value,
 }
 
 // Which (VT-independent) fast-path instantiation serves g, if any.
-enum class Fast { None, M8L4K4, M4L4K4, M16L4K4, M8L1K4, M8L4K8, M8L3K4, M8L4K1 };
+enum class Fast { None, M8L4K4, M4L4K4, M16L4K4, M8L1K4, M8L4K8, M8L3K4, M8L4K1, M8L5K4, M8L4K2 };
 
 Fast fast_kind(const Geometry &g)
 {
@@ -2092,6 +2092,8 @@ Fast fast_kind(const Geometry &g)
         if (g.L == 4 && g.K == 8) return Fast::M8L4K8;
         if (g.L == 3 && g.K == 4) return Fast::M8L3K4;
         if (g.L == 4 && g.K == 1) return Fast::M8L4K1;
+        if (g.L == 5 && g.K == 4) return Fast::M8L5K4;
+        if (g.L == 4 && g.K == 2) return Fast::M8L4K2;
     }
     return Fast::None;
 }
@@ -2173,6 +2175,8 @@ hipError_t launch_typed(const Geometry &g, const TilePlan *tpp, const void *valu
     case Fast::M8L4K8: MSDA_FAST(8, 4, 8) break;
     case Fast::M8L3K4: MSDA_FAST(8, 3, 4) break;
     case Fast::M8L4K1: MSDA_FAST(8, 4, 1) break;
+    case Fast::M8L5K4: MSDA_FAST(8, 5, 4) break;
+    case Fast::M8L4K2: MSDA_FAST(8, 4, 2) break;
     case Fast::None: break;
     }
 #undef MSDA_FAST

@@ -665,6 +665,8 @@ hipError_t launch_typed(const Geometry &g, const void *value, const float *loc, 
         if (g.L == 4 && g.K == 8) return launch_c256<VT, 8, 4, 8>(g, value, loc, attn, out, fi, mask, st);
         if (g.L == 3 && g.K == 4) return launch_c256<VT, 8, 3, 4>(g, value, loc, attn, out, fi, mask, st);
         if (g.L == 4 && g.K == 1) return launch_c256<VT, 8, 4, 1>(g, value, loc, attn, out, fi, mask, st);
+        if (g.L == 5 && g.K == 4) return launch_c256<VT, 8, 5, 4>(g, value, loc, attn, out, fi, mask, st);
+        if (g.L == 4 && g.K == 2) return launch_c256<VT, 8, 4, 2>(g, value, loc, attn, out, fi, mask, st);
     }
     if (fi) {
         // no fused kernel for this shape: the three steps, through the caller's

@@ -116,6 +116,10 @@ GEOMS = [
     dict(batch=1, heads=8, channels=32, points=2, spatial_shapes=((9, 13), (5, 7)), num_query=None),
     dict(batch=1, heads=1, channels=1, points=1, spatial_shapes=((1, 1),), num_query=3),
     dict(batch=2, heads=2, channels=8, points=5, spatial_shapes=((6, 4), (3, 2), (2, 1), (1, 1), (1, 1)), num_query=None),
+    # more compiled shapes: five levels (L*K = 20 does not divide the wave); two points
+    dict(batch=2, heads=8, channels=32, points=4, spatial_shapes=((12, 10), (6, 5), (3, 3), (2, 2), (1, 1)),
+         num_query=None),
+    dict(batch=2, heads=8, channels=32, points=2, spatial_shapes=((9, 13), (5, 7), (3, 4), (1, 2)), num_query=23),
 ]
 
 
@@ -128,6 +132,25 @@ def test_shapes_forward_backward(gpu_lib, geom, vdtype):
     ci = build(wl, seed=3)
     check_forward(ci, tol=FWD_TOL if vdtype == torch.float32 else BF16_TOL, name=str(geom))
     check_backward(ci, name=str(geom))
+
+
+@pytest.mark.parametrize("geom", [GEOMS[11], GEOMS[12]], ids=["m8l5k4", "m8l4k2"])
+def test_compiled_shapes_take_the_fast_path(gpu_lib, geom):
+    """The added compiled shapes run the per-query forward and the tiled
+    backward (not the generic kernels) and match the oracle."""
+    print(f"[shape parity] compiled shape {geom}", flush=True)
+    wl = workloads.custom(name="geom", offset_sigma_px=2.5, random_valid_ratios=True, backward=True, **geom)
+    ci = build(wl, seed=7)
+    value, loc, attn, go = dev(ci.value), dev(ci.loc), dev(ci.attn), dev(ci.grad_output)
+    out, ran = _kernels_run(lambda: msda.msda_forward(value, ci.shapes, ci.lsi, loc, attn))
+    assert ran == {"forward_c256_kernel"}, ran
+    tolerance_check(out.cpu(), oracle.forward(ci.value, ci.shapes, ci.lsi, ci.loc, ci.attn), FWD_TOL, "forward")
+    (gv, gl, ga), ran = _kernels_run(lambda: msda.msda_backward(value, ci.shapes, ci.lsi, loc, attn, go))
+    assert "backward_c256_kernel" in ran and not any("generic" in k for k in ran), ran
+    rgv, rgl, rga = oracle.backward(ci.value, ci.shapes, ci.lsi, ci.loc, ci.attn, ci.grad_output)
+    tolerance_check(gv.cpu(), rgv, BWD_TOL, "grad_value")
+    tolerance_check(gl.cpu(), rgl, BWD_TOL, "grad_loc")
+    tolerance_check(ga.cpu(), rga, BWD_TOL, "grad_attn")
 
 
 def _kernels_run(fn):

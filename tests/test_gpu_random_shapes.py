@@ -16,7 +16,7 @@ from tests.core_inputs import build, tolerance_check
 pytestmark = pytest.mark.gpu
 
 # (M, L, K) combinations the fast path is compiled for
-COMBOS = [(8, 4, 4), (4, 4, 4), (16, 4, 4), (8, 1, 4), (8, 4, 8), (8, 3, 4), (8, 4, 1)]
+COMBOS = [(8, 4, 4), (4, 4, 4), (16, 4, 4), (8, 1, 4), (8, 4, 8), (8, 3, 4), (8, 4, 1), (8, 5, 4), (8, 4, 2)]
 
 
 def _case(i):
@@ -30,7 +30,7 @@ def _case(i):
                 spatial_shapes=tuple(shapes), num_query=nq, offset_sigma_px=float(rng.choice([0.5, 2.0, 6.0])))
 
 
-@pytest.mark.parametrize("i", range(14))
+@pytest.mark.parametrize("i", range(18))
 def test_random_shape(gpu_lib, i):
     geom = _case(i)
     wl = workloads.custom(name=f"random{i}", backward=True, random_valid_ratios=True, **geom)
