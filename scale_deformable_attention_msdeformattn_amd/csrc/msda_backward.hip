@@ -117,6 +117,12 @@ __device__ __forceinline__ uint4 tile_record(uint32_t bq, int cell, float fx, fl
                       __float_as_uint(a * fy));
 }
 
+// n / d for 0 <= n < 2^20 and 1 <= d <= 128, given inv_d = 1.0f / d (float
+// division, rounded to nearest): floor((n + 0.5) * inv_d) is exact over that
+// range (every pair checked on the host in float32), and costs two VALU
+// operations and a conversion instead of an integer division.
+__device__ __forceinline__ int small_div(int n, float inv_d) { return (int)(((float)n + 0.5f) * inv_d); }
+
 __device__ __forceinline__ SampleTiles sample_tiles(const TileLevel &tl, int W, int H, int cx, int cy)
 {
     const int ntw = tl.ntw, base = tl.base;
@@ -1112,6 +1118,8 @@ tile_accum_kernel(Geometry g, TilePlan tp, const float4 *__restrict__ grad_out, 
     const int npix = ph * pw;
     const int S = ncells >= NG ? 1 : NG / ncells;   // lane groups per cell
     const int ntask = ncells * S;
+    // divisors of the task and pixel numbering (S <= NG, cw and pw <= kTilePix + 1)
+    const float inv_s = 1.0f / (float)S, inv_cw = 1.0f / (float)cw, inv_pw = 1.0f / (float)pw;
     const uint32_t nqueries = (uint32_t)g.queries();
     const int grp = threadIdx.x / LG;
     const int lig = threadIdx.x % LG;
@@ -1159,7 +1167,7 @@ tile_accum_kernel(Geometry g, TilePlan tp, const float4 *__restrict__ grad_out, 
             for (int j = 0; j < kBatch; ++j) {
                 // the record's cell (ry, rx) has its top-left corner at tile pixel (ry - 1, rx - 1)
                 const int cell = (int)(rec[j].x & ((1u << kCellBits) - 1));
-                const int ry = cell / cw, rx = cell - (cell / cw) * cw;
+                const int ry = small_div(cell, inv_cw), rx = cell - ry * cw;
                 const bool in = (rec[j].x >> kCellBits) < nqueries;
                 const float fx = __uint_as_float(rec[j].y);
                 const float ay0 = __uint_as_float(rec[j].z), ay1 = __uint_as_float(rec[j].w);
@@ -1279,7 +1287,7 @@ tile_accum_kernel(Geometry g, TilePlan tp, const float4 *__restrict__ grad_out, 
         for (int t = 0; t < kTaskSlots; ++t) {
             const int task = grp + t * NG;
             if (task >= ntask) break;
-            const int cell = task / S, split = task - (task / S) * S;
+            const int cell = small_div(task, inv_s), split = task - cell * S;
             float4 acc[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[r] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -1310,7 +1318,7 @@ tile_accum_kernel(Geometry g, TilePlan tp, const float4 *__restrict__ grad_out, 
             // role r: 0 top-left, 1 top-right, 2 bottom-left, 3 bottom-right
             // corner of the cell; cell (ry, rx) (relative, halo row/column at
             // 0) has its top-left corner at tile pixel (ry-1, rx-1)
-            const int ry = cell / cw, rx = cell - (cell / cw) * cw;
+            const int ry = small_div(cell, inv_cw), rx = cell - ry * cw;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int py = ry - 1 + (r >> 1), px = rx - 1 + (r & 1);
@@ -1333,7 +1341,8 @@ tile_accum_kernel(Geometry g, TilePlan tp, const float4 *__restrict__ grad_out, 
             v.z += t.z;
             v.w += t.w;
         }
-        const int py = r0 + pix / pw, px = c0 + pix % pw;
+        const int pr = small_div(pix, inv_pw);
+        const int py = r0 + pr, px = c0 + (pix - pr * pw);
         const int64_t row = (int64_t)b * g.S + lstart + (int64_t)py * W + px;
         if (mask && mask[row]) v = make_float4(0.f, 0.f, 0.f, 0.f);  // padded: no gradient
         float4 *dst = grad_value + (row * g.M + m) * LG + lig;
