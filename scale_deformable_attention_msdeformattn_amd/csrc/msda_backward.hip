@@ -1447,6 +1447,7 @@ dense_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, cons
     const int qa1 = (int)((int64_t)g.Nq * (split + 1) / tp.dsplits);
     const int spq = ndl * K;                   // dense samples per query
     const int QS = min(kDenseQ, kDenseSub / spq);  // queries per sub-chunk
+    const float inv_spq = 1.0f / (float)spq;       // spq <= L*K <= 128, sample numbers < kDenseSub
     constexpr int64_t LKs = (int64_t)L * K;
     const int grp = threadIdx.x / LG;
     const int lig = threadIdx.x % LG;
@@ -1472,7 +1473,7 @@ dense_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, cons
 #pragma unroll
         for (int t = 0; t < kPer; ++t) {
             const int i = threadIdx.x + t * kDenseThreads;
-            const int qi = i / spq, r = i - (i / spq) * spq;
+            const int qi = small_div(i, inv_spq), r = i - qi * spq;
             const int64_t sidx = (((int64_t)b * g.Nq + qa + qi) * g.M + m) * LKs + (int64_t)lfirst * K + r;
             u[t] = i < ns ? loc[sidx] : make_float2(-1e30f, -1e30f);
             a[t] = i < ns ? attn[sidx] : 0.0f;
@@ -1512,7 +1513,7 @@ dense_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, cons
 #pragma unroll
         for (int t = 0; t < kPer; ++t) {
             const int i = threadIdx.x + t * kDenseThreads;
-            const int dl = (i - (i / spq) * spq) / K;
+            const int dl = (i - small_div(i, inv_spq) * spq) / K;
             const LevelRec lv = s_lv[dl < ndl ? dl : 0];
             const int H = (int)lv.Hf, W = lv.W;
             const int pbase = s_dbase[dl < ndl ? dl : 0] - p0;
@@ -1560,7 +1561,7 @@ dense_accum_kernel(Geometry g, TilePlan tp, const float2 *__restrict__ loc, cons
         lds_barrier();
 #pragma unroll
         for (int t = 0; t < kPer; ++t) {
-            const uint32_t qi = (uint32_t)((threadIdx.x + t * kDenseThreads) / spq);
+            const uint32_t qi = (uint32_t)small_div((int)threadIdx.x + t * kDenseThreads, inv_spq);
 #pragma unroll
             for (int c = 0; c < 4; ++c)
                 if (pix[t][c] >= 0)
@@ -1637,12 +1638,15 @@ __device__ void dense_reduce_one(const Geometry &g, const TilePlan &tp, const fl
     // the thread count is a whole number of outputs, so an output's lanes are
     // all present or all gone
     if (tp.dsplits <= 1 || t >= (int64_t)g.B * tp.ndpix * g.M * LG * R) return;
+    constexpr int M = 64 / LG;  // 256 channels: M heads of 4*LG
     const int c = (int)(t % LG);
     const int r = (int)((t / LG) % R);
     const int64_t o = t / (LG * R);  // (b, p, m)
-    const int m = (int)(o % g.M);
-    const int p = (int)((o / g.M) % tp.ndpix);
-    const int b = (int)(o / ((int64_t)g.M * tp.ndpix));
+    const int m = (int)(o % M);
+    // b * ndpix + p < B * S < 2^31: 32-bit division
+    const uint32_t bp = (uint32_t)(o / M);
+    const int b = (int)(bp / (uint32_t)tp.ndpix);
+    const int p = (int)(bp - (uint32_t)b * (uint32_t)tp.ndpix);
     const int64_t p0 = (int64_t)(b * g.M + m) * tp.ppb + p;
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 4
