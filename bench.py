@@ -321,9 +321,9 @@ def _counter_summary(t):
     lines = [f"# Counters per kernel — {t['workload']} step (plain path), one MI355X", "",
              "Generated by `python bench.py --ingest-counters DIR` from the rocprofv3 passes below, each run as",
              "", "```", "cd /tmp && export TMPDIR=/tmp",
-             "rocprofv3 --pmc <counters of the pass> --output-format csv -d <repo>/gpurun_out/pmc/<pass> -o run \\",
+             "rocprofv3 --pmc <counters of the pass> --output-format csv -d <out>/pmc/<pass> -o run \\",
              "    -- python3 <repo>/bench.py --eager --profile-run --steps 3 --warmup 1 \\",
-             "    > <repo>/gpurun_out/pmc/<pass>/bench.log", "```", ""]
+             "    > <out>/pmc/<pass>/bench.log", "```", ""]
     for k, v in t["passes"].items():
         lines.append(f"- `{k}`: {', '.join(v)}")
     lines += ["", f"Kernel sources hash `{t['source_hash']}`. Bytes are L2 -> fabric traffic, exact by request "
@@ -411,8 +411,8 @@ def trace_summary(d, steps, warmup):
     spans = sorted(((max(r[1] for r in seg) - seg[0][0]) / 1e3, i) for i, seg in enumerate(graph))
     med = graph[spans[len(spans) // 2][1]]
     flags = "" if (steps, warmup) == (50, 10) else f" --steps {steps} --warmup {warmup}"  # the defaults, or not
-    cmd = (f"cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <repo>/gpurun_out/"
-           f"trace -o run -- python3 <repo>/bench.py{flags} > <repo>/gpurun_out/trace/bench.log")
+    cmd = (f"cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <out>/"
+           f"trace -o run -- python3 <repo>/bench.py{flags} > <out>/trace/bench.log")
     lines = ["# Kernel trace — encoder_backward step (B=2, M=8, D=32, L=4 76x106..8x13, S=Nq=10687, K=4, fp32)", "",
              "Generated by `python bench.py --trace-summary DIR --steps {0} --warmup {1}` from the csv output of".format(
                  steps, warmup), "", "```", cmd, "```", "",
@@ -784,8 +784,8 @@ def generic_path(msda, workloads, dev, shapes):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: this build runs on a "
-              "single GPU (the op shards by batch or by head with no exchange between GPUs)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the figure is one GPU's "
+              "share (the op shards by batch or by head with no exchange between GPUs)", file=sys.stderr)
         sys.exit(2)
     if args.ingest_counters:
         ingest_counters(args.ingest_counters, args.workload)
