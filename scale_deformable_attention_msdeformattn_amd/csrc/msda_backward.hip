@@ -734,12 +734,12 @@ backward_head_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
     for (int i = threadIdx.x; i < nkeys; i += kHeadThreads) {
         uint32_t t = 0, pre = 0;
         int rr = 0;
-        for (; rr + 8 <= tp.hqr; rr += 8) {
-            uint32_t c[8];
+        for (; rr + 32 <= tp.hqr; rr += 32) {
+            uint32_t c[32];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) c[k] = cnt[(int64_t)(rr + k) * nkeys + i];
+            for (int k = 0; k < 32; ++k) c[k] = cnt[(int64_t)(rr + k) * nkeys + i];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
+            for (int k = 0; k < 32; ++k) {
                 pre += rr + k < r ? c[k] : 0u;
                 t += c[k];
             }
