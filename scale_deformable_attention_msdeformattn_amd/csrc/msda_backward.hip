@@ -682,6 +682,7 @@ backward_head_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
     uint32_t *s_cursor = reinterpret_cast<uint32_t *>(s_raw + stage_bytes);  // [tpb + kWave]
     uint32_t *s_pre = s_cursor + tp.tpb + kWave;  // [tpb]: counts of the head's workgroups before this one
     __shared__ LevelRec s_lv[L];
+    __shared__ float2 s_inv[L];  // (1/W_l, 1/H_l): the offsets' gradient in the fused form
     __shared__ TileLevel s_tl[L];
     __shared__ int4 s_off[kHeadWaves][QPW * PAD];
     // (fx, fy, A*W_l, A*H_l) per sample, overwritten in place by (grad_attn,
@@ -700,6 +701,7 @@ backward_head_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
     if (threadIdx.x < L) {
         const int l = threadIdx.x;
         s_lv[l] = LevelRec{(float)g.lv.W[l], (float)g.lv.H[l], g.lv.W[l], g.lv.start[l]};
+        s_inv[l] = make_float2(1.0f / (float)g.lv.W[l], 1.0f / (float)g.lv.H[l]);
         s_tl[l] = tile_level(tp, l);
     }
     // head m's rows of the staged levels, then a zero row that off-map
@@ -990,10 +992,10 @@ backward_head_kernel(Geometry g, TilePlan tp, const VT *__restrict__ value, cons
                     }
                     if (valid) {
                         grad_attn[si] = pa[p] * (rr[p].x - tsum);
-                        const LevelRec lv = s_lv[l];
+                        const float2 inv = s_inv[l];
                         grad_loc[si] = fg.ref_dims == 4 ? make_float2(rr[p].y * (bx.z * 0.5f / (float)K),
                                                                       rr[p].z * (bx.w * 0.5f / (float)K))
-                                                        : make_float2(rr[p].y / lv.Wf, rr[p].z / lv.Hf);
+                                                        : make_float2(rr[p].y * inv.x, rr[p].z * inv.y);
                     }
                     if (fg.grad_ref) {
                         // (x, y) from grad_loc; for boxes (w, h) from grad_loc * offset / (2K); summed

@@ -325,10 +325,10 @@ forward_staged_kernel(Geometry g, const VT *__restrict__ value, const float2 *__
                 e[p] = expf(x[p] - mx);
                 es += e[p];
             }
-            es = group_sum<SPS>(es);
+            const float ies = 1.0f / group_sum<SPS>(es);
 #pragma unroll
             for (int p = 0; p < NP1; ++p) {
-                pa[p] = e[p] / es;
+                pa[p] = e[p] * ies;
                 if (ok[p]) {
                     fi.loc_out[si[p]] = pu[p];
                     fi.attn_out[si[p]] = pa[p];
