@@ -781,6 +781,48 @@ def generic_path(msda, workloads, dev, shapes):
     return out
 
 
+def decoder_backward(msda, workloads, dev):
+    """The backward of the decoder's 300 object queries per image (the tiled
+    per-query path: binning, the per-query main kernel, tile_accum and the
+    dense levels): HIP events around 20 back-to-back calls, and the kernels
+    each timed alone by the library's event pairs."""
+    import torch
+    base = workloads.WORKLOADS["decoder"]
+    wl = workloads.custom(name="decoder_backward", batch=base.batch, heads=base.heads, channels=base.channels,
+                          points=base.points, spatial_shapes=base.spatial_shapes, num_query=base.num_query,
+                          offset_sigma_px=base.offset_sigma_px, random_valid_ratios=True, backward=True)
+    d = workloads.draw(wl, 0)
+    shapes = d.spatial_shapes
+    lsi, _ = msda.level_start_index_host(shapes)
+    ref = msda.msda_reference_points(shapes, valid_ratios=d.valid_ratios.to(dev), query_ref=d.query_ref.to(dev))
+    loc = msda.msda_sampling_locations(shapes, ref, d.offsets_px.to(dev))
+    A = msda.msda_attention_softmax(shapes, d.logits.to(dev), wl.points)
+    value, G = d.value.to(dev), d.grad_output.to(dev)
+    f = lambda: msda.msda_backward(value, shapes, lsi, loc, A, G)
+    for _ in range(3):
+        f()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(20):
+        f()
+    e1.record()
+    torch.cuda.synchronize()
+    call_us = e0.elapsed_time(e1) * 1e3 / 20
+    msda.msda_timing_reset()
+    msda.msda_timing_enable(True)
+    for _ in range(5):
+        f()
+    torch.cuda.synchronize()
+    msda.msda_timing_enable(False)
+    kernels = {k: round(v[0] * 1e3 / v[1], 2) for k, v in msda.msda_timing_read().items()}
+    msda.msda_timing_reset()
+    queries = wl.batch * wl.nq
+    return {"workload": f"decoder backward fp32: B={wl.batch} M={wl.heads} D={wl.channels} L={wl.levels} "
+                        f"Nq={wl.nq} K={wl.points}", "call_us": round(call_us, 2),
+            "queries_per_s": queries / (call_us * 1e-6), "kernels_alone_us": kernels}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -1091,6 +1133,7 @@ def main():
     if not args.no_extra_configs:
         result["other_forward_configs"] = forward_configs(msda, workloads, dev, args)
         result["generic_path"] = generic_path(msda, workloads, dev, shapes)
+        result["decoder_backward"] = decoder_backward(msda, workloads, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.workload)
     print(json.dumps(result), flush=True)

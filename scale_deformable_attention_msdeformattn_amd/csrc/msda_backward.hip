@@ -54,6 +54,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kBlock = kWaves * kWave;
 constexpr int kQueriesPerGroup = 32;     // queries per workgroup of bin_count and main
+constexpr int kMinQueryWGs = 256;        // workgroups the per-query path aims at, at least
 constexpr int kMainAhead = 2;            // samples whose gathers run ahead in the main kernel
 constexpr int kChunk = 512;              // records per LDS chunk in tile_accum
 constexpr int kTileTarget = 768;         // expected records per tile the planner aims at
@@ -2327,7 +2328,11 @@ bool make_tile_plan(const Geometry &g, TilePlan &tp)
     }
     tp.tpb = base;
     tp.ipb = ibase;
+    // queries per workgroup of the per-query path: kQueriesPerGroup, halved
+    // down to 8 (a workgroup's waves) while the workgroups would not cover
+    // the CUs (few queries: the decoder's 300 per image)
     tp.qpw = kQueriesPerGroup;
+    while (tp.qpw > 8 && (int64_t)g.B * ((g.Nq + tp.qpw - 1) / tp.qpw) < kMinQueryWGs) tp.qpw /= 2;
     tp.wpb = (g.Nq + tp.qpw - 1) / tp.qpw;
     tp.hqr = std::max(1, (kHeadTargetWGs + g.B * g.M - 1) / (g.B * g.M));
     tp.hqpr = std::max(1, (g.Nq + tp.hqr - 1) / tp.hqr);
