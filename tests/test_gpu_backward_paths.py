@@ -11,7 +11,9 @@ path, against the fp64 oracle at the backward tolerance 1e-4 * (1 + |ref|):
   - dense levels split over queries, with the accumulate flag;
   - only the last run of adjacent dense levels summed from the samples;
   - three dense levels numbered across two pixel parts, beside the per-head
-    main kernel.
+    main kernel;
+  - sparse levels (a decoder's few queries on large maps): tiles with a few
+    records or none, with the accumulate flag.
 """
 import numpy as np
 import pytest
@@ -127,3 +129,12 @@ def test_dense_levels_over_several_parts(gpu_lib):
     msda.msda_timing_reset()
     assert {"backward_head_kernel", "dense_accum_kernel", "dense_reduce_kernel", "tile_accum_kernel"} <= ran, ran
     _check(ci, "dense parts")
+
+
+def test_sparse_levels(gpu_lib):
+    print("[backward paths] sparse levels", flush=True)
+    # 300 queries on a 100x150 level: under 0.1 samples per pixel, about 3
+    # records per 32-pixel tile and some tiles without any
+    ci = _decoder("sparse", ((100, 150), (50, 75), (25, 38), (13, 19)), 300, 2.0, seed=12, batch=2)
+    assert _plan(ci) == {"dense": [], "direct": [], "split": []}
+    _check(ci, "sparse")
