@@ -161,6 +161,8 @@ def algorithmic_bytes(B, M, D, Nq, shapes, K, vbytes):
         "reference_points_kernel": B * L * 2 * f32 + B * Nq * L * 2 * f32,
         "sampling_locations_kernel": B * Nq * L * 2 * f32 + 2 * samples * 2 * f32,
         "softmax_vec_kernel": 2 * samples * f32,
+        # the three above in one launch: the reference points are not read back
+        "prologue_kernel": B * L * 2 * f32 + B * Nq * L * 2 * f32 + 2 * samples * 2 * f32 + 2 * samples * f32,
         "forward_c256_kernel": vbytes + samples * 3 * f32 + rows,
         # the same op with the coarse levels staged in LDS (same algorithmic bytes)
         "forward_staged_kernel": vbytes + samples * 3 * f32 + rows,
@@ -343,7 +345,7 @@ def _counter_summary(t):
         f.write("\n".join(lines) + "\n")
 
 
-LIB_KERNELS = ("reference_points_kernel", "sampling_locations_kernel", "softmax_vec_kernel", "forward_",
+LIB_KERNELS = ("prologue_kernel", "reference_points_kernel", "sampling_locations_kernel", "softmax_vec_kernel", "forward_",
                "bin_count", "backward_", "clear_totals_kernel", "tile_accum_kernel", "dense_accum_kernel",
                "dense_reduce_kernel", "zero_", "ref_grad_sum_kernel", "fused_grads_kernel")
 
@@ -351,8 +353,8 @@ LIB_KERNELS = ("reference_points_kernel", "sampling_locations_kernel", "softmax_
 def trace_summary(d, steps, warmup):
     """profiles/kernel_trace_encoder_step.md from the kernel trace of
     `bench.py --steps K --warmup W` under rocprofv3 --kernel-trace --stats.
-    The run's plain steps (reference points, then sampling locations, ...)
-    come in this order: max(1, W) warm-up steps and one captured step
+    The run's plain steps (the prologue kernel, then the forward, ...) come
+    in this order: max(1, W) warm-up steps and one captured step
     (eager), 3 + W + K graph replays, then K eager steps timed per entry
     point and K eager steps timed per kernel by the library's event pairs
     (the figures of the bench line). Per kernel: rocprofv3's average over
@@ -372,12 +374,13 @@ def trace_summary(d, steps, warmup):
             all_avg[n] = (c + int(r["Calls"]), t + float(r["TotalDurationNs"]))
     rows = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), _short_kernel_name(r["Kernel_Name"]))
                   for r in csv.DictReader(open(trace[0])))
-    starts = [i for i, r in enumerate(rows)
-              if r[2] == "reference_points_kernel" and i + 1 < len(rows) and rows[i + 1][2] == "sampling_locations_kernel"]
+    # a plain step opens with the prologue kernel; it runs until the next
+    # step of any kind (the fused and box steps open with the reference points)
+    starts = [i for i, r in enumerate(rows) if r[2] == "prologue_kernel"]
     plain = []
     for si in starts:
         j = si + 1
-        while j < len(rows) and rows[j][2] != "reference_points_kernel":
+        while j < len(rows) and rows[j][2] not in ("prologue_kernel", "reference_points_kernel"):
             j += 1
         plain.append(rows[si:j])
     w0 = max(1, warmup) + 1
@@ -864,14 +867,8 @@ def main():
 
     state = {}
 
-    def k_ref():
-        state["ref"] = msda.msda_reference_points(shapes, valid_ratios=vr)
-
-    def k_loc():
-        state["loc"] = msda.msda_sampling_locations(shapes, state["ref"], off)
-
-    def k_softmax():
-        state["A"] = msda.msda_attention_softmax(shapes, logits, K)
+    def k_prologue():  # reference points, sampling locations and softmax, one launch
+        state["ref"], state["loc"], state["A"] = msda.msda_prologue(shapes, off, logits, valid_ratios=vr)
 
     def k_fwd():
         state["out"] = msda.msda_forward(value, shapes, lsi, state["loc"], state["A"])
@@ -879,8 +876,7 @@ def main():
     def k_bwd():
         state["grads"] = msda.msda_backward(value, shapes, lsi, state["loc"], state["A"], G)
 
-    calls = [("msda_reference_points", k_ref), ("msda_sampling_locations", k_loc),
-             ("msda_attention_softmax", k_softmax), ("msda_forward", k_fwd), ("msda_backward", k_bwd)]
+    calls = [("msda_prologue", k_prologue), ("msda_forward", k_fwd), ("msda_backward", k_bwd)]
 
     def step():
         for _, f in calls:
@@ -1077,7 +1073,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f32" if value.dtype == torch.float32 else "bf16 value, f32 compute",
         "data": "synthetic (seeded draws with Deformable DETR's encoder shapes and distributions; no dataset)",
-        "config": {"workload": w.description, "step": "reference points + locations + softmax + forward + "
+        "config": {"workload": w.description, "step": "reference points + locations + softmax (one launch) + forward + "
                    "backward", "graph_replay": graph is not None},
         "source_hash": kernel_source_hash(),
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS,

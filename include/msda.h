@@ -57,7 +57,7 @@ extern "C" {
 #define MSDA_API
 #endif
 
-#define MSDA_ABI_VERSION 10
+#define MSDA_ABI_VERSION 11
 #define MSDA_MAX_LEVELS 16
 
 typedef enum {
@@ -127,6 +127,21 @@ MSDA_API int msda_sampling_locations(const msda_shape *shape, const float *ref,
  * each (b, q, m), so that they sum to 1 over all levels and points (paper
  * notes, "Insight 2"). weights_out [B,Nq,M,L,K] fp32; may alias logits. */
 MSDA_API int msda_attention_softmax(const msda_shape *shape, const float *logits,
+                           float *weights_out, void *stream);
+
+/* The three calls above in one: reference points (as msda_reference_points,
+ * into ref_out [B,Nq,L,2]), the sampling locations from them (as
+ * msda_sampling_locations, offset_px -> loc_out [B,Nq,M,L,K,2]) and the
+ * softmax of logits [B,Nq,M,L*K] (as msda_attention_softmax, into
+ * weights_out [B,Nq,M,L,K]); all fp32, with the same arguments and rules
+ * as those three, and bit for bit the same results. For K in {2, 4, 8},
+ * L*K in {4, 8, 16, 32} and 16-byte aligned offset_px, loc_out, logits and
+ * weights_out it is a single kernel launch (each location thread forms its
+ * reference point itself instead of reading ref_out back); otherwise the
+ * three kernels run in turn on `stream`. weights_out may alias logits; no
+ * other output may alias an input. */
+MSDA_API int msda_prologue(const msda_shape *shape, const float *valid_ratios, const float *query_ref,
+                           const float *offset_px, const float *logits, float *ref_out, float *loc_out,
                            float *weights_out, void *stream);
 
 /* Forward of the core (the bracketed sum of the MSDeformAttn equation).

@@ -90,6 +90,8 @@ def load():
     lib.msda_sampling_locations.argtypes = [_shp, _vp, _vp, _vp, _vp]
     lib.msda_attention_softmax.restype = ctypes.c_int
     lib.msda_attention_softmax.argtypes = [_shp, _vp, _vp, _vp]
+    lib.msda_prologue.restype = ctypes.c_int
+    lib.msda_prologue.argtypes = [_shp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     lib.msda_forward.restype = ctypes.c_int
     lib.msda_forward.argtypes = [_shp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp]
     lib.msda_backward_workspace_size.restype = ctypes.c_int
@@ -292,6 +294,38 @@ def msda_attention_softmax(spatial_shapes, logits: torch.Tensor, points: int) ->
     sh = _shape(sv, B, M, 1, points, Nq)
     _check(load().msda_attention_softmax(sh.ptr, _p(x), _p(out), _stream(out)), "msda_attention_softmax")
     return out
+
+
+def msda_prologue(spatial_shapes, offsets_px: torch.Tensor, logits: torch.Tensor,
+                  valid_ratios: Optional[torch.Tensor] = None, query_ref: Optional[torch.Tensor] = None):
+    """Reference points, sampling locations and attention weights in one call:
+    (ref [B,Nq,L,2], loc [B,Nq,M,L,K,2], weights [B,Nq,M,L,K]), the same bits
+    as msda_reference_points, msda_sampling_locations and
+    msda_attention_softmax in turn. Encoder mode when query_ref is None."""
+    off = _dev(offsets_px, "offsets_px")
+    x = _dev(logits, "logits")
+    if off.dim() != 6 or off.shape[-1] != 2:
+        raise ValueError("offsets_px must be [B, Nq, M, L, K, 2]")
+    B, Nq, M, L, K, _ = off.shape
+    if tuple(x.shape) != (B, Nq, M, L * K):
+        raise ValueError(f"logits must be [{B}, {Nq}, {M}, {L * K}], got {tuple(x.shape)}")
+    if valid_ratios is not None:
+        valid_ratios = _dev(valid_ratios, "valid_ratios")
+        if tuple(valid_ratios.shape) != (B, L, 2):
+            raise ValueError(f"valid_ratios must be [{B}, {L}, 2], got {tuple(valid_ratios.shape)}")
+    if query_ref is not None:
+        query_ref = _dev(query_ref, "query_ref")
+        if tuple(query_ref.shape) != (B, Nq, 2):
+            raise ValueError(f"query_ref must be [{B}, {Nq}, 2], got {tuple(query_ref.shape)}")
+    sh = _shape(spatial_shapes, B, M, 1, K, Nq)
+    if sh.levels != L:
+        raise ValueError("spatial_shapes and offsets_px disagree on the level count")
+    ref = torch.empty(B, Nq, L, 2, dtype=torch.float32, device=off.device)
+    loc = torch.empty_like(off)
+    w = torch.empty(B, Nq, M, L, K, dtype=torch.float32, device=off.device)
+    _check(load().msda_prologue(sh.ptr, _p(valid_ratios), _p(query_ref), _p(off), _p(x), _p(ref), _p(loc), _p(w),
+                                _stream(off)), "msda_prologue")
+    return ref, loc, w
 
 
 def _core_shape(value, spatial_shapes, level_start_index, loc, attn):

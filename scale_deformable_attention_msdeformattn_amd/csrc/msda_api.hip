@@ -174,6 +174,25 @@ int msda_attention_softmax(const msda_shape *shape, const float *logits, float *
     return launched(msda::launch_softmax(g, logits, weights_out, (hipStream_t)stream), "attention_softmax");
 }
 
+int msda_prologue(const msda_shape *shape, const float *valid_ratios, const float *query_ref,
+                  const float *offset_px, const float *logits, float *ref_out, float *loc_out, float *weights_out,
+                  void *stream)
+{
+    msda::Geometry g;
+    if (int st = make_geometry(shape, g)) return st;
+    if (g.B == 0 || g.Nq == 0) return ok();
+    if (!offset_px || !logits || !ref_out || !loc_out || !weights_out) return fail(MSDA_E_NULL, "NULL tensor");
+    if (!query_ref && g.Nq != g.S)
+        return fail(MSDA_E_SHAPE, "encoder reference points need num_query == num_value (%d != %d)", g.Nq, g.S);
+    if (!aligned(ref_out, 8) || !aligned(loc_out, 8) || !aligned(offset_px, 8) || (query_ref && !aligned(query_ref, 8)))
+        return fail(MSDA_E_ALIGN, "(x, y) tensors need 8-byte alignment");
+    if (!aligned(logits, 4) || !aligned(weights_out, 4) || (valid_ratios && !aligned(valid_ratios, 4)))
+        return fail(MSDA_E_ALIGN, "fp32 tensors need 4-byte alignment");
+    return launched(msda::launch_prologue(g, valid_ratios, query_ref, offset_px, logits, ref_out, loc_out,
+                                          weights_out, (hipStream_t)stream),
+                    "prologue");
+}
+
 static int check_core(const msda::Geometry &g, const void *value, msda_dtype vt, const float *loc,
                       const float *attn)
 {

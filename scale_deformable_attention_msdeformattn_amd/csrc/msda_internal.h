@@ -174,6 +174,10 @@ hipError_t launch_reference_points(const Geometry &g, const float *valid_ratios,
 hipError_t launch_sampling_locations(const Geometry &g, const float *ref, const float *off,
                                      float *loc, hipStream_t st);
 hipError_t launch_softmax(const Geometry &g, const float *logits, float *w, hipStream_t st);
+// The three above in one launch where the shapes allow (else in turn).
+hipError_t launch_prologue(const Geometry &g, const float *valid_ratios, const float *query_ref,
+                           const float *offset_px, const float *logits, float *ref, float *loc, float *w,
+                           hipStream_t st);
 hipError_t launch_forward(const Geometry &g, const void *value, msda_dtype vt, const float *loc,
                           const float *attn, float *out, hipStream_t st);
 hipError_t launch_forward_fused(const Geometry &g, const void *value, msda_dtype vt, const FusedInputs &fi,

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.msda_abi_version() == 10
+    assert lib.msda_abi_version() == 11
     assert lib.msda_status_string(0) == b"ok"
     for code in range(-8, 0):
         assert lib.msda_status_string(code) not in (b"", b"unknown status")
@@ -94,6 +94,24 @@ def test_null_arguments(lib):
 
 
 @cpu_only
+def test_prologue_validates_on_the_host(lib):
+    enc = _shape(Nq=None)
+
+    def call(sh, vr=None, u=None, off=FAKE, x=FAKE, ref=FAKE, loc=FAKE, w=FAKE):
+        return lib.msda_prologue(sh.ptr, vr, u, off, x, ref, loc, w, None)
+    for k in ("off", "x", "ref", "loc", "w"):
+        assert call(enc, **{k: None}) == B.MSDA_E_NULL, k
+    # encoder reference points need Nq == S; decoder mode (u given) does not
+    dec = _shape(Nq=300)
+    assert call(dec) == B.MSDA_E_SHAPE
+    odd = ctypes.c_void_p(0x10004)   # 4-byte aligned, not 8
+    assert call(enc, loc=odd) == B.MSDA_E_ALIGN
+    assert call(dec, u=odd) == B.MSDA_E_ALIGN
+    assert call(enc, w=ctypes.c_void_p(0x10002)) == B.MSDA_E_ALIGN
+    # no queries: nothing to do, no device work
+    assert call(_shape(Nq=0), u=FAKE) == B.MSDA_OK
+
+
 def test_fused_entry_points_validate_on_the_host(lib):
     ptrs = [FAKE] * 6   # ref, offsets, logits, output, loc_out, attn_out
 
