@@ -1,4 +1,4 @@
-"""The backward under HIP graph capture. On the fast path its dense levels run
+"""The backward (and the one-launch prologue) under HIP graph capture. On the fast path its dense levels run
 on a stream of the library's own, forked from and joined back into the
 caller's stream by events; a graph captured from the caller's stream must
 take that branch in, and every replay must match the eager call. Replays are
@@ -104,3 +104,24 @@ def test_backward_on_two_streams_in_turn(gpu_lib):
     assert torch.allclose(r1, want, rtol=1e-5, atol=1e-5)
     s2.synchronize()
     assert torch.allclose(r2, want2, rtol=1e-5, atol=1e-5)
+
+
+def test_prologue_graph_replays_equal_eager(gpu_lib):
+    """The step's first call, captured: every replay writes the same bits as
+    the eager call (reference points, locations and weights have one writer
+    per element and a fixed order of operations)."""
+    d = workloads.draw("encoder_backward", 0)
+    shapes = d.spatial_shapes
+    vr, off, logits = d.valid_ratios.cuda(), d.offsets_px.cuda(), d.logits.cuda()
+    eager = [t.clone() for t in msda.msda_prologue(shapes, off, logits, valid_ratios=vr)]
+    torch.cuda.synchronize()
+    graph, out = _capture(lambda: msda.msda_prologue(shapes, off, logits, valid_ratios=vr))
+    for i in range(3):
+        for t in out:
+            t.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("ref", "loc", "weights"), out, eager):
+            assert torch.equal(a, b), (i, name)
+        msda.msda_attention_softmax(shapes, logits, d.workload.points)  # eager work between the replays
+        torch.cuda.synchronize()
