@@ -1,8 +1,9 @@
 """Host logic of bench.py that needs no GPU: the single-GPU guard, the kernel
 names it groups counters by, the exact L2 byte arithmetic of the counter
 ingestion, the kernel-source hash that keeps counter figures attached to the
-code they were measured on, and its mirror of the library's dense-level rule
-(checked against the library's own planner through the C ABI)."""
+code they were measured on, its mirror of the library's dense-level rule
+(checked against the library's own planner through the C ABI), and the trace
+summary's segmentation of a kernel trace into plain steps."""
 import csv
 import json
 import os
@@ -126,3 +127,71 @@ def test_kernel_source_hash_ignores_comments_only(tmp_path, monkeypatch):
 def test_dense_levels_mirror_the_library(shapes, nq, k):
     sh = B.Shape(shapes, 2, 8, 32, k, nq)
     assert bench.dense_levels(shapes, nq, k) == B.msda_backward_plan(sh)["dense"]
+
+
+def _k(name):
+    return f"void msda::(anonymous namespace)::{name}<8, 4, 4>(msda::Geometry)"
+
+
+# a plain step as the trace shows it: (kernel, start offset, duration) in ns
+PLAIN = [("prologue_kernel", 0, 16000), ("forward_staged_kernel", 16000, 38000),
+         ("dense_accum_kernel", 60000, 40000), ("bin_count_head_kernel", 66000, 28000),
+         ("backward_head_kernel", 94000, 64000), ("dense_reduce_kernel", 101000, 23000),
+         ("tile_accum_kernel", 158000, 44000)]
+FUSED = [("reference_points_kernel", 0, 5000), ("forward_staged_kernel<float, 8, 4, 4, 2, true>", 5000, 50000)]
+
+
+def test_trace_summary_segments_plain_steps(tmp_path, monkeypatch):
+    """The trace summary finds the plain steps by their opening prologue
+    kernel, ends each at the next step of any kind (a fused step opens with
+    the reference points), drops torch's kernels, and takes the replays and
+    the event-timed eager steps from their places in the run's order."""
+    steps, warmup = 4, 2
+    w0 = max(1, warmup) + 1
+    nrep = 3 + warmup + steps
+    n_plain = w0 + nrep + 2 * steps
+    rows, t = [], 0
+    for i in range(n_plain):
+        scale = 1.0 + 0.01 * i  # later steps a little slower: the medians pick the middle
+        for name, s0, dur in PLAIN:
+            rows.append((_k(name), t + int(s0 * scale), t + int((s0 + dur) * scale)))
+        # a torch kernel inside the segment (the replays' comparison kernels)
+        rows.append(("void at::native::vectorized_elementwise_kernel<4>(int)", t + 210000, t + 211000))
+        t += 300000
+    for _ in range(3):  # fused steps after the plain ones
+        for name, s0, dur in FUSED:
+            full = f"void msda::(anonymous namespace)::{name}(msda::Geometry)" if "<" in name else _k(name)
+            rows.append((full, t + s0, t + s0 + dur))
+        t += 300000
+    d = tmp_path / "trace"
+    d.mkdir()
+    with open(d / "run_kernel_trace.csv", "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        wr.writeheader()
+        for k, s0, e0 in rows:
+            wr.writerow({"Kernel_Name": k, "Start_Timestamp": s0, "End_Timestamp": e0})
+    counts = {}
+    for k, s0, e0 in rows:
+        c, tot = counts.get(k, (0, 0))
+        counts[k] = (c + 1, tot + e0 - s0)
+    with open(d / "run_kernel_stats.csv", "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=["Name", "Calls", "TotalDurationNs"])
+        wr.writeheader()
+        for k, (c, tot) in counts.items():
+            wr.writerow({"Name": k, "Calls": c, "TotalDurationNs": tot})
+    out = tmp_path / "trace.md"
+    monkeypatch.setattr(bench, "TRACE_MD", str(out))
+    bench.trace_summary(str(d), steps, warmup)
+    md = out.read_text()
+    # replays w0+3 .. w0+nrep-1 and eager steps w0+nrep+steps .. end
+    assert f"over the {nrep - 3} graph replays" in md and f"over the {steps} eager plain steps" in md
+    timeline = md.split("| start | end | µs | kernel |")[1].strip().splitlines()[1:]
+    assert [ln.split("`")[1] for ln in timeline] == [n for n, _, _ in PLAIN]
+    # the median replay is the middle one of the replays taken
+    mid = sorted(range(w0 + 3, w0 + nrep))[(nrep - 3) // 2]
+    first = timeline[1].split("|")
+    assert abs(float(first[1]) - 16.0 * (1.0 + 0.01 * mid)) < 0.05
+    # the fused step's kernels are not in the plain steps' medians
+    row = [ln for ln in md.splitlines() if ln.startswith("| `reference_points_kernel`")][0]
+    assert row.split("|")[4].strip() == "" and row.split("|")[5].strip() == ""
+    assert "vectorized_elementwise_kernel" not in md
