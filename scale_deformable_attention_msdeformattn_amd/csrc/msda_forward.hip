@@ -181,9 +181,52 @@ forward_c256_kernel(Geometry g, const VT *__restrict__ value, const float2 *__re
 // QPW queries at once. The fused form forms the locations and the L*K softmax
 // in phase 1, as the per-query kernel does (a query-head's samples sit in L*K
 // adjacent lanes of a pass).
-constexpr int kStagedWaves = 16;
+// Lane layout of the staged path: every lane owns CPL channels of its query's
+// head row, so that each corner is one 16-byte load (fp32: 4 channels; bf16:
+// 8, which halves the load, LDS-record and staged-read instructions per query
+// against 4 bf16 channels per lane), and a workgroup holds kWaves waves (the
+// bf16 layout puts twice the queries in a wave, so half the waves keep the
+// records' LDS the same).
+template <typename VT> struct StagedLayout;
+template <> struct StagedLayout<float> {
+    static constexpr int kCpl = 4;
+    static constexpr int kWaves = 16;
+    __device__ __forceinline__ static void widen(const uint4 &r, float (&f)[4])
+    {
+        f[0] = __uint_as_float(r.x);
+        f[1] = __uint_as_float(r.y);
+        f[2] = __uint_as_float(r.z);
+        f[3] = __uint_as_float(r.w);
+    }
+};
+template <> struct StagedLayout<uint16_t> {  // bf16 bit patterns, widened next to their FMAs
+    static constexpr int kCpl = 8;
+    static constexpr int kWaves = 8;
+};
+
+__device__ __forceinline__ uint4 load_raw16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// acc + w * (the bf16 in the low or high half of r, widened exactly to fp32),
+// the widening and the fused multiply-add in one block: left to itself the
+// scheduler widens every loaded corner early and sinks the FMAs, keeping all
+// widened values live at once (twice the registers of the raw chunks).
+__device__ __forceinline__ float fma_bf16_lo(float w, uint32_t r, float acc)
+{
+    uint32_t t;
+    asm("v_lshlrev_b32 %1, 16, %2\n\tv_fmac_f32 %0, %3, %1" : "+v"(acc), "=&v"(t) : "v"(r), "v"(w));
+    return acc;
+}
+__device__ __forceinline__ float fma_bf16_hi(float w, uint32_t r, float acc)
+{
+    uint32_t t;
+    asm("v_and_b32 %1, 0xffff0000, %2\n\tv_fmac_f32 %0, %3, %1" : "+v"(acc), "=&v"(t) : "v"(r), "v"(w));
+    return acc;
+}
+
 constexpr int kStageRowPad = 0;           // chunks of padding after each staged row (padding did not pay)
-constexpr int kStagedThreads = kStagedWaves * kWave;
 constexpr int kStagedTargetWGs = 512;     // two rounds of one workgroup per CU (the staging fills most of its LDS)
 constexpr int kStagedMinQueries = 1024;   // fewer queries per (batch, head) do not repay the staging
 constexpr size_t kLdsPerWG = 160 * 1024;  // gfx950
@@ -194,29 +237,33 @@ struct StagePlan {
 };
 
 template <typename VT, int M, int L, int K, int LS, bool FUSED>
-__global__ void __launch_bounds__(kStagedThreads)
+__global__ void __launch_bounds__(StagedLayout<VT>::kWaves * kWave)
 forward_staged_kernel(Geometry g, const VT *__restrict__ value, const float2 *__restrict__ loc,
                       const float *__restrict__ attn, float4 *__restrict__ out, StagePlan sp, uint32_t grid,
                       FusedInputs fi, const uint8_t *__restrict__ mask)
 {
+    using Lay = StagedLayout<VT>;
+    constexpr int CPL = Lay::kCpl;     // channels per lane
+    constexpr int NW = Lay::kWaves;    // waves per workgroup
+    constexpr int NT = NW * kWave;
     constexpr int C = 256;
     constexpr int D = C / M;
-    constexpr int LPH = D / 4;         // lanes (4 channels each) per query
+    constexpr int LPH = D / CPL;       // lanes (one 16-byte chunk each) per query
     constexpr int QPW = kWave / LPH;   // queries side by side in a wave
     constexpr int RS = LPH + kStageRowPad;  // staged row stride in chunks
     constexpr int LK = L * K;
     constexpr int PAD = LK + 1;
     constexpr uint32_t RB = C * sizeof(VT);
+    constexpr int RC = RB / 16;        // 16-byte chunks per value row (all heads)
+    static_assert(D % CPL == 0 && kWave % LPH == 0, "a head row is whole 16-byte chunks over lanes of a wave");
     static_assert(0 < LS && LS < L, "some levels from memory, some from LDS");
     static_assert(!FUSED || (kWave % LK == 0 && (QPW * LK) % kWave == 0), "softmax groups within a pass");
-    using Chunk = typename StageChunk<VT>::type;
 
     extern __shared__ __align__(16) unsigned char s_raw[];
-    Chunk *s_stage = reinterpret_cast<Chunk *>(s_raw);  // [(rows + 1) * RS], the last row zeros
+    uint4 *s_stage = reinterpret_cast<uint4 *>(s_raw);  // [(rows + 1) * RS], the last row zeros
     __shared__ LevelRec s_lv[L];
-    __shared__ int4 s_off[kStagedWaves][QPW * PAD];
-    __shared__ float4 s_w[kStagedWaves][QPW * PAD];
-
+    __shared__ int4 s_off[NW][QPW * PAD];
+    __shared__ float4 s_w[NW][QPW * PAD];
     const int lane = threadIdx.x % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const uint32_t wg = xcd_tile(blockIdx.x, grid);
@@ -236,31 +283,31 @@ forward_staged_kernel(Geometry g, const VT *__restrict__ value, const float2 *__
     {
         // kStageBatch loads in flight per thread before their LDS stores
         constexpr int kStageBatch = 8;
-        const Chunk *src = reinterpret_cast<const Chunk *>(value + ((int64_t)b * g.S + srow0) * C + m * D);
+        const uint4 *src = reinterpret_cast<const uint4 *>(value + ((int64_t)b * g.S + srow0) * C + m * D);
         const int n = nrows * LPH;
-        for (int i0 = threadIdx.x; i0 < n; i0 += kStagedThreads * kStageBatch) {
-            Chunk v[kStageBatch];
+        for (int i0 = threadIdx.x; i0 < n; i0 += NT * kStageBatch) {
+            uint4 v[kStageBatch];
 #pragma unroll
             for (int k = 0; k < kStageBatch; ++k) {
-                const int i = i0 + k * kStagedThreads;
+                const int i = i0 + k * NT;
                 const bool keep = i < n && !(mask && mask[(int64_t)b * g.S + srow0 + i / LPH]);
-                v[k] = keep ? src[(int64_t)(i / LPH) * (C / 4) + i % LPH] : StageChunk<VT>::zero();
+                v[k] = keep ? src[(int64_t)(i / LPH) * RC + i % LPH] : make_uint4(0u, 0u, 0u, 0u);
             }
 #pragma unroll
             for (int k = 0; k < kStageBatch; ++k) {
-                const int i = i0 + k * kStagedThreads;
+                const int i = i0 + k * NT;
                 if (i < n) s_stage[(i / LPH) * RS + i % LPH] = v[k];
             }
         }
-        if (threadIdx.x < LPH) s_stage[nrows * RS + threadIdx.x] = StageChunk<VT>::zero();
+        if (threadIdx.x < LPH) s_stage[nrows * RS + threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
     }
     __syncthreads();
 
     const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(value + (int64_t)b * g.S * C, (uint32_t)g.S * RB);
     const int jq = lane / LPH, c = lane - (lane / LPH) * LPH;
-    const uint32_t lane_off = (uint32_t)(m * D + c * 4) * sizeof(VT);
+    const uint32_t lane_off = (uint32_t)(m * D + c * CPL) * sizeof(VT);
     const int zero_row = nrows * RS;
-    for (int qb = q0 + wave * QPW; qb < q1; qb += kStagedWaves * QPW) {
+    for (int qb = q0 + wave * QPW; qb < q1; qb += NW * QPW) {
         // ---- phase 1: the QPW*L*K samples of this pass, one per lane ----
         // Step p takes samples [p*SPS, (p+1)*SPS) of every query of the pass
         // (SPS adjacent lanes per query), so that with the levels split
@@ -403,44 +450,48 @@ forward_staged_kernel(Geometry g, const VT *__restrict__ value, const float2 *__
         // ---- phase 2: each lane its query's samples, memory and LDS levels interleaved ----
         const int4 *offs = &s_off[wave][jq * PAD];
         const float4 *ws = &s_w[wave][jq * PAD];
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        auto blend = [&](const float4 &w, const float4 &v00, const float4 &v01, const float4 &v10,
-                         const float4 &v11) {
-            acc.x = __builtin_fmaf(w.x, v00.x, acc.x);
-            acc.y = __builtin_fmaf(w.x, v00.y, acc.y);
-            acc.z = __builtin_fmaf(w.x, v00.z, acc.z);
-            acc.w = __builtin_fmaf(w.x, v00.w, acc.w);
-            acc.x = __builtin_fmaf(w.y, v01.x, acc.x);
-            acc.y = __builtin_fmaf(w.y, v01.y, acc.y);
-            acc.z = __builtin_fmaf(w.y, v01.z, acc.z);
-            acc.w = __builtin_fmaf(w.y, v01.w, acc.w);
-            acc.x = __builtin_fmaf(w.z, v10.x, acc.x);
-            acc.y = __builtin_fmaf(w.z, v10.y, acc.y);
-            acc.z = __builtin_fmaf(w.z, v10.z, acc.z);
-            acc.w = __builtin_fmaf(w.z, v10.w, acc.w);
-            acc.x = __builtin_fmaf(w.w, v11.x, acc.x);
-            acc.y = __builtin_fmaf(w.w, v11.y, acc.y);
-            acc.z = __builtin_fmaf(w.w, v11.z, acc.z);
-            acc.w = __builtin_fmaf(w.w, v11.w, acc.w);
+        float acc[CPL];
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) acc[e] = 0.0f;
+        auto corner = [&](float w, const uint4 &r) {
+            if constexpr (CPL == 8) {
+                const uint32_t u[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    acc[2 * h] = fma_bf16_lo(w, u[h], acc[2 * h]);
+                    acc[2 * h + 1] = fma_bf16_hi(w, u[h], acc[2 * h + 1]);
+                }
+            } else {
+                float v[CPL];
+                Lay::widen(r, v);
+#pragma unroll
+                for (int e = 0; e < CPL; ++e) acc[e] = __builtin_fmaf(w, v[e], acc[e]);
+            }
+        };
+        // corner by corner, each channel's sum in the order w00, w01, w10, w11
+        auto blend = [&](const float4 &w, const uint4 &r00, const uint4 &r01, const uint4 &r10, const uint4 &r11) {
+            corner(w.x, r00);
+            corner(w.y, r01);
+            corner(w.z, r10);
+            corner(w.w, r11);
         };
         auto blend_staged = [&](int i) {
             const int4 o = offs[i];
-            blend(ws[i], StageChunk<VT>::widen(s_stage[o.x + c]), StageChunk<VT>::widen(s_stage[o.y + c]),
-                  StageChunk<VT>::widen(s_stage[o.z + c]), StageChunk<VT>::widen(s_stage[o.w + c]));
+            blend(ws[i], s_stage[o.x + c], s_stage[o.y + c], s_stage[o.z + c], s_stage[o.w + c]);
         };
         // level by level: a memory level's gathers are issued, then a staged
         // level is summed from LDS while they are in flight, then the memory
         // level is summed (i, l and k are compile-time here)
 #pragma unroll
         for (int l = 0; l < LS; ++l) {
-            float4 v[K][4];
+            uint4 v[K][4];
 #pragma unroll
             for (int k = 0; k < K; ++k) {
                 const int4 o = offs[l * K + k];
-                v[k][0] = ValueTraits<VT>::load4(rsrc, (uint32_t)o.x + lane_off);
-                v[k][1] = ValueTraits<VT>::load4(rsrc, (uint32_t)o.y + lane_off);
-                v[k][2] = ValueTraits<VT>::load4(rsrc, (uint32_t)o.z + lane_off);
-                v[k][3] = ValueTraits<VT>::load4(rsrc, (uint32_t)o.w + lane_off);
+                v[k][0] = load_raw16(rsrc, (uint32_t)o.x + lane_off);
+                v[k][1] = load_raw16(rsrc, (uint32_t)o.y + lane_off);
+                v[k][2] = load_raw16(rsrc, (uint32_t)o.z + lane_off);
+                v[k][3] = load_raw16(rsrc, (uint32_t)o.w + lane_off);
             }
             if (LS + l < L) {
 #pragma unroll
@@ -454,7 +505,12 @@ forward_staged_kernel(Geometry g, const VT *__restrict__ value, const float2 *__
 #pragma unroll
             for (int k = 0; k < K; ++k) blend_staged(l * K + k);
         const int q = qb + jq;
-        if (q < q1) out[(((int64_t)b * g.Nq + q) * M + m) * LPH + c] = acc;
+        if (q < q1) {
+            float4 *dst = out + ((((int64_t)b * g.Nq + q) * M + m) * D + c * CPL) / 4;
+#pragma unroll
+            for (int e = 0; e < CPL / 4; ++e)
+                dst[e] = make_float4(acc[4 * e], acc[4 * e + 1], acc[4 * e + 2], acc[4 * e + 3]);
+        }
         wave_lds_sync();  // the next pass rewrites this wave's records
     }
 }
@@ -580,7 +636,7 @@ hipError_t launch_staged_ls(const Geometry &g, const void *value, const float *l
     sp.nqr = (g.Nq + sp.qpr - 1) / sp.qpr;
     const uint32_t grid = round_up8((uint32_t)(g.B * M * sp.nqr));
     KernelScope ks_(FUSED ? "forward_fused_staged_kernel" : "forward_staged_kernel", st);
-    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kStagedThreads), dyn, st, g, static_cast<const VT *>(value),
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(StagedLayout<VT>::kWaves * kWave), dyn, st, g, static_cast<const VT *>(value),
                        reinterpret_cast<const float2 *>(loc), attn, reinterpret_cast<float4 *>(out), sp, grid, fi, mask);
     return hipGetLastError();
 }
@@ -588,15 +644,17 @@ hipError_t launch_staged_ls(const Geometry &g, const void *value, const float *l
 // The first level whose rows (with those of every coarser level) fit in LDS
 // beside the records, or 0 when the staged kernel does not apply.
 template <typename VT, int M, int L, int K>
-int staged_first_level(const Geometry &g, size_t &dyn)
+int staged_first_level(const Geometry &g, const void *value, size_t &dyn)
 {
-    constexpr int LPH = 256 / M / 4;
+    using Lay = StagedLayout<VT>;
+    constexpr int LPH = 256 / M / Lay::kCpl;
     constexpr int QPW = kWave / LPH;
-    constexpr size_t kStatic = (size_t)kStagedWaves * QPW * (L * K + 1) * 32 + L * 16;
+    constexpr size_t kStatic = (size_t)Lay::kWaves * QPW * (L * K + 1) * 32 + L * 16;
     if (g.Nq < kStagedMinQueries) return 0;
+    if (reinterpret_cast<uintptr_t>(value) % 16 != 0) return 0;  // the staged path reads whole 16-byte chunks
     for (int ls = 1; ls < L; ++ls) {
         const int64_t rows = (int64_t)g.S - g.lv.start[ls];
-        const size_t bytes = (size_t)(rows + 1) * (LPH + kStageRowPad) * sizeof(typename StageChunk<VT>::type);
+        const size_t bytes = (size_t)(rows + 1) * (LPH + kStageRowPad) * sizeof(uint4);
         if (kStatic + bytes + 1024 <= kLdsPerWG) {
             dyn = bytes;
             return ls;
@@ -612,7 +670,7 @@ hipError_t launch_c256(const Geometry &g, const void *value, const float *loc, c
     if constexpr (M == 8 && L == 4 && K == 4) {
         size_t dyn = 0;
         const FusedInputs f = fi ? *fi : FusedInputs{};
-        switch (staged_first_level<VT, M, L, K>(g, dyn)) {
+        switch (staged_first_level<VT, M, L, K>(g, value, dyn)) {
 #define MSDA_STAGED(LS_)                                                                                      \
     case LS_:                                                                                                 \
         return fi ? launch_staged_ls<VT, M, L, K, LS_, true>(g, value, loc, attn, out, f, mask, dyn, st)      \
